@@ -1,0 +1,183 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 weight-quantized linear layer.
+ *
+ * NVFP4 block format ("Serving Qwen3.8-27B in 4-bit with a masked speculative
+ * decoding head", section "What the artifact is"): every element is a 4-bit
+ * e2m1 float (sign, 2 exponent bits with bias 1, 1 mantissa bit; values
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}) and each run of 16 consecutive K-elements
+ * shares one FP8 E4M3 scale (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; "What 350+ Experiments Taught Us About Serving Qwen 3.6 35B-A3B",
+ * section 3 "KV cache and memory capacity").  An element's value is
+ * e2m1(code) * e4m3(scale); the product is exact in bf16.
+ *
+ * Layout of an NVFP4 matrix with R rows and K columns ("NF4W(R, K)"):
+ *   codes  uint8 [R][K/2], row-major; element 2j of a row sits in the low
+ *          nibble of byte j, element 2j+1 in the high nibble;
+ *   scales uint8 [R][K/16], row-major E4M3 codes; byte b scales elements
+ *          16b .. 16b+15 of its row.  No swizzle, no per-tensor scale.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers (HBM) owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after the call
+ *     returns, and keeps no state between calls (calls are re-entrant).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Every call only enqueues work on `stream` and returns without
+ *     synchronising.  A failure to launch returns NVFP4_ERROR_LAUNCH; faults
+ *     during execution surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call: null pointers,
+ *     sizes (> 0, K % 32 == 0 unless stated), 16-byte alignment of every
+ *     array base, and workspace size.  Violations return an error status and
+ *     touch no device state.  Properties of device-resident contents (row
+ *     indices sorted, offsets non-decreasing, expert ids in range) are
+ *     preconditions and are not checked.
+ *   - Inputs are never written.  Outputs are fully overwritten and must not
+ *     alias an input.
+ *   - Results are bit-identical from run to run on the same device, shape
+ *     and inputs: reductions use a fixed order and no floating-point atomics.
+ *   - bf16 values are passed as their uint16_t bit patterns.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_SUCCESS = 0,
+    NVFP4_ERROR_INVALID_VALUE = 1, /* null pointer, non-positive size, misalignment */
+    NVFP4_ERROR_NOT_SUPPORTED = 2, /* e.g. K not a multiple of 32, unsupported dtype */
+    NVFP4_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    NVFP4_ERROR_LAUNCH = 4         /* a kernel launch failed (hipGetLastError) */
+} nvfp4_status_t;
+
+typedef enum {
+    NVFP4_BF16 = 0,  /* bfloat16 */
+    NVFP4_FP32 = 1,  /* IEEE binary32 */
+    NVFP4_NVFP4 = 2  /* NVFP4 codes + E4M3 scales */
+} nvfp4_dtype_t;
+
+typedef enum {
+    NVFP4_EPI_NONE = 0,   /* out = h */
+    NVFP4_EPI_SWIGLU = 1  /* out[:, i] = silu(h[:, i]) * h[:, i + N/2], i < N/2 */
+} nvfp4_epilogue_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *nvfp4_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int nvfp4_version(void);
+
+/*
+ * Dequantize an NVFP4 matrix NF4W(N, K) to bf16 out[N][K]:
+ *   out[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k/16])
+ * (format: "Serving Qwen3.8-27B in 4-bit ...", section "What the artifact
+ * is").  The result is exact; the sign of zero follows the code's sign bit
+ * times the scale's sign.  A NaN scale code (0x7F, 0xFF) gives NaN elements.
+ * K % 32 == 0.
+ */
+int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                     uint16_t *out, void *stream);
+
+/*
+ * Quantize bf16 activations x[M][K] to NVFP4 for the W4A4 path ("52.6% more
+ * tokens, 1.53x less GPU time: production inference with Minima and Rafay":
+ * NVFP4 W4A4 execution).  Per row and per block of 16 elements:
+ *   a     = max |x|,
+ *   scale = a/6 rounded to the nearest E4M3 value, ties to even code,
+ *           saturating to 448 (code 0x7E) -- scales are never negative;
+ *   code  = sign of x (negative zero included) | index of the e2m1 magnitude
+ *           nearest to |x|/scale, ties to the even index, saturating at 6;
+ *           a zero scale gives magnitude 0.
+ * Outputs: codes[M][K/2], scales[M][K/16] (the NF4W(M, K) layout).  The
+ * result is unique and bit-exact.  Non-finite inputs are outside the
+ * contract.  K % 32 == 0.
+ */
+int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
+                   void *stream);
+
+/*
+ * Bytes of device workspace nvfp4_gemm needs for this shape (0 if none).
+ * n_out is the number of output columns (N, or the row_idx length).
+ */
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out);
+
+/*
+ * NVFP4 linear layer, y = a . W^T with W = NF4W(N, K) and fp32 accumulation:
+ *   out[m][j] = sum_k a[m][k] * w[n_j][k],   n_j = row_idx ? row_idx[j] : j.
+ *   a_dtype == NVFP4_BF16  : W4A16 -- a is bf16 [M][K], a_scales must be NULL
+ *                            ("What 350+ Experiments ...", section 1).
+ *   a_dtype == NVFP4_NVFP4 : W4A4 -- a is codes [M][K/2], a_scales is
+ *                            [M][K/16] (output of nvfp4_quantize).
+ *   row_idx (optional, int32 [n_out], sorted ascending, unique, < N): compute
+ *            only those weight rows; the output is compact [M][n_out] in
+ *            row_idx order ("Serving Qwen3.8-27B in 4-bit ...", section "The
+ *            masked head trick").  NULL means all rows, n_out must equal N.
+ *   out_dtype: NVFP4_BF16 (round to nearest even) or NVFP4_FP32.
+ * Decode shapes (small M) stream the weights once with a split-K GEMV;
+ * large M uses an MFMA GEMM.  workspace: >= nvfp4_gemm_workspace_size(...)
+ * bytes of device memory (may be NULL when that is 0).
+ */
+int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, int64_t N,
+               int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+               const int32_t *row_idx, int64_t n_out, int out_dtype, void *out,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Routing preparation for a routed mixture-of-experts layer ("What 350+
+ * Experiments ...", section 1: a routed-expert model).  topk_ids int32
+ * [T][topk] holds, for each token, the experts it is routed to (each in
+ * [0, E)).  A stable counting sort by expert produces:
+ *   expert_offsets int32 [E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1,
+ *                               offsets[E] = T*topk;
+ *   gather_idx     int32 [T*topk]: token whose activation row r reads;
+ *   slot_pos       int32 [T*topk]: row that assignment p = t*topk + j landed in.
+ * Rows of one expert keep ascending p.  The result is unique.  topk <= 32,
+ * E <= 1024.
+ */
+int nvfp4_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
+                    int32_t *expert_offsets, int32_t *gather_idx, int32_t *slot_pos,
+                    void *stream);
+
+/* Bytes of device workspace nvfp4_grouped_gemm needs (0 if none). */
+size_t nvfp4_grouped_gemm_workspace_size(int64_t R, int64_t E, int64_t N, int64_t K);
+
+/*
+ * Grouped W4A16 GEMM over experts ("What 350+ Experiments ...", sections 1
+ * and 7: NVFP4 expert weights run by a grouped mixture-of-experts kernel).
+ * Row r < R belongs to the expert e with offsets[e] <= r < offsets[e+1]
+ * (expert_offsets is device int32 [E+1], offsets[0] = 0, offsets[E] = R,
+ * non-decreasing).  It reads activation row src = gather_idx ? gather_idx[r]
+ * : r of a (bf16 [a_rows][K]) and computes, with fp32 accumulation,
+ *   h[n] = sum_k a[src][k] * w_e[n][k],   n < N,
+ * where w_e is NF4W(N, K) of expert e (w_codes [E][N][K/2], w_scales
+ * [E][N][K/16]).  Epilogue: NVFP4_EPI_NONE writes h (width N);
+ * NVFP4_EPI_SWIGLU writes silu(h[i]) * h[i + N/2] (width N/2; the first half
+ * of each expert's rows is the gate projection, the second half the up
+ * projection; N even).  If row_scale (fp32 [R]) is given, the row is then
+ * multiplied by row_scale[r].  The result is rounded to bf16 into out
+ * [R][width].  K % 32 == 0.
+ */
+int nvfp4_grouped_gemm(const uint16_t *a, int64_t a_rows, int64_t K, const int32_t *gather_idx,
+                       const int32_t *expert_offsets, int64_t E, int64_t R, int64_t N,
+                       const uint8_t *w_codes, const uint8_t *w_scales, const float *row_scale,
+                       int epilogue, uint16_t *out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Combine the per-slot expert outputs of a routed layer:
+ *   out[t][c] = bf16( sum_{j < topk} y[slot_pos[t*topk + j]][c] )
+ * summed in fp32 in slot order.  y is bf16 [R][H] with R = T*topk, out is
+ * bf16 [T][H].  H % 8 == 0.
+ */
+int nvfp4_moe_combine(const uint16_t *y, const int32_t *slot_pos, int64_t T, int64_t topk,
+                      int64_t H, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

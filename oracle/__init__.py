@@ -1,0 +1,241 @@
+"""CPU oracle for the NVFP4 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 reference (``nvfp4_oracle.c``) plus its ctypes wrapper.  Only
+the test suite, the smoke check and the CPU-baseline leg of the benchmark may
+import it; the library never does, and the two share no code.
+
+Every function returns plain numpy arrays.  bf16 values travel as ``uint16``
+bit patterns.  GEMM-like functions return the unrounded fp64 sums; use
+:func:`bf16_round` for the single rounding to a bf16 output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (host only, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
+               "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+_p = np.ctypeslib.ndpointer
+_i64 = ctypes.c_int64
+_U8 = _p(dtype=np.uint8, flags="C_CONTIGUOUS")
+_U16 = _p(dtype=np.uint16, flags="C_CONTIGUOUS")
+_I32 = _p(dtype=np.int32, flags="C_CONTIGUOUS")
+_F32 = _p(dtype=np.float32, flags="C_CONTIGUOUS")
+_F64 = _p(dtype=np.float64, flags="C_CONTIGUOUS")
+
+
+def _nullable(base):
+    """ndpointer that also accepts None (passed as NULL)."""
+
+    class _N(base):
+        @classmethod
+        def from_param(cls, obj):
+            if obj is None:
+                return None
+            return base.from_param(obj)
+
+    return _N
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_round.argtypes = [ctypes.c_double]
+        L.oracle_bf16_round.restype = ctypes.c_uint16
+        L.oracle_bf16_round_array.argtypes = [_F64, _i64, _U16]
+        L.oracle_bf16_round_array.restype = None
+        L.oracle_scale_code.argtypes = [ctypes.c_double]
+        L.oracle_scale_code.restype = ctypes.c_uint
+        L.oracle_e2m1_index.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.oracle_e2m1_index.restype = ctypes.c_uint
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_uint16, ctypes.c_uint]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint
+        L.oracle_scale_code_array.argtypes = [_F64, _i64, _U8]
+        L.oracle_scale_code_array.restype = None
+        L.oracle_e2m1_encode_array.argtypes = [_U16, _i64, ctypes.c_uint, _U8]
+        L.oracle_e2m1_encode_array.restype = None
+        L.oracle_dequantize.argtypes = [_U8, _U8, _i64, _i64, _U16]
+        L.oracle_dequantize.restype = None
+        L.oracle_quantize.argtypes = [_U16, _i64, _i64, _U8, _U8]
+        L.oracle_quantize.restype = None
+        L.oracle_gemm_w4a16.argtypes = [_U16, _i64, _i64, _U8, _U8, _nullable(_I32), _i64, _F64]
+        L.oracle_gemm_w4a16.restype = None
+        L.oracle_gemm_w4a4.argtypes = [_U8, _U8, _i64, _i64, _U8, _U8, _nullable(_I32), _i64,
+                                       _F64]
+        L.oracle_gemm_w4a4.restype = None
+        L.oracle_moe_align.argtypes = [_I32, _i64, _i64, _i64, _I32, _I32, _I32]
+        L.oracle_moe_align.restype = ctypes.c_int
+        L.oracle_grouped_gemm.argtypes = [_U16, _i64, _nullable(_I32), _I32, _i64, _i64, _i64,
+                                          _U8, _U8, _nullable(_F32), ctypes.c_int, _F64]
+        L.oracle_grouped_gemm.restype = None
+        L.oracle_moe_combine.argtypes = [_U16, _I32, _i64, _i64, _i64, _F64]
+        L.oracle_moe_combine.restype = None
+        L.oracle_moe_layer.argtypes = [_U16, _i64, _i64, _I32, _F32, _i64, _i64, _i64,
+                                       _U8, _U8, _U8, _U8, _F64]
+        L.oracle_moe_layer.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- scalar format functions ------------------------------------------------
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(code)
+
+
+def bf16_value(bits: int) -> float:
+    return lib().oracle_bf16_value(bits)
+
+
+def scale_code(amax: float) -> int:
+    return lib().oracle_scale_code(amax)
+
+
+def e2m1_encode(x_bits: int, scale_code_: int) -> int:
+    return lib().oracle_e2m1_encode(x_bits, scale_code_)
+
+
+def scale_codes(amax) -> np.ndarray:
+    """Scale code for every block maximum in amax (fp64 array)."""
+    a = np.ascontiguousarray(amax, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib().oracle_scale_code_array(a.reshape(-1), a.size, out.reshape(-1))
+    return out
+
+
+def e2m1_encodes(x_bits, scale_code_: int) -> np.ndarray:
+    """4-bit code of every bf16 value in x_bits under one scale code."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_e2m1_encode_array(x.reshape(-1), x.size, scale_code_, out.reshape(-1))
+    return out
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+# ---- array functions ---------------------------------------------------------
+
+def bf16_round(v) -> np.ndarray:
+    """fp64 array -> bf16 bit patterns (uint16), nearest-even, one rounding."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_bf16_round_array(v.reshape(-1), v.size, out.reshape(-1))
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def dequantize(codes, scales, N: int, K: int) -> np.ndarray:
+    out = np.empty((N, K), dtype=np.uint16)
+    lib().oracle_dequantize(_c(codes, np.uint8), _c(scales, np.uint8), N, K, out)
+    return out
+
+
+def quantize(x_bits, M: int, K: int):
+    codes = np.empty((M, K // 2), dtype=np.uint8)
+    scales = np.empty((M, K // 16), dtype=np.uint8)
+    lib().oracle_quantize(_c(x_bits, np.uint16), M, K, codes, scales)
+    return codes, scales
+
+
+def gemm_w4a16(x_bits, M: int, K: int, w_codes, w_scales, row_idx=None, n_out=None):
+    if n_out is None:
+        n_out = len(row_idx) if row_idx is not None else np.asarray(w_codes).shape[0]
+    out = np.empty((M, n_out), dtype=np.float64)
+    ri = None if row_idx is None else _c(row_idx, np.int32)
+    lib().oracle_gemm_w4a16(_c(x_bits, np.uint16), M, K, _c(w_codes, np.uint8),
+                            _c(w_scales, np.uint8), ri, n_out, out)
+    return out
+
+
+def gemm_w4a4(a_codes, a_scales, M: int, K: int, w_codes, w_scales, row_idx=None, n_out=None):
+    if n_out is None:
+        n_out = len(row_idx) if row_idx is not None else np.asarray(w_codes).shape[0]
+    out = np.empty((M, n_out), dtype=np.float64)
+    ri = None if row_idx is None else _c(row_idx, np.int32)
+    lib().oracle_gemm_w4a4(_c(a_codes, np.uint8), _c(a_scales, np.uint8), M, K,
+                           _c(w_codes, np.uint8), _c(w_scales, np.uint8), ri, n_out, out)
+    return out
+
+
+def moe_align(topk_ids, E: int):
+    ids = _c(topk_ids, np.int32)
+    T, topk = ids.shape
+    offsets = np.empty(E + 1, dtype=np.int32)
+    gather = np.empty(T * topk, dtype=np.int32)
+    slot = np.empty(T * topk, dtype=np.int32)
+    rc = lib().oracle_moe_align(ids, T, topk, E, offsets, gather, slot)
+    if rc != 0:
+        raise ValueError("expert id out of range")
+    return offsets, gather, slot.reshape(T, topk)
+
+
+def grouped_gemm(a_bits, K: int, gather_idx, offsets, E: int, R: int, N: int, w_codes,
+                 w_scales, row_scale=None, epilogue: int = 0):
+    width = N // 2 if epilogue == 1 else N
+    out = np.empty((R, width), dtype=np.float64)
+    gi = None if gather_idx is None else _c(gather_idx, np.int32)
+    rs = None if row_scale is None else _c(row_scale, np.float32)
+    lib().oracle_grouped_gemm(_c(a_bits, np.uint16), K, gi, _c(offsets, np.int32), E, R, N,
+                              _c(w_codes, np.uint8), _c(w_scales, np.uint8), rs, epilogue, out)
+    return out
+
+
+def moe_combine(y_bits, slot_pos, T: int, topk: int, H: int):
+    out = np.empty((T, H), dtype=np.float64)
+    lib().oracle_moe_combine(_c(y_bits, np.uint16), _c(slot_pos, np.int32), T, topk, H, out)
+    return out
+
+
+def moe_layer(x_bits, ids, gates, E: int, I: int, w1_codes, w1_scales, w2_codes, w2_scales):
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    topk = np.asarray(ids).shape[1]
+    out = np.empty((T, H), dtype=np.float64)
+    lib().oracle_moe_layer(x, T, H, _c(ids, np.int32), _c(gates, np.float32), topk, E, I,
+                           _c(w1_codes, np.uint8), _c(w1_scales, np.uint8),
+                           _c(w2_codes, np.uint8), _c(w2_scales, np.uint8), out)
+    return out

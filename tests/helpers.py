@@ -1,0 +1,85 @@
+"""Shared test helpers: golden-file parsers, an independent fp64 decoder built
+from library routines (torch's float8_e4m3fn) and the golden e2m1 table, and
+the GEMM tolerance check."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def e2m1_table():
+    """16 e2m1 values from the golden file (float64, -0.0 kept)."""
+    t = np.zeros(16)
+    for line in golden_lines("e2m1_values.txt"):
+        c, v = line.split()
+        t[int(c)] = float(v)
+    return t
+
+
+def e4m3_table_torch():
+    """All 256 E4M3 codes decoded by torch's float8_e4m3fn (a library routine)."""
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def dequant_independent(codes, scales):
+    """fp64 dequantization by table lookup (golden e2m1, torch E4M3)."""
+    codes = np.asarray(codes)
+    lo = codes & 15
+    hi = codes >> 4
+    el = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    vals = e2m1_table()[el]
+    s = e4m3_table_torch()[np.asarray(scales)]
+    s = np.repeat(s, 16, axis=-1)
+    return vals * s
+
+
+def bf16_bits_to_f64(b):
+    b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits_exact(v):
+    """fp64 values that are exactly representable in bf16 -> bits."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64), equal_nan=True)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def all_bf16_nonneg_finite():
+    """Every non-negative finite bf16 bit pattern (0x0000 .. 0x7F7F)."""
+    return np.arange(0, 0x7F80, dtype=np.uint16)
+
+
+def gemm_close(got, ref_f64, out_is_bf16=True, rel_frob=1e-3, elem=1e-2):
+    """Tolerance of the GEMM outputs: relative Frobenius error <= 1e-3 and every
+    element within 1e-2*(|ref|+1).  For a bf16 output the reference is the fp64
+    sum rounded once to bf16 (the comparison an exact kernel would pass).
+    Returns (ok, rel_frobenius, worst_element_ratio)."""
+    import oracle
+    ref = np.asarray(ref_f64, dtype=np.float64)
+    if out_is_bf16:
+        ref = bf16_bits_to_f64(oracle.bf16_round(ref))
+        g = bf16_bits_to_f64(got)
+    else:
+        g = np.asarray(got, dtype=np.float64)
+    if not np.all(np.isfinite(g)):
+        return False, float("inf"), float("inf")
+    diff = g - ref
+    denom = np.linalg.norm(ref)
+    rf = float(np.linalg.norm(diff) / denom) if denom > 0 else float(np.linalg.norm(diff))
+    worst = float(np.max(np.abs(diff) / (elem * (np.abs(ref) + 1.0)))) if diff.size else 0.0
+    return (rf <= rel_frob and worst <= 1.0), rf, worst
