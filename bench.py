@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 linear layer on one MI355X.
+
+Workload of the headline metric (weight-stream GB/s at M = 1..32): the
+decode-shaped W4A16 set -- M in {1, 8, 32} x (K, N) in {(5120, 17408),
+(17408, 5120), (5120, 248320)} plus the masked head (32,768 of the 248,320
+rows) -- 12 nvfp4_gemm calls.  One step runs all 12 calls once; `value` is the
+weight bytes the step streams (rows * K * 9/16 per call) divided by the step
+time, with every input resident in HBM before the timed region starts.
+
+Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies and
+the head in two copies; calls alternate copies and the masked head always
+reads the copy the full head did not just read, so no call re-reads weights
+that are still cached.
+
+Also reported on the same JSON line:
+  roofline      -- the decode GEMV kernel: algorithmic weight bytes per launch
+                   over its mean launch time (HIP events on the launch stream),
+                   against the 8 TB/s HBM peak;
+  cpu_baseline  -- the CPU oracle timed on this host on a bounded sample of the
+                   same workload (a subset of output rows), scaled to GB/s;
+  secondary     -- the other rows of the layer (prefill GEMM TFLOP/s,
+                   quantizer GB/s, W4A4 GEMM TFLOP/s, MoE layer T=32 / T=4096).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "NVFP4 GEMM: weight-stream GB/s at M=1..32; TFLOP/s at M=8192 (1 GPU)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes(rows: int, K: int) -> int:
+    return rows * K * 9 // 16
+
+
+class Decode:
+    """The 12-call decode set with its weight copies, all resident on the GPU."""
+
+    def __init__(self, nv, torch, helpers_dev):
+        import workloads as wl
+        self.nv, self.torch = nv, torch
+        dev_u8, dev_bf16, dev_i32 = helpers_dev
+        self.calls = []  # (name, M, K, rows, fn)
+        shapes = wl.DECODE_SHAPES
+        self.weights = {}
+        for (K, N) in shapes:
+            w = wl.decode_weights(K, N)
+            copies = [(dev_u8(w.codes), dev_u8(w.scales))]
+            copies.append((copies[0][0].clone(), copies[0][1].clone()))
+            self.weights[(K, N)] = copies
+            del w
+        self.idx = dev_i32(wl.decode_masked_rows())
+        self.x = {(M, K): dev_bf16(wl.decode_activations(M, K))
+                  for M in wl.DECODE_M for K in {s[0] for s in shapes}}
+        self.keep = []
+        head = (wl.HIDDEN, wl.VOCAB)
+        call_no = 0
+        for M in wl.DECODE_M:
+            for (K, N) in shapes:
+                c = call_no % 2
+                self._add(f"M{M}_K{K}_N{N}", M, K, N, self.weights[(K, N)][c], None, N)
+                call_no += 1
+            # masked head: the copy the full head call of this M did not read
+            K, N = head
+            c_full = (call_no - 1) % 2
+            self._add(f"M{M}_masked_head", M, K, N, self.weights[head][1 - c_full], self.idx,
+                      self.idx.numel())
+        torch.cuda.synchronize()
+
+    def _add(self, name, M, K, N, w, idx, n_out):
+        """One nvfp4_gemm call with its arguments marshalled once: the timed loop
+        calls the C entry point directly on torch's current stream."""
+        import ctypes
+        torch, nv = self.torch, self.nv
+        out = torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda")
+        wsb = nv.gemm_workspace_size(M, N, K, n_out)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+        x = self.x[(M, K)]
+        wc, wsc = w
+        self.keep.append((out, ws))
+        vp = ctypes.c_void_p
+        args = (nv.BF16, vp(x.data_ptr()), None, M, N, K, vp(wc.data_ptr()), vp(wsc.data_ptr()),
+                None if idx is None else vp(idx.data_ptr()), n_out, nv.BF16, vp(out.data_ptr()),
+                None if ws is None else vp(ws.data_ptr()), wsb,
+                vp(torch.cuda.current_stream().cuda_stream))
+        f = nv.lib().nvfp4_gemm
+
+        def fn(f=f, args=args):
+            rc = f(*args)
+            if rc != 0:
+                raise RuntimeError(nv.lib().nvfp4_status_string(rc).decode())
+
+        self.calls.append((name, M, K, n_out, fn))
+
+    def step_bytes(self):
+        return sum(weight_bytes(rows, K) for (_, _, K, rows, _) in self.calls)
+
+
+def time_decode(dec, torch, steps, warmup):
+    for _ in range(warmup):
+        for c in dec.calls:
+            c[4]()
+    torch.cuda.synchronize()
+    n = len(dec.calls)
+    starts = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+    ends = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, c in enumerate(dec.calls):
+            starts[s][i].record()
+            c[4]()
+            ends[s][i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = np.array([[starts[s][i].elapsed_time(ends[s][i]) for i in range(n)]
+                            for s in range(steps)])
+    return wall, per_call_ms
+
+
+def cpu_baseline(target_s=15.0):
+    """The oracle on this host, on a bounded sample of the same workload: every
+    call of the decode step restricted to an evenly spaced subset of its output
+    rows (same activations, same weight rows), scaled to weight-stream GB/s.
+    A 1/512-row pass calibrates the subset so the timed pass takes ~target_s."""
+    import oracle
+    import workloads as wl
+    calls = []  # (M, K, x, codes, scales) with all rows the step reads
+    for M in wl.DECODE_M:
+        for (K, N) in wl.DECODE_SHAPES:
+            calls.append((M, K, N, None))
+        calls.append((M, wl.HIDDEN, wl.VOCAB, wl.decode_masked_rows()))
+    weights = {s: wl.decode_weights(*s) for s in wl.DECODE_SHAPES}
+    xs = {(M, K): wl.decode_activations(M, K) for M in wl.DECODE_M for K in (wl.HIDDEN, wl.MLP)}
+
+    def run(frac):
+        t, b = 0.0, 0
+        for (M, K, N, idx) in calls:
+            rows = np.arange(N) if idx is None else idx
+            n = max(1, int(len(rows) * frac))
+            sel = rows[np.linspace(0, len(rows) - 1, n).astype(np.int64)]
+            w = weights[(K, N)]
+            wc, ws = w.codes[sel], w.scales[sel]
+            t0 = time.perf_counter()
+            oracle.gemm_w4a16(xs[(M, K)], M, K, wc, ws)
+            t += time.perf_counter() - t0
+            b += weight_bytes(n, K)
+        return t, b
+
+    t1, _ = run(1 / 512)
+    frac = min(1.0, (1 / 512) * target_s / max(t1, 1e-3))
+    t, b = run(frac)
+    return {
+        "value": round(b / t / 1e9, 5),
+        "unit": "GB/s",
+        "cores": int(oracle.num_threads()),
+        "kind": "oracle",
+        "sample": (f"all 12 decode calls, each on {frac:.4%} of its output rows (evenly spaced): "
+                   f"{b} weight bytes in {t:.2f} s"),
+    }
+
+
+def secondary(nv, torch, helpers_dev, reps=3):
+    """Single-GPU timings of the other rows of the layer (GPU events)."""
+    import workloads as wl
+    dev_u8, dev_bf16, dev_i32 = helpers_dev
+    res = {}
+
+    def timeit(fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n / 1e3
+
+    # prefill GEMM, M = 8192
+    for (K, N) in [(wl.HIDDEN, wl.MLP), (wl.MLP, wl.HIDDEN)]:
+        log(f"secondary: prefill K={K} N={N}")
+        x, w = wl.prefill(K, N)
+        xd, wc, ws = dev_bf16(x), dev_u8(w.codes), dev_u8(w.scales)
+        del x, w
+        out = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda")
+        wsz = nv.gemm_workspace_size(8192, N, K, N)
+        wsb = torch.empty(max(wsz, 1), dtype=torch.uint8, device="cuda")
+        t = timeit(lambda: nv.gemm(xd, wc, ws, out=out, workspace=wsb), n=1)
+        res[f"prefill_M8192_K{K}_N{N}_tflops"] = round(2 * 8192 * N * K / t / 1e12, 2)
+        del xd, wc, ws, out, wsb
+    # quantizer and W4A4 GEMM
+    log("secondary: quantize + W4A4")
+    x, w = wl.w4a4()
+    xd = dev_bf16(x)
+    t = timeit(lambda: nv.quantize(xd), n=20)
+    res["quantize_M512_K5120_GBs"] = round(512 * 5120 * (2 + 9 / 16) / t / 1e9, 2)
+    xq = dev_bf16(wl.normal_bf16(np.random.default_rng(0), 8192, 5120, 0.001))
+    t = timeit(lambda: nv.quantize(xq), n=20)
+    res["quantize_M8192_K5120_GBs"] = round(8192 * 5120 * (2 + 9 / 16) / t / 1e9, 2)
+    codes, scales = nv.quantize(xd)
+    wc, ws = dev_u8(w.codes), dev_u8(w.scales)
+    t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales))
+    res["w4a4_M512_N17408_K5120_tflops"] = round(2 * 512 * 17408 * 5120 / t / 1e12, 2)
+    del xd, xq, wc, ws
+    # MoE layer
+    for T in (32, 4096):
+        log(f"secondary: MoE T={T}")
+        m = wl.moe(T)
+        args = (dev_bf16(m.x), dev_i32(m.ids), torch.from_numpy(m.gates).cuda(),
+                dev_u8(m.w1.codes), dev_u8(m.w1.scales), dev_u8(m.w2.codes), dev_u8(m.w2.scales))
+        t = timeit(lambda: nv.moe_layer(*args))
+        touched = len(np.unique(m.ids))
+        if T == 32:
+            b = touched * (1536 * 2048 + 2048 * 768) * 9 // 16
+            res["moe_T32_weight_GBs"] = round(b / t / 1e9, 2)
+        res[f"moe_T{T}_tflops"] = round(2 * T * 8 * (1536 * 2048 + 2048 * 768) / t / 1e12, 3)
+        res[f"moe_T{T}_ms"] = round(t * 1e3, 3)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: the NVFP4 layer is built for a single GPU "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_gemm_nvfp4_amd as nv
+    nv.lib()  # raises if the HIP library is missing
+    assert torch.cuda.is_available(), "no GPU visible"
+
+    def dev_u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+    def dev_bf16(b):
+        return torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint16).view(np.int16)).cuda().view(
+            torch.bfloat16)
+
+    def dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    hd = (dev_u8, dev_bf16, dev_i32)
+    log("generating decode workload")
+    dec = Decode(nv, torch, hd)
+    log(f"timing {args.steps} steps x {len(dec.calls)} calls (warmup {args.warmup})")
+    wall, per_call = time_decode(dec, torch, args.steps, args.warmup)
+    step_bytes = dec.step_bytes()
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes * args.steps / wall / 1e9
+
+    # roofline of the decode GEMV kernel: algorithmic weight bytes per launch over
+    # the mean launch time, from HIP events on the launch stream
+    launch_bytes = np.array([weight_bytes(rows, K) for (_, _, K, rows, _) in dec.calls])
+    mean_ms = per_call.mean(axis=0)
+    achieved = float(launch_bytes.sum() / (mean_ms.sum() / 1e3) / 1e9)
+    per_call_gbs = {c[0]: round(float(b / (t / 1e3) / 1e9), 1)
+                    for c, b, t in zip(dec.calls, launch_bytes, mean_ms)}
+    per_call_us = {c[0]: round(float(t * 1e3), 2) for c, t in zip(dec.calls, mean_ms)}
+    del dec
+    torch.cuda.empty_cache()
+
+    sec = None
+    if not args.no_secondary:
+        sec = secondary(nv, torch, hd)
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; NVFP4 e2m1 codes + E4M3 scales, bf16 activations)",
+        "config": {
+            "workload": ("decode W4A16 GEMV set: M in {1,8,32} x (K,N) in {(5120,17408),"
+                         "(17408,5120),(5120,248320)} + masked head 32768/248320 rows"),
+            "step_weight_bytes": int(step_bytes),
+            "calls_per_step": len(per_call_us),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "k_gemv (decode GEMV, all 12 launches of a step)",
+        },
+        "per_call_GBs": per_call_gbs,
+        "per_call_us": per_call_us,
+    }
+    if sec is not None:
+        line["secondary"] = sec
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+// api.hip -- the C ABI of the NVFP4 linear layer (declared in include/nvfp4.h).
+//
+// Every entry point validates its arguments on the host before it makes any
+// HIP call, picks a kernel plan as a pure function of the shape, and enqueues
+// on the caller's stream.  The library allocates nothing and keeps no state.
+#include <stdlib.h>
+#include <stdio.h>
+
+#include "../../include/nvfp4.h"
+#include "launch.h"
+#include "moe.h"
+
+using namespace nvfp4;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launched(int rc) { return rc == 0 ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH; }
+
+bool log_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("NVFP4_LOG");
+    on = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+// Rows of M handled by one GEMV launch; larger M loops over chunks of this size.
+constexpr int64_t kGemvMaxM = 32;
+
+struct GemmPlan {
+  GemvPlan gemv;
+  int64_t m_chunk;       // activation rows per GEMV launch
+  size_t a_dequant_bytes;  // W4A4: bf16 copy of the dequantized activations
+  size_t partial_bytes;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4) {
+  (void)N;
+  GemmPlan g;
+  g.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
+  g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs);
+  g.partial_bytes = gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
+  g.a_dequant_bytes = w4a4 ? (size_t)M * (size_t)K * 2 : 0;
+  return g;
+}
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_SUCCESS: return "NVFP4_SUCCESS";
+    case NVFP4_ERROR_INVALID_VALUE: return "NVFP4_ERROR_INVALID_VALUE: null pointer, bad size or misaligned array";
+    case NVFP4_ERROR_NOT_SUPPORTED: return "NVFP4_ERROR_NOT_SUPPORTED: shape or dtype not supported";
+    case NVFP4_ERROR_WORKSPACE: return "NVFP4_ERROR_WORKSPACE: workspace missing or too small";
+    case NVFP4_ERROR_LAUNCH: return "NVFP4_ERROR_LAUNCH: kernel launch failed";
+    default: return "NVFP4 unknown status";
+  }
+}
+
+int nvfp4_version(void) { return 100; }
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                     uint16_t* out, void* stream) {
+  if (!codes || !scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return NVFP4_ERROR_INVALID_VALUE;
+  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_dequantize(codes, scales, N, K, out, as_stream(stream)));
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  if (!x || !codes || !scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERROR_INVALID_VALUE;
+  if (M * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_quantize(x, M, K, codes, scales, as_stream(stream)));
+}
+
+size_t nvfp4_gemm_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K, int64_t n_out) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return 0;
+  GemmPlan g = plan_gemm(M, N, K, n_out, a_dtype == NVFP4_NVFP4);
+  return round_up(g.a_dequant_bytes, 256) + g.partial_bytes;
+}
+
+int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_FP32) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (a_dtype == NVFP4_BF16 && a_scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_dtype == NVFP4_NVFP4 && !a_scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (row_idx ? n_out > N : n_out != N) return NVFP4_ERROR_INVALID_VALUE;
+  if (n_out > INT32_MAX || N > INT32_MAX || M > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(out) ||
+      (a_scales && !aligned16(a_scales)) || (row_idx && !aligned16(row_idx)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  const bool w4a4 = a_dtype == NVFP4_NVFP4;
+  GemmPlan g = plan_gemm(M, N, K, n_out, w4a4);
+  const size_t a_off = 0, p_off = round_up(g.a_dequant_bytes, 256);
+  const size_t need = p_off + g.partial_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+
+  hipStream_t st = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(a);
+  if (w4a4) {
+    uint16_t* xa = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + a_off);
+    if (launch_dequantize(static_cast<const uint8_t*>(a), a_scales, M, K, xa, st) != 0)
+      return NVFP4_ERROR_LAUNCH;
+    x = xa;
+  }
+  void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
+  const size_t osz = out_dtype == NVFP4_FP32 ? 4 : 2;
+  if (log_enabled())
+    fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: gemv mt=%d tr=%d nw=%d z=%d m_chunk=%lld\n",
+            (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16",
+            g.gemv.mt, g.gemv.tr, g.gemv.nw, g.gemv.z, (long long)g.m_chunk);
+  for (int64_t m0 = 0; m0 < M; m0 += g.m_chunk) {
+    const int64_t mc = (M - m0) < g.m_chunk ? (M - m0) : g.m_chunk;
+    int rc = launch_gemv(g.gemv, x + m0 * K, mc, K, w_codes, w_scales, row_idx, n_out,
+                         out_dtype == NVFP4_FP32, static_cast<char*>(out) + m0 * n_out * osz,
+                         partial, st);
+    if (rc != 0) return NVFP4_ERROR_LAUNCH;
+  }
+  return NVFP4_SUCCESS;
+}
+
+size_t nvfp4_moe_align_workspace_size(int64_t T, int64_t topk, int64_t E) {
+  if (T <= 0 || topk <= 0 || E <= 0) return 0;
+  return moe_align_workspace_bytes(T, topk, E);
+}
+
+int nvfp4_moe_align(const int32_t* topk_ids, const float* gates, int64_t T, int64_t topk,
+                    int64_t E, int32_t* expert_offsets, int32_t* gather_idx,
+                    int32_t* slot_pos, float* row_gates, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!topk_ids || !expert_offsets || !gather_idx || !slot_pos) return NVFP4_ERROR_INVALID_VALUE;
+  if ((gates == nullptr) != (row_gates == nullptr)) return NVFP4_ERROR_INVALID_VALUE;
+  if ((gates && !aligned16(gates)) || (row_gates && !aligned16(row_gates)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (T <= 0 || topk <= 0 || E <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (topk > 32 || E > kMoeMaxExperts || T * topk > INT32_MAX / 2) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(topk_ids) || !aligned16(expert_offsets) || !aligned16(gather_idx) ||
+      !aligned16(slot_pos))
+    return NVFP4_ERROR_INVALID_VALUE;
+  const size_t need = moe_align_workspace_bytes(T, topk, E);
+  if (!workspace || workspace_bytes < need) return NVFP4_ERROR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+  return launched(launch_moe_align(topk_ids, gates, T, topk, E, expert_offsets, gather_idx,
+                                   slot_pos, row_gates, workspace, as_stream(stream)));
+}
+
+size_t nvfp4_grouped_gemm_workspace_size(int64_t R, int64_t E, int64_t N, int64_t K) {
+  if (R <= 0 || E <= 0 || N <= 0 || K <= 0) return 0;
+  return moe_grouped_workspace_bytes(R, E, N, K);
+}
+
+int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather_idx,
+                       const int32_t* expert_offsets, int64_t E, int64_t R, int64_t N,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* row_scale,
+                       int epilogue, uint16_t* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!a || !expert_offsets || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_rows <= 0 || K <= 0 || E <= 0 || R <= 0 || N <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_SWIGLU) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (epilogue == NVFP4_EPI_SWIGLU && (N % 32 != 0)) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (N % 16 != 0 || E > kMoeMaxExperts || R > INT32_MAX || a_rows > INT32_MAX)
+    return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!gather_idx && a_rows < R) return NVFP4_ERROR_INVALID_VALUE;
+  if (!aligned16(a) || !aligned16(expert_offsets) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(out) || (gather_idx && !aligned16(gather_idx)) ||
+      (row_scale && !aligned16(row_scale)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  const size_t need = moe_grouped_workspace_bytes(R, E, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
+  return launched(launch_grouped_gemm(a, K, gather_idx, expert_offsets, E, R, N, w_codes,
+                                      w_scales, row_scale, epilogue == NVFP4_EPI_SWIGLU, out,
+                                      workspace, as_stream(stream)));
+}
+
+int nvfp4_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,
+                      int64_t H, uint16_t* out, void* stream) {
+  if (!y || !slot_pos || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (T <= 0 || topk <= 0 || H <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (H % 8 != 0 || topk > 32 || T * topk > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(y) || !aligned16(slot_pos) || !aligned16(out)) return NVFP4_ERROR_INVALID_VALUE;
+  return launched(launch_moe_combine(y, slot_pos, T, topk, H, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// device.h -- gfx950 device helpers shared by the NVFP4 kernels (internal).
+//
+// NVFP4: 4-bit e2m1 elements, one FP8 E4M3 scale per 16 consecutive
+// K-elements ("Serving Qwen3.8-27B in 4-bit with a masked speculative
+// decoding head", section "What the artifact is"; E4M3 = 4 exponent and 3
+// mantissa bits: "What 350+ Experiments Taught Us About Serving Qwen 3.6
+// 35B-A3B", section 3).
+//
+// Decoding on gfx950:
+//  * v_cvt_f32_fp8 decodes an OCP E4M3FN byte to f32 exactly (all 256 codes,
+//    NaN for 0x7F/0xFF).
+//  * v_cvt_scalef32_pk_{f32,bf16}_fp4 decode two e2m1 nibbles of one byte
+//    (low nibble -> element 0) exactly, but apply only the EXPONENT of their
+//    f32 scale operand (the scale behaves like an E8M0 power of two).  An
+//    E4M3 scale has a 3-bit mantissa, so the per-16 scale is applied with an
+//    ordinary f32 multiply (or on the accumulator), never through that operand.
+//  * e2m1 * e4m3 has <= 6 significant bits within [2^-10, 2688]: exact in f32
+//    and in bf16, so dequantized operands are exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// E4M3 byte `sel` (0..3) of `w` -> f32 (exact).
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// Two e2m1 codes in byte SEL of w -> f32 pair (exact, unscaled).
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Two e2m1 codes in byte SEL of w -> bf16 pair (exact, unscaled).
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Eight consecutive elements (one 32-bit word of codes) times one f32 scale
+// -> eight exact bf16 values, element order preserved (word i holds elements
+// 2i, 2i+1 in its low/high half).
+__device__ __forceinline__ u32x4 dequant8_bf16(uint32_t codes, float s) {
+  f32x2 p0 = e2m1x2_to_f32<0>(codes);
+  f32x2 p1 = e2m1x2_to_f32<1>(codes);
+  f32x2 p2 = e2m1x2_to_f32<2>(codes);
+  f32x2 p3 = e2m1x2_to_f32<3>(codes);
+  u32x4 r;
+  r[0] = pack_bf16x2(p0[0] * s, p0[1] * s);
+  r[1] = pack_bf16x2(p1[0] * s, p1[1] * s);
+  r[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
+  r[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __builtin_bit_cast(float, h16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,32 @@
+// launch.h -- host-side launchers of the NVFP4 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Compute units of an MI355X; launch plans are a pure function of the shape
+// and this constant, so workspace queries need no device.
+constexpr int kNumCUs = 256;
+
+int launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                      uint16_t* out, hipStream_t stream);
+int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                    hipStream_t stream);
+
+struct GemvPlan {
+  int mt;  // 16-row activation tiles (M <= 16 * mt)
+  int tr;  // 16-row weight tiles per wave
+  int nw;  // waves per workgroup (split-K inside the workgroup)
+  int z;   // split-K across workgroups (fp32 partials + reduce kernel)
+};
+
+GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus);
+size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
+int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
+                const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
+                void* out, void* workspace, hipStream_t stream);
+
+}  // namespace nvfp4

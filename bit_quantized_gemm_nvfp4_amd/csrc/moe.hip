@@ -1,0 +1,304 @@
+// moe.hip -- routed mixture-of-experts pieces of the NVFP4 linear layer.
+//
+// The pages' MoE model routes every token to a few experts out of many
+// ("What 350+ Experiments Taught Us About Serving Qwen 3.6 35B-A3B", section 1)
+// and runs its NVFP4 experts through a grouped kernel (section 7).  The layer
+// is built from three device steps on one stream, with no host round trip:
+//   align    -- stable counting sort of (token, slot) assignments by expert;
+//   grouped  -- per-expert W4A16 GEMM over the gathered rows, with a SwiGLU
+//               (gate+up) or a per-row scale (gate weight) epilogue;
+//   combine  -- per-token sum of its slots' outputs.
+#include "gemv_core.h"
+#include "moe.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kAlignBlock = 256;  // assignments per align workgroup
+
+// ---- align: block histograms -> per-(block, expert) bases -> ranked scatter ----
+
+__global__ void __launch_bounds__(256) k_align_hist(const int32_t* __restrict__ ids, int64_t R,
+                                                    int E, int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMoeMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * kAlignBlock + threadIdx.x;
+  if (p < R) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);  // integer counts: order-free
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.  offsets = exclusive scan of the expert
+// totals; hist[b][e] is replaced by the first row of expert e owned by block b.
+__global__ void __launch_bounds__(1024) k_align_scan(int32_t* __restrict__ hist, int nblocks,
+                                                     int E, int32_t* __restrict__ offsets) {
+  __shared__ int tot[kMoeMaxExperts];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nblocks; ++b) total += hist[(int64_t)b * E + e];
+  tot[e] = e < E ? total : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 1024 slots
+  for (int d = 1; d < kMoeMaxExperts; d <<= 1) {
+    const int v = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    int run = tot[e] - total;  // exclusive prefix
+    offsets[e] = run;
+    for (int b = 0; b < nblocks; ++b) {
+      const int h = hist[(int64_t)b * E + e];
+      hist[(int64_t)b * E + e] = run;
+      run += h;
+    }
+  }
+  if (e == E - 1) offsets[E] = tot[e];
+}
+
+__global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ gates,
+                                                       int64_t R, int topk, int E,
+                                                       const int32_t* __restrict__ base,
+                                                       int32_t* __restrict__ gather_idx,
+                                                       int32_t* __restrict__ slot_pos,
+                                                       float* __restrict__ row_gates) {
+  __shared__ int sid[kAlignBlock];
+  const int i = threadIdx.x;
+  const int64_t p = (int64_t)blockIdx.x * kAlignBlock + i;
+  sid[i] = p < R ? ids[p] : -1;
+  __syncthreads();
+  if (p >= R) return;
+  const int e = sid[i];
+  if (e < 0 || e >= E) return;
+  int rank = 0;
+  for (int j = 0; j < i; ++j) rank += sid[j] == e;  // earlier assignments, same expert
+  const int dest = base[(int64_t)blockIdx.x * E + e] + rank;
+  gather_idx[dest] = (int32_t)(p / topk);
+  slot_pos[p] = dest;
+  if (gates) row_gates[dest] = gates[p];
+}
+
+// ---- grouped GEMV -------------------------------------------------------------
+
+constexpr int kGroupRows = 32;  // rows of one expert per workgroup (two 16-row MFMA tiles)
+
+struct GroupedArgs {
+  const uint16_t* a;
+  const int32_t* gather;
+  const int32_t* offsets;
+  const uint8_t* wc;
+  const uint8_t* ws;
+  const float* row_scale;
+  uint16_t* out;
+  int64_t K;
+  int64_t N;
+  int E;
+  int steps;
+  int swiglu;
+};
+
+// Find (expert, chunk) of workgroup `bx` in the device-side schedule where
+// expert e owns ceil(rows_e / kGroupRows) consecutive chunks.  Wave-uniform.
+__device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx, int& e_out,
+                                           int& c_out) {
+  const int lane = threadIdx.x & 63;
+  int run = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int ch = e < E ? (offsets[e + 1] - offsets[e] + kGroupRows - 1) / kGroupRows : 0;
+    int inc = ch;  // inclusive prefix over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += v;
+    }
+    const int total = __shfl(inc, 63, 64);
+    if (bx < run + total) {
+      const unsigned long long hit = __ballot(run + inc > bx);
+      const int l = __builtin_ctzll(hit);
+      e_out = base + l;
+      c_out = bx - run - (__shfl(inc, l, 64) - __shfl(ch, l, 64));
+      return true;
+    }
+    run += total;
+  }
+  return false;
+}
+
+template <int TR>
+__global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
+  extern __shared__ float red[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int ln = lane & 15;
+  const int64_t K = g.K;
+
+  int e, c;
+  if (!find_chunk(g.offsets, g.E, blockIdx.x, e, c)) return;  // uniform over the workgroup
+  const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * kGroupRows;
+  const int64_t r1 = min((int64_t)g.offsets[e + 1], r0 + kGroupRows);
+
+  const int s0 = (int)(((int64_t)g.steps * wave) / nw);
+  const int s1 = (int)(((int64_t)g.steps * (wave + 1)) / nw);
+
+  // weight rows: NONE -> tiles blockIdx.y*TR + t; SWIGLU (TR == 2) -> gate tile
+  // blockIdx.y and the matching up tile N/2 + 16*blockIdx.y.
+  const uint8_t* we_c = g.wc + (int64_t)e * g.N * (K / 2);
+  const uint8_t* we_s = g.ws + (int64_t)e * g.N * (K / 16);
+  const uint8_t* cptr[TR];
+  const uint8_t* sptr[TR];
+  bool rvalid[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const int64_t n = g.swiglu ? (int64_t)t * (g.N / 2) + (int64_t)blockIdx.y * 16 + ln
+                               : ((int64_t)blockIdx.y * TR + t) * 16 + ln;
+    rvalid[t] = n < g.N;
+    cptr[t] = we_c + (rvalid[t] ? n : 0) * (K / 2);
+    sptr[t] = we_s + (rvalid[t] ? n : 0) * (K / 16);
+  }
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int64_t r = r0 + mt * 16 + ln;
+    xrow[mt] = r < r1 ? g.a + (int64_t)(g.gather ? g.gather[r] : r) * K : nullptr;
+  }
+
+  f32x4 acc[TR][2];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gemv_accumulate<2, TR>(acc, xrow, cptr, sptr, rvalid, K, s0, s1);
+
+  const int rr = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t width = g.swiglu ? g.N / 2 : g.N;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int64_t r = r0 + mt * 16 + 4 * (l >> 4) + rr;
+    if (g.swiglu) {
+      const float hg = wave_sum_f32x4(red, acc[0][mt]);
+      const float hu = wave_sum_f32x4(red, acc[TR - 1][mt]);
+      const int64_t col = (int64_t)blockIdx.y * 16 + (l & 15);
+      if (threadIdx.x < 256 && r < r1 && col < width) {
+        float v = hg / (1.0f + expf(-hg)) * hu;
+        if (g.row_scale) v *= g.row_scale[r];
+        g.out[r * width + col] = f32_to_bf16_bits(v);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TR; ++t) {
+        const float h = wave_sum_f32x4(red, acc[t][mt]);
+        const int64_t col = ((int64_t)blockIdx.y * TR + t) * 16 + (l & 15);
+        if (threadIdx.x < 256 && r < r1 && col < width) {
+          float v = h;
+          if (g.row_scale) v *= g.row_scale[r];
+          g.out[r * width + col] = f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+// ---- combine --------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_moe_combine(const uint16_t* __restrict__ y,
+                                                     const int32_t* __restrict__ slot_pos,
+                                                     int64_t T, int topk, int64_t H,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (token, 8 columns)
+  const int64_t per_row = H / 8;
+  if (i >= T * per_row) return;
+  const int64_t t = i / per_row, c8 = (i - t * per_row) * 8;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const int64_t row = slot_pos[t * topk + j];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(y + row * H + c8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s[2 * w] += bf16_bits_to_f32(v[w] & 0xFFFFu);
+      s[2 * w + 1] += bf16_bits_to_f32(v[w] >> 16);
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    o[w] = (uint32_t)f32_to_bf16_bits(s[2 * w]) | ((uint32_t)f32_to_bf16_bits(s[2 * w + 1]) << 16);
+  *reinterpret_cast<u32x4*>(out + t * H + c8) = o;
+}
+
+}  // namespace
+
+size_t moe_align_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
+  const int64_t R = T * topk;
+  const int64_t nb = (R + kAlignBlock - 1) / kAlignBlock;
+  return (size_t)nb * (size_t)E * sizeof(int32_t);
+}
+
+int launch_moe_align(const int32_t* ids, const float* gates, int64_t T, int64_t topk, int64_t E,
+                     int32_t* offsets, int32_t* gather_idx, int32_t* slot_pos, float* row_gates,
+                     void* workspace, hipStream_t stream) {
+  const int64_t R = T * topk;
+  const int nb = (int)((R + kAlignBlock - 1) / kAlignBlock);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  hipLaunchKernelGGL(k_align_hist, dim3(nb), dim3(kAlignBlock), 0, stream, ids, R, (int)E, hist);
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kMoeMaxExperts), 0, stream, hist, nb, (int)E,
+                     offsets);
+  hipLaunchKernelGGL(k_align_scatter, dim3(nb), dim3(kAlignBlock), 0, stream, ids, gates, R,
+                     (int)topk, (int)E, hist, gather_idx, slot_pos, row_gates);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+size_t moe_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
+  (void)R;
+  (void)E;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+int launch_grouped_gemm(const uint16_t* a, int64_t K, const int32_t* gather,
+                        const int32_t* offsets, int64_t E, int64_t R, int64_t N,
+                        const uint8_t* wc, const uint8_t* ws, const float* row_scale,
+                        bool swiglu, uint16_t* out, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  GroupedArgs g;
+  g.a = a;
+  g.gather = gather;
+  g.offsets = offsets;
+  g.wc = wc;
+  g.ws = ws;
+  g.row_scale = row_scale;
+  g.out = out;
+  g.K = K;
+  g.N = N;
+  g.E = (int)E;
+  g.steps = (int)((K + kGemvStep - 1) / kGemvStep);
+  g.swiglu = swiglu ? 1 : 0;
+  const int nw = 4;
+  const int64_t chunks = (R + kGroupRows - 1) / kGroupRows + E;  // upper bound
+  const int64_t ytiles = swiglu ? (N / 2 + 15) / 16 : (N + 31) / 32;
+  hipLaunchKernelGGL(k_grouped_gemv<2>, dim3((unsigned)chunks, (unsigned)ytiles), dim3(64 * nw),
+                     nw * 64 * 4 * sizeof(float), stream, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,
+                       int64_t H, uint16_t* out, hipStream_t stream) {
+  const int64_t n = T * (H / 8);
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, y,
+                     slot_pos, T, (int)topk, H, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace nvfp4

@@ -100,10 +100,11 @@ int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint
                    void *stream);
 
 /*
- * Bytes of device workspace nvfp4_gemm needs for this shape (0 if none).
- * n_out is the number of output columns (N, or the row_idx length).
+ * Bytes of device workspace nvfp4_gemm needs for this activation dtype and
+ * shape (0 if none).  n_out is the number of output columns (N, or the
+ * row_idx length).  Pure function of its arguments.
  */
-size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out);
+size_t nvfp4_gemm_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K, int64_t n_out);
 
 /*
  * NVFP4 linear layer, y = a . W^T with W = NF4W(N, K) and fp32 accumulation:
@@ -134,13 +135,22 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
  *   expert_offsets int32 [E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1,
  *                               offsets[E] = T*topk;
  *   gather_idx     int32 [T*topk]: token whose activation row r reads;
- *   slot_pos       int32 [T*topk]: row that assignment p = t*topk + j landed in.
+ *   slot_pos       int32 [T*topk]: row that assignment p = t*topk + j landed in;
+ *   row_gates      optional fp32 [T*topk]: row_gates[slot_pos[p]] = gates[p], the
+ *                  per-token gate weights (gates, fp32 [T][topk]) in row order,
+ *                  ready to scale the rows of the down projection.  Both NULL
+ *                  or both given.
  * Rows of one expert keep ascending p.  The result is unique.  topk <= 32,
- * E <= 1024.
+ * E <= 1024.  Ids outside [0, E) are a precondition violation: such
+ * assignments are skipped (never written out of bounds) and the outputs are
+ * then unspecified.  workspace: >= nvfp4_moe_align_workspace_size(T, topk, E)
+ * bytes of device memory.
  */
-int nvfp4_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
-                    int32_t *expert_offsets, int32_t *gather_idx, int32_t *slot_pos,
-                    void *stream);
+size_t nvfp4_moe_align_workspace_size(int64_t T, int64_t topk, int64_t E);
+int nvfp4_moe_align(const int32_t *topk_ids, const float *gates, int64_t T, int64_t topk,
+                    int64_t E, int32_t *expert_offsets, int32_t *gather_idx,
+                    int32_t *slot_pos, float *row_gates, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace nvfp4_grouped_gemm needs (0 if none). */
 size_t nvfp4_grouped_gemm_workspace_size(int64_t R, int64_t E, int64_t N, int64_t K);

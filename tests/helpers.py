@@ -83,3 +83,37 @@ def gemm_close(got, ref_f64, out_is_bf16=True, rel_frob=1e-3, elem=1e-2):
     rf = float(np.linalg.norm(diff) / denom) if denom > 0 else float(np.linalg.norm(diff))
     worst = float(np.max(np.abs(diff) / (elem * (np.abs(ref) + 1.0)))) if diff.size else 0.0
     return (rf <= rel_frob and worst <= 1.0), rf, worst
+
+
+# ---- GPU helpers (only used by tests marked gpu) ------------------------------------
+
+def announce(msg):
+    """Name the case on stdout before a GPU step (flushed)."""
+    print(f"[case] {msg}", flush=True)
+
+
+def dev_u8(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def dev_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dev_bf16(bits):
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bits(t):
+    """bf16 GPU tensor -> uint16 bit patterns (numpy)."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/nvfp4.h declares, and rejects invalid arguments on the host with the
+documented status codes before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_gemm_nvfp4_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+SUCCESS, INVALID, NOT_SUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
+
+# fake, 256-byte aligned "device" addresses: validation must fail before any use
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+P4 = ctypes.c_void_p(0x40000)
+MIS = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.library_path()):
+        import bit_quantized_gemm_nvfp4_amd.build as b
+        b.build()
+    return nv.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in nv._SIGS, f"binding misses {n}"
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.nvfp4_status_string(s).decode().startswith("NVFP4")
+    assert b"unknown" in L.nvfp4_status_string(99)
+    assert L.nvfp4_version() >= 100
+
+
+def test_dequantize_validation(L):
+    assert L.nvfp4_dequantize(NULL, P2, 4, 64, P3, NULL) == INVALID
+    assert L.nvfp4_dequantize(P, P2, 0, 64, P3, NULL) == INVALID
+    assert L.nvfp4_dequantize(P, P2, 4, 48, P3, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_dequantize(MIS, P2, 4, 64, P3, NULL) == INVALID
+
+
+def test_quantize_validation(L):
+    assert L.nvfp4_quantize(P, 4, 64, NULL, P3, NULL) == INVALID
+    assert L.nvfp4_quantize(P, -1, 64, P2, P3, NULL) == INVALID
+    assert L.nvfp4_quantize(P, 4, 40, P2, P3, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_quantize(P, 4, 64, P2, MIS, NULL) == INVALID
+
+
+def _gemm(L, a_dtype=0, a=P, a_scales=NULL, M=4, N=64, K=256, wc=P2, ws=P3, row_idx=NULL,
+          n_out=64, out_dtype=0, out=P4, workspace=NULL, wbytes=0):
+    return L.nvfp4_gemm(a_dtype, a, a_scales, M, N, K, wc, ws, row_idx, n_out, out_dtype, out,
+                        workspace, wbytes, NULL)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, a=NULL) == INVALID
+    assert _gemm(L, M=0) == INVALID
+    assert _gemm(L, K=48) == NOT_SUPPORTED
+    assert _gemm(L, a_dtype=7) == NOT_SUPPORTED
+    assert _gemm(L, out_dtype=2) == NOT_SUPPORTED
+    assert _gemm(L, a_scales=P) == INVALID             # bf16 activations take no scales
+    assert _gemm(L, a_dtype=2) == INVALID              # NVFP4 activations need scales
+    assert _gemm(L, n_out=32) == INVALID               # no row_idx: n_out must be N
+    assert _gemm(L, row_idx=P, n_out=65) == INVALID    # more rows than N
+    assert _gemm(L, wc=MIS) == INVALID
+    # a shape that needs workspace, given none
+    need = L.nvfp4_gemm_workspace_size(0, 32, 5120, 17408, 5120)
+    assert need > 0
+    assert _gemm(L, M=32, N=5120, K=17408, n_out=5120) == WORKSPACE
+    assert _gemm(L, M=32, N=5120, K=17408, n_out=5120, workspace=P, wbytes=need - 1) == WORKSPACE
+
+
+def test_workspace_queries_are_pure(L):
+    a = L.nvfp4_gemm_workspace_size(0, 8, 17408, 5120, 17408)
+    b = L.nvfp4_gemm_workspace_size(0, 8, 17408, 5120, 17408)
+    assert a == b
+    assert L.nvfp4_gemm_workspace_size(2, 8, 17408, 5120, 17408) >= a + 8 * 5120 * 2
+    assert L.nvfp4_gemm_workspace_size(0, 0, 1, 1, 1) == 0
+    assert L.nvfp4_moe_align_workspace_size(4096, 8, 128) >= 128 * 4
+    assert L.nvfp4_grouped_gemm_workspace_size(-1, 1, 1, 1) == 0
+
+
+def test_moe_validation(L):
+    ws = L.nvfp4_moe_align_workspace_size(32, 8, 128)
+    assert L.nvfp4_moe_align(NULL, NULL, 32, 8, 128, P, P2, P3, NULL, P4, ws, NULL) == INVALID
+    assert L.nvfp4_moe_align(P, NULL, 32, 64, 128, P, P2, P3, NULL, P4, ws, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_moe_align(P, NULL, 32, 8, 2048, P, P2, P3, NULL, P4, ws, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_moe_align(P, P2, 32, 8, 128, P, P2, P3, NULL, P4, ws, NULL) == INVALID
+    assert L.nvfp4_moe_align(P, NULL, 32, 8, 128, P, P2, P3, NULL, NULL, 0, NULL) == WORKSPACE
+    g = L.nvfp4_grouped_gemm
+    assert g(NULL, 32, 256, P, P2, 4, 32, 64, P3, P4, NULL, 0, P, NULL, 0, NULL) == INVALID
+    assert g(P, 32, 240, P, P2, 4, 32, 64, P3, P4, NULL, 0, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 32, 256, P, P2, 4, 32, 48, P3, P4, NULL, 1, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 32, 256, P, P2, 4, 32, 64, P3, P4, NULL, 5, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 8, 256, NULL, P2, 4, 32, 64, P3, P4, NULL, 0, P, NULL, 0, NULL) == INVALID
+    c = L.nvfp4_moe_combine
+    assert c(P, NULL, 4, 8, 64, P2, NULL) == INVALID
+    assert c(P, P2, 4, 8, 60, P3, NULL) == NOT_SUPPORTED
+    assert c(P, P2, 0, 8, 64, P3, NULL) == INVALID
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="GPU"):
+        nv.quantize(x)

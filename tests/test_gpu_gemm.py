@@ -1,0 +1,179 @@
+"""GPU parity of nvfp4_gemm (W4A16 and W4A4, full and masked rows) against the
+fp64 oracle.  Tolerance: relative Frobenius error <= 1e-3 and every element
+within 1e-2*(|ref|+1), against the oracle rounded once to bf16 for bf16 outputs
+and unrounded for fp32 outputs."""
+import numpy as np
+import pytest
+
+import helpers
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    assert torch.cuda.is_available()
+    import bit_quantized_gemm_nvfp4_amd as m
+    m.lib()
+    return m
+
+
+def _run(nv, x, w, row_idx=None, out_f32=False):
+    import torch
+    xd = helpers.dev_bf16(x)
+    ri = None if row_idx is None else helpers.dev_i32(row_idx)
+    y = nv.gemm(xd, helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), row_idx=ri,
+                out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    return y.cpu().numpy() if out_f32 else helpers.host_bits(y)
+
+
+def _assert_close(got, ref, out_f32=False, what=""):
+    ok, rf, worst = helpers.gemm_close(got, ref, out_is_bf16=not out_f32)
+    assert ok, f"{what}: rel_frob={rf:.3e} worst_elem_ratio={worst:.3f}"
+    return rf
+
+
+def test_tiny_config(nv, orc):
+    """M=1, K=512, N=1024 -- the tiny seeded workload, bf16 and fp32 outputs."""
+    helpers.announce("gemm tiny M=1 K=512 N=1024")
+    x, w = workloads.tiny()
+    ref = orc.gemm_w4a16(x, 1, 512, w.codes, w.scales)
+    _assert_close(_run(nv, x, w), ref, what="tiny bf16")
+    rf = _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what="tiny fp32")
+    assert rf < 1e-5
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 32, 16), (1, 64, 5), (3, 288, 33), (8, 1024, 560), (16, 2080, 100), (17, 512, 48),
+    (32, 1536, 272), (33, 768, 64), (70, 256, 40), (5, 8192, 24),
+])
+def test_ragged_shapes(nv, orc, M, K, N):
+    """Shapes spanning several tiles with ragged tails in M (16-row MFMA tiles),
+    N (16-row weight tiles), and K (256-element steps, K % 32 == 0)."""
+    helpers.announce(f"gemm ragged M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 1000 + N)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    _assert_close(_run(nv, x, w), ref, what=f"{M}x{K}x{N}")
+    _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
+
+
+def test_identity_activations_reproduce_weights(nv, orc):
+    """x = one-hot rows: y[m][n] = w[n][k_m] exactly (a single exact product), so
+    the GEMV's in-register dequantization is checked bit-exactly against the
+    oracle's dequantization (zero signs aside)."""
+    helpers.announce("gemm identity activations")
+    K, N = 1024, 96
+    w = workloads.nvfp4_weight(np.random.default_rng(9), N, K)
+    ks = np.array([0, 1, 15, 16, 31, 32, 127, 128, 255, 256, 511, 512, 777, 1000, 1022, 1023,
+                   3, 64, 200, 300, 400, 500, 600, 700, 800, 900, 33, 34, 35, 36, 37, 38])
+    M = len(ks)
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80  # 1.0
+    got = _run(nv, x, w)
+    deq = orc.dequantize(w.codes, w.scales, N, K)
+    want = deq[:, ks].T
+    assert np.array_equal(got & 0x7FFF, want & 0x7FFF)
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz])
+
+
+def test_masked_rows(nv, orc):
+    helpers.announce("gemm masked rows")
+    rng = np.random.default_rng(10)
+    M, K, N = 8, 512, 4000
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    idx = np.sort(rng.choice(N, 333, replace=False)).astype(np.int32)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx)
+    _assert_close(_run(nv, x, w, row_idx=idx), ref, what="masked")
+    # degenerate: a single kept row, and every row kept through row_idx
+    one = np.array([N - 1], np.int32)
+    _assert_close(_run(nv, x, w, row_idx=one),
+                  orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=one), what="one row")
+    allr = np.arange(N, dtype=np.int32)
+    _assert_close(_run(nv, x, w, row_idx=allr), orc.gemm_w4a16(x, M, K, w.codes, w.scales),
+                  what="all rows via idx")
+
+
+def test_zero_and_extreme_weights(nv, orc):
+    """All-zero codes give exact zeros; maximal scales (448) with +-6 codes and
+    outlier activations stay within tolerance (|w| = 2688)."""
+    helpers.announce("gemm zero / extreme weights")
+    import torch
+    M, K, N = 4, 512, 64
+    x = workloads.normal_bf16(np.random.default_rng(11), M, K, outlier_frac=0.02)
+    w = workloads.NF4W(np.zeros((N, K // 2), np.uint8), np.full((N, K // 16), 0x7E, np.uint8))
+    assert np.all((_run(nv, x, w) & 0x7FFF) == 0)
+    w = workloads.NF4W(np.full((N, K // 2), 0xF7, np.uint8), np.full((N, K // 16), 0x7E, np.uint8))
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    _assert_close(_run(nv, x, w), ref, what="extreme")
+
+
+@pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
+def test_decode_full_size_sampled(nv, orc, K, N):
+    """The decode shapes at full size for M in {1, 8, 32}, in the launch
+    configuration the benchmark times; 512 output columns sampled per M are
+    recomputed by the oracle (whole rows of W, all M rows of x)."""
+    import torch
+    w = workloads.decode_weights(K, N)
+    wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    cols = np.sort(np.random.default_rng(K + N).choice(N, 512, replace=False)).astype(np.int32)
+    for M in workloads.DECODE_M:
+        helpers.announce(f"gemm decode full size K={K} N={N} M={M}")
+        x = workloads.decode_activations(M, K)
+        y = helpers.host_bits(nv.gemm(helpers.dev_bf16(x), wc, ws))
+        ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=cols)
+        _assert_close(y[:, cols], ref, what=f"K={K} N={N} M={M}")
+        torch.cuda.synchronize()
+
+
+def test_masked_head_full_size_sampled(nv, orc):
+    """Masked head: 32,768 of 248,320 rows, K = 5120, M in {1, 8, 32}; sampled
+    output columns against the oracle, and the masked result must equal the same
+    columns of the full-head result bit for bit (same kernel, same sums)."""
+    import torch
+    K, N = workloads.HIDDEN, workloads.VOCAB
+    w = workloads.decode_weights(K, N)
+    idx = workloads.decode_masked_rows()
+    wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    sel = np.sort(np.random.default_rng(3).choice(len(idx), 256, replace=False))
+    for M in workloads.DECODE_M:
+        helpers.announce(f"gemm masked head M={M}")
+        x = workloads.decode_activations(M, K)
+        xd = helpers.dev_bf16(x)
+        y = helpers.host_bits(nv.gemm(xd, wc, ws, row_idx=helpers.dev_i32(idx)))
+        ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx[sel])
+        _assert_close(y[:, sel], ref, what=f"masked M={M}")
+        torch.cuda.synchronize()
+
+
+def test_w4a4_gemm(nv, orc):
+    """W4A4: quantize the 512 x 5120 activations on the GPU, then GEMM against
+    NF4W(17408, 5120); sampled columns against the oracle's W4A4 on the oracle's
+    (bit-identical) codes."""
+    helpers.announce("gemm W4A4 512x5120 -> 17408")
+    x, w = workloads.w4a4()
+    gc, gs = nv.quantize(helpers.dev_bf16(x))
+    rc, rs = orc.quantize(x, 512, 5120)
+    assert np.array_equal(gc.cpu().numpy(), rc) and np.array_equal(gs.cpu().numpy(), rs)
+    y = helpers.host_bits(nv.gemm(gc, helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                                  a_scales=gs))
+    cols = np.sort(np.random.default_rng(4).choice(17408, 256, replace=False)).astype(np.int32)
+    ref = orc.gemm_w4a4(rc, rs, 512, 5120, w.codes, w.scales, row_idx=cols)
+    _assert_close(y[:, cols], ref, what="w4a4")
+
+
+def test_run_to_run_bit_identical(nv):
+    """Fixed reduction order: two runs of a split-K shape give the same bits."""
+    helpers.announce("gemm determinism")
+    rng = np.random.default_rng(12)
+    M, K, N = 32, 17408, 1024
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    a = _run(nv, x, w)
+    b = _run(nv, x, w)
+    assert np.array_equal(a, b)

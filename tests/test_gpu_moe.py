@@ -1,0 +1,170 @@
+"""GPU parity of the routed mixture-of-experts path: align (bit-exact),
+grouped GEMM (per expert, both epilogues), combine, and the whole layer
+against the oracle's token-by-token definition."""
+import numpy as np
+import pytest
+
+import helpers
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    assert torch.cuda.is_available()
+    import bit_quantized_gemm_nvfp4_amd as m
+    m.lib()
+    return m
+
+
+@pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 2, 7), (32, 8, 128), (4096, 8, 128),
+                                      (300, 4, 1024)])
+def test_align_bit_exact(nv, orc, T, topk, E):
+    helpers.announce(f"moe align T={T} topk={topk} E={E}")
+    if E == 128 and topk == 8:
+        wl = workloads.moe(T)
+        ids, gates = wl.ids, wl.gates
+    else:
+        rng = np.random.default_rng(T + E)
+        ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+        gates = rng.random((T, topk)).astype(np.float32)
+    off, gather, slot, rg = nv.moe_align(helpers.dev_i32(ids), E, helpers.dev_f32(gates))
+    ro, rgat, rslot = orc.moe_align(ids, E)
+    assert np.array_equal(off.cpu().numpy(), ro)
+    assert np.array_equal(gather.cpu().numpy(), rgat)
+    assert np.array_equal(slot.cpu().numpy(), rslot)
+    want_rg = np.empty(T * topk, np.float32)
+    want_rg[rslot.reshape(-1)] = gates.reshape(-1)
+    assert np.array_equal(rg.cpu().numpy(), want_rg)
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_grouped_gemm_matches_oracle(nv, orc, epi):
+    """Uneven groups (empty experts, one row, > 32 rows -> several chunks), with
+    gather and row scale."""
+    helpers.announce(f"moe grouped gemm epi={epi}")
+    rng = np.random.default_rng(30 + epi)
+    E, K, N, rows = 6, 512, 96, 50
+    counts = np.array([0, 1, 40, 0, 70, 9])
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, rows, K)
+    w = workloads.nvfp4_weight(rng, E, N, K)
+    gather = rng.integers(0, rows, R).astype(np.int32)
+    rs = (rng.random(R) + 0.5).astype(np.float32)
+    y = nv.grouped_gemm(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+                        helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), R,
+                        row_scale=helpers.dev_f32(rs), epilogue=epi)
+    ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
+                           epilogue=epi)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+    assert ok, (rf, worst)
+
+
+def test_combine_matches_oracle(nv, orc):
+    helpers.announce("moe combine")
+    rng = np.random.default_rng(40)
+    T, topk, H = 33, 8, 2048
+    y = workloads.normal_bf16(rng, T * topk, H)
+    slot = rng.permutation(T * topk).astype(np.int32).reshape(T, topk)
+    got = helpers.host_bits(nv.moe_combine(helpers.dev_bf16(y), helpers.dev_i32(slot)))
+    ref = orc.moe_combine(y, slot, T, topk, H)
+    ok, rf, worst = helpers.gemm_close(got, ref)
+    assert ok, (rf, worst)
+
+
+def _layer(nv, wl):
+    import torch
+    out = nv.moe_layer(helpers.dev_bf16(wl.x), helpers.dev_i32(wl.ids), helpers.dev_f32(wl.gates),
+                       helpers.dev_u8(wl.w1.codes), helpers.dev_u8(wl.w1.scales),
+                       helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales))
+    torch.cuda.synchronize()
+    return helpers.host_bits(out)
+
+
+def _slot_magnitude(orc, wl, toks):
+    """sum_j |y_j| per output element, from the oracle's own grouped steps: the
+    scale of the terms the combine adds (each stored in bf16)."""
+    ids, gates = wl.ids[toks], wl.gates[toks]
+    T, topk = ids.shape
+    E = wl.w1.codes.shape[0]
+    I = wl.w2.codes.shape[2] * 2
+    H = wl.x.shape[1]
+    off, gather, slot = orc.moe_align(ids, E)
+    R = T * topk
+    act = orc.bf16_round(orc.grouped_gemm(wl.x[toks], H, gather, off, E, R, 2 * I, wl.w1.codes,
+                                          wl.w1.scales, epilogue=1))
+    rg = np.empty(R, np.float32)
+    rg[slot.reshape(-1)] = gates.reshape(-1)
+    y = helpers.bf16_bits_to_f64(orc.bf16_round(orc.grouped_gemm(
+        act, I, None, off, E, R, H, wl.w2.codes, wl.w2.scales, row_scale=rg)))
+    return np.abs(y)[slot].sum(axis=1)
+
+
+def _layer_close(got_bits, ref, mag):
+    """Layer tolerance: relative Frobenius <= 1e-3 (as for a GEMM output) and
+    every element within 1e-2*(sum_j |y_j| + 1): the output is a sum of topk
+    terms that are each stored in bf16, so its element error scales with the
+    terms, not with their (possibly cancelling) sum."""
+    g = helpers.bf16_bits_to_f64(got_bits)
+    import oracle
+    r = helpers.bf16_bits_to_f64(oracle.bf16_round(ref))
+    rf = np.linalg.norm(g - r) / np.linalg.norm(r)
+    worst = np.max(np.abs(g - r) / (1e-2 * (mag + 1.0)))
+    return rf <= 1e-3 and worst <= 1.0, rf, worst
+
+
+def test_moe_layer_decode_full(nv, orc):
+    """T = 32 decode batch, 128 experts, top-8, H = 2048, I = 768: every token."""
+    helpers.announce("moe layer T=32 full")
+    wl = workloads.moe(32)
+    got = _layer(nv, wl)
+    ref = orc.moe_layer(wl.x, wl.ids, wl.gates, 128, 768, wl.w1.codes, wl.w1.scales,
+                        wl.w2.codes, wl.w2.scales)
+    ok, rf, worst = _layer_close(got, ref, _slot_magnitude(orc, wl, np.arange(32)))
+    assert ok, (rf, worst)
+
+
+def test_moe_layer_steps_chained(nv, orc):
+    """Every GPU step of the T = 32 layer against the oracle fed the GPU's own
+    inputs to that step: each stored intermediate is a plain GEMM output and
+    meets the GEMM tolerance elementwise."""
+    import torch
+    helpers.announce("moe layer T=32 chained steps")
+    wl = workloads.moe(32)
+    E, H, I = 128, 2048, 768
+    T, topk = wl.ids.shape
+    R = T * topk
+    w1c, w1s = helpers.dev_u8(wl.w1.codes), helpers.dev_u8(wl.w1.scales)
+    w2c, w2s = helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales)
+    off, gather, slot, rg = nv.moe_align(helpers.dev_i32(wl.ids), E, helpers.dev_f32(wl.gates))
+    act = nv.grouped_gemm(helpers.dev_bf16(wl.x), gather, off, w1c, w1s, R, epilogue=1)
+    y = nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg)
+    out = nv.moe_combine(y, slot)
+    torch.cuda.synchronize()
+    off_h, gather_h, slot_h = off.cpu().numpy(), gather.cpu().numpy(), slot.cpu().numpy()
+    rg_h, act_h, y_h = rg.cpu().numpy(), helpers.host_bits(act), helpers.host_bits(y)
+    ref_act = orc.grouped_gemm(wl.x, H, gather_h, off_h, E, R, 2 * I, wl.w1.codes, wl.w1.scales,
+                               epilogue=1)
+    assert helpers.gemm_close(act_h, ref_act)[0]
+    ref_y = orc.grouped_gemm(act_h, I, None, off_h, E, R, H, wl.w2.codes, wl.w2.scales,
+                             row_scale=rg_h)
+    ok, rf, worst = helpers.gemm_close(y_h, ref_y)
+    assert ok, (rf, worst)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(out), orc.moe_combine(y_h, slot_h, T, topk, H))
+    assert ok, (rf, worst)
+
+
+def test_moe_layer_prefill_sampled(nv, orc):
+    """T = 4096 prefill batch: the full layer on the GPU, 48 sampled tokens
+    recomputed by the oracle."""
+    helpers.announce("moe layer T=4096 sampled")
+    wl = workloads.moe(4096)
+    got = _layer(nv, wl)
+    toks = np.sort(np.random.default_rng(41).choice(4096, 48, replace=False))
+    ref = orc.moe_layer(wl.x[toks], wl.ids[toks], wl.gates[toks], 128, 768, wl.w1.codes,
+                        wl.w1.scales, wl.w2.codes, wl.w2.scales)
+    ok, rf, worst = _layer_close(got[toks], ref, _slot_magnitude(orc, wl, toks))
+    assert ok, (rf, worst)
