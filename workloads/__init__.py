@@ -65,15 +65,16 @@ class NF4W:
         return self.codes.shape[-1] * 2
 
 
-def nvfp4_weight(rng: np.random.Generator, *shape_rows_k) -> NF4W:
+def nvfp4_weight(rng: np.random.Generator, *shape_rows_k, exp_field=(3, 9)) -> NF4W:
     """Random NVFP4 weights.  Draw order: codes, scale exponents, scale
     mantissas.  Codes: every byte uniform over 0..255 (both nibbles uniform
     over all 16 e2m1 codes, negative zero included).  Scales: E4M3 with the
-    biased exponent field uniform over 3..9 (values 2^-4 .. 2^2 before the
-    mantissa) and the 3-bit mantissa uniform; sign 0."""
+    biased exponent field uniform over exp_field (inclusive; the default 3..9
+    gives 2^-4 .. 2^2 before the mantissa) and the 3-bit mantissa uniform;
+    sign 0."""
     *lead, R, K = shape_rows_k
     codes = rng.integers(0, 256, size=(*lead, R, K // 2), dtype=np.uint8)
-    e = rng.integers(3, 10, size=(*lead, R, K // 16), dtype=np.uint8)
+    e = rng.integers(exp_field[0], exp_field[1] + 1, size=(*lead, R, K // 16), dtype=np.uint8)
     m = rng.integers(0, 8, size=(*lead, R, K // 16), dtype=np.uint8)
     return NF4W(codes, (e << 3) | m)
 
@@ -170,13 +171,20 @@ def zipf_routing(rng: np.random.Generator, T: int, E: int, topk: int, s: float =
     return ids, gates
 
 
+# Expert weights look like a trained checkpoint quantized with the amax/6 rule
+# and no per-tensor scale: element rms near 1/sqrt(fan-in) puts the E4M3 block
+# scales around 2^-9 .. 2^-5 -- exponent fields 0 (subnormal, including the zero
+# scale) to 2 -- which keeps the routed layer's activations of order one to ten.
+MOE_SCALE_EXP_FIELD = (0, 2)
+
+
 def moe(T: int, E: int = MOE_EXPERTS, topk: int = MOE_TOPK, H: int = MOE_HIDDEN,
         I: int = MOE_INTER, seed: int = 0) -> MoEWorkload:
     """Routed MoE layer.  Draws: x [T, H] N(0,1), routing, W1 NF4W(E x 2I, H),
-    W2 NF4W(E x H, I)."""
+    W2 NF4W(E x H, I), both with scale exponent fields MOE_SCALE_EXP_FIELD."""
     rng = np.random.default_rng(seed)
     x = normal_bf16(rng, T, H)
     ids, gates = zipf_routing(rng, T, E, topk)
-    w1 = nvfp4_weight(rng, E, 2 * I, H)
-    w2 = nvfp4_weight(rng, E, H, I)
+    w1 = nvfp4_weight(rng, E, 2 * I, H, exp_field=MOE_SCALE_EXP_FIELD)
+    w2 = nvfp4_weight(rng, E, H, I, exp_field=MOE_SCALE_EXP_FIELD)
     return MoEWorkload(x, ids, gates, w1, w2)
