@@ -128,9 +128,10 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
   void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
   const size_t osz = out_dtype == NVFP4_FP32 ? 4 : 2;
   if (log_enabled())
-    fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: gemv mt=%d tr=%d nw=%d z=%d m_chunk=%lld\n",
+    fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: gemv%s mt=%d tr=%d nw=%d z=%d m_chunk=%lld\n",
             (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16",
-            g.gemv.mt, g.gemv.tr, g.gemv.nw, g.gemv.z, (long long)g.m_chunk);
+            g.gemv.small ? "4x4x4" : "16x16x32", g.gemv.mt, g.gemv.tr, g.gemv.nw, g.gemv.z,
+            (long long)g.m_chunk);
   for (int64_t m0 = 0; m0 < M; m0 += g.m_chunk) {
     const int64_t mc = (M - m0) < g.m_chunk ? (M - m0) : g.m_chunk;
     int rc = launch_gemv(g.gemv, x + m0 * K, mc, K, w_codes, w_scales, row_idx, n_out,

@@ -6,25 +6,19 @@
 // About Serving Qwen 3.6 35B-A3B", section 1).  With row_idx only the listed
 // weight rows are read ("The masked head trick" on the first page).
 //
-// The weights are read exactly once, so the kernel is bound by HBM.  Design:
-//  * A wave owns TR tiles of 16 weight rows and a contiguous range of
-//    256-element K steps.  The NW waves of a workgroup take different K ranges
-//    of the same rows (split-K inside the workgroup); gridDim.y splits K
-//    further across workgroups when the row count alone cannot fill the chip.
-//  * Per step a lane (n = lane % 16, q = lane / 16) loads two 16-byte words of
-//    codes of row n: bytes [16q, 16q+16) and [64+16q, 80+16q) of the step, i.e.
-//    elements [32q, 32q+32) and [128+32q, 160+32q).  A wave's load covers 16
-//    rows x 64 contiguous bytes -- coalesced 128-bit loads.
-//  * Each 32-bit code word (8 elements, one scale) is decoded exactly to bf16
-//    in registers and becomes the B operand of one v_mfma_f32_16x16x32_bf16
-//    (B[k][n]: lane holds k = 8*(lane/16) .. +7 of column lane%16).  The
-//    A operand holds the matching 8 activations of row m = lane % 16, so the
-//    32 "k slots" of an MFMA map to scattered physical k -- any bijection works
-//    for a dot product as long as A and B agree.
-//  * M > 16 uses a second 16-row MFMA tile on the same B operand.
-//  * Partial sums are reduced across the NW waves through LDS in wave order,
-//    and across workgroups (if gridDim.y > 1) by k_splitk_reduce in split
-//    order: results are bit-identical from run to run.
+// The weights are read exactly once, so the kernel is bound by HBM.  Grid:
+// blockIdx.x picks nw*TR tiles of 16 weight rows (TR per wave), blockIdx.y a
+// contiguous part of K (split-K across workgroups when the rows alone cannot
+// fill the chip, or when the activations of all of K do not fit LDS).  Each
+// workgroup stages the activations of its K part in LDS; each wave streams its
+// own rows over that part (gemv_core.h).  With one K part the wave stores its
+// bf16/fp32 results directly; otherwise it stores fp32 partials and
+// k_splitk_reduce adds them in part order, so results are bit-identical from
+// run to run.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "gemv4_core.h"
 #include "gemv_core.h"
 #include "launch.h"
 
@@ -42,42 +36,36 @@ struct GemvArgs {
   int64_t K;
   int64_t n_out;
   int M;
-  int steps;               // ceil(K / kGemvStep)
+  int steps;               // ceil(K / step) for the kernel's step size
   int out_f32;
 };
 
-template <int MT, int TR>
-__global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
-  extern __shared__ float red[];  // [nw][64][4]
+template <int MT, int TR, int NW>
+__global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
+  constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
+  __shared__ uint16_t win[2 * 16 * MT * kXWin];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int ln = lane & 15;
+  const int ln = lane & 15, q = lane >> 4;
   const int64_t K = a.K;
 
-  // K range of this wave: part g of G = gridDim.y * nw equal parts.
-  const int G = gridDim.y * nw;
-  const int g = blockIdx.y * nw + wave;
-  const int s0 = (int)(((int64_t)a.steps * g) / G);
-  const int s1 = (int)(((int64_t)a.steps * (g + 1)) / G);
+  const int zs0 = (int)(((int64_t)a.steps * blockIdx.y) / gridDim.y);
+  const int zs1 = (int)(((int64_t)a.steps * (blockIdx.y + 1)) / gridDim.y);
 
+  const int64_t tile0 = ((int64_t)blockIdx.x * NW + wave) * TR;
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
-  bool rvalid[TR];
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
-    const int64_t j = ((int64_t)blockIdx.x * TR + t) * 16 + ln;
-    rvalid[t] = j < a.n_out;
-    const int64_t row = rvalid[t] ? (a.row_idx ? (int64_t)a.row_idx[j] : j) : 0;
+    int64_t j = (tile0 + t) * 16 + ln;
+    if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
+    const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
     cptr[t] = a.wc + row * (K / 2);
     sptr[t] = a.ws + row * (K / 16);
   }
-  const uint16_t* xrow[MT];
+  int xrow_off[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + ln;
-    xrow[mt] = m < a.M ? a.x + (int64_t)m * K : nullptr;
-  }
+  for (int mt = 0; mt < MT; ++mt) xrow_off[mt] = (16 * mt + ln) * kXWin + 64 * q;
 
   f32x4 acc[TR][MT];
 #pragma unroll
@@ -85,27 +73,101 @@ __global__ void __launch_bounds__(256) k_gemv(GemvArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemv_accumulate<MT, TR>(acc, xrow, cptr, sptr, rvalid, K, s0, s1);
+  const uint16_t* x = a.x;
+  gemv_accumulate_win<MT, TR, XP>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
+                                  (int)(K / kGemvStep),
+                                  [x, K](int m) { return x + (int64_t)m * K; });
 
-  // Reduce over the waves (fixed order), then store.
-  const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
+  // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
+    const int64_t j = (tile0 + t) * 16 + ln;
+    if (j >= a.n_out) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float v = wave_sum_f32x4(red, acc[t][mt]);
-      if (threadIdx.x < 256) {
-        const int m = mt * 16 + 4 * (l >> 4) + r;
-        const int64_t j = ((int64_t)blockIdx.x * TR + t) * 16 + (l & 15);
-        if (m < a.M && j < a.n_out) {
-          const int64_t o = (int64_t)m * a.n_out + j;
-          if (gridDim.y > 1)
-            a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
-          else if (a.out_f32)
-            static_cast<float*>(a.out)[o] = v;
-          else
-            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(v);
-        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + 4 * q + r;
+        if (m >= a.M) continue;
+        const int64_t o = (int64_t)m * a.n_out + j;
+        const float v = acc[t][mt][r];
+        if (gridDim.y > 1)
+          a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
+        else if (a.out_f32)
+          static_cast<float*>(a.out)[o] = v;
+        else
+          static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
+// Very small M (<= 8): 4x4x4-block MFMA with per-block scaling of the MFMA
+// result (gemv4_core.h).  blockIdx.x picks nw*TR tiles of 4 weight rows, a wave
+// TR of them; blockIdx.y a contiguous part of K.
+template <int MG, int TR>
+__global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
+  extern __shared__ uint16_t xs[];  // [M][steps of this part * 512 + kXPad]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int cn = lane & 3, blk = lane >> 2;
+  const int64_t K = a.K;
+
+  const int zs0 = (int)(((int64_t)a.steps * blockIdx.y) / gridDim.y);
+  const int zs1 = (int)(((int64_t)a.steps * (blockIdx.y + 1)) / gridDim.y);
+  const int nsteps = zs1 - zs0;
+  const uint16_t* x = a.x;
+  const int stride = nsteps * kG4Step + kXPad;
+  stage_activations(xs, a.M, (int64_t)zs0 * kG4Step, nsteps * kG4Step, stride, K,
+                    [x, K](int m) { return x + (int64_t)m * K; });
+
+  const int64_t tile0 = ((int64_t)blockIdx.x * nw + wave) * TR;
+  const uint8_t* cptr[TR];
+  const uint8_t* sptr[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    int64_t j = (tile0 + t) * 4 + cn;
+    if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
+    const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
+    cptr[t] = a.wc + row * (K / 2);
+    sptr[t] = a.ws + row * (K / 16);
+  }
+  const uint16_t* xl[MG];
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int m = min(4 * g + cn, a.M - 1);  // padding row: never stored
+    xl[g] = xs + m * stride + 32 * blk;
+  }
+
+  f32x4 acc[TR][MG];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  g4_accumulate<MG, TR>(acc, cptr, sptr, xl, K, zs0, zs1, (int)(K / kG4Step));
+
+  // acc[t][g][r] of lane (blk, cn) is block blk's part of row 4g+r, column
+  // 4*tile + cn; sum the 16 blocks, then lane blk == m stores row m.
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const int64_t j = (tile0 + t) * 4 + cn;
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * g + r;
+        if (m >= a.M) continue;  // uniform
+        const float v = gemv4_reduce(acc[t][g][r]);
+        if (blk != m || j >= a.n_out) continue;
+        const int64_t o = (int64_t)m * a.n_out + j;
+        if (gridDim.y > 1)
+          a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
+        else if (a.out_f32)
+          static_cast<float*>(a.out)[o] = v;
+        else
+          static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(v);
       }
     }
   }
@@ -127,25 +189,60 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
 template <int MT, int TR>
 void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 15) / 16;
-  dim3 grid((unsigned)((tiles + TR - 1) / TR), (unsigned)zsplit);
-  hipLaunchKernelGGL((k_gemv<MT, TR>), grid, dim3(64 * nw), nw * 64 * 4 * sizeof(float), stream,
-                     a);
+  const int64_t per_wg = (int64_t)nw * TR;
+  dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
+  if (nw == 8)
+    hipLaunchKernelGGL((k_gemv<MT, TR, 8>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_gemv<MT, TR, 4>), grid, dim3(256), 0, stream, a);
+}
+
+template <int MG, int TR>
+void launch_gemv4_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
+  const int64_t tiles = (a.n_out + 3) / 4;
+  const int64_t per_wg = (int64_t)nw * TR;
+  dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
+  const int max_steps = (a.steps + zsplit - 1) / zsplit;
+  const size_t lds = (size_t)a.M * (max_steps * kG4Step + kXPad) * sizeof(uint16_t);
+  hipLaunchKernelGGL((k_gemv4<MG, TR>), grid, dim3(64 * nw), lds, stream, a);
 }
 
 }  // namespace
 
 GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   GemvPlan p;
-  p.mt = M <= 16 ? 1 : 2;
-  p.tr = M <= 16 ? 2 : 4;
+  p.small = M <= 4;  // 4x4x4-block kernel with per-block scaling
+  p.mt = p.small ? 1 : (M <= 16 ? 1 : 2);
+  p.tr = p.small ? 4 : 2;
   p.nw = 4;
-  const int64_t steps = (K + kGemvStep - 1) / kGemvStep;
-  const int64_t tiles = (n_out + 15) / 16;
-  const int64_t wgs = (tiles + p.tr - 1) / p.tr;
+  int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
+  // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
+  // the waves per workgroup and the LDS budget of the staged activations.
+  if (const char* e = getenv("NVFP4_GEMV_PLAN")) {
+    int tr = 0, nw = 0, kib = 0;
+    const int n = sscanf(e, "%d,%d,%d", &tr, &nw, &kib);
+    const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || tr == 8)
+                               : (tr == 1 || tr == 2 || (tr == 4 && p.mt == 1));
+    const bool nw_ok = p.small ? (nw >= 1 && nw <= 8) : (nw == 4 || nw == 8);
+    if (n >= 2 && tr_ok && nw_ok) p.tr = tr, p.nw = nw;
+    if (n == 3 && kib >= 8 && kib <= 160) lds_budget = (int64_t)kib * 1024;
+  }
+  const int64_t step = p.small ? kG4Step : kGemvStep;
+  const int64_t rows_per_tile = p.small ? 4 : 16;
+  const int64_t steps = (K + step - 1) / step;
+  int64_t z = 1;
+  if (p.small) {  // the 4x4x4 kernel stages its whole K part: it must fit LDS
+    int64_t max_steps = (lds_budget / (2 * M) - kXPad) / step;
+    if (max_steps < 1) max_steps = 1;
+    z = (steps + max_steps - 1) / max_steps;
+  }
+  // enough waves to fill the chip
+  const int64_t tiles = (n_out + rows_per_tile - 1) / rows_per_tile;
+  const int64_t wgs = (tiles + (int64_t)p.nw * p.tr - 1) / ((int64_t)p.nw * p.tr);
   const int64_t want_waves = (int64_t)num_cus * 8;
-  int64_t z = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
-  int64_t zmax = steps / p.nw;  // keep >= 1 step per wave
-  if (z > zmax) z = zmax;
+  const int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
+  if (zw > z) z = zw;
+  if (z > steps) z = steps;
   if (z < 1) z = 1;
   p.z = (int)z;
   return p;
@@ -168,16 +265,26 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
   a.K = K;
   a.n_out = n_out;
   a.M = (int)M;
-  a.steps = (int)((K + kGemvStep - 1) / kGemvStep);
+  const int64_t step = p.small ? kG4Step : kGemvStep;
+  a.steps = (int)((K + step - 1) / step);
   a.out_f32 = out_f32 ? 1 : 0;
-  if (p.mt == 1 && p.tr == 2)
+  if (p.small) {
+    if (p.mt == 1 && p.tr == 4)
+      launch_gemv4_t<1, 4>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 2)
+      launch_gemv4_t<1, 2>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 8)
+      launch_gemv4_t<1, 8>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 1)
+      launch_gemv4_t<1, 1>(a, p.nw, p.z, stream);
+    else
+      return -2;
+  } else if (p.mt == 1 && p.tr == 2)
     launch_gemv_t<1, 2>(a, p.nw, p.z, stream);
   else if (p.mt == 1 && p.tr == 1)
     launch_gemv_t<1, 1>(a, p.nw, p.z, stream);
   else if (p.mt == 1 && p.tr == 4)
     launch_gemv_t<1, 4>(a, p.nw, p.z, stream);
-  else if (p.mt == 2 && p.tr == 4)
-    launch_gemv_t<2, 4>(a, p.nw, p.z, stream);
   else if (p.mt == 2 && p.tr == 2)
     launch_gemv_t<2, 2>(a, p.nw, p.z, stream);
   else if (p.mt == 2 && p.tr == 1)

@@ -1,15 +1,33 @@
 // gemv_core.h -- the weight-streaming inner loop shared by the decode GEMV and
 // the grouped (mixture-of-experts) GEMV kernels (internal).
 //
-// A wave accumulates, for TR tiles of 16 weight rows and MT tiles of 16
-// activation rows, the partial dot products over K steps [s0, s1) of 256
-// elements.  Lane (n = lane % 16, q = lane / 16) loads, per step and weight
-// tile, two 16-byte code words of its weight row -- elements [32q, 32q+32) and
-// [128+32q, 160+32q) of the step -- plus the two scale bytes of each.  Each
-// 32-bit word (8 elements sharing one scale) is decoded exactly to bf16 and is
-// the B operand of one v_mfma_f32_16x16x32_bf16; the A operand carries the
-// matching 8 activations of activation row (lane % 16) of the m-tile.
-// Result layout (per tile pair): lane holds C[m = 4*(lane/16) + r][n = lane%16].
+// A workgroup stages the activations of its K range in LDS once (coalesced
+// 16-byte loads), then each wave streams the NVFP4 codes and scales of its own
+// TR tiles of 16 weight rows over that K range, 256 elements per step, and
+// accumulates with bf16 MFMA.  Keeping the activations out of the per-step
+// vector-memory loads leaves the texture-address path to the weights alone.
+//
+// Lane (n = lane % 16, q = lane / 16) owns, per step and weight tile, the 64
+// contiguous elements [64q, 64q+64) of weight row n: two 16-byte code words and
+// the four scale bytes that cover them (one 32-bit load).  A wave's code loads
+// cover 16 rows x 128 contiguous bytes.  Each 32-bit code word (8 elements, one
+// scale) is decoded exactly to bf16 in registers and is the B operand of one
+// v_mfma_f32_16x16x32_bf16 (B[k][n]: lane holds k-slots 8*(lane/16) .. +7 of
+// column lane%16).  The A operand (read from LDS) carries the matching 8
+// activations of activation row lane % 16, so an MFMA's 32 k-slots map to
+// scattered physical k; any bijection gives the same dot product as long as A
+// and B agree.
+//
+// Code/scale loads of step s+1 are issued before step s is computed (register
+// double buffer, pinned with scheduling barriers).  Main-loop loads are
+// unconditional: weight rows past the end are clamped to a valid row and
+// activation rows past M read a valid row -- both only feed accumulator
+// entries that are never stored.  Only the last step, when K is not a multiple
+// of 256, takes the masked path (K % 32 == 0: each 32-element half of a lane's
+// range is either in or out); its absent elements get zero codes, zero scales
+// and zero-filled activations.
+//
+// Result layout: lane holds C[m = 4*(lane/16) + r][n = lane % 16], r = 0..3.
 #pragma once
 
 #include "device.h"
@@ -17,78 +35,234 @@
 namespace nvfp4 {
 
 constexpr int kGemvStep = 256;  // K elements per step
+constexpr int kXPad = 8;        // bf16 elements of padding per LDS activation row
 
-__device__ __forceinline__ u32x4 load16_or_zero(const uint8_t* p, bool ok) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+template <int TR>
+struct WStep {
+  u32x4 c[TR][2];   // code words: elements [64q, 64q+32) and [64q+32, 64q+64)
+  uint32_t sc[TR];  // the four E4M3 scale bytes of those 64 elements
+};
+
+// LDS row stride (bf16 elements) for a K range of `steps` 256-element steps.
+__host__ __device__ inline int lds_x_stride(int steps) { return steps * kGemvStep + kXPad; }
+
+// Stage activation rows [0, m_rows) x [k_lo, k_lo + klen) into LDS as
+// [m_rows][stride] bf16; elements at or past K are zero.  row_ptr(m) gives the
+// global row (bf16, K elements).  klen % 8 == 0.  All threads of the workgroup
+// take part; ends with a barrier.
+template <typename RowPtr>
+__device__ __forceinline__ void stage_activations(uint16_t* lds, int m_rows, int64_t k_lo,
+                                                  int klen, int stride, int64_t K,
+                                                  RowPtr row_ptr) {
+  const int chunks_per_row = klen / 8;
+  const int total = m_rows * chunks_per_row;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+    const int m = c / chunks_per_row, c8 = c - m * chunks_per_row;
+    const int64_t k = k_lo + (int64_t)c8 * 8;
+    const u32x4 v = k < K ? *reinterpret_cast<const u32x4*>(row_ptr(m) + k) : z;
+    *reinterpret_cast<u32x4*>(lds + m * stride + c8 * 8) = v;
+  }
+  __syncthreads();
 }
 
-// xrow[mt]: this lane's activation row (bf16, K elements) for m-tile mt, or
-// nullptr for a padding row.  cptr/sptr: this lane's weight-row code and scale
-// pointers per weight tile; rvalid false for padding rows.
+template <int TR, bool TAIL>
+__device__ __forceinline__ void load_wstep(WStep<TR>& b, const uint8_t* const (&cptr)[TR],
+                                           const uint8_t* const (&sptr)[TR], int64_t K,
+                                           bool scale_dword, int s) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const int64_t k0 = (int64_t)s * kGemvStep + 64 * q;  // first element of this lane
+  const bool h0 = !TAIL || k0 + 32 <= K;                // halves present (tail step only)
+  const bool h1 = !TAIL || k0 + 64 <= K;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const uint8_t* c = cptr[t] + k0 / 2;
+    const uint8_t* sc = sptr[t] + k0 / 16;
+    if (TAIL) {
+      b.c[t][0] = h0 ? *reinterpret_cast<const u32x4*>(c) : z;
+      b.c[t][1] = h1 ? *reinterpret_cast<const u32x4*>(c + 16) : z;
+      const uint32_t lo = h0 ? *reinterpret_cast<const uint16_t*>(sc) : 0u;
+      const uint32_t hi = h1 ? *reinterpret_cast<const uint16_t*>(sc + 2) : 0u;
+      b.sc[t] = lo | (hi << 16);
+    } else {
+      b.c[t][0] = *reinterpret_cast<const u32x4*>(c);
+      b.c[t][1] = *reinterpret_cast<const u32x4*>(c + 16);
+      if (scale_dword)
+        b.sc[t] = *reinterpret_cast<const uint32_t*>(sc);
+      else
+        b.sc[t] = (uint32_t)*reinterpret_cast<const uint16_t*>(sc) |
+                  ((uint32_t)*reinterpret_cast<const uint16_t*>(sc + 2) << 16);
+    }
+  }
+}
+
+// One step: A operands from LDS (xl[mt]: this lane's activation row in LDS at
+// the step's element 64q), B operands decoded from the codes.
+template <int MT, int TR>
+__device__ __forceinline__ void compute_wstep(f32x4 (&acc)[TR][MT], const WStep<TR>& b,
+                                              const uint16_t* const (&xl)[MT]) {
+  u32x4 a[MT][8];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[mt][j] = *reinterpret_cast<const u32x4*>(xl[mt] + 8 * j);
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    float s[4];
+    s[0] = e4m3_to_f32<0>(b.sc[t]);
+    s[1] = e4m3_to_f32<1>(b.sc[t]);
+    s[2] = e4m3_to_f32<2>(b.sc[t]);
+    s[3] = e4m3_to_f32<3>(b.sc[t]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 w = dequant8_bf16(b.c[t][j >> 2][j & 3], s[j >> 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma_16x16x32_bf16(a[mt][j], w, acc[t][mt]);
+    }
+  }
+}
+
+// Accumulate steps [s0, s1) (absolute step indices).  xl0[mt] points at this
+// lane's activation row in LDS at element 64q of step s0.  `steps_full` is the
+// number of complete 256-element steps of K; step steps_full (if < s1) is the
+// partial last step.
 template <int MT, int TR>
 __device__ __forceinline__ void gemv_accumulate(f32x4 (&acc)[TR][MT],
-                                                const uint16_t* const (&xrow)[MT],
                                                 const uint8_t* const (&cptr)[TR],
                                                 const uint8_t* const (&sptr)[TR],
-                                                const bool (&rvalid)[TR], int64_t K, int s0,
-                                                int s1) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane >> 4;
-  for (int s = s0; s < s1; ++s) {
-    const int64_t kb = (int64_t)s * kGemvStep;
-    const int64_t k0 = kb + 32 * q, k1 = kb + 128 + 32 * q;
-    const bool ok0 = k0 + 32 <= K, ok1 = k1 + 32 <= K;
-
-    u32x4 xa[MT][8];
+                                                const uint16_t* const (&xl0)[MT], int64_t K,
+                                                int s0, int s1, int steps_full) {
+  const bool sdw = (K % 64) == 0;  // scale rows 4-byte aligned
+  const int e = s1 < steps_full ? s1 : steps_full;  // end of the unmasked steps
+  int s = s0;
+  const uint16_t* xl[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bool mok = xrow[mt] != nullptr;
-      const uint8_t* xr = mok ? reinterpret_cast<const uint8_t*>(xrow[mt]) : cptr[0];
+  for (int mt = 0; mt < MT; ++mt) xl[mt] = xl0[mt];
+  if (s < e) {
+    // Prefetches are unconditional so the compiler can count outstanding loads
+    // exactly; past the last step they re-read it and the data is unused.  The
+    // scheduling barriers keep each prefetch batch ahead of the compute it
+    // overlaps.
+    WStep<TR> b0, b1;
+    load_wstep<TR, false>(b0, cptr, sptr, K, sdw, s);
+    while (true) {
+      load_wstep<TR, false>(b1, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_wstep<MT, TR>(acc, b0, xl);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xa[mt][j] = load16_or_zero(xr + (k0 + 8 * j) * 2, mok && ok0);
-        xa[mt][4 + j] = load16_or_zero(xr + (k1 + 8 * j) * 2, mok && ok1);
-      }
+      for (int mt = 0; mt < MT; ++mt) xl[mt] += kGemvStep;
+      if (++s >= e) break;
+      load_wstep<TR, false>(b0, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_wstep<MT, TR>(acc, b1, xl);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xl[mt] += kGemvStep;
+      if (++s >= e) break;
     }
-
-#pragma unroll
-    for (int t = 0; t < TR; ++t) {
-      const bool v0 = rvalid[t] && ok0, v1 = rvalid[t] && ok1;
-      const u32x4 c0 = load16_or_zero(cptr[t] + k0 / 2, v0);
-      const u32x4 c1 = load16_or_zero(cptr[t] + k1 / 2, v1);
-      const uint32_t sc0 = v0 ? *reinterpret_cast<const uint16_t*>(sptr[t] + k0 / 16) : 0u;
-      const uint32_t sc1 = v1 ? *reinterpret_cast<const uint16_t*>(sptr[t] + k1 / 16) : 0u;
-      const float f00 = e4m3_to_f32<0>(sc0), f01 = e4m3_to_f32<1>(sc0);
-      const float f10 = e4m3_to_f32<0>(sc1), f11 = e4m3_to_f32<1>(sc1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t cw = j < 4 ? c0[j] : c1[j - 4];
-        const float sf = j < 2 ? f00 : j < 4 ? f01 : j < 6 ? f10 : f11;
-        const u32x4 b = dequant8_bf16(cw, sf);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[t][mt] = mfma_16x16x32_bf16(xa[mt][j], b, acc[t][mt]);
-      }
-    }
+  }
+  if (s == steps_full && s < s1) {  // partial last step
+    WStep<TR> bt;
+    load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
+    compute_wstep<MT, TR>(acc, bt, xl);
   }
 }
 
-// Sum one f32x4 accumulator over the nw waves of the workgroup in wave order.
-// Returns, for threads 0..255, the total of element r = tid/64 of lane tid%64
-// (i.e. C[4*((tid%64)/16) + tid/64][tid%16]); other threads get 0.  `red` is
-// nw*256 floats of LDS.  Contains two barriers; every thread must call it.
-__device__ __forceinline__ float wave_sum_f32x4(float* red, const f32x4& v) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  *reinterpret_cast<f32x4*>(&red[(wave * 64 + lane) * 4]) = v;
-  __syncthreads();
-  float s = 0.f;
-  if (threadIdx.x < 256) {
-    const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
-    for (int w = 0; w < nw; ++w) s += red[(w * 64 + l) * 4 + r];
+// Activation window: the workgroup streams the activations through a double
+// buffer of two 256-element steps in LDS ([2][16*MT][kXWin] bf16), one step
+// ahead of the weights, with one barrier per step.  The window always holds
+// 16*MT rows (rows past M repeat row M-1) so every thread moves the same
+// number of 16-byte pieces, XP = 16*MT*32 / blockDim, with no branches: loads
+// past K read a clamped address and are replaced by zero.
+constexpr int kXWin = kGemvStep + kXPad;  // LDS row stride of the window
+
+template <int XP, typename RowPtr>
+__device__ __forceinline__ void xwin_load(u32x4 (&v)[XP], int M, int64_t K, int s,
+                                          RowPtr row_ptr) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = threadIdx.x + i * blockDim.x;
+    const int m = min(c >> 5, M - 1), c8 = c & 31;
+    const int64_t k = (int64_t)s * kGemvStep + c8 * 8;
+    const u32x4 t = *reinterpret_cast<const u32x4*>(row_ptr(m) + min(k, K - 8));
+    v[i] = k < K ? t : z;
   }
+}
+
+template <int XP>
+__device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) {
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = threadIdx.x + i * blockDim.x;
+    *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = v[i];
+  }
+}
+
+// Accumulate steps [s0, s1) with the activations streamed through the LDS
+// window `win` ([2][16*MT][kXWin]).  xrow_off[mt] = (16*mt + lane%16) * kXWin +
+// 64q (rows past M hold copies, their results are never stored).  Every thread
+// of the workgroup calls this with the same arguments except the weight
+// pointers.  blockDim.x * XP == 16*MT*32.
+template <int MT, int TR, int XP, typename RowPtr>
+__device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
+                                                    const uint8_t* const (&cptr)[TR],
+                                                    const uint8_t* const (&sptr)[TR],
+                                                    uint16_t* win, const int (&xrow_off)[MT],
+                                                    int M, int64_t K, int s0, int s1,
+                                                    int steps_full, RowPtr row_ptr) {
+  if (s0 >= s1) return;
+  const bool sdw = (K % 64) == 0;  // scale rows 4-byte aligned
+  constexpr int wsz = 16 * MT * kXWin;
+  u32x4 xv[XP];
+  xwin_load<XP>(xv, M, K, s0, row_ptr);
+  xwin_store<XP>(win, xv);
   __syncthreads();
-  return s;
+  const int e = s1 < steps_full ? s1 : steps_full;  // end of the full steps
+  int s = s0, cur = 0;
+  if (s < e) {
+    // Prefetches (weights of step s+1, activations of step s+1) are issued
+    // before step s is computed and are unconditional: past the end they
+    // re-read a valid step and the data is unused.
+    WStep<TR> b0, b1;
+    load_wstep<TR, false>(b0, cptr, sptr, K, sdw, s);
+    while (true) {
+      xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+      load_wstep<TR, false>(b1, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const uint16_t* xl[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+        compute_wstep<MT, TR>(acc, b0, xl);
+      }
+      xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
+      __syncthreads();
+      cur ^= 1;
+      if (++s >= e) break;
+      xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+      load_wstep<TR, false>(b0, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const uint16_t* xl[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+        compute_wstep<MT, TR>(acc, b1, xl);
+      }
+      xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
+      __syncthreads();
+      cur ^= 1;
+      if (++s >= e) break;
+    }
+  }
+  if (s == steps_full && s < s1) {  // partial last step; its activations are in `cur`
+    WStep<TR> bt;
+    load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
+    const uint16_t* xl[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+    compute_wstep<MT, TR>(acc, bt, xl);
+  }
 }
 
 }  // namespace nvfp4

@@ -17,6 +17,7 @@ int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uin
                     hipStream_t stream);
 
 struct GemvPlan {
+  bool small;  // M <= 4: 4x4x4-block kernel (tiles of 4 rows)
   int mt;  // 16-row activation tiles (M <= 16 * mt)
   int tr;  // 16-row weight tiles per wave
   int nw;  // waves per workgroup (split-K inside the workgroup)

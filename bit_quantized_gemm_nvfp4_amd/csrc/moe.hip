@@ -89,7 +89,8 @@ __global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict
 
 // ---- grouped GEMV -------------------------------------------------------------
 
-constexpr int kGroupRows = 32;  // rows of one expert per workgroup (two 16-row MFMA tiles)
+constexpr int kGroupRows = 16;  // rows of one expert per workgroup (one 16-row MFMA tile)
+constexpr int kGroupWaves = 4;
 
 struct GroupedArgs {
   const uint16_t* a;
@@ -134,76 +135,75 @@ __device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx
   return false;
 }
 
+// One workgroup: up to 16 grouped rows of one expert (staged in LDS) against
+// kGroupWaves weight tiles (SWIGLU: tile pairs gate/up) of that expert.
 template <int TR>
 __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
-  extern __shared__ float red[];
+  extern __shared__ uint16_t xs[];  // [kGroupRows][lds_x_stride(steps)]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int ln = lane & 15;
+  const int ln = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
 
   int e, c;
   if (!find_chunk(g.offsets, g.E, blockIdx.x, e, c)) return;  // uniform over the workgroup
   const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * kGroupRows;
   const int64_t r1 = min((int64_t)g.offsets[e + 1], r0 + kGroupRows);
+  const int rows = (int)(r1 - r0);
+  const uint16_t* a = g.a;
+  const int32_t* gather = g.gather;
+  const int stride = lds_x_stride(g.steps);
+  stage_activations(xs, rows, 0, g.steps * kGemvStep, stride, K, [a, gather, r0, K](int m) {
+    const int64_t r = r0 + m;
+    return a + (int64_t)(gather ? gather[r] : r) * K;
+  });
 
-  const int s0 = (int)(((int64_t)g.steps * wave) / nw);
-  const int s1 = (int)(((int64_t)g.steps * (wave + 1)) / nw);
-
-  // weight rows: NONE -> tiles blockIdx.y*TR + t; SWIGLU (TR == 2) -> gate tile
-  // blockIdx.y and the matching up tile N/2 + 16*blockIdx.y.
+  // weight rows: NONE -> tiles (blockIdx.y*nw + wave)*TR + t; SWIGLU (TR == 2) ->
+  // gate tile blockIdx.y*nw + wave and the matching up tile N/2 further.
+  const int64_t gt = (int64_t)blockIdx.y * kGroupWaves + wave;
   const uint8_t* we_c = g.wc + (int64_t)e * g.N * (K / 2);
   const uint8_t* we_s = g.ws + (int64_t)e * g.N * (K / 16);
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
-  bool rvalid[TR];
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
-    const int64_t n = g.swiglu ? (int64_t)t * (g.N / 2) + (int64_t)blockIdx.y * 16 + ln
-                               : ((int64_t)blockIdx.y * TR + t) * 16 + ln;
-    rvalid[t] = n < g.N;
-    cptr[t] = we_c + (rvalid[t] ? n : 0) * (K / 2);
-    sptr[t] = we_s + (rvalid[t] ? n : 0) * (K / 16);
+    int64_t n = g.swiglu ? (int64_t)t * (g.N / 2) + gt * 16 + ln : (gt * TR + t) * 16 + ln;
+    if (n >= g.N) n = g.N - 1;  // padding column: never stored
+    cptr[t] = we_c + n * (K / 2);
+    sptr[t] = we_s + n * (K / 16);
   }
-  const uint16_t* xrow[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int64_t r = r0 + mt * 16 + ln;
-    xrow[mt] = r < r1 ? g.a + (int64_t)(g.gather ? g.gather[r] : r) * K : nullptr;
-  }
+  const uint16_t* xl[1] = {xs + min(ln, rows - 1) * stride + 64 * q};
 
-  f32x4 acc[TR][2];
+  f32x4 acc[TR][1];
 #pragma unroll
-  for (int t = 0; t < TR; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TR; ++t) acc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemv_accumulate<2, TR>(acc, xrow, cptr, sptr, rvalid, K, s0, s1);
+  gemv_accumulate<1, TR>(acc, cptr, sptr, xl, K, 0, g.steps, (int)(K / kGemvStep));
 
-  const int rr = threadIdx.x >> 6, l = threadIdx.x & 63;
+  // lane holds C[m = 4*q + r][column 16*tile + ln]
   const int64_t width = g.swiglu ? g.N / 2 : g.N;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int64_t r = r0 + mt * 16 + 4 * (l >> 4) + rr;
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * q + r;
+    if (m >= rows) continue;
+    const int64_t row = r0 + m;
+    const float rs = g.row_scale ? g.row_scale[row] : 1.0f;
     if (g.swiglu) {
-      const float hg = wave_sum_f32x4(red, acc[0][mt]);
-      const float hu = wave_sum_f32x4(red, acc[TR - 1][mt]);
-      const int64_t col = (int64_t)blockIdx.y * 16 + (l & 15);
-      if (threadIdx.x < 256 && r < r1 && col < width) {
+      const int64_t col = gt * 16 + ln;
+      if (col < width) {
+        const float hg = acc[0][0][r], hu = acc[TR - 1][0][r];
         float v = hg / (1.0f + expf(-hg)) * hu;
-        if (g.row_scale) v *= g.row_scale[r];
-        g.out[r * width + col] = f32_to_bf16_bits(v);
+        if (g.row_scale) v *= rs;
+        g.out[row * width + col] = f32_to_bf16_bits(v);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < TR; ++t) {
-        const float h = wave_sum_f32x4(red, acc[t][mt]);
-        const int64_t col = ((int64_t)blockIdx.y * TR + t) * 16 + (l & 15);
-        if (threadIdx.x < 256 && r < r1 && col < width) {
-          float v = h;
-          if (g.row_scale) v *= g.row_scale[r];
-          g.out[r * width + col] = f32_to_bf16_bits(v);
+        const int64_t col = (gt * TR + t) * 16 + ln;
+        if (col < width) {
+          float v = acc[t][0][r];
+          if (g.row_scale) v *= rs;
+          g.out[row * width + col] = f32_to_bf16_bits(v);
         }
       }
     }
@@ -283,13 +283,14 @@ int launch_grouped_gemm(const uint16_t* a, int64_t K, const int32_t* gather,
   g.K = K;
   g.N = N;
   g.E = (int)E;
-  g.steps = (int)((K + kGemvStep - 1) / kGemvStep);
+  g.steps = (int)((K + kGemvStep - 1) / kGemvStep);  // including a partial last step
   g.swiglu = swiglu ? 1 : 0;
-  const int nw = 4;
   const int64_t chunks = (R + kGroupRows - 1) / kGroupRows + E;  // upper bound
-  const int64_t ytiles = swiglu ? (N / 2 + 15) / 16 : (N + 31) / 32;
-  hipLaunchKernelGGL(k_grouped_gemv<2>, dim3((unsigned)chunks, (unsigned)ytiles), dim3(64 * nw),
-                     nw * 64 * 4 * sizeof(float), stream, g);
+  const int64_t tiles_y = swiglu ? (N / 2 + 15) / 16 : (N + 31) / 32;  // gate tiles or tile pairs
+  const int64_t ytiles = (tiles_y + kGroupWaves - 1) / kGroupWaves;
+  const size_t lds = (size_t)kGroupRows * lds_x_stride(g.steps) * sizeof(uint16_t);
+  hipLaunchKernelGGL(k_grouped_gemv<2>, dim3((unsigned)chunks, (unsigned)ytiles),
+                     dim3(64 * kGroupWaves), lds, stream, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
