@@ -119,8 +119,10 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
   const int nsteps = zs1 - zs0;
   const uint16_t* x = a.x;
   const int stride = nsteps * kG4Step + kXPad;
-  stage_activations(xs, a.M, (int64_t)zs0 * kG4Step, nsteps * kG4Step, stride, K,
-                    [x, K](int m) { return x + (int64_t)m * K; });
+  auto stage = [&]() {
+    stage_activations(xs, a.M, (int64_t)zs0 * kG4Step, nsteps * kG4Step, stride, K,
+                      [x, K](int m) { return x + (int64_t)m * K; });
+  };
 
   const int64_t tile0 = ((int64_t)blockIdx.x * nw + wave) * TR;
   const uint8_t* cptr[TR];
@@ -146,7 +148,7 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
 #pragma unroll
     for (int g = 0; g < MG; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  g4_accumulate<MG, TR>(acc, cptr, sptr, xl, K, zs0, zs1, (int)(K / kG4Step));
+  g4_accumulate<MG, TR>(acc, cptr, sptr, xl, K, zs0, zs1, (int)(K / kG4Step), stage);
 
   // acc[t][g][r] of lane (blk, cn) is block blk's part of row 4g+r, column
   // 4*tile + cn; sum the 16 blocks, then lane blk == m stores row m.
@@ -211,9 +213,14 @@ void launch_gemv4_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
 
 GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   GemvPlan p;
-  p.small = M <= 4;  // 4x4x4-block kernel with per-block scaling
-  p.mt = p.small ? 1 : (M <= 16 ? 1 : 2);
-  p.tr = p.small ? 4 : 2;
+  int64_t small_max = 4;  // largest M for the 4x4x4-block kernel with per-block scaling
+  if (const char* e = getenv("NVFP4_GEMV_SMALL_MAX")) {
+    const int v = atoi(e);
+    if (v >= 0 && v <= 8) small_max = v;
+  }
+  p.small = M <= small_max;
+  p.mt = p.small ? (int)((M + 3) / 4) : (M <= 16 ? 1 : 2);
+  p.tr = 2;
   p.nw = 4;
   int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
   // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
@@ -221,7 +228,7 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   if (const char* e = getenv("NVFP4_GEMV_PLAN")) {
     int tr = 0, nw = 0, kib = 0;
     const int n = sscanf(e, "%d,%d,%d", &tr, &nw, &kib);
-    const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || tr == 8)
+    const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || (tr == 8 && p.mt == 1))
                                : (tr == 1 || tr == 2 || (tr == 4 && p.mt == 1));
     const bool nw_ok = p.small ? (nw >= 1 && nw <= 8) : (nw == 4 || nw == 8);
     if (n >= 2 && tr_ok && nw_ok) p.tr = tr, p.nw = nw;
@@ -277,6 +284,12 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
       launch_gemv4_t<1, 8>(a, p.nw, p.z, stream);
     else if (p.mt == 1 && p.tr == 1)
       launch_gemv4_t<1, 1>(a, p.nw, p.z, stream);
+    else if (p.mt == 2 && p.tr == 4)
+      launch_gemv4_t<2, 4>(a, p.nw, p.z, stream);
+    else if (p.mt == 2 && p.tr == 2)
+      launch_gemv4_t<2, 2>(a, p.nw, p.z, stream);
+    else if (p.mt == 2 && p.tr == 1)
+      launch_gemv4_t<2, 1>(a, p.nw, p.z, stream);
     else
       return -2;
   } else if (p.mt == 1 && p.tr == 2)

@@ -100,20 +100,24 @@ __device__ __forceinline__ void g4_compute(f32x4 (&acc)[TR][MG], const G4Step<TR
 
 // Steps [s0, s1); steps_full complete 512-element steps, step steps_full (if
 // < s1) partial.  Same unconditional-prefetch double buffer as gemv_core.h.
-template <int MG, int TR>
+// `stage` is called after the first weight loads are issued (so their latency
+// overlaps the activation staging) and before any activation is read.
+template <int MG, int TR, typename Stage>
 __device__ __forceinline__ void g4_accumulate(f32x4 (&acc)[TR][MG],
                                               const uint8_t* const (&cptr)[TR],
                                               const uint8_t* const (&sptr)[TR],
                                               const uint16_t* const (&xl0)[MG], int64_t K,
-                                              int s0, int s1, int steps_full) {
+                                              int s0, int s1, int steps_full, Stage stage) {
   const int e = s1 < steps_full ? s1 : steps_full;
   int s = s0;
   const uint16_t* xl[MG];
 #pragma unroll
   for (int g = 0; g < MG; ++g) xl[g] = xl0[g];
+  if (s >= e) stage();
   if (s < e) {
     G4Step<TR> b0, b1;
     g4_load<TR, false>(b0, cptr, sptr, K, s);
+    stage();
     while (true) {
       g4_load<TR, false>(b1, cptr, sptr, K, min(s + 1, e - 1));
       __builtin_amdgcn_sched_barrier(0);
