@@ -31,21 +31,32 @@ bool log_enabled() {
 
 // Rows of M handled by one GEMV launch; larger M loops over chunks of this size.
 constexpr int64_t kGemvMaxM = 32;
+// From this many activation rows on, the MFMA GEMM (weights read once per
+// 256-row tile) replaces the weight-streaming GEMV (weights read once per
+// 32-row chunk).
+constexpr int64_t kGemmMinM = 65;
 
 struct GemmPlan {
+  bool mfma;             // large-M MFMA GEMM
   GemvPlan gemv;
   int64_t m_chunk;       // activation rows per GEMV launch
-  size_t a_dequant_bytes;  // W4A4: bf16 copy of the dequantized activations
+  size_t a_dequant_bytes;  // W4A4 GEMV: bf16 copy of the dequantized activations
   size_t partial_bytes;
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4) {
   (void)N;
   GemmPlan g;
+  int64_t min_m = kGemmMinM;
+  if (const char* e = getenv("NVFP4_GEMM_MIN_M")) {  // tuning knob
+    const long v = atol(e);
+    if (v >= 1) min_m = v;
+  }
+  g.mfma = M >= min_m;
   g.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
   g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs);
-  g.partial_bytes = gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
-  g.a_dequant_bytes = w4a4 ? (size_t)M * (size_t)K * 2 : 0;
+  g.partial_bytes = g.mfma ? 0 : gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
+  g.a_dequant_bytes = (w4a4 && !g.mfma) ? (size_t)M * (size_t)K * 2 : 0;
   return g;
 }
 
@@ -118,6 +129,14 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
   if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
 
   hipStream_t st = as_stream(stream);
+  if (g.mfma) {
+    if (((M + 255) / 256) * ((n_out + 255) / 256) > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+    if (log_enabled())
+      fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: mfma 256x256\n",
+              (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16");
+    return launched(launch_gemm(w4a4, a, a_scales, M, K, w_codes, w_scales, row_idx, n_out,
+                                out_dtype == NVFP4_FP32, out, st));
+  }
   const uint16_t* x = static_cast<const uint16_t*>(a);
   if (w4a4) {
     uint16_t* xa = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + a_off);

@@ -30,4 +30,10 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
                 void* out, void* workspace, hipStream_t stream);
 
+// Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
+// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].
+int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
+                const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
+                bool out_f32, void* out, hipStream_t stream);
+
 }  // namespace nvfp4

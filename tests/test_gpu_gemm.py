@@ -177,3 +177,104 @@ def test_run_to_run_bit_identical(nv):
     a = _run(nv, x, w)
     b = _run(nv, x, w)
     assert np.array_equal(a, b)
+
+
+# ---- large M: the LDS-tiled MFMA GEMM (256 x 256 tiles, 64-element K steps) ----
+
+@pytest.mark.parametrize("M,K,N", [
+    (65, 64, 16),       # smallest M on the MFMA path, one K step
+    (300, 160, 520),    # ragged in every dimension; K % 64 == 32 (partial and padding steps)
+    (257, 96, 257),     # N % 4 != 0: element-wise epilogue
+    (512, 5120, 300),   # long K
+    (1000, 1088, 777),  # several tiles in M and N, ragged tails
+])
+def test_mfma_ragged_shapes(nv, orc, M, K, N):
+    helpers.announce(f"gemm mfma ragged M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = workloads.normal_bf16(rng, M, K, outlier_frac=0.01)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    _assert_close(_run(nv, x, w), ref, what=f"{M}x{K}x{N}")
+    _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
+
+
+def test_mfma_identity_activations_reproduce_weights(nv, orc):
+    """One-hot activation rows through the MFMA path: y[m][n] = w[n][k_m], the
+    LDS-staged dequantization compared bit for bit with the oracle's."""
+    helpers.announce("gemm mfma identity activations")
+    K, N, M = 1056, 300, 300
+    w = workloads.nvfp4_weight(np.random.default_rng(19), N, K)
+    ks = np.random.default_rng(20).integers(0, K, M)
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80  # 1.0
+    got = _run(nv, x, w)
+    want = orc.dequantize(w.codes, w.scales, N, K)[:, ks].T
+    assert np.array_equal(got & 0x7FFF, want & 0x7FFF)
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz])
+
+
+def test_mfma_masked_rows(nv, orc):
+    helpers.announce("gemm mfma masked rows")
+    rng = np.random.default_rng(21)
+    M, K, N = 300, 512, 4000
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    idx = np.sort(rng.choice(N, 333, replace=False)).astype(np.int32)
+    _assert_close(_run(nv, x, w, row_idx=idx),
+                  orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx), what="masked")
+    one = np.array([7], np.int32)
+    _assert_close(_run(nv, x, w, row_idx=one),
+                  orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=one), what="one row")
+
+
+def test_mfma_matches_gemv_chunks(nv):
+    """The same product through both paths (NVFP4_GEMM_MIN_M is read per call):
+    both are fp32 sums of exact products, so they agree to fp32 rounding."""
+    import os
+    helpers.announce("gemm mfma vs gemv")
+    rng = np.random.default_rng(22)
+    M, K, N = 96, 2048, 512
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    a = _run(nv, x, w, out_f32=True)
+    os.environ["NVFP4_GEMM_MIN_M"] = "100000"
+    try:
+        b = _run(nv, x, w, out_f32=True)
+    finally:
+        del os.environ["NVFP4_GEMM_MIN_M"]
+    scale = np.abs(a).max() + 1.0
+    assert np.max(np.abs(a - b)) <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 160, 520), (700, 2048, 1000)])
+def test_mfma_w4a4_ragged(nv, orc, M, K, N):
+    helpers.announce(f"gemm mfma w4a4 M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + N)
+    x = workloads.normal_bf16(rng, M, K, outlier_frac=0.01)
+    w = workloads.nvfp4_weight(rng, N, K)
+    rc, rs = orc.quantize(x, M, K)
+    y = helpers.host_bits(nv.gemm(helpers.dev_u8(rc), helpers.dev_u8(w.codes),
+                                  helpers.dev_u8(w.scales), a_scales=helpers.dev_u8(rs)))
+    _assert_close(y, orc.gemm_w4a4(rc, rs, M, K, w.codes, w.scales), what="w4a4")
+
+
+@pytest.mark.parametrize("K,N", [(5120, 17408), (17408, 5120)])
+def test_prefill_full_size_sampled(nv, orc, K, N):
+    """The prefill shapes at full size (M = 8192, outlier activations), in the
+    launch configuration the benchmark times; 48 rows x 256 columns sampled are
+    recomputed by the oracle."""
+    import torch
+    helpers.announce(f"gemm prefill full size M=8192 K={K} N={N}")
+    x, w = workloads.prefill(K, N)
+    y = helpers.host_bits(nv.gemm(helpers.dev_bf16(x), helpers.dev_u8(w.codes),
+                                  helpers.dev_u8(w.scales)))
+    sr = np.random.default_rng(K)
+    rows = np.sort(np.concatenate([sr.choice(8192, 46, replace=False), [0, 8191]]))
+    rows = np.unique(rows)
+    cols = np.sort(np.concatenate([sr.choice(N, 254, replace=False), [0, N - 1]]))
+    cols = np.unique(cols).astype(np.int32)
+    xs = np.ascontiguousarray(x[rows])
+    ref = orc.gemm_w4a16(xs, len(rows), K, w.codes, w.scales, row_idx=cols)
+    _assert_close(y[np.ix_(rows, cols)], ref, what=f"prefill K={K} N={N}")
+    torch.cuda.synchronize()
