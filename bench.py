@@ -16,7 +16,10 @@ that are still cached.
 Also reported on the same JSON line:
   roofline      -- the decode GEMV kernel: algorithmic weight bytes per launch
                    over its mean launch time (HIP events on the launch stream),
-                   against the 8 TB/s HBM peak;
+                   against the 8 TB/s HBM peak; `traffic` is the HBM bytes per
+                   step measured with the FETCH_SIZE / WRITE_SIZE counters
+                   (profiles/decode_gemv_set_hbm_traffic.md), null once the
+                   kernel sources differ from the ones measured;
   cpu_baseline  -- the CPU oracle timed on this host on a bounded sample of the
                    same workload (a subset of output rows), scaled to GB/s;
   secondary     -- the other rows of the layer (prefill GEMM TFLOP/s,
@@ -39,11 +42,43 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+COPY_PROBE_BYTES = 256 << 20
 METRIC = "NVFP4 GEMM: weight-stream GB/s at M=1..32; TFLOP/s at M=8192 (1 GPU)"
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_gemv_set_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per decode step from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary, or None when the GEMV kernel sources have changed since
+    the counters were taken (their SHA-256 is recorded beside the figure)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        k, sep, v = line.partition(":")
+        if sep and k.strip() in ("traffic_bytes_per_step", "kernel_sources_sha256", "kernel_sources"):
+            fields[k.strip()] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for name in fields["kernel_sources"].split():
+        path = os.path.join(ROOT, "bit_quantized_gemm_nvfp4_amd", "csrc", name)
+        try:
+            h.update(open(path, "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest() != fields["kernel_sources_sha256"]:
+        return None
+    return int(fields["traffic_bytes_per_step"])
 
 
 def weight_bytes(rows: int, K: int) -> int:
@@ -244,6 +279,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 256 MiB device-to-device copy 3 times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: the NVFP4 layer is built for a single GPU "
@@ -284,6 +322,14 @@ def main():
     per_call_us = {c[0]: round(float(t * 1e3), 2) for c, t in zip(dec.calls, mean_ms)}
     del dec
     torch.cuda.empty_cache()
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {COPY_PROBE_BYTES} bytes")
+        del src, dst
 
     sec = None
     if not args.no_secondary:
@@ -315,8 +361,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "k_gemv (decode GEMV, all 12 launches of a step)",
+            "traffic": measured_traffic(),
+            "algorithmic_bytes": int(step_bytes),
+            "kernel": "k_gemv / k_gemv4 (decode GEMV, all 12 launches of a step; bytes per step)",
         },
         "per_call_GBs": per_call_gbs,
         "per_call_us": per_call_us,
