@@ -9,23 +9,31 @@
 // the kernel is bound by the bf16 MFMA rate, not by HBM.
 //
 // Tiling: a workgroup of 4 waves computes a 256 x 256 tile of y; each wave a
-// 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  K advances
-// 64 elements per step through a double buffer in LDS:
+// 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (accumulators
+// in AGPRs).  K advances 64 elements per step through a double buffer in LDS:
 //   A tile  [256 rows][64] bf16 (32 KB): 16-byte pieces copied from global;
-//   B tile  [256 cols][64] bf16 (32 KB): each thread loads one weight row's
-//           32 code bytes and 4 scale bytes and writes the 64 exactly
-//           dequantized bf16 values (the NVFP4 decode is done once per tile,
-//           not per use).  NVFP4 activations are decoded the same way.
-// Rows are stored as eight 16-byte pieces with piece c of row r at position
-// c ^ (r & 7), so the 32 lanes of an MFMA operand read (rows r..r+31, the same
-// piece) hit distinct LDS banks.
+//   B tile  [256 cols][64] bf16 (32 KB): NVFP4 weight rows decoded exactly to
+//           bf16 as they are written (once per tile, not per use).  NVFP4
+//           activations are decoded the same way into the A tile.
+// LDS layout: [A buffer 0][A buffer 1][B buffer 0][B buffer 1], so every LDS
+// access is a per-lane base register plus an immediate offset.  Rows are eight
+// 16-byte pieces, piece c of row r at c ^ f(r), f(r) = (r ^ (r >> 3)) & 7: the
+// 16 consecutive rows of an MFMA operand read or of a tile write fall on
+// distinct banks.
+//
+// Global loads: the bf16 activation tile is read 8 rows x 128 bytes per load
+// instruction; NVFP4 rows cooperatively, two lanes per row (one 16-byte half
+// each), so a load instruction touches 32 cache lines and every line is looked
+// up once per step -- the line count per instruction, not bandwidth, is what
+// these loads cost.
 //
 // Pipeline: the global loads of step s+2 are issued at the start of step s
 // into one of two register sets; the other set (step s+1, loaded a whole step
-// earlier) is decoded and written to the idle LDS buffer in four parts, one per
-// 16-element substep, between the MFMAs of step s; one barrier per step.  Each
-// substep's MFMA fragments are read from LDS while the previous substep's
-// MFMAs run.
+// earlier) is decoded and written to the idle LDS buffers while step s is
+// computed.  A step is 16 chunks (substep kk = 0..3, accumulator row i =
+// 0..3): chunk (kk, i) issues the 4 MFMAs of row i, reads fragments x[i], w[i]
+// of substep kk+1 and writes one 16-byte piece of the next tile; scheduling
+// barriers keep that interleave.  One workgroup barrier per step.
 //
 // The weight tile is the MFMA's A operand and the activation tile its B
 // operand, so an accumulator block holds y^T: lane l has output row l % 32 and
@@ -45,7 +53,9 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGemmThreads = 256;
-constexpr int kTileElems = BM * BK;  // one bf16 operand tile in LDS
+constexpr uint32_t kTileBytes = BM * BK * 2;  // one bf16 operand tile (32 KB)
+constexpr uint32_t kBOffset = 2 * kTileBytes;  // B buffers follow both A buffers
+constexpr uint32_t kLdsBytes = 4 * kTileBytes;
 
 struct GemmArgs {
   const void* a;            // bf16 [M][K], or NVFP4 codes [M][K/2]
@@ -59,88 +69,140 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int row, int piece) { return row * BK + ((piece ^ (row & 7)) << 3); }
+__device__ __forceinline__ uint32_t swz_f(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
 
-// A thread's share of one step's global loads, exactly as loaded: every load
-// is unconditional (addresses clamped into the arrays); the bytes past a
-// partial last step (K % 64 == 32) are replaced by zeros when the set is
-// written to LDS, so no wait for the loads is needed before then.
-template <bool A_NVFP4>
-struct GemmLoad {
-  u32x4 a[A_NVFP4 ? 2 : 8];  // bf16: 8 pieces of 16 B; NVFP4: one row's 32 code bytes
-  uint32_t a_sc[2];          // NVFP4: the row's 4 scale bytes as two 16-bit loads
-  u32x4 w[2];                // one weight row's 32 code bytes
-  uint32_t w_sc[2];          // its 4 scale bytes
+template <typename T>
+__device__ __forceinline__ T& lds_ref(char* lds, uint32_t off) {
+  return *reinterpret_cast<T*>(lds + off);
+}
+
+// Per-lane LDS byte offsets.  With r = lane % 32, h = lane / 32 and
+// g = h ^ f(r): fragment (substep kk, block i) of the wave's activation rows
+// wm*128 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
+// it is rd_x[kk ^ 2(i&1)] + 32 KB * buffer + 4096 i (likewise rd_w for the
+// weight rows wn*128 + ...).  A bf16 activation write of piece i (row t/8 +
+// 32 i, piece t % 8) is wr_a[i & 1] + 32 KB * buffer + 4096 i; an NVFP4 row
+// write (row t/2 + 128 q, piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j]
+// (NVFP4 activations) + 32 KB * buffer + 16384 q.  (Immediate offsets of LDS
+// instructions stop at 64 KB, so the B-tile base is part of the registers.)
+struct LdsOffsets {
+  uint32_t rd_x[4], rd_w[4];
+  uint32_t wr_a[2];
+  uint32_t wr_w[4], wr_na[4];
 };
 
+__device__ __forceinline__ LdsOffsets lds_offsets(int wm, int wn) {
+  LdsOffsets o;
+  const uint32_t t = threadIdx.x, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const uint32_t g = (h ^ swz_f(r)) & 7u;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    o.rd_x[kk] = (wm * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
+    o.rd_w[kk] = kBOffset + (wn * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
+  }
+  const uint32_t pa = ((t & 7) ^ ((t >> 3) & 7) ^ (t >> 6)) & 7u;
+  o.wr_a[0] = (t >> 3) * 128 + (pa << 4);
+  o.wr_a[1] = (t >> 3) * 128 + ((pa ^ 4u) << 4);
+  const uint32_t fw = ((t >> 1) ^ (t >> 4)) & 7u, hh = t & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o.wr_na[j] = (t >> 1) * 128 + (((4u * hh + j) ^ fw) << 4);
+    o.wr_w[j] = kBOffset + o.wr_na[j];
+  }
+  return o;
+}
+
+// A thread's share of one step's global loads, exactly as loaded.  Every load
+// is unconditional: on a partial last step (K % 64 == 32) the missing half is
+// re-read from inside the row and zeroed when the set is written to LDS, so no
+// wait for the loads is needed before then.
+struct Nvfp4Rows {
+  u32x4 c[2];     // codes of half (t & 1) of tile rows t/2 and 128 + t/2
+  uint32_t s[2];  // their two E4M3 scale bytes (one 16-bit load each)
+};
 template <bool A_NVFP4>
-__device__ __forceinline__ void gemm_load(GemmLoad<A_NVFP4>& L, const GemmArgs& g, int64_t arow,
-                                          int64_t wrow, int64_t k0) {
-  const int t = threadIdx.x;
-  const int64_t K = g.K;
+struct GemmLoad;
+template <>
+struct GemmLoad<false> {
+  u32x4 a[8];  // bf16 activations: piece t % 8 of tile rows t/8 + 32 i
+  Nvfp4Rows w;
+};
+template <>
+struct GemmLoad<true> {
+  Nvfp4Rows a;
+  Nvfp4Rows w;
+};
+
+// Where a thread loads from: bf16 activations as byte offsets (32-bit) from
+// the tile's first row; NVFP4 rows as pointers to this lane's half of rows
+// t/2 and 128 + t/2 at k = 0.
+struct GemmSrc {
+  uint32_t a_off[8];
+  const uint8_t* ac[2];
+  const uint8_t* as[2];
+  const uint8_t* wc[2];
+  const uint8_t* ws[2];
+};
+
+__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* const (&c)[2],
+                                                const uint8_t* const (&s)[2], int64_t k0,
+                                                bool kfull) {
+  const int hh = threadIdx.x & 1;
+  const int64_t coff = k0 / 2 - (kfull ? 0 : 16 * hh);
+  const int64_t soff = k0 / 16 - (kfull ? 0 : 2 * hh);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    R.c[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c[q] + coff));
+    R.s[q] = *reinterpret_cast<const uint16_t*>(s[q] + soff);
+  }
+}
+
+template <bool A_NVFP4>
+__device__ __forceinline__ void gemm_load(GemmLoad<A_NVFP4>& L, const GemmSrc& src,
+                                          const uint8_t* a_tile_base, int64_t K, int64_t k0) {
   const bool kfull = k0 + BK <= K;
-  const int hi = kfull ? 16 : 0;  // byte offset of the second code load (clamped)
   if constexpr (A_NVFP4) {
-    const uint8_t* c = static_cast<const uint8_t*>(g.a) + arow * (K / 2) + k0 / 2;
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(g.a_scales + arow * (K / 16) + k0 / 16);
-    L.a[0] = *reinterpret_cast<const u32x4*>(c);
-    L.a[1] = *reinterpret_cast<const u32x4*>(c + hi);
-    L.a_sc[0] = s[0];
-    L.a_sc[1] = s[kfull ? 1 : 0];
+    load_nvfp4_rows(L.a, src.ac, src.as, k0, kfull);
   } else {
-    // piece i of this thread: tile row t/8 + 32 i, piece t % 8
-    const int p = t & 7;
-    const int64_t k = k0 + 8 * p < K ? k0 + 8 * p : K - 8;
-    const uint16_t* src = static_cast<const uint16_t*>(g.a) + arow * K + k;
+    // pieces 4..7 of a partial step re-read pieces 0..3 (zeroed when stored)
+    const uint32_t back = (!kfull && (threadIdx.x & 4)) ? 64u : 0u;
+    const uint8_t* base = a_tile_base + 2 * k0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t dm = min(arow + 32 * i, g.M - 1) - arow;  // rows past M repeat the last
-      L.a[i] = *reinterpret_cast<const u32x4*>(src + dm * K);
-    }
+    for (int i = 0; i < 8; ++i)
+      L.a[i] = *reinterpret_cast<const u32x4*>(base + (src.a_off[i] - back));
   }
-  const uint8_t* c = g.wc + wrow * (K / 2) + k0 / 2;
-  const uint16_t* s = reinterpret_cast<const uint16_t*>(g.ws + wrow * (K / 16) + k0 / 16);
-  L.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c));
-  L.w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c + hi));
-  L.w_sc[0] = s[0];
-  L.w_sc[1] = s[kfull ? 1 : 0];
+  load_nvfp4_rows(L.w, src.wc, src.ws, k0, kfull);
 }
 
-// Pieces 2q, 2q+1 (elements 16q .. 16q+15, one NVFP4 block) of one row ->
-// exact bf16, written to the row's swizzled pieces.  A block at or past `kval`
-// (the valid elements of the step, 0..64, a multiple of 32) gets scale 0: its
-// codes were read from a clamped address inside the row and are finite, so it
-// is written as zeros.
-__device__ __forceinline__ void store_nvfp4_pieces(uint16_t* tile, int row, const u32x4 (&c)[2],
-                                                   const uint32_t (&sc)[2], int q, int kval) {
-  const uint32_t sw = sc[q >> 1];
-  const float s_blk = (q & 1) ? e4m3_to_f32<1>(sw) : e4m3_to_f32<0>(sw);
-  const float s = 16 * q < kval ? s_blk : 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = 2 * q + h;
-    *reinterpret_cast<u32x4*>(tile + swz(row, p)) = dequant8_bf16(c[p >> 2][p & 3], s);
-  }
+// Piece j (0..3) of this thread's half of NVFP4 tile row t/2 + 128 q -> 8
+// exact bf16 values.  A block at or past `kval` (the valid elements of the
+// step, 0..64, a multiple of 32) gets scale 0; its codes are finite, so it is
+// written as zeros.
+__device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const Nvfp4Rows& R,
+                                                  int q, int j, int kval) {
+  const int p = 4 * (threadIdx.x & 1) + j;
+  const float s_blk = (j >> 1) ? e4m3_to_f32<1>(R.s[q]) : e4m3_to_f32<0>(R.s[q]);
+  const float s = 16 * (p >> 1) < kval ? s_blk : 0.f;
+  lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
 }
 
-// Part q (of 4) of writing a loaded set to LDS.
+// Piece c (0..15) of writing a loaded set to LDS buffer `buf`: weight pieces
+// for c < 8, activation pieces for c >= 8.
 template <bool A_NVFP4>
-__device__ __forceinline__ void gemm_store_part(const GemmLoad<A_NVFP4>& L, uint16_t* a_tile,
-                                                uint16_t* b_tile, int q, int kval) {
-  const int t = threadIdx.x;
-  if constexpr (A_NVFP4) {
-    store_nvfp4_pieces(a_tile, t, L.a, L.a_sc, q, kval);
+__device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
+                                                 const GemmLoad<A_NVFP4>& L, int c, int kval) {
+  if (c < 8) {
+    const int q = c >> 2, j = c & 3;
+    store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
+  } else if constexpr (A_NVFP4) {
+    const int q = (c - 8) >> 2, j = (c - 8) & 3;
+    store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
   } else {
-    const int p = t & 7;
-    const bool live = 8 * p < kval;
+    const int i = c - 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * q + h;
-      *reinterpret_cast<u32x4*>(a_tile + swz((t >> 3) + 32 * i, p)) = live ? L.a[i] : z;
-    }
+    lds_ref<u32x4>(lds, o.wr_a[i & 1] + buf * kTileBytes + i * 4096) =
+        8 * (threadIdx.x & 7) < kval ? L.a[i] : z;
   }
-  store_nvfp4_pieces(b_tile, t, L.w, L.w_sc, q, kval);
 }
 
 struct Frags {
@@ -149,47 +211,41 @@ struct Frags {
 };
 
 // Operand layout (lane l): A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32],
-// i.e. both read row l%32 of their tile block, piece 2*kk + l/32.
-__device__ __forceinline__ void read_frags(Frags& f, const uint16_t* a_tile,
-                                           const uint16_t* b_tile, int wm, int wn, int kk) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.x[i] = *reinterpret_cast<const u32x4*>(a_tile + swz(wm * 128 + i * 32 + r, 2 * kk + h));
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.w[j] = *reinterpret_cast<const u32x4*>(b_tile + swz(wn * 128 + j * 32 + r, 2 * kk + h));
+// i.e. both read row l%32 of their tile block, piece 2*kk + l/32 (substep kk).
+__device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
+                                          int kk, int i) {
+  const int kq = kk ^ (2 * (i & 1));
+  f.x[i] = lds_ref<const u32x4>(lds, o.rd_x[kq] + buf * kTileBytes + i * 4096);
+  f.w[i] = lds_ref<const u32x4>(lds, o.rd_w[kq] + buf * kTileBytes + i * 4096);
 }
 
-__device__ __forceinline__ void mfma_block(f32x16 (&acc)[4][4], const Frags& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16_bf16(f.w[j], f.x[i], acc[i][j]);
-}
-
-// One 64-element step on LDS buffer `cur` while set L is written to buffer
-// `nxt`.
+// One 64-element step on LDS buffer `cur` while set L is decoded into buffer
+// `nxt` (see the pipeline description above).
 template <bool A_NVFP4>
-__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], const uint16_t* cur, uint16_t* nxt,
-                                          const GemmLoad<A_NVFP4>& L, int kval, int wm, int wn) {
-  Frags f0, f1;
-  read_frags(f0, cur, cur + kTileElems, wm, wn, 0);
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], char* lds, const LdsOffsets& o,
+                                          uint32_t cur, uint32_t nxt, const GemmLoad<A_NVFP4>& L,
+                                          int kval) {
+  Frags f[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; kk += 2) {
-    read_frags(f1, cur, cur + kTileElems, wm, wn, kk + 1);
-    gemm_store_part<A_NVFP4>(L, nxt, nxt + kTileElems, kk, kval);
-    mfma_block(acc, f0);
-    if (kk + 2 < 4) read_frags(f0, cur, cur + kTileElems, wm, wn, kk + 2);
-    gemm_store_part<A_NVFP4>(L, nxt, nxt + kTileElems, kk + 1, kval);
-    mfma_block(acc, f1);
+  for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, cur, 0, i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kk < 3) read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
+      gemm_store_piece<A_NVFP4>(lds, o, nxt, L, 4 * kk + i, kval);
+      const Frags& fc = f[kk & 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
 template <bool A_NVFP4>
 __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
-  extern __shared__ uint16_t lds[];  // [2 buffers][A tile, B tile]
+  extern __shared__ char lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -216,12 +272,29 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   const int64_t K = g.K;
   const int steps = (int)((K + BK - 1) / BK);
   const int steps2 = (steps + 1) & ~1;  // the loop runs step pairs; a padding step adds zeros
-  // rows this thread loads: activation row (NVFP4: m0 + t; bf16: m0 + t/8, + 32 i)
-  // and weight row `wrow` (into row t of the B tile)
   const int t = threadIdx.x;
-  const int64_t arow = min(m0 + (A_NVFP4 ? t : (t >> 3)), g.M - 1);
-  const int64_t n = min(n0 + (int64_t)t, g.N - 1);
-  const int64_t wrow = g.row_idx ? (int64_t)g.row_idx[n] : n;
+
+  // sources (rows past M or N are clamped to the last one; never stored)
+  GemmSrc src;
+  const uint8_t* a_tile_base = static_cast<const uint8_t*>(g.a) + (A_NVFP4 ? 0 : m0 * K * 2);
+  const int hh = t & 1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t n = min(n0 + (t >> 1) + 128 * q, g.N - 1);
+    const int64_t wr = g.row_idx ? (int64_t)g.row_idx[n] : n;
+    src.wc[q] = g.wc + wr * (K / 2) + 16 * hh;
+    src.ws[q] = g.ws + wr * (K / 16) + 2 * hh;
+    const int64_t ar = min(m0 + (t >> 1) + 128 * q, g.M - 1);
+    src.ac[q] = static_cast<const uint8_t*>(g.a) + ar * (K / 2) + 16 * hh;
+    src.as[q] = g.a_scales + ar * (K / 16) + 2 * hh;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t dm = min(m0 + (t >> 3) + 32 * i, g.M - 1) - m0;
+    src.a_off[i] = (uint32_t)((dm * K + 8 * (t & 7)) * 2);
+  }
+  const LdsOffsets o = lds_offsets(wm, wn);
+
   // loads past the last step re-read it (their LDS copy is never used or is
   // zeroed through kval)
   auto kstep = [&](int s) -> int64_t { return (int64_t)(s < steps ? s : steps - 1) * BK; };
@@ -231,26 +304,23 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   };
 
   GemmLoad<A_NVFP4> L0, L1;
-  gemm_load<A_NVFP4>(L0, g, arow, wrow, kstep(0));
-  gemm_load<A_NVFP4>(L1, g, arow, wrow, kstep(1));
+  gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(0));
+  gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gemm_store_part<A_NVFP4>(L0, lds, lds + kTileElems, q, kval(0));
+  for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
   __syncthreads();
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
   // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
-  // written during the last step is not read.
-  uint16_t* b0 = lds;
-  uint16_t* b1 = lds + 2 * kTileElems;
-  // (the scheduling barriers keep each step's global loads at its start, a
-  // whole step ahead of their use)
+  // written during the last step is not read.  The scheduling barriers keep
+  // each step's global loads at its start, a whole step ahead of their use.
   for (int s = 0; s < steps2; s += 2) {
-    gemm_load<A_NVFP4>(L0, g, arow, wrow, kstep(s + 2));
+    gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, b0, b1, L1, kval(s + 1), wm, wn);
+    gemm_step<A_NVFP4>(acc, lds, o, 0, 1, L1, kval(s + 1));
     __syncthreads();
-    gemm_load<A_NVFP4>(L1, g, arow, wrow, kstep(s + 3));
+    gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, b1, b0, L0, kval(s + 2), wm, wn);
+    gemm_step<A_NVFP4>(acc, lds, o, 1, 0, L0, kval(s + 2));
     __syncthreads();
   }
 
@@ -267,16 +337,16 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * h;
-        const int64_t o = row * g.N + col;
+        const int64_t off = row * g.N + col;
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
         const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
         if (vec && col + 3 < g.N) {
           if (g.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + o) = f32x4{v0, v1, v2, v3};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + off) = f32x4{v0, v1, v2, v3};
           } else {
             const u32x2 pk = {(uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16),
                               (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16)};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + o) = pk;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = pk;
           }
         } else {
           const float v[4] = {v0, v1, v2, v3};
@@ -284,9 +354,9 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
           for (int e = 0; e < 4; ++e) {
             if (col + e >= g.N) break;
             if (g.out_f32)
-              static_cast<float*>(g.out)[o + e] = v[e];
+              static_cast<float*>(g.out)[off + e] = v[e];
             else
-              static_cast<uint16_t*>(g.out)[o + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+              static_cast<uint16_t*>(g.out)[off + e] = (uint16_t)f32_to_bf16_bits(v[e]);
           }
         }
       }
@@ -299,6 +369,8 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
                 bool out_f32, void* out, hipStream_t stream) {
+  // activation offsets inside a 256-row tile are 32-bit byte offsets
+  if (K > ((int64_t)1 << 22)) return -1;
   GemmArgs g;
   g.a = a;
   g.a_scales = a_scales;
@@ -314,11 +386,10 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
   g.tiles_n = (int)((n_out + BN - 1) / BN);
   const int total = g.tiles_m * g.tiles_n;
   const int grid = ((total + 7) / 8) * 8;
-  const size_t lds = 2 * 2 * (size_t)kTileElems * sizeof(uint16_t);
   if (a_nvfp4)
-    hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(kGemmThreads), lds, stream, g);
+    hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, g);
   else
-    hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(kGemmThreads), lds, stream, g);
+    hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
