@@ -80,14 +80,12 @@ __device__ __forceinline__ T& lds_ref(char* lds, uint32_t off) {
 // g = h ^ f(r): fragment (substep kk, block i) of the wave's activation rows
 // wm*128 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
 // it is rd_x[kk ^ 2(i&1)] + 32 KB * buffer + 4096 i (likewise rd_w for the
-// weight rows wn*128 + ...).  A bf16 activation write of piece i (row t/8 +
-// 32 i, piece t % 8) is wr_a[i & 1] + 32 KB * buffer + 4096 i; an NVFP4 row
+// weight rows wn*128 + ...).  An NVFP4 row
 // write (row t/2 + 128 q, piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j]
 // (NVFP4 activations) + 32 KB * buffer + 16384 q.  (Immediate offsets of LDS
 // instructions stop at 64 KB, so the B-tile base is part of the registers.)
 struct LdsOffsets {
   uint32_t rd_x[4], rd_w[4];
-  uint32_t wr_a[2];
   uint32_t wr_w[4], wr_na[4];
 };
 
@@ -100,9 +98,6 @@ __device__ __forceinline__ LdsOffsets lds_offsets(int wm, int wn) {
     o.rd_x[kk] = (wm * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
     o.rd_w[kk] = kBOffset + (wn * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
   }
-  const uint32_t pa = ((t & 7) ^ ((t >> 3) & 7) ^ (t >> 6)) & 7u;
-  o.wr_a[0] = (t >> 3) * 128 + (pa << 4);
-  o.wr_a[1] = (t >> 3) * 128 + ((pa ^ 4u) << 4);
   const uint32_t fw = ((t >> 1) ^ (t >> 4)) & 7u, hh = t & 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -124,8 +119,7 @@ template <bool A_NVFP4>
 struct GemmLoad;
 template <>
 struct GemmLoad<false> {
-  u32x4 a[8];  // bf16 activations: piece t % 8 of tile rows t/8 + 32 i
-  Nvfp4Rows w;
+  Nvfp4Rows w;  // bf16 activations go to LDS directly (dma_a_tile)
 };
 template <>
 struct GemmLoad<true> {
@@ -134,10 +128,11 @@ struct GemmLoad<true> {
 };
 
 // Where a thread loads from: bf16 activations as byte offsets (32-bit) from
-// the tile's first row; NVFP4 rows as pointers to this lane's half of rows
-// t/2 and 128 + t/2 at k = 0.
+// the tile's first row at k = 0 (see dma_a_tile); NVFP4 rows as pointers to
+// this lane's half of rows t/2 and 128 + t/2 at k = 0.
 struct GemmSrc {
   uint32_t a_off[8];
+  uint32_t a_back[2];
   const uint8_t* ac[2];
   const uint8_t* as[2];
   const uint8_t* wc[2];
@@ -152,7 +147,7 @@ __device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* con
   const int64_t soff = k0 / 16 - (kfull ? 0 : 2 * hh);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    R.c[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c[q] + coff));
+    R.c[q] = *reinterpret_cast<const u32x4*>(c[q] + coff);
     R.s[q] = *reinterpret_cast<const uint16_t*>(s[q] + soff);
   }
 }
@@ -161,17 +156,27 @@ template <bool A_NVFP4>
 __device__ __forceinline__ void gemm_load(GemmLoad<A_NVFP4>& L, const GemmSrc& src,
                                           const uint8_t* a_tile_base, int64_t K, int64_t k0) {
   const bool kfull = k0 + BK <= K;
-  if constexpr (A_NVFP4) {
-    load_nvfp4_rows(L.a, src.ac, src.as, k0, kfull);
-  } else {
-    // pieces 4..7 of a partial step re-read pieces 0..3 (zeroed when stored)
-    const uint32_t back = (!kfull && (threadIdx.x & 4)) ? 64u : 0u;
-    const uint8_t* base = a_tile_base + 2 * k0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      L.a[i] = *reinterpret_cast<const u32x4*>(base + (src.a_off[i] - back));
-  }
+  if constexpr (A_NVFP4) load_nvfp4_rows(L.a, src.ac, src.as, k0, kfull);
   load_nvfp4_rows(L.w, src.wc, src.ws, k0, kfull);
+}
+
+// bf16 activation tile of the step at k0 -> LDS A buffer at `dst`, straight
+// from global memory (global_load_lds_dwordx4: lane l of a load lands at the
+// wave's LDS base + 16 l).  Wave w fills rows 64 w .. 64 w + 63, eight rows
+// (1 KB of LDS) per load; lane l takes row 8 i + l/8 of its band and physical
+// piece l % 8, i.e. logical piece (l % 8) ^ f(row) = (l % 8) ^ (l / 8) ^ i.
+// On a partial last step (K % 64 == 32) logical pieces 4..7 re-read pieces
+// 0..3: those k have zero weights, so the products vanish.
+__device__ __forceinline__ void dma_a_tile(char* dst, const GemmSrc& src,
+                                           const uint8_t* a_tile_base, int64_t k0, bool kfull) {
+  const uint8_t* base = a_tile_base + 2 * k0;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t keep = kfull ? 0u : ~0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint8_t* gp = base + (src.a_off[i] - (src.a_back[(i >> 2) & 1] & keep));
+    __builtin_amdgcn_global_load_lds(gp, dst + (64 * wave + 8 * i) * 128, 16, 0, 0);
+  }
 }
 
 // Piece j (0..3) of this thread's half of NVFP4 tile row t/2 + 128 q -> 8
@@ -186,22 +191,21 @@ __device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const
   lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
 }
 
-// Piece c (0..15) of writing a loaded set to LDS buffer `buf`: weight pieces
-// for c < 8, activation pieces for c >= 8.
+// Chunk c (0..15) of writing a loaded set to LDS buffer `buf`.  NVFP4
+// activations: weight pieces in chunks 0..7, activation pieces in 8..15; bf16
+// activations (copied by dma_a_tile): one weight piece in every even chunk.
 template <bool A_NVFP4>
 __device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
                                                  const GemmLoad<A_NVFP4>& L, int c, int kval) {
-  if (c < 8) {
-    const int q = c >> 2, j = c & 3;
+  if constexpr (A_NVFP4) {
+    const int q = (c & 7) >> 2, j = c & 3;
+    if (c < 8)
+      store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
+    else
+      store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
+  } else if ((c & 1) == 0) {
+    const int q = c >> 3, j = (c >> 1) & 3;
     store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
-  } else if constexpr (A_NVFP4) {
-    const int q = (c - 8) >> 2, j = (c - 8) & 3;
-    store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
-  } else {
-    const int i = c - 8;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    lds_ref<u32x4>(lds, o.wr_a[i & 1] + buf * kTileBytes + i * 4096) =
-        8 * (threadIdx.x & 7) < kval ? L.a[i] : z;
   }
 }
 
@@ -288,10 +292,17 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
     src.ac[q] = static_cast<const uint8_t*>(g.a) + ar * (K / 2) + 16 * hh;
     src.as[q] = g.a_scales + ar * (K / 16) + 2 * hh;
   }
+  {
+    const int lw = t & 63, band = 64 * (t >> 6);
+    const uint32_t lp = (uint32_t)((lw & 7) ^ (lw >> 3));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t dm = min(m0 + (t >> 3) + 32 * i, g.M - 1) - m0;
-    src.a_off[i] = (uint32_t)((dm * K + 8 * (t & 7)) * 2);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t dm = min(m0 + band + 8 * i + (lw >> 3), g.M - 1) - m0;
+      src.a_off[i] = (uint32_t)((dm * K + 8 * ((lp ^ i) & 7)) * 2);
+    }
+    // partial step: logical pieces 4..7 step back 32 elements (bit 2 of lp ^ i)
+    src.a_back[0] = (lp & 4) ? 64u : 0u;
+    src.a_back[1] = (lp & 4) ? 0u : 64u;
   }
   const LdsOffsets o = lds_offsets(wm, wn);
 
@@ -303,24 +314,41 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
     return v <= 0 ? 0 : (v >= BK ? BK : (int)v);
   };
 
+  // bf16 activations: the step's tile is copied into the next buffer during
+  // the step before; each wave waits for its own copies (they are the loads
+  // issued before the step's 4 weight loads) before the workgroup barrier.
+  constexpr int kWaitDma = 0x0F74;  // s_waitcnt vmcnt(4), no expcnt/lgkmcnt wait
+  auto dma = [&](int s, uint32_t buf) {
+    if constexpr (!A_NVFP4)
+      dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
+  };
+
   GemmLoad<A_NVFP4> L0, L1;
+  dma(0, 0);
   gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(0));
   gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
   for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
   // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
   // written during the last step is not read.  The scheduling barriers keep
-  // each step's global loads at its start, a whole step ahead of their use.
+  // each step's global loads at its start, ahead of their use.
   for (int s = 0; s < steps2; s += 2) {
+    dma(s + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
     gemm_step<A_NVFP4>(acc, lds, o, 0, 1, L1, kval(s + 1));
+    if constexpr (!A_NVFP4) __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
+    dma(s + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
     gemm_step<A_NVFP4>(acc, lds, o, 1, 0, L0, kval(s + 2));
+    if constexpr (!A_NVFP4) __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
   }
 
