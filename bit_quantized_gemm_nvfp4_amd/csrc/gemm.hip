@@ -191,22 +191,29 @@ __device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const
   lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
 }
 
-// Chunk c (0..15) of writing a loaded set to LDS buffer `buf`.  NVFP4
-// activations: weight pieces in chunks 0..7, activation pieces in 8..15; bf16
-// activations (copied by dma_a_tile): one weight piece in every even chunk.
+// Piece c of writing a loaded set to LDS buffer `buf`: weight pieces 0..7,
+// then (NVFP4 activations only) activation pieces 8..15.
 template <bool A_NVFP4>
 __device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
                                                  const GemmLoad<A_NVFP4>& L, int c, int kval) {
-  if constexpr (A_NVFP4) {
-    const int q = (c & 7) >> 2, j = c & 3;
-    if (c < 8)
-      store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
-    else
-      store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
-  } else if ((c & 1) == 0) {
-    const int q = c >> 3, j = (c >> 1) & 3;
+  const int q = (c & 7) >> 2, j = c & 3;
+  if (c < 8) {
     store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
+  } else if constexpr (A_NVFP4) {
+    store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
   }
+}
+
+// Workgroup barrier for LDS data: this wave's LDS writes are complete (the
+// LDS-only fences wait for them and nothing else), and with kDmaWait its
+// global->LDS copies too (s_waitcnt vmcnt(0): the copies and the weight loads
+// issued after them); other global loads are not waited for.
+template <bool kDmaWait>
+__device__ __forceinline__ void lds_barrier() {
+  if constexpr (kDmaWait) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 struct Frags {
@@ -224,21 +231,30 @@ __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets&
 }
 
 // One 64-element step on LDS buffer `cur` while set L is decoded into buffer
-// `nxt` (see the pipeline description above).
+// `nxt`.  On entry f[0] holds the step's substep-0 fragments; substeps 0..2
+// read the fragments of the next substep and write the pieces of the next
+// tile; then the workgroup barrier publishes `nxt`, and substep 3 reads the
+// next step's substep-0 fragments from it into f[0] while its MFMAs run, so no
+// fragment read is left exposed behind the barrier.
 template <bool A_NVFP4>
-__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], char* lds, const LdsOffsets& o,
-                                          uint32_t cur, uint32_t nxt, const GemmLoad<A_NVFP4>& L,
-                                          int kval) {
-  Frags f[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, cur, 0, i);
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], char* lds,
+                                          const LdsOffsets& o, uint32_t cur, uint32_t nxt,
+                                          const GemmLoad<A_NVFP4>& L, int kval) {
+  constexpr int kPieces = A_NVFP4 ? 16 : 8;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
+    if (kk == 3) lds_barrier<!A_NVFP4>();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (kk < 3) read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
-      gemm_store_piece<A_NVFP4>(lds, o, nxt, L, 4 * kk + i, kval);
+      if (kk < 3)
+        read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
+      else
+        read_frag(f[0], lds, o, nxt, 0, i);
+      const int c = 4 * kk + i;  // chunk 0..11 carries pieces c and c + 12
+      if (kk < 3) {
+        if (c < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c, kval);
+        if (c + 12 < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c + 12, kval);
+      }
       const Frags& fc = f[kk & 1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
@@ -315,22 +331,23 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   };
 
   // bf16 activations: the step's tile is copied into the next buffer during
-  // the step before; each wave waits for its own copies (they are the loads
-  // issued before the step's 4 weight loads) before the workgroup barrier.
-  constexpr int kWaitDma = 0x0F74;  // s_waitcnt vmcnt(4), no expcnt/lgkmcnt wait
+  // the step before; each wave waits for its own copies before the barrier
+  // that publishes the buffer.
   auto dma = [&](int s, uint32_t buf) {
     if constexpr (!A_NVFP4)
       dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
   };
 
   GemmLoad<A_NVFP4> L0, L1;
+  Frags f[2];
   dma(0, 0);
   gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(0));
   gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
   for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier<!A_NVFP4>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, 0, 0, i);
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
   // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
   // written during the last step is not read.  The scheduling barriers keep
@@ -340,16 +357,12 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, lds, o, 0, 1, L1, kval(s + 1));
-    if constexpr (!A_NVFP4) __builtin_amdgcn_s_waitcnt(kWaitDma);
-    __syncthreads();
+    gemm_step<A_NVFP4>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
     dma(s + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, lds, o, 1, 0, L0, kval(s + 2));
-    if constexpr (!A_NVFP4) __builtin_amdgcn_s_waitcnt(kWaitDma);
-    __syncthreads();
+    gemm_step<A_NVFP4>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
   }
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
