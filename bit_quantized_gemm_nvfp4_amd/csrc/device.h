@@ -88,4 +88,19 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Workgroup barrier that publishes LDS data.  The wave first waits until at
+// most kVm of its vector-memory operations are outstanding (kVm >= 0; its
+// global->LDS copies must be older than those kVm), then for its own LDS
+// accesses (LDS-only release fence), then meets the other waves.  Unlike
+// __syncthreads() it leaves the other global loads in flight.
+template <int kVm>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(kVm < 64, "vmcnt has 6 bits");
+  if constexpr (kVm >= 0)  // s_waitcnt vmcnt(kVm) expcnt(7) lgkmcnt(15)
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace nvfp4

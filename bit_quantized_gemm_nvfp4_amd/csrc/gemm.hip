@@ -204,18 +204,6 @@ __device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o,
   }
 }
 
-// Workgroup barrier for LDS data: this wave's LDS writes are complete (the
-// LDS-only fences wait for them and nothing else), and with kDmaWait its
-// global->LDS copies too (s_waitcnt vmcnt(0): the copies and the weight loads
-// issued after them); other global loads are not waited for.
-template <bool kDmaWait>
-__device__ __forceinline__ void lds_barrier() {
-  if constexpr (kDmaWait) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 struct Frags {
   u32x4 w[4];  // weight rows (MFMA A operand), 4 blocks of 32
   u32x4 x[4];  // activation rows (MFMA B operand), 4 blocks of 32
@@ -243,7 +231,7 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], ch
   constexpr int kPieces = A_NVFP4 ? 16 : 8;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk == 3) lds_barrier<!A_NVFP4>();
+    if (kk == 3) lds_barrier<A_NVFP4 ? -1 : 0>();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (kk < 3)
@@ -345,7 +333,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
   for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
-  lds_barrier<!A_NVFP4>();
+  lds_barrier<A_NVFP4 ? -1 : 0>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, 0, 0, i);
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
