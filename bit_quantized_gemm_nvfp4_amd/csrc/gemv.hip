@@ -221,7 +221,9 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   p.small = M <= small_max;
   p.mt = p.small ? (int)((M + 3) / 4) : (M <= 16 ? 1 : 2);
   p.tr = 2;
-  p.nw = 4;
+  // 16x16 path: wide workgroups (8 waves share one activation window) when
+  // there are rows enough to fill the chip with them; 4 waves otherwise
+  p.nw = (!p.small && n_out >= 32768) ? 8 : 4;
   int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
   // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
   // the waves per workgroup and the LDS budget of the staged activations.

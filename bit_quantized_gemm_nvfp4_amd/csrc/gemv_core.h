@@ -98,27 +98,36 @@ __device__ __forceinline__ void load_wstep(WStep<TR>& b, const uint8_t* const (&
 }
 
 // One step: A operands from LDS (xl[mt]: this lane's activation row in LDS at
-// the step's element 64q), B operands decoded from the codes.
+// the step's element 64q), B operands decoded from the codes.  The A operands
+// are read one 8-element chunk at a time, one chunk ahead of their MFMAs, so
+// only two chunks per m-tile are live (fewer registers, more waves per SIMD).
 template <int MT, int TR>
 __device__ __forceinline__ void compute_wstep(f32x4 (&acc)[TR][MT], const WStep<TR>& b,
                                               const uint16_t* const (&xl)[MT]) {
-  u32x4 a[MT][8];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a[mt][j] = *reinterpret_cast<const u32x4*>(xl[mt] + 8 * j);
+  float s[TR][4];
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
-    float s[4];
-    s[0] = e4m3_to_f32<0>(b.sc[t]);
-    s[1] = e4m3_to_f32<1>(b.sc[t]);
-    s[2] = e4m3_to_f32<2>(b.sc[t]);
-    s[3] = e4m3_to_f32<3>(b.sc[t]);
+    s[t][0] = e4m3_to_f32<0>(b.sc[t]);
+    s[t][1] = e4m3_to_f32<1>(b.sc[t]);
+    s[t][2] = e4m3_to_f32<2>(b.sc[t]);
+    s[t][3] = e4m3_to_f32<3>(b.sc[t]);
+  }
+  u32x4 a[2][MT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 w = dequant8_bf16(b.c[t][j >> 2][j & 3], s[j >> 1]);
+  for (int mt = 0; mt < MT; ++mt) a[0][mt] = *reinterpret_cast<const u32x4*>(xl[mt]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma_16x16x32_bf16(a[mt][j], w, acc[t][mt]);
+  for (int j = 0; j < 8; ++j) {
+    if (j + 1 < 8) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        a[(j + 1) & 1][mt] = *reinterpret_cast<const u32x4*>(xl[mt] + 8 * (j + 1));
+    }
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      const u32x4 w = dequant8_bf16(b.c[t][j >> 2][j & 3], s[t][j >> 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[t][mt] = mfma_16x16x32_bf16(a[j & 1][mt], w, acc[t][mt]);
     }
   }
 }
