@@ -210,7 +210,7 @@ int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32
     return NVFP4_ERROR_INVALID_VALUE;
   const size_t need = moe_grouped_workspace_bytes(R, E, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
-  return launched(launch_grouped_gemm(a, K, gather_idx, expert_offsets, E, R, N, w_codes,
+  return launched(launch_grouped_gemm(a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
                                       w_scales, row_scale, epilogue == NVFP4_EPI_SWIGLU, out,
                                       workspace, as_stream(stream)));
 }

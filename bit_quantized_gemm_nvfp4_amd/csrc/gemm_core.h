@@ -1,0 +1,332 @@
+// gemm_core.h -- the 256 x 256 MFMA tile of the NVFP4 GEMM kernels (internal):
+// the large-M linear layer (gemm.hip) and the grouped expert GEMM (moe.hip).
+//
+// A workgroup of 4 waves computes a 256 x 256 tile of y = a . W^T; each wave a
+// 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (accumulators
+// in AGPRs).  K advances 64 elements per step through a double buffer in LDS:
+//   A tile  [256 rows][64] bf16 (32 KB): bf16 activations copied global->LDS
+//           (global_load_lds_dwordx4), or NVFP4 activations decoded exactly;
+//   B tile  [256 cols][64] bf16 (32 KB): NVFP4 weight rows decoded exactly to
+//           bf16 as they are written (once per tile, not per use).
+// LDS layout: [A buffer 0][A buffer 1][B buffer 0][B buffer 1], so every LDS
+// access is a per-lane base register plus an immediate offset.  Rows are eight
+// 16-byte pieces, piece c of row r at c ^ f(r), f(r) = (r ^ (r >> 3)) & 7: the
+// 16 consecutive rows of an MFMA operand read or of a tile write fall on
+// distinct banks.
+//
+// Global loads: the activation tile is copied 8 rows x 128 bytes per load
+// instruction; NVFP4 rows are loaded cooperatively, two lanes per row (one
+// 16-byte half each), so a load instruction touches 32 cache lines and every
+// line is looked up once per step -- the line count per instruction, not
+// bandwidth, is what these loads cost.
+//
+// Pipeline: the weight (and NVFP4 activation) loads of step s+2 are issued at
+// the start of step s into one of two register sets, the bf16 activation copy
+// of step s+1 straight into the idle LDS buffer; the other register set (step
+// s+1) is decoded into the idle buffer while step s is computed.  A step is 16
+// chunks (substep kk = 0..3, accumulator row i = 0..3): chunk (kk, i) issues
+// the 4 MFMAs of row i, reads fragments x[i], w[i] of substep kk+1 and writes
+// pieces of the next tile; scheduling barriers keep that interleave.  One
+// LDS-only workgroup barrier per step, between substeps 2 and 3.
+//
+// The weight tile is the MFMA's A operand and the activation tile its B
+// operand, so an accumulator block holds y^T: lane l has output row l % 32 and
+// 4 consecutive output columns per register group (gemm_tile_acc).
+#pragma once
+
+#include "device.h"
+
+namespace nvfp4 {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kGemmThreads = 256;
+constexpr uint32_t kTileBytes = BM * BK * 2;  // one bf16 operand tile (32 KB)
+constexpr uint32_t kBOffset = 2 * kTileBytes;  // B buffers follow both A buffers
+constexpr uint32_t kLdsBytes = 4 * kTileBytes;
+
+
+__device__ __forceinline__ uint32_t swz_f(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
+
+template <typename T>
+__device__ __forceinline__ T& lds_ref(char* lds, uint32_t off) {
+  return *reinterpret_cast<T*>(lds + off);
+}
+
+// Per-lane LDS byte offsets.  With r = lane % 32, h = lane / 32 and
+// g = h ^ f(r): fragment (substep kk, block i) of the wave's activation rows
+// wm*128 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
+// it is rd_x[kk ^ 2(i&1)] + 32 KB * buffer + 4096 i (likewise rd_w for the
+// weight rows wn*128 + ...).  An NVFP4 row
+// write (row t/2 + 128 q, piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j]
+// (NVFP4 activations) + 32 KB * buffer + 16384 q.  (Immediate offsets of LDS
+// instructions stop at 64 KB, so the B-tile base is part of the registers.)
+struct LdsOffsets {
+  uint32_t rd_x[4], rd_w[4];
+  uint32_t wr_w[4], wr_na[4];
+};
+
+__device__ __forceinline__ LdsOffsets lds_offsets(int wm, int wn) {
+  LdsOffsets o;
+  const uint32_t t = threadIdx.x, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const uint32_t g = (h ^ swz_f(r)) & 7u;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    o.rd_x[kk] = (wm * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
+    o.rd_w[kk] = kBOffset + (wn * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
+  }
+  const uint32_t fw = ((t >> 1) ^ (t >> 4)) & 7u, hh = t & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o.wr_na[j] = (t >> 1) * 128 + (((4u * hh + j) ^ fw) << 4);
+    o.wr_w[j] = kBOffset + o.wr_na[j];
+  }
+  return o;
+}
+
+// A thread's share of one step's global loads, exactly as loaded.  Every load
+// is unconditional: on a partial last step (K % 64 == 32) the missing half is
+// re-read from inside the row and zeroed when the set is written to LDS, so no
+// wait for the loads is needed before then.
+struct Nvfp4Rows {
+  u32x4 c[2];     // codes of half (t & 1) of tile rows t/2 and 128 + t/2
+  uint32_t s[2];  // their two E4M3 scale bytes (one 16-bit load each)
+};
+template <bool A_NVFP4>
+struct GemmLoad;
+template <>
+struct GemmLoad<false> {
+  Nvfp4Rows w;  // bf16 activations go to LDS directly (dma_a_tile)
+};
+template <>
+struct GemmLoad<true> {
+  Nvfp4Rows a;
+  Nvfp4Rows w;
+};
+
+// Where a thread loads from: bf16 activations as byte offsets (32-bit) from a
+// base pointer at k = 0 (see dma_a_tile); NVFP4 rows as pointers to this
+// lane's half of rows t/2 and 128 + t/2 at k = 0 (gemm_src_nvfp4_row).
+struct GemmSrc {
+  uint32_t a_off[8];
+  uint32_t a_back[2];
+  const uint8_t* ac[2];
+  const uint8_t* as[2];
+  const uint8_t* wc[2];
+  const uint8_t* ws[2];
+};
+
+__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* const (&c)[2],
+                                                const uint8_t* const (&s)[2], int64_t k0,
+                                                bool kfull) {
+  const int hh = threadIdx.x & 1;
+  const int64_t coff = k0 / 2 - (kfull ? 0 : 16 * hh);
+  const int64_t soff = k0 / 16 - (kfull ? 0 : 2 * hh);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    R.c[q] = *reinterpret_cast<const u32x4*>(c[q] + coff);
+    R.s[q] = *reinterpret_cast<const uint16_t*>(s[q] + soff);
+  }
+}
+
+template <bool A_NVFP4>
+__device__ __forceinline__ void gemm_load(GemmLoad<A_NVFP4>& L, const GemmSrc& src,
+                                          const uint8_t* a_tile_base, int64_t K, int64_t k0) {
+  const bool kfull = k0 + BK <= K;
+  if constexpr (A_NVFP4) load_nvfp4_rows(L.a, src.ac, src.as, k0, kfull);
+  load_nvfp4_rows(L.w, src.wc, src.ws, k0, kfull);
+}
+
+// bf16 activation tile of the step at k0 -> LDS A buffer at `dst`, straight
+// from global memory (global_load_lds_dwordx4: lane l of a load lands at the
+// wave's LDS base + 16 l).  Wave w fills rows 64 w .. 64 w + 63, eight rows
+// (1 KB of LDS) per load; lane l takes row 8 i + l/8 of its band and physical
+// piece l % 8, i.e. logical piece (l % 8) ^ f(row) = (l % 8) ^ (l / 8) ^ i.
+// On a partial last step (K % 64 == 32) logical pieces 4..7 re-read pieces
+// 0..3: those k have zero weights, so the products vanish.
+__device__ __forceinline__ void dma_a_tile(char* dst, const GemmSrc& src,
+                                           const uint8_t* a_tile_base, int64_t k0, bool kfull) {
+  const uint8_t* base = a_tile_base + 2 * k0;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t keep = kfull ? 0u : ~0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint8_t* gp = base + (src.a_off[i] - (src.a_back[(i >> 2) & 1] & keep));
+    __builtin_amdgcn_global_load_lds(gp, dst + (64 * wave + 8 * i) * 128, 16, 0, 0);
+  }
+}
+
+// Piece j (0..3) of this thread's half of NVFP4 tile row t/2 + 128 q -> 8
+// exact bf16 values.  A block at or past `kval` (the valid elements of the
+// step, 0..64, a multiple of 32) gets scale 0; its codes are finite, so it is
+// written as zeros.
+__device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const Nvfp4Rows& R,
+                                                  int q, int j, int kval) {
+  const int p = 4 * (threadIdx.x & 1) + j;
+  const float s_blk = (j >> 1) ? e4m3_to_f32<1>(R.s[q]) : e4m3_to_f32<0>(R.s[q]);
+  const float s = 16 * (p >> 1) < kval ? s_blk : 0.f;
+  lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
+}
+
+// Piece c of writing a loaded set to LDS buffer `buf`: weight pieces 0..7,
+// then (NVFP4 activations only) activation pieces 8..15.
+template <bool A_NVFP4>
+__device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
+                                                 const GemmLoad<A_NVFP4>& L, int c, int kval) {
+  const int q = (c & 7) >> 2, j = c & 3;
+  if (c < 8) {
+    store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
+  } else if constexpr (A_NVFP4) {
+    store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
+  }
+}
+
+struct Frags {
+  u32x4 w[4];  // weight rows (MFMA A operand), 4 blocks of 32
+  u32x4 x[4];  // activation rows (MFMA B operand), 4 blocks of 32
+};
+
+// Operand layout (lane l): A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32],
+// i.e. both read row l%32 of their tile block, piece 2*kk + l/32 (substep kk).
+__device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
+                                          int kk, int i) {
+  const int kq = kk ^ (2 * (i & 1));
+  f.x[i] = lds_ref<const u32x4>(lds, o.rd_x[kq] + buf * kTileBytes + i * 4096);
+  f.w[i] = lds_ref<const u32x4>(lds, o.rd_w[kq] + buf * kTileBytes + i * 4096);
+}
+
+// One 64-element step on LDS buffer `cur` while set L is decoded into buffer
+// `nxt`.  On entry f[0] holds the step's substep-0 fragments; substeps 0..2
+// read the fragments of the next substep and write the pieces of the next
+// tile; then the workgroup barrier publishes `nxt`, and substep 3 reads the
+// next step's substep-0 fragments from it into f[0] while its MFMAs run, so no
+// fragment read is left exposed behind the barrier.
+template <bool A_NVFP4>
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], char* lds,
+                                          const LdsOffsets& o, uint32_t cur, uint32_t nxt,
+                                          const GemmLoad<A_NVFP4>& L, int kval) {
+  constexpr int kPieces = A_NVFP4 ? 16 : 8;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk == 3) lds_barrier<A_NVFP4 ? -1 : 0>();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kk < 3)
+        read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
+      else
+        read_frag(f[0], lds, o, nxt, 0, i);
+      const int c = 4 * kk + i;  // chunk 0..11 carries pieces c and c + 12
+      if (kk < 3) {
+        if (c < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c, kval);
+        if (c + 12 < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c + 12, kval);
+      }
+      const Frags& fc = f[kk & 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Sources of the tile's rows for this thread.  Activation rows: abs_row(t)
+// gives the global row (clamped to a valid one) of tile row t for t < 256;
+// bf16 offsets are relative to `a_base`.  Weight and NVFP4 activation rows:
+// the pointer to this lane's half of the row at k = 0.
+template <typename ARow>
+__device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_t K) {
+  const int t = threadIdx.x;
+  const int lw = t & 63, band = 64 * (t >> 6);
+  const uint32_t lp = (uint32_t)((lw & 7) ^ (lw >> 3));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = abs_row(band + 8 * i + (lw >> 3));
+    src.a_off[i] = (uint32_t)((r * K + 8 * ((lp ^ i) & 7)) * 2);
+  }
+  // partial step: logical pieces 4..7 step back 32 elements (bit 2 of lp ^ i)
+  src.a_back[0] = (lp & 4) ? 64u : 0u;
+  src.a_back[1] = (lp & 4) ? 0u : 64u;
+}
+
+__device__ __forceinline__ void gemm_src_nvfp4_row(const uint8_t*& c, const uint8_t*& s,
+                                                   const uint8_t* codes, const uint8_t* scales,
+                                                   int64_t row, int64_t K) {
+  const int hh = threadIdx.x & 1;
+  c = codes + row * (K / 2) + 16 * hh;
+  s = scales + row * (K / 16) + 2 * hh;
+}
+
+__device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+}
+
+// The whole K loop of one tile: acc += a_tile . w_tile^T.  `lds` is the
+// kLdsBytes of dynamic LDS; every thread of the workgroup calls it.
+template <bool A_NVFP4>
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, const GemmSrc& src,
+                                              const uint8_t* a_tile_base, int64_t K) {
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int steps = (int)((K + BK - 1) / BK);
+  const int steps2 = (steps + 1) & ~1;  // the loop runs step pairs; a padding step adds zeros
+  const LdsOffsets o = lds_offsets(wm, wn);
+
+  // loads past the last step re-read it (their LDS copy is never used or is
+  // zeroed through kval)
+  auto kstep = [&](int s) -> int64_t { return (int64_t)(s < steps ? s : steps - 1) * BK; };
+  auto kval = [&](int s) -> int {
+    const int64_t v = K - (int64_t)s * BK;
+    return v <= 0 ? 0 : (v >= BK ? BK : (int)v);
+  };
+
+  // bf16 activations: the step's tile is copied into the next buffer during
+  // the step before; each wave waits for its own copies before the barrier
+  // that publishes the buffer.
+  auto dma = [&](int s, uint32_t buf) {
+    if constexpr (!A_NVFP4)
+      dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
+  };
+
+  GemmLoad<A_NVFP4> L0, L1;
+  Frags f[2];
+  dma(0, 0);
+  gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(0));
+  gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
+#pragma unroll
+  for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
+  lds_barrier<A_NVFP4 ? -1 : 0>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, 0, 0, i);
+  // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
+  // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
+  // written during the last step is not read.  The scheduling barriers keep
+  // each step's global loads at its start, ahead of their use.
+  for (int s = 0; s < steps2; s += 2) {
+    dma(s + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(s + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_step<A_NVFP4>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
+    dma(s + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(s + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_step<A_NVFP4>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
+  }
+
+}
+
+// Output coordinates of accumulator register e of acc[i][j] in this lane:
+// tile row wm*128 + i*32 + l%32, tile column wn*128 + j*32 + 8*(e/4) +
+// 4*(l/32) + e%4 (registers 4q .. 4q+3 are 4 consecutive columns).
+__device__ __forceinline__ int gemm_tile_row(int i) {
+  return ((threadIdx.x >> 6) >> 1) * 128 + i * 32 + (threadIdx.x & 31);
+}
+__device__ __forceinline__ int gemm_tile_col(int j, int q) {
+  return ((threadIdx.x >> 6) & 1) * 128 + j * 32 + 8 * q + 4 * ((threadIdx.x & 63) >> 5);
+}
+
+}  // namespace nvfp4

@@ -6,8 +6,14 @@
 // is built from three device steps on one stream, with no host round trip:
 //   align    -- stable counting sort of (token, slot) assignments by expert;
 //   grouped  -- per-expert W4A16 GEMM over the gathered rows, with a SwiGLU
-//               (gate+up) or a per-row scale (gate weight) epilogue;
+//               (gate+up) or a per-row scale (gate weight) epilogue: a
+//               weight-streaming GEMV kernel (16 rows of one expert per
+//               workgroup) when experts get few rows, the 256 x 256 MFMA tile
+//               of gemm_core.h when they get many;
 //   combine  -- per-token sum of its slots' outputs.
+#include <stdlib.h>
+
+#include "gemm_core.h"
 #include "gemv_core.h"
 #include "moe.h"
 
@@ -108,14 +114,14 @@ struct GroupedArgs {
 };
 
 // Find (expert, chunk) of workgroup `bx` in the device-side schedule where
-// expert e owns ceil(rows_e / kGroupRows) consecutive chunks.  Wave-uniform.
-__device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx, int& e_out,
-                                           int& c_out) {
+// expert e owns ceil(rows_e / chunk_rows) consecutive chunks.  Wave-uniform.
+__device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx, int chunk_rows,
+                                           int& e_out, int& c_out) {
   const int lane = threadIdx.x & 63;
   int run = 0;
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;
-    const int ch = e < E ? (offsets[e + 1] - offsets[e] + kGroupRows - 1) / kGroupRows : 0;
+    const int ch = e < E ? (offsets[e + 1] - offsets[e] + chunk_rows - 1) / chunk_rows : 0;
     int inc = ch;  // inclusive prefix over the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -146,7 +152,7 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
   const int64_t K = g.K;
 
   int e, c;
-  if (!find_chunk(g.offsets, g.E, blockIdx.x, e, c)) return;  // uniform over the workgroup
+  if (!find_chunk(g.offsets, g.E, blockIdx.x, kGroupRows, e, c)) return;  // uniform
   const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * kGroupRows;
   const int64_t r1 = min((int64_t)g.offsets[e + 1], r0 + kGroupRows);
   const int rows = (int)(r1 - r0);
@@ -210,6 +216,119 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
   }
 }
 
+// ---- grouped MFMA GEMM (many rows per expert) ---------------------------------
+
+struct GroupedMfmaArgs {
+  const uint16_t* a;
+  const int32_t* gather;
+  const int32_t* offsets;
+  const uint8_t* wc;
+  const uint8_t* ws;
+  const float* row_scale;
+  uint16_t* out;
+  int64_t K;
+  int64_t N;
+  int E;
+  int swiglu;
+  int n_tiles;  // tiles per chunk: ceil(N / 256), or ceil(N/2 / 128) with SWIGLU
+  int total;    // upper bound of chunks * n_tiles
+};
+
+// One workgroup: one 256-row chunk of one expert's gathered rows against one
+// tile of that expert's weight rows.  Workgroups beyond the schedule (the grid
+// is sized for the worst case) return at once.  SWIGLU tiles hold, for 128
+// outputs o0 .. o0+127, gate rows o0 + h*64 + u and up rows N/2 + o0 + h*64 + u
+// (h = 0, 1; u < 64) at tile columns 128 h + u and 128 h + 64 + u: each gate
+// accumulator and its up partner sit in the same lane and register (blocks j
+// and j + 2 of the wave), so the epilogue needs no exchange.
+__global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g) {
+  extern __shared__ char lds[];
+  const int per_xcd = (g.total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);  // XCD-aware order
+  if (lin >= g.total) return;
+  const int chunk = lin / g.n_tiles, tn = lin - chunk * g.n_tiles;
+  int e, c;
+  if (!find_chunk(g.offsets, g.E, chunk, BM, e, c)) return;  // uniform over the workgroup
+  const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * BM;
+  const int rows = (int)(min((int64_t)g.offsets[e + 1], r0 + BM) - r0);
+  const int64_t K = g.K, N = g.N, half_n = N / 2;
+  const int t = threadIdx.x;
+
+  GemmSrc src;
+  const int32_t* gather = g.gather;
+  gemm_src_bf16(src, [&](int tr) {
+    const int64_t r = r0 + min(tr, rows - 1);  // rows past the chunk repeat its last row
+    return (int64_t)(gather ? gather[r] : r);
+  }, K);
+  const uint8_t* we_c = g.wc + (int64_t)e * N * (K / 2);
+  const uint8_t* we_s = g.ws + (int64_t)e * N * (K / 16);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int u = t >> 1;  // tile row u + 128 q
+    int64_t n;
+    if (g.swiglu) {
+      const int64_t o = min((int64_t)tn * 128 + q * 64 + (u & 63), half_n - 1);
+      n = u < 64 ? o : half_n + o;
+    } else {
+      n = min((int64_t)tn * BN + u + 128 * q, N - 1);
+    }
+    gemm_src_nvfp4_row(src.wc[q], src.ws[q], we_c, we_s, n, K);
+  }
+
+  f32x16 acc[4][4];
+  gemm_zero_acc(acc);
+  gemm_mainloop<false>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K);
+
+  const int wn = (t >> 6) & 1, h = (t & 63) >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = gemm_tile_row(i);
+    if (tr >= rows) continue;
+    const int64_t row = r0 + tr;
+    const float rs = g.row_scale ? g.row_scale[row] : 1.0f;
+    if (g.swiglu) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = (int64_t)tn * 128 + wn * 64 + j * 32 + 8 * q + 4 * h;
+          if (col >= half_n) continue;  // half_n % 16 == 0: the 4 columns are in or out
+          uint32_t pk[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            float v[2];
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const float hg = acc[i][j][4 * q + 2 * p + w], hu = acc[i][j + 2][4 * q + 2 * p + w];
+              v[w] = hg / (1.0f + expf(-hg)) * hu;
+              if (g.row_scale) v[w] *= rs;
+            }
+            pk[p] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+          }
+          *reinterpret_cast<u32x2*>(g.out + row * half_n + col) = u32x2{pk[0], pk[1]};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = (int64_t)tn * BN + gemm_tile_col(j, q);
+          if (col >= N) continue;  // N % 16 == 0
+          uint32_t pk[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            float v0 = acc[i][j][4 * q + 2 * p], v1 = acc[i][j][4 * q + 2 * p + 1];
+            if (g.row_scale) v0 *= rs, v1 *= rs;
+            pk[p] = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+          }
+          *reinterpret_cast<u32x2*>(g.out + row * N + col) = u32x2{pk[0], pk[1]};
+        }
+      }
+    }
+  }
+}
+
 // ---- combine --------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256) k_moe_combine(const uint16_t* __restrict__ y,
@@ -267,11 +386,36 @@ size_t moe_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
   return 0;
 }
 
-int launch_grouped_gemm(const uint16_t* a, int64_t K, const int32_t* gather,
+int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather,
                         const int32_t* offsets, int64_t E, int64_t R, int64_t N,
                         const uint8_t* wc, const uint8_t* ws, const float* row_scale,
                         bool swiglu, uint16_t* out, void* workspace, hipStream_t stream) {
   (void)workspace;
+  // MFMA tiles once experts average enough rows to fill them (tuning knob:
+  // NVFP4_GROUPED_MFMA_MIN_ROWS, the average rows per expert from which the
+  // MFMA kernel is used); its activation offsets are 32-bit.
+  int64_t min_avg = 32;
+  if (const char* env = getenv("NVFP4_GROUPED_MFMA_MIN_ROWS")) min_avg = atol(env);
+  if (R >= min_avg * E && a_rows * K * 2 < ((int64_t)1 << 32)) {
+    GroupedMfmaArgs m;
+    m.a = a;
+    m.gather = gather;
+    m.offsets = offsets;
+    m.wc = wc;
+    m.ws = ws;
+    m.row_scale = row_scale;
+    m.out = out;
+    m.K = K;
+    m.N = N;
+    m.E = (int)E;
+    m.swiglu = swiglu ? 1 : 0;
+    m.n_tiles = (int)(swiglu ? (N / 2 + 127) / 128 : (N + BN - 1) / BN);
+    const int64_t chunks = (R + BM - 1) / BM + E;  // upper bound
+    m.total = (int)(chunks * m.n_tiles);
+    const int grid = ((m.total + 7) / 8) * 8;
+    hipLaunchKernelGGL(k_grouped_mfma, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, m);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   GroupedArgs g;
   g.a = a;
   g.gather = gather;

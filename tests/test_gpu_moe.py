@@ -63,6 +63,38 @@ def test_grouped_gemm_matches_oracle(nv, orc, epi):
     assert ok, (rf, worst)
 
 
+@pytest.mark.parametrize("epi,gathered,scaled", [(0, True, True), (1, True, False), (1, False, True),
+                                                (0, False, False)])
+def test_grouped_mfma_matches_oracle(nv, orc, epi, gathered, scaled):
+    """The MFMA grouped kernel (forced for these sizes through
+    NVFP4_GROUPED_MFMA_MIN_ROWS): experts with 0 rows, 1 row, a partial
+    256-row chunk, exactly 256 rows and several chunks; N and N/2 not multiples
+    of the 256 / 128 output tile; K % 64 == 32 (a partial last K step)."""
+    import os
+    helpers.announce(f"moe grouped mfma epi={epi} gather={gathered} scale={scaled}")
+    rng = np.random.default_rng(50 + 2 * epi + gathered + 4 * scaled)
+    E, K, N = 7, 416, 352
+    counts = np.array([0, 1, 300, 256, 0, 600, 37])
+    R = int(counts.sum())
+    rows = R if not gathered else 129
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, rows, K)
+    w = workloads.nvfp4_weight(rng, E, N, K)
+    gather = rng.integers(0, rows, R).astype(np.int32) if gathered else None
+    rs = (rng.random(R) + 0.5).astype(np.float32) if scaled else None
+    os.environ["NVFP4_GROUPED_MFMA_MIN_ROWS"] = "1"
+    try:
+        y = nv.grouped_gemm(helpers.dev_bf16(a), None if gather is None else helpers.dev_i32(gather),
+                            helpers.dev_i32(off), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                            R, row_scale=None if rs is None else helpers.dev_f32(rs), epilogue=epi)
+    finally:
+        del os.environ["NVFP4_GROUPED_MFMA_MIN_ROWS"]
+    ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
+                           epilogue=epi)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+    assert ok, (rf, worst)
+
+
 def test_combine_matches_oracle(nv, orc):
     helpers.announce("moe combine")
     rng = np.random.default_rng(40)
