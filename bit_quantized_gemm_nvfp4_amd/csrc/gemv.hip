@@ -193,6 +193,14 @@ void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 15) / 16;
   const int64_t per_wg = (int64_t)nw * TR;
   dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
+  if constexpr (MT == 2 && TR <= 2) {
+    // 16 waves: plan_gemv asks for them only here (the window has one piece
+    // per thread and the kernel fits 128 registers)
+    if (nw == 16) {
+      hipLaunchKernelGGL((k_gemv<MT, TR, 16>), grid, dim3(1024), 0, stream, a);
+      return;
+    }
+  }
   if (nw == 8)
     hipLaunchKernelGGL((k_gemv<MT, TR, 8>), grid, dim3(512), 0, stream, a);
   else
@@ -232,7 +240,8 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
     const int n = sscanf(e, "%d,%d,%d", &tr, &nw, &kib);
     const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || (tr == 8 && p.mt == 1))
                                : (tr == 1 || tr == 2 || (tr == 4 && p.mt == 1));
-    const bool nw_ok = p.small ? (nw >= 1 && nw <= 8) : (nw == 4 || nw == 8);
+    const bool nw_ok = p.small ? (nw >= 1 && nw <= 8)
+                               : (nw == 4 || nw == 8 || (nw == 16 && p.mt == 2 && tr <= 2));
     if (n >= 2 && tr_ok && nw_ok) p.tr = tr, p.nw = nw;
     if (n == 3 && kib >= 8 && kib <= 160) lds_budget = (int64_t)kib * 1024;
   }
