@@ -6,7 +6,10 @@ decode-shaped W4A16 set -- M in {1, 8, 32} x (K, N) in {(5120, 17408),
 (17408, 5120), (5120, 248320)} plus the masked head (32,768 of the 248,320
 rows) -- 12 nvfp4_gemm calls.  One step runs all 12 calls once; `value` is the
 weight bytes the step streams (rows * K * 9/16 per call) divided by the step
-time, with every input resident in HBM before the timed region starts.
+time, with every input resident in HBM before the timed region starts.  The
+step is captured once as a HIP graph and replayed (as a serving engine replays
+its decode step); the same calls launched one by one give config.eager_GBs and
+the per-call event times of the roofline.
 
 Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies and
 the head in two copies; calls alternate copies and the masked head always
@@ -133,12 +136,12 @@ class Decode:
         vp = ctypes.c_void_p
         args = (nv.BF16, vp(x.data_ptr()), None, M, N, K, vp(wc.data_ptr()), vp(wsc.data_ptr()),
                 None if idx is None else vp(idx.data_ptr()), n_out, nv.BF16, vp(out.data_ptr()),
-                None if ws is None else vp(ws.data_ptr()), wsb,
-                vp(torch.cuda.current_stream().cuda_stream))
+                None if ws is None else vp(ws.data_ptr()), wsb)
         f = nv.lib().nvfp4_gemm
 
-        def fn(f=f, args=args):
-            rc = f(*args)
+        def fn(stream=None, f=f, args=args):
+            st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+            rc = f(*args, vp(st))
             if rc != 0:
                 raise RuntimeError(nv.lib().nvfp4_status_string(rc).decode())
 
@@ -146,6 +149,30 @@ class Decode:
 
     def step_bytes(self):
         return sum(weight_bytes(rows, K) for (_, _, K, rows, _) in self.calls)
+
+
+def time_decode_graph(dec, torch, steps, warmup):
+    """The step captured once as a HIP graph (how a serving engine replays a
+    decode step) and replayed: returns the wall time of `steps` replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in dec.calls:
+            c[4](side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for c in dec.calls:
+            c[4](side.cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def time_decode(dec, torch, steps, warmup):
@@ -306,11 +333,14 @@ def main():
     hd = (dev_u8, dev_bf16, dev_i32)
     log("generating decode workload")
     dec = Decode(nv, torch, hd)
-    log(f"timing {args.steps} steps x {len(dec.calls)} calls (warmup {args.warmup})")
-    wall, per_call = time_decode(dec, torch, args.steps, args.warmup)
+    log(f"timing {args.steps} steps x {len(dec.calls)} calls (warmup {args.warmup}): "
+        "eager with per-call events, then as a replayed graph")
+    wall_eager, per_call = time_decode(dec, torch, args.steps, args.warmup)
+    wall = time_decode_graph(dec, torch, args.steps, args.warmup)
     step_bytes = dec.step_bytes()
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes * args.steps / wall / 1e9
+    eager_value = step_bytes * args.steps / wall_eager / 1e9
 
     # roofline of the decode GEMV kernel: algorithmic weight bytes per launch over
     # the mean launch time, from HIP events on the launch stream
@@ -354,6 +384,8 @@ def main():
                          "(17408,5120),(5120,248320)} + masked head 32768/248320 rows"),
             "step_weight_bytes": int(step_bytes),
             "calls_per_step": len(per_call_us),
+            "step": "12 nvfp4_gemm calls captured as one HIP graph, replayed",
+            "eager_GBs": round(eager_value, 2),
         },
         "roofline": {
             "bound": "hbm",
