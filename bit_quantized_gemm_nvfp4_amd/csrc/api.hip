@@ -55,7 +55,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4) {
   g.mfma = M >= min_m;
   g.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
   g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs);
-  g.partial_bytes = g.mfma ? 0 : gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
+  g.partial_bytes = g.mfma ? gemm_workspace_bytes(M, n_out, K, kNumCUs)
+                           : gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
   g.a_dequant_bytes = (w4a4 && !g.mfma) ? (size_t)M * (size_t)K * 2 : 0;
   return g;
 }
@@ -134,8 +135,9 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
     if (log_enabled())
       fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: mfma 256x256\n",
               (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16");
+    void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
     return launched(launch_gemm(w4a4, a, a_scales, M, K, w_codes, w_scales, row_idx, n_out,
-                                out_dtype == NVFP4_FP32, out, st));
+                                out_dtype == NVFP4_FP32, out, partial, st));
   }
   const uint16_t* x = static_cast<const uint16_t*>(a);
   if (w4a4) {

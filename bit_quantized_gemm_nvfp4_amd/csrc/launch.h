@@ -31,9 +31,13 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
                 void* out, void* workspace, hipStream_t stream);
 
 // Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
-// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].
+// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  When
+// the tiles cannot fill the chip, K is split (fp32 partials in workspace,
+// gemm_workspace_bytes of it, summed in split order by a second kernel).
+int gemm_splits(int64_t M, int64_t n_out, int64_t K, int num_cus);
+size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
-                bool out_f32, void* out, hipStream_t stream);
+                bool out_f32, void* out, void* workspace, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -186,7 +186,8 @@ def test_run_to_run_bit_identical(nv):
     (300, 160, 520),    # ragged in every dimension; K % 64 == 32 (partial and padding steps)
     (257, 96, 257),     # N % 4 != 0: element-wise epilogue
     (512, 5120, 300),   # long K
-    (1000, 1088, 777),  # several tiles in M and N, ragged tails
+    (1000, 1088, 777),  # several tiles in M and N, ragged tails (split-K: 2 parts)
+    (300, 2080, 300),   # split-K in 4 parts, the last ending on a partial K step
 ])
 def test_mfma_ragged_shapes(nv, orc, M, K, N):
     helpers.announce(f"gemm mfma ragged M={M} K={K} N={N}")
