@@ -100,6 +100,8 @@ def lib():
         L.oracle_moe_layer.argtypes = [_U16, _i64, _i64, _I32, _F32, _i64, _i64, _i64,
                                        _U8, _U8, _U8, _U8, _F64]
         L.oracle_moe_layer.restype = None
+        L.oracle_topk.argtypes = [_F64, _i64, _i64, _i64, _nullable(_I32), _F64, _I32]
+        L.oracle_topk.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -239,3 +241,28 @@ def moe_layer(x_bits, ids, gates, E: int, I: int, w1_codes, w1_scales, w2_codes,
                            _c(w1_codes, np.uint8), _c(w1_scales, np.uint8),
                            _c(w2_codes, np.uint8), _c(w2_scales, np.uint8), out)
     return out
+
+
+def topk(v, k: int, ids_map=None):
+    """Top-k of each row of v ([M][n], fp64 or fp32) -- best first.
+
+    Returns (values fp64 [M][k], ids int32 [M][k]); ids are ids_map[col] when
+    ids_map (the masked head's row indices) is given, else the column.
+    Equal values rank the smaller column first; -0 ranks below +0."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    M, n = v.shape
+    if not 1 <= k <= n:
+        raise ValueError("need 1 <= k <= n")
+    out_v = np.empty((M, k), dtype=np.float64)
+    out_i = np.empty((M, k), dtype=np.int32)
+    im = None if ids_map is None else _c(ids_map, np.int32)
+    lib().oracle_topk(v, M, n, k, im, out_v, out_i)
+    return out_v, out_i
+
+
+def head_topk(x_bits, M: int, K: int, w_codes, w_scales, k: int, row_idx=None, n_out=None):
+    """Draft proposal of the masked head: fp64 logits of the W4A16 layer over
+    the masked rows, then their top-k (ids are weight-row ids)."""
+    logits = gemm_w4a16(x_bits, M, K, w_codes, w_scales, row_idx=row_idx, n_out=n_out)
+    vals, ids = topk(logits, k, ids_map=row_idx)
+    return vals, ids, logits

@@ -464,6 +464,59 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, const int32_t *id
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Draft proposal from the masked head                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Order of two head outputs for the draft proposal: the larger logit first.
+ * Readings (the pages only say that the draft proposes tokens from the
+ * masked head [P3 "The masked head trick"]): equal logits rank the smaller
+ * column first (the column is the position in the ranked mask, so the more
+ * frequent token wins), and -0 ranks below +0 (the order of the fp32 bit
+ * patterns).  NaN is outside the contract. */
+typedef struct {
+    double v;
+    int64_t col;
+} topk_item;
+
+static int topk_before(const void *pa, const void *pb)
+{
+    const topk_item *a = (const topk_item *)pa, *b = (const topk_item *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    if (signbit(a->v) != signbit(b->v)) return signbit(a->v) ? 1 : -1;
+    if (a->col < b->col) return -1;
+    if (a->col > b->col) return 1;
+    return 0;
+}
+
+/* Top-k of each row of v [M][n] under the order above, best first:
+ * out_v[m][i] is the i-th best value, out_ids[m][i] its vocabulary id
+ * (ids_map[col] when the columns are a masked subset, else col).  A full
+ * sort per row; k <= n. */
+void oracle_topk(const double *v, int64_t M, int64_t n, int64_t k, const int32_t *ids_map,
+                 double *out_v, int32_t *out_ids)
+{
+#pragma omp parallel
+    {
+        topk_item *items = (topk_item *)malloc(sizeof(topk_item) * (size_t)n);
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t c = 0; c < n; ++c) {
+                items[c].v = v[m * n + c];
+                items[c].col = c;
+            }
+            qsort(items, (size_t)n, sizeof(topk_item), topk_before);
+            for (int64_t i = 0; i < k; ++i) {
+                out_v[m * k + i] = items[i].v;
+                out_ids[m * k + i] =
+                    ids_map ? ids_map[items[i].col] : (int32_t)items[i].col;
+            }
+        }
+        free(items);
+    }
+}
+
 /* Number of threads the parallel loops above use. */
 int oracle_num_threads(void)
 {

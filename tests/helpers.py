@@ -117,3 +117,34 @@ def host_bits(t):
     """bf16 GPU tensor -> uint16 bit patterns (numpy)."""
     import torch
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def topk_valid(vals, ids, logits_f64, row_idx, tol):
+    """Whether (vals, ids) [M][k] is a valid draft proposal for exact logits
+    logits_f64 [M][n] (columns are row_idx, or 0..n-1) when the proposer saw
+    the logits with an error of at most tol: ids distinct and kept; each value
+    within tol of its exact logit; values non-increasing; and no id's exact
+    logit below the exact k-th best by more than 2*tol."""
+    logits = np.asarray(logits_f64, dtype=np.float64)
+    M, n = logits.shape
+    cols_of = {int(r): c for c, r in enumerate(row_idx)} if row_idx is not None else None
+    vals = np.asarray(vals, dtype=np.float64)
+    for m in range(M):
+        k = len(ids[m])
+        if len(set(int(i) for i in ids[m])) != k:
+            return False
+        cols = []
+        for i in ids[m]:
+            c = cols_of.get(int(i)) if cols_of is not None else (int(i) if 0 <= int(i) < n else None)
+            if c is None:
+                return False
+            cols.append(c)
+        exact = logits[m, cols]
+        if np.any(np.abs(vals[m] - exact) > tol):
+            return False
+        if np.any(np.diff(vals[m]) > 0):
+            return False
+        kth = np.sort(logits[m])[::-1][k - 1]
+        if np.any(exact < kth - 2 * tol):
+            return False
+    return True
