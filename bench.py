@@ -26,7 +26,9 @@ Also reported on the same JSON line:
   cpu_baseline  -- the CPU oracle timed on this host on a bounded sample of the
                    same workload (a subset of output rows), scaled to GB/s;
   secondary     -- the other rows of the layer (prefill GEMM TFLOP/s,
-                   quantizer GB/s, W4A4 GEMM TFLOP/s, MoE layer T=32 / T=4096).
+                   quantizer GB/s, W4A4 GEMM TFLOP/s, MoE layer T=32 / T=4096);
+  draft_proposal -- the masked head with its top-8 proposal (nvfp4_head_topk)
+                   against the head GEMV alone, graph-replayed, M in {1, 8, 32}.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
 """
@@ -197,6 +199,67 @@ def time_decode(dec, torch, steps, warmup):
     return wall, per_call_ms
 
 
+def time_draft(dec, torch, nv, k=8, reps=20, replays=5):
+    """Draft proposal of the masked head (nvfp4_head_topk: head GEMV over the
+    32,768 kept rows, then the top-k) against the head GEMV alone, each call
+    captured `reps` times in a HIP graph and replayed, for M in {1, 8, 32}."""
+    import ctypes
+    import workloads as wl
+    K, N = wl.HIDDEN, wl.VOCAB
+    wc, wsc = dec.weights[(K, N)][0]
+    idx = dec.idx
+    n_out = idx.numel()
+    vp = ctypes.c_void_p
+    L = nv.lib()
+    res = {}
+
+    def graph_us(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(side.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(reps):
+                fn(side.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (replays * reps) * 1e6
+
+    for M in wl.DECODE_M:
+        x = dec.x[(M, K)]
+        vals = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        logits = torch.empty((M, n_out), dtype=torch.float32, device="cuda")
+        wsb = max(nv.head_topk_workspace_size(M, N, K, n_out, k),
+                  nv.gemm_workspace_size(M, N, K, n_out))
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+        def head(st):
+            rc = L.nvfp4_head_topk(vp(x.data_ptr()), M, N, K, vp(wc.data_ptr()),
+                                   vp(wsc.data_ptr()), vp(idx.data_ptr()), n_out, k,
+                                   vp(vals.data_ptr()), vp(ids.data_ptr()), vp(ws.data_ptr()),
+                                   wsb, vp(st))
+            assert rc == 0, rc
+
+        def gemv(st):
+            rc = L.nvfp4_gemm(nv.BF16, vp(x.data_ptr()), None, M, N, K, vp(wc.data_ptr()),
+                              vp(wsc.data_ptr()), vp(idx.data_ptr()), n_out, nv.FP32,
+                              vp(logits.data_ptr()), vp(ws.data_ptr()), wsb, vp(st))
+            assert rc == 0, rc
+
+        th, tg = graph_us(head), graph_us(gemv)
+        res[f"M{M}_head_topk{k}_us"] = round(th, 2)
+        res[f"M{M}_head_gemv_us"] = round(tg, 2)
+        res[f"M{M}_head_topk{k}_weight_GBs"] = round(weight_bytes(n_out, K) / (th * 1e-6) / 1e9, 1)
+    return res
+
+
 def cpu_baseline(target_s=15.0):
     """The oracle on this host, on a bounded sample of the same workload: every
     call of the decode step restricted to an evenly spaced subset of its output
@@ -350,6 +413,10 @@ def main():
     per_call_gbs = {c[0]: round(float(b / (t / 1e3) / 1e9), 1)
                     for c, b, t in zip(dec.calls, launch_bytes, mean_ms)}
     per_call_us = {c[0]: round(float(t * 1e3), 2) for c, t in zip(dec.calls, mean_ms)}
+    draft = None
+    if not args.no_secondary:
+        log("secondary: masked head draft proposal (top-8)")
+        draft = time_draft(dec, torch, nv)
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:
@@ -402,6 +469,8 @@ def main():
     }
     if sec is not None:
         line["secondary"] = sec
+    if draft is not None:
+        line["draft_proposal"] = draft
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "library_path", "dequantize", "quantize", "gemm", "gemm_workspace_size", "moe_align",
-    "grouped_gemm", "moe_combine", "moe_layer", "BF16", "FP32", "NVFP4", "EPI_NONE",
+    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "BF16", "FP32", "NVFP4", "EPI_NONE",
     "EPI_SWIGLU",
 ]
 
@@ -42,6 +42,11 @@ _SIGS = {
     "nvfp4_gemm_workspace_size": ([_int, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_gemm": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp, _vp, _sz,
                     _vp], _int),
+    "nvfp4_topk_workspace_size": ([_i64, _i64, _i64], _sz),
+    "nvfp4_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_head_topk_workspace_size": ([_i64, _i64, _i64, _i64, _i64], _sz),
+    "nvfp4_head_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz,
+                         _vp], _int),
     "nvfp4_moe_align_workspace_size": ([_i64, _i64, _i64], _sz),
     "nvfp4_moe_align": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_workspace_size": ([_i64, _i64, _i64, _i64], _sz),
@@ -160,6 +165,48 @@ def gemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, a_scale
                             _ptr(w_codes), _ptr(w_scales), _ptr(row_idx), n_out, odt, _ptr(out),
                             _ptr(ws), wsz, _stream(a.device)))
     return out
+
+
+# ---- draft proposal from the masked head ----------------------------------------------
+
+def topk(logits: torch.Tensor, k: int, ids_map=None, workspace=None):
+    """Top-k of each row of fp32 logits [M, n], best first (larger value, then
+    smaller column; -0 below +0) -> (values fp32 [M, k], ids int32 [M, k]).
+    ids are ids_map[column] when ids_map (int32 [n]) is given."""
+    _gpu(logits, ids_map, workspace)
+    if logits.dtype != torch.float32:
+        raise RuntimeError("topk expects fp32 logits")
+    M, n = logits.shape
+    values = torch.empty((M, k), dtype=torch.float32, device=logits.device)
+    ids = torch.empty((M, k), dtype=torch.int32, device=logits.device)
+    ws, wsz = _workspace(int(lib().nvfp4_topk_workspace_size(M, n, k)), logits.device, workspace)
+    _check(lib().nvfp4_topk(_ptr(logits), M, n, k, _ptr(ids_map), _ptr(values), _ptr(ids),
+                            _ptr(ws), wsz, _stream(logits.device)))
+    return values, ids
+
+
+def head_topk_workspace_size(M: int, N: int, K: int, n_out: int, k: int) -> int:
+    return int(lib().nvfp4_head_topk_workspace_size(M, N, K, n_out, k))
+
+
+def head_topk(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, k: int,
+              row_idx=None, workspace=None):
+    """Masked draft head and its proposal: fp32 logits of the W4A16 head over
+    the rows row_idx (all rows if None), then their top-k -> (values fp32
+    [M, k], ids int32 [M, k]); ids are weight-row (token) ids."""
+    _gpu(a, w_codes, w_scales, row_idx, workspace)
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise RuntimeError(f"K mismatch: activations K={K}, weights K={w_codes.shape[1] * 2}")
+    n_out = N if row_idx is None else row_idx.numel()
+    values = torch.empty((M, k), dtype=torch.float32, device=a.device)
+    ids = torch.empty((M, k), dtype=torch.int32, device=a.device)
+    ws, wsz = _workspace(head_topk_workspace_size(M, N, K, n_out, k), a.device, workspace)
+    _check(lib().nvfp4_head_topk(_ptr(a), M, N, K, _ptr(w_codes), _ptr(w_scales), _ptr(row_idx),
+                                 n_out, k, _ptr(values), _ptr(ids), _ptr(ws), wsz,
+                                 _stream(a.device)))
+    return values, ids
 
 
 # ---- routed mixture of experts --------------------------------------------------------

@@ -163,6 +163,65 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
   return NVFP4_SUCCESS;
 }
 
+size_t nvfp4_topk_workspace_size(int64_t M, int64_t n, int64_t k) {
+  if (M <= 0 || n <= 0 || k <= 0) return 0;
+  return topk_workspace_bytes(M, n, k);
+}
+
+int nvfp4_topk(const float* logits, int64_t M, int64_t n, int64_t k, const int32_t* ids_map,
+               float* values, int32_t* ids, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!logits || !values || !ids) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || n <= 0 || k <= 0 || k > n) return NVFP4_ERROR_INVALID_VALUE;
+  if (k > kTopkMaxK || n > INT32_MAX || M > 65535) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(logits) || !aligned16(values) || !aligned16(ids) ||
+      (ids_map && !aligned16(ids_map)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  const size_t need = topk_workspace_bytes(M, n, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+  return launched(launch_topk(logits, M, n, k, ids_map, values, ids, workspace,
+                              as_stream(stream)));
+}
+
+size_t nvfp4_head_topk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out,
+                                      int64_t k) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0 || k <= 0) return 0;
+  return round_up((size_t)M * (size_t)n_out * sizeof(float), 256) +
+         round_up(nvfp4_gemm_workspace_size(NVFP4_BF16, M, N, K, n_out), 256) +
+         topk_workspace_bytes(M, n_out, k);
+}
+
+int nvfp4_head_topk(const uint16_t* a, int64_t M, int64_t N, int64_t K, const uint8_t* w_codes,
+                    const uint8_t* w_scales, const int32_t* row_idx, int64_t n_out, int64_t k,
+                    float* values, int32_t* ids, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!a || !w_codes || !w_scales || !values || !ids) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0 || k <= 0 || k > n_out)
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (k > kTopkMaxK || M > 65535) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (row_idx ? n_out > N : n_out != N) return NVFP4_ERROR_INVALID_VALUE;
+  if (n_out > INT32_MAX || N > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(values) ||
+      !aligned16(ids) || (row_idx && !aligned16(row_idx)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  const size_t need = nvfp4_head_topk_workspace_size(M, N, K, n_out, k);
+  if (!workspace || workspace_bytes < need) return NVFP4_ERROR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws);
+  const size_t g_off = round_up((size_t)M * (size_t)n_out * sizeof(float), 256);
+  const size_t g_bytes = nvfp4_gemm_workspace_size(NVFP4_BF16, M, N, K, n_out);
+  const size_t t_off = g_off + round_up(g_bytes, 256);
+  const int rc = nvfp4_gemm(NVFP4_BF16, a, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
+                            NVFP4_FP32, logits, g_bytes ? ws + g_off : nullptr, g_bytes, stream);
+  if (rc != NVFP4_SUCCESS) return rc;
+  const size_t t_bytes = topk_workspace_bytes(M, n_out, k);
+  return launched(launch_topk(logits, M, n_out, k, row_idx, values, ids,
+                              t_bytes ? ws + t_off : nullptr, as_stream(stream)));
+}
+
 size_t nvfp4_moe_align_workspace_size(int64_t T, int64_t topk, int64_t E) {
   if (T <= 0 || topk <= 0 || E <= 0) return 0;
   return moe_align_workspace_bytes(T, topk, E);

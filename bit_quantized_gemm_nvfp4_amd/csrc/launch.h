@@ -40,4 +40,12 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
                 bool out_f32, void* out, void* workspace, hipStream_t stream);
 
+// Top-k of each row of fp32 logits [M][n] (k <= kTopkMaxK), best first: larger
+// value, then smaller column; -0 below +0.  ids are ids_map[column] (or the
+// column).  Rows longer than 2048 need topk_workspace_bytes of workspace.
+constexpr int kTopkMaxK = 256;
+size_t topk_workspace_bytes(int64_t M, int64_t n, int64_t k);
+int launch_topk(const float* logits, int64_t M, int64_t n, int64_t k, const int32_t* ids_map,
+                float* values, int32_t* ids, void* workspace, hipStream_t stream);
+
 }  // namespace nvfp4

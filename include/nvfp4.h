@@ -128,6 +128,42 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Draft proposal from a head's logits ("Serving Qwen3.8-27B in 4-bit ...",
+ * section "The masked head trick": the draft proposes tokens only from the
+ * kept rows of the head).  For each row m of logits (fp32 [M][n]) the k best
+ * entries, best first:
+ *   values[m][i] = logits[m][c_i],  ids[m][i] = ids_map ? ids_map[c_i] : c_i,
+ * ordered by larger value, then smaller column c (the rank in the mask);
+ * -0 ranks below +0.  The result is unique and bit-exact.  NaN logits are
+ * outside the contract (they are ranked by their bit patterns).
+ * 1 <= k <= min(n, 256), n <= INT32_MAX, M <= 65535.  ids_map (optional,
+ * int32 [n]) maps columns to token ids.  values fp32 [M][k], ids int32 [M][k].
+ * workspace: >= nvfp4_topk_workspace_size(M, n, k) bytes (0 for n <= 2048).
+ */
+size_t nvfp4_topk_workspace_size(int64_t M, int64_t n, int64_t k);
+int nvfp4_topk(const float *logits, int64_t M, int64_t n, int64_t k, const int32_t *ids_map,
+               float *values, int32_t *ids, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * Masked draft head with its proposal ("Serving Qwen3.8-27B in 4-bit ...",
+ * section "The masked head trick"): the W4A16 head over the kept rows, then
+ * the top-k of each row,
+ *   logits[m][j] = sum_k a[m][k] * w[row_idx[j]][k]   (fp32, as nvfp4_gemm),
+ *   values/ids   = nvfp4_topk(logits, k, ids_map = row_idx)
+ * so ids are weight-row (token) ids.  a is bf16 [M][K]; row_idx as in
+ * nvfp4_gemm (NULL: every row, n_out = N).  The logits stay in the workspace
+ * and are not returned.  1 <= k <= min(n_out, 256), M <= 65535, K % 32 == 0.
+ * workspace: >= nvfp4_head_topk_workspace_size(M, N, K, n_out, k) bytes.
+ */
+size_t nvfp4_head_topk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out,
+                                      int64_t k);
+int nvfp4_head_topk(const uint16_t *a, int64_t M, int64_t N, int64_t K, const uint8_t *w_codes,
+                    const uint8_t *w_scales, const int32_t *row_idx, int64_t n_out, int64_t k,
+                    float *values, int32_t *ids, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
  * Routing preparation for a routed mixture-of-experts layer ("What 350+
  * Experiments ...", section 1: a routed-expert model).  topk_ids int32
  * [T][topk] holds, for each token, the experts it is routed to (each in

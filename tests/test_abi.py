@@ -124,3 +124,34 @@ def test_binding_refuses_cpu_tensors(L):
     x = torch.zeros(2, 64, dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="GPU"):
         nv.quantize(x)
+
+
+def test_topk_validation(L):
+    def tk(logits=P, M=2, n=5000, k=8, ids_map=NULL, values=P2, ids=P3, ws=P4, wbytes=1 << 20):
+        return L.nvfp4_topk(logits, M, n, k, ids_map, values, ids, ws, wbytes, NULL)
+    assert tk(logits=NULL) == INVALID
+    assert tk(k=0) == INVALID
+    assert tk(k=5001) == INVALID                       # k > n
+    assert tk(n=300, k=257) == NOT_SUPPORTED           # k above 256
+    assert tk(M=70000) == NOT_SUPPORTED
+    assert tk(values=MIS) == INVALID
+    assert L.nvfp4_topk_workspace_size(2, 2048, 64) == 0   # one chunk: no workspace
+    need = L.nvfp4_topk_workspace_size(2, 5000, 8)
+    assert need >= 2 * 3 * 8 * 8
+    assert tk(ws=NULL, wbytes=0) == WORKSPACE
+    assert tk(wbytes=need - 1) == WORKSPACE
+
+
+def test_head_topk_validation(L):
+    def hk(a=P, M=1, N=1000, K=256, ri=P4, n_out=100, k=4, ws=P, wbytes=1 << 30):
+        return L.nvfp4_head_topk(a, M, N, K, P2, P3, ri, n_out, k, P2, P3, ws, wbytes, NULL)
+    assert hk(a=NULL) == INVALID
+    assert hk(k=101) == INVALID            # k > n_out
+    assert hk(k=300, n_out=500) == NOT_SUPPORTED
+    assert hk(K=48) == NOT_SUPPORTED
+    assert hk(ri=NULL) == INVALID          # no mask: n_out must be N
+    assert hk(n_out=1001) == INVALID
+    need = L.nvfp4_head_topk_workspace_size(1, 1000, 256, 100, 4)
+    assert need >= 100 * 4
+    assert hk(ws=NULL, wbytes=0) == WORKSPACE
+    assert hk(wbytes=need - 1) == WORKSPACE
