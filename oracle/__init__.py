@@ -102,6 +102,13 @@ def lib():
         L.oracle_moe_layer.restype = None
         L.oracle_topk.argtypes = [_F64, _i64, _i64, _i64, _nullable(_I32), _F64, _I32]
         L.oracle_topk.restype = None
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint
+        L.oracle_kv_store_e4m3.argtypes = [_U16, _i64, _i64, _I32, ctypes.c_float, _U8, _i64]
+        L.oracle_kv_store_e4m3.restype = None
+        L.oracle_kv_load_e4m3.argtypes = [_U8, _i64, _i64, _I32, _I32, _i64, _i64, _i64, _i64,
+                                          ctypes.c_float, _U16]
+        L.oracle_kv_load_e4m3.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -266,3 +273,31 @@ def head_topk(x_bits, M: int, K: int, w_codes, w_scales, k: int, row_idx=None, n
     logits = gemm_w4a16(x_bits, M, K, w_codes, w_scales, row_idx=row_idx, n_out=n_out)
     vals, ids = topk(logits, k, ids_map=row_idx)
     return vals, ids, logits
+
+
+def e4m3_encode(v: float) -> int:
+    """E4M3 code of v: nearest, ties to even code, saturating at +-448."""
+    return lib().oracle_e4m3_encode(v)
+
+
+def kv_store_e4m3(x_bits, slot_mapping, scale: float, cache):
+    """Write tokens x (bf16 bits [T][W]) into cache (uint8 [num_slots][W],
+    updated in place) at rows slot_mapping[t]; returns cache."""
+    x = _c(x_bits, np.uint16)
+    T, W = x.shape
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.shape[1] == W
+    lib().oracle_kv_store_e4m3(x, T, W, _c(slot_mapping, np.int32), scale, cache,
+                               cache.shape[0])
+    return cache
+
+
+def kv_load_e4m3(cache, block_table, seq_lens, page_size: int, max_len: int, scale: float):
+    """Sequences back from the cache: bf16 bits [B][max_len][W]."""
+    cache = _c(cache, np.uint8)
+    bt = _c(block_table, np.int32)
+    B, max_pages = bt.shape
+    W = cache.shape[1]
+    out = np.empty((B, max_len, W), dtype=np.uint16)
+    lib().oracle_kv_load_e4m3(cache, cache.shape[0], W, bt, _c(seq_lens, np.int32), B,
+                              max_pages, page_size, max_len, scale, out)
+    return out

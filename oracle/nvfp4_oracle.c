@@ -517,6 +517,92 @@ void oracle_topk(const double *v, int64_t M, int64_t n, int64_t k, const int32_t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 KV-cache codec                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 code of a real value v [P4 section 3: the KV cache stored as FP8
+ * E4M3].  Readings: round to the nearest E4M3 value, ties to the even code;
+ * magnitudes at or above 448 saturate to 448 (satfinite: there is no
+ * infinity); the sign is kept, zero included.  Written as the plain nearest
+ * search over the 127 non-negative finite values; every comparison is exact
+ * in double (E4M3 values and their midpoints have at most 5 significant
+ * bits). */
+unsigned oracle_e4m3_encode(double v)
+{
+    unsigned sign = signbit(v) ? 0x80u : 0u;
+    double a = fabs(v);
+    unsigned c = 0;
+    for (unsigned cand = 1; cand <= 0x7E; ++cand)
+        if (oracle_e4m3_value(cand) <= a)
+            c = cand;
+    if (c < 0x7E) {
+        double mid = 0.5 * (oracle_e4m3_value(c) + oracle_e4m3_value(c + 1));
+        if (a > mid || (a == mid && ((c + 1) & 1u) == 0))
+            c = c + 1;
+    }
+    return sign | c;
+}
+
+/* Quotient x / scale rounded once to binary32 (nearest even).  The double
+ * quotient is rounded to 53 bits first; for a division that second rounding
+ * cannot change the binary32 result (53 >= 2*24 + 2). */
+static double f32_quotient(double x, double scale)
+{
+    return (double)(float)(x / scale);
+}
+
+/* Store tokens into an FP8 E4M3 KV cache [P4 section 3: FP8 E4M3 KV cache,
+ * 16-token pages by default].  x is bf16 [T][W] (W = heads * head size of
+ * one of K or V); cache is [num_slots][W] codes, where a slot is
+ * page * page_size + position in the page, so the paged layout
+ * [pages][page_size][W] is this array.  Reading (the pages give no scale
+ * rule): one positive fp32 scale per cache, code = E4M3(fl32(x / scale)).
+ * slot_mapping[t] < 0 (padding) or >= num_slots leaves the cache untouched. */
+void oracle_kv_store_e4m3(const uint16_t *x, int64_t T, int64_t W, const int32_t *slot_mapping,
+                          float scale, uint8_t *cache, int64_t num_slots)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        for (int64_t w = 0; w < W; ++w)
+            cache[slot * W + w] = (uint8_t)oracle_e4m3_encode(
+                f32_quotient(oracle_bf16_value(x[t * W + w]), (double)scale));
+    }
+}
+
+/* Read B sequences back from the cache: out bf16 [B][max_len][W],
+ *   out[b][i][w] = bf16(fl32(e4m3(cache[s][w]) * scale)),
+ *   s = block_table[b][i / page_size] * page_size + i % page_size,
+ * for i < seq_lens[b]; zero for i >= seq_lens[b] and for a slot outside the
+ * cache.  The product is formed exactly, rounded to binary32, then to bf16
+ * (both nearest even): dequantize in fp32, store bf16. */
+void oracle_kv_load_e4m3(const uint8_t *cache, int64_t num_slots, int64_t W,
+                         const int32_t *block_table, const int32_t *seq_lens, int64_t B,
+                         int64_t max_pages, int64_t page_size, int64_t max_len, float scale,
+                         uint16_t *out)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i < max_len; ++i) {
+            uint16_t *o = out + (b * max_len + i) * W;
+            int64_t slot = -1;
+            if (i < seq_lens[b] && i / page_size < max_pages) {
+                int64_t page = block_table[b * max_pages + i / page_size];
+                slot = page * page_size + i % page_size;
+            }
+            if (slot < 0 || slot >= num_slots) {
+                for (int64_t w = 0; w < W; ++w)
+                    o[w] = 0;
+                continue;
+            }
+            for (int64_t w = 0; w < W; ++w) {
+                double p = oracle_e4m3_value(cache[slot * W + w]) * (double)scale;
+                o[w] = oracle_bf16_round((double)(float)p);
+            }
+        }
+}
+
 /* Number of threads the parallel loops above use. */
 int oracle_num_threads(void)
 {
