@@ -26,7 +26,8 @@ Also reported on the same JSON line:
   cpu_baseline  -- the CPU oracle timed on this host on a bounded sample of the
                    same workload (a subset of output rows), scaled to GB/s;
   secondary     -- the other rows of the layer (prefill GEMM TFLOP/s,
-                   quantizer GB/s, W4A4 GEMM TFLOP/s, MoE layer T=32 / T=4096);
+                   quantizer GB/s, W4A4 GEMM TFLOP/s, FP8 KV-cache store/load
+                   GB/s, MoE layer T=32 / T=4096);
   draft_proposal -- the masked head with its top-8 proposal (nvfp4_head_topk)
                    against the head GEMV alone, graph-replayed, M in {1, 8, 32}.
 
@@ -346,6 +347,21 @@ def secondary(nv, torch, helpers_dev, reps=3):
     t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales))
     res["w4a4_M512_N17408_K5120_tflops"] = round(2 * 512 * 17408 * 5120 / t / 1e12, 2)
     del xd, xq, wc, ws
+    # FP8 E4M3 KV-cache codec: bytes moved (bf16 in + codes out; codes in + bf16 out)
+    log("secondary: KV cache store / load")
+    kw = wl.kv_store(8192)
+    kx, ksm = dev_bf16(kw.x), dev_i32(kw.slot_mapping)
+    kc = torch.zeros((kw.num_slots, wl.KV_W), dtype=torch.uint8, device="cuda")
+    t = timeit(lambda: nv.kv_store_e4m3(kx, ksm, kw.scale, kc), n=20)
+    res["kv_store_T8192_W1024_GBs"] = round(8192 * wl.KV_W * 3 / t / 1e9, 1)
+    cache, bt, lens, kscale = wl.kv_load(32, 4096)
+    kc2, kbt, kl = dev_u8(cache), dev_i32(bt), dev_i32(lens)
+    kout = torch.empty((32, 4096, wl.KV_W), dtype=torch.bfloat16, device="cuda")
+    t = timeit(lambda: nv.kv_load_e4m3(kc2, kbt, kl, wl.KV_PAGE, 4096, kscale, out=kout), n=10)
+    used = int(lens.sum()) * wl.KV_W
+    res["kv_load_B32_L4096_W1024_GBs"] = round((used * 3 + (32 * 4096 * wl.KV_W - used) * 2)
+                                               / t / 1e9, 1)
+    del kx, ksm, kc, kc2, kbt, kl, kout, cache
     # MoE layer
     for T in (32, 4096):
         log(f"secondary: MoE T={T}")

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "library_path", "dequantize", "quantize", "gemm", "gemm_workspace_size", "moe_align",
-    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "BF16", "FP32", "NVFP4", "EPI_NONE",
+    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3", "kv_load_e4m3", "BF16", "FP32", "NVFP4", "EPI_NONE",
     "EPI_SWIGLU",
 ]
 
@@ -47,6 +47,9 @@ _SIGS = {
     "nvfp4_head_topk_workspace_size": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_head_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz,
                          _vp], _int),
+    "nvfp4_kv_store_e4m3": ([_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp], _int),
+    "nvfp4_kv_load_e4m3": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                            _vp, _vp], _int),
     "nvfp4_moe_align_workspace_size": ([_i64, _i64, _i64], _sz),
     "nvfp4_moe_align": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_workspace_size": ([_i64, _i64, _i64, _i64], _sz),
@@ -207,6 +210,36 @@ def head_topk(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, k:
                                  n_out, k, _ptr(values), _ptr(ids), _ptr(ws), wsz,
                                  _stream(a.device)))
     return values, ids
+
+
+# ---- FP8 E4M3 KV cache ------------------------------------------------------------------
+
+def kv_store_e4m3(x: torch.Tensor, slot_mapping: torch.Tensor, scale: float,
+                  cache: torch.Tensor) -> torch.Tensor:
+    """Write token rows x (bf16 [T, W]) into cache (uint8 [num_slots, W], updated
+    in place) at rows slot_mapping (int32 [T]; < 0 skips).  Returns cache."""
+    _gpu(x, slot_mapping, cache)
+    T, W = x.shape
+    if cache.dtype != torch.uint8 or cache.shape[1] != W:
+        raise RuntimeError("cache must be uint8 [num_slots, W]")
+    _check(lib().nvfp4_kv_store_e4m3(_ptr(x), T, W, _ptr(slot_mapping), float(scale),
+                                     _ptr(cache), cache.shape[0], _stream(x.device)))
+    return cache
+
+
+def kv_load_e4m3(cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                 page_size: int, max_len: int, scale: float, out=None) -> torch.Tensor:
+    """Sequences back from the cache through their block tables (int32
+    [B, max_pages]) -> bf16 [B, max_len, W]; rows past seq_lens[b] are zero."""
+    _gpu(cache, block_table, seq_lens, out)
+    B, max_pages = block_table.shape
+    W = cache.shape[1]
+    if out is None:
+        out = torch.empty((B, max_len, W), dtype=torch.bfloat16, device=cache.device)
+    _check(lib().nvfp4_kv_load_e4m3(_ptr(cache), cache.shape[0], W, _ptr(block_table),
+                                    _ptr(seq_lens), B, max_pages, page_size, max_len,
+                                    float(scale), _ptr(out), _stream(cache.device)))
+    return out
 
 
 # ---- routed mixture of experts --------------------------------------------------------

@@ -222,6 +222,35 @@ int nvfp4_head_topk(const uint16_t* a, int64_t M, int64_t N, int64_t K, const ui
                               t_bytes ? ws + t_off : nullptr, as_stream(stream)));
 }
 
+int nvfp4_kv_store_e4m3(const uint16_t* x, int64_t T, int64_t W, const int32_t* slot_mapping,
+                        float scale, uint8_t* cache, int64_t num_slots, void* stream) {
+  if (!x || !slot_mapping || !cache) return NVFP4_ERROR_INVALID_VALUE;
+  if (T <= 0 || W <= 0 || num_slots <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (!(scale >= 0x1p-126f && scale <= 3.4028235e38f)) return NVFP4_ERROR_INVALID_VALUE;
+  if (W % 16 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(x) || !aligned16(cache)) return NVFP4_ERROR_INVALID_VALUE;
+  if (T * W > ((int64_t)1 << 40) || num_slots * W > ((int64_t)1 << 40))
+    return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_kv_store(x, T, W, slot_mapping, scale, cache, num_slots,
+                                  as_stream(stream)));
+}
+
+int nvfp4_kv_load_e4m3(const uint8_t* cache, int64_t num_slots, int64_t W,
+                       const int32_t* block_table, const int32_t* seq_lens, int64_t B,
+                       int64_t max_pages, int64_t page_size, int64_t max_len, float scale,
+                       uint16_t* out, void* stream) {
+  if (!cache || !block_table || !seq_lens || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (num_slots <= 0 || W <= 0 || B <= 0 || max_pages <= 0 || page_size <= 0 || max_len <= 0)
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (!(scale >= 0x1p-126f && scale <= 3.4028235e38f)) return NVFP4_ERROR_INVALID_VALUE;
+  if (W % 16 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(cache) || !aligned16(out)) return NVFP4_ERROR_INVALID_VALUE;
+  if (B * max_len * W > ((int64_t)1 << 40) || num_slots * W > ((int64_t)1 << 40))
+    return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_kv_load(cache, num_slots, W, block_table, seq_lens, B, max_pages,
+                                 page_size, max_len, scale, out, as_stream(stream)));
+}
+
 size_t nvfp4_moe_align_workspace_size(int64_t T, int64_t topk, int64_t E) {
   if (T <= 0 || topk <= 0 || E <= 0) return 0;
   return moe_align_workspace_bytes(T, topk, E);

@@ -48,4 +48,12 @@ size_t topk_workspace_bytes(int64_t M, int64_t n, int64_t k);
 int launch_topk(const float* logits, int64_t M, int64_t n, int64_t k, const int32_t* ids_map,
                 float* values, int32_t* ids, void* workspace, hipStream_t stream);
 
+// FP8 E4M3 KV-cache codec: rows of W elements (W % 16 == 0) between bf16
+// tokens and a cache of num_slots code rows.
+int launch_kv_store(const uint16_t* x, int64_t T, int64_t W, const int32_t* slot_mapping,
+                    float scale, uint8_t* cache, int64_t num_slots, hipStream_t stream);
+int launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t W, const int32_t* block_table,
+                   const int32_t* seq_lens, int64_t B, int64_t max_pages, int64_t page_size,
+                   int64_t max_len, float scale, uint16_t* out, hipStream_t stream);
+
 }  // namespace nvfp4

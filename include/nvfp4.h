@@ -164,6 +164,36 @@ int nvfp4_head_topk(const uint16_t *a, int64_t M, int64_t N, int64_t K, const ui
                     void *stream);
 
 /*
+ * FP8 E4M3 KV cache ("What 350+ Experiments ...", section 3 "KV cache and
+ * memory capacity": the key/value cache held as FP8 E4M3 in 16-token pages).
+ * A cache is uint8 [num_slots][W] (W = heads * head size of the keys or of
+ * the values); slot = page * page_size + position in the page, so the paged
+ * layout [pages][page_size][W] is the same array.  One fp32 scale per cache
+ * (finite, >= 2^-126).
+ *
+ * nvfp4_kv_store_e4m3: token rows x (bf16 [T][W]) into their slots,
+ *   cache[slot_mapping[t]][w] = E4M3(fl32(x[t][w] / scale)),
+ * fl32 = binary32 division, nearest even; E4M3 = nearest code, ties to the
+ * even code, saturating to +-448, sign kept.  The result is bit-exact.  The
+ * cache is updated in place (the one exception to "outputs are fully
+ * overwritten"): slot_mapping[t] < 0 (padding) or >= num_slots leaves it
+ * untouched; slots must be distinct.  W % 16 == 0.
+ *
+ * nvfp4_kv_load_e4m3: B sequences back to bf16 out [B][max_len][W],
+ *   out[b][i][w] = bf16(fl32(e4m3(cache[s][w]) * scale)),
+ *   s = block_table[b][i / page_size] * page_size + i % page_size,
+ * for i < seq_lens[b] (block_table int32 [B][max_pages], seq_lens int32 [B]);
+ * rows i >= seq_lens[b], and rows whose slot falls outside the cache, are
+ * zero.  Bit-exact.  W % 16 == 0.
+ */
+int nvfp4_kv_store_e4m3(const uint16_t *x, int64_t T, int64_t W, const int32_t *slot_mapping,
+                        float scale, uint8_t *cache, int64_t num_slots, void *stream);
+int nvfp4_kv_load_e4m3(const uint8_t *cache, int64_t num_slots, int64_t W,
+                       const int32_t *block_table, const int32_t *seq_lens, int64_t B,
+                       int64_t max_pages, int64_t page_size, int64_t max_len, float scale,
+                       uint16_t *out, void *stream);
+
+/*
  * Routing preparation for a routed mixture-of-experts layer ("What 350+
  * Experiments ...", section 1: a routed-expert model).  topk_ids int32
  * [T][topk] holds, for each token, the experts it is routed to (each in

@@ -135,7 +135,8 @@ def test_topk_validation(L):
     assert tk(n=300, k=257) == NOT_SUPPORTED           # k above 256
     assert tk(M=70000) == NOT_SUPPORTED
     assert tk(values=MIS) == INVALID
-    assert L.nvfp4_topk_workspace_size(2, 2048, 64) == 0   # one chunk: no workspace
+    assert L.nvfp4_topk_workspace_size(2, 512, 64) == 0    # one chunk: no workspace
+    assert L.nvfp4_topk_workspace_size(2, 2048, 100) == 0
     need = L.nvfp4_topk_workspace_size(2, 5000, 8)
     assert need >= 2 * 3 * 8 * 8
     assert tk(ws=NULL, wbytes=0) == WORKSPACE
@@ -155,3 +156,24 @@ def test_head_topk_validation(L):
     assert need >= 100 * 4
     assert hk(ws=NULL, wbytes=0) == WORKSPACE
     assert hk(wbytes=need - 1) == WORKSPACE
+
+
+def test_kv_codec_validation(L):
+    def st(x=P, T=4, W=128, sm=P2, scale=1.0, cache=P3, slots=64):
+        return L.nvfp4_kv_store_e4m3(x, T, W, sm, scale, cache, slots, NULL)
+
+    def ld(cache=P, slots=64, W=128, bt=P2, lens=P3, B=2, mp=4, ps=16, ml=64, scale=1.0, out=P4):
+        return L.nvfp4_kv_load_e4m3(cache, slots, W, bt, lens, B, mp, ps, ml, scale, out, NULL)
+    assert st(x=NULL) == INVALID
+    assert st(T=0) == INVALID
+    assert st(W=24) == NOT_SUPPORTED
+    assert st(scale=0.0) == INVALID
+    assert st(scale=float("inf")) == INVALID
+    assert st(scale=float("nan")) == INVALID
+    assert st(scale=-1.0) == INVALID
+    assert st(cache=MIS) == INVALID
+    assert ld(bt=NULL) == INVALID
+    assert ld(ps=0) == INVALID
+    assert ld(W=40) == NOT_SUPPORTED
+    assert ld(out=MIS) == INVALID
+    assert ld(scale=1e-40) == INVALID

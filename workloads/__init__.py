@@ -188,3 +188,54 @@ def moe(T: int, E: int = MOE_EXPERTS, topk: int = MOE_TOPK, H: int = MOE_HIDDEN,
     w1 = nvfp4_weight(rng, E, 2 * I, H, exp_field=MOE_SCALE_EXP_FIELD)
     w2 = nvfp4_weight(rng, E, H, I, exp_field=MOE_SCALE_EXP_FIELD)
     return MoEWorkload(x, ids, gates, w1, w2)
+
+
+# ---- FP8 E4M3 KV cache ------------------------------------------------------------
+# Synthetic attention-cache shape: 8 key/value heads of 128 elements, so a token
+# row of K (or of V) holds KV_W = 1024 elements; 16-token pages, the default the
+# pages report (32-token pages were slower there).
+KV_HEADS, KV_HEAD_DIM = 8, 128
+KV_W = KV_HEADS * KV_HEAD_DIM
+KV_PAGE = 16
+
+
+@dataclass
+class KVWorkload:
+    x: np.ndarray             # bf16 bits [T, W]: token rows to store
+    slot_mapping: np.ndarray  # int32 [T]: cache slot of each token
+    scale: float              # per-cache scale: amax / 448, rounded to fp32
+    num_slots: int
+
+
+def kv_store(T: int, W: int = KV_W, page: int = KV_PAGE, spare_pages: int = 64,
+             seed: int = 0) -> KVWorkload:
+    """Prefill-shaped KV store: T new tokens of one sequence.  Draws: x [T, W]
+    N(0,1) with 0.1% outlier channels x20 (bf16), then a permutation of the
+    cache's pages.  The cache has ceil(T/page) + spare_pages pages; token t
+    goes to position t % page of the sequence's (t // page)-th page."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, T, W, outlier_frac=0.001)
+    n_pages = (T + page - 1) // page + spare_pages
+    pages = rng.permutation(n_pages)[: (T + page - 1) // page].astype(np.int64)
+    t = np.arange(T)
+    slot = (pages[t // page] * page + t % page).astype(np.int32)
+    amax = float(np.abs(bf16_bits_to_f32(x)).max())
+    return KVWorkload(x, slot, float(np.float32(amax / 448.0)), n_pages * page)
+
+
+def kv_load(B: int, max_len: int, W: int = KV_W, page: int = KV_PAGE, seed: int = 0):
+    """Decode-shaped KV read: B sequences of lengths uniform in [1, max_len]
+    (the longest set to max_len), pages assigned by one permutation of the
+    cache.  Draws: lengths, the page permutation, then the cache codes (uniform
+    over the 254 finite E4M3 codes).  Returns (cache uint8 [slots, W],
+    block_table int32 [B, max_pages], seq_lens int32 [B], scale)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=B).astype(np.int32)
+    lens[0] = max_len
+    max_pages = (max_len + page - 1) // page
+    n_pages = B * max_pages
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm.reshape(B, max_pages)
+    codes = rng.integers(0, 254, size=(n_pages * page, W)).astype(np.uint8)
+    codes[codes >= 0x7F] += 1            # skip the NaN code 0x7F (0xFF is out of range)
+    return codes, bt, lens, 0.0123
