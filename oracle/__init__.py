@@ -109,6 +109,14 @@ def lib():
         L.oracle_kv_load_e4m3.argtypes = [_U8, _i64, _i64, _I32, _I32, _i64, _i64, _i64, _i64,
                                           ctypes.c_float, _U16]
         L.oracle_kv_load_e4m3.restype = None
+        L.oracle_global_scale.argtypes = [ctypes.c_double]
+        L.oracle_global_scale.restype = ctypes.c_float
+        L.oracle_quantize_scaled.argtypes = [_U16, _i64, _i64, ctypes.c_float, _U8, _U8]
+        L.oracle_quantize_scaled.restype = None
+        L.oracle_quantize_weight.argtypes = [_U16, _i64, _i64, _U8, _U8]
+        L.oracle_quantize_weight.restype = ctypes.c_float
+        L.oracle_dequantize_scaled.argtypes = [_U8, _U8, ctypes.c_float, _i64, _i64, _U16]
+        L.oracle_dequantize_scaled.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -301,3 +309,43 @@ def kv_load_e4m3(cache, block_table, seq_lens, page_size: int, max_len: int, sca
     lib().oracle_kv_load_e4m3(cache, cache.shape[0], W, bt, _c(seq_lens, np.int32), B,
                               max_pages, page_size, max_len, scale, out)
     return out
+
+
+# ---- two-level NVFP4 (per-tensor fp32 scale) ----------------------------------------
+
+def global_scale(amax: float) -> float:
+    """Per-tensor scale of the offline quantizer: fl32(amax / 2688), 1 for 0."""
+    return lib().oracle_global_scale(amax)
+
+
+def quantize_scaled(x_bits, M: int, K: int, g: float):
+    """bf16 [M][K] with a given global scale g -> (codes, scales) of fl32(x/g)."""
+    codes = np.empty((M, K // 2), dtype=np.uint8)
+    scales = np.empty((M, K // 16), dtype=np.uint8)
+    lib().oracle_quantize_scaled(_c(x_bits, np.uint16), M, K, g, codes, scales)
+    return codes, scales
+
+
+def quantize_weight(w_bits, N: int, K: int):
+    """Offline weight quantizer: bf16 [N][K] -> (codes, scales, g)."""
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 16), dtype=np.uint8)
+    g = lib().oracle_quantize_weight(_c(w_bits, np.uint16), N, K, codes, scales)
+    return codes, scales, float(g)
+
+
+def dequantize_scaled(codes, scales, g: float, N: int, K: int) -> np.ndarray:
+    out = np.empty((N, K), dtype=np.uint16)
+    lib().oracle_dequantize_scaled(_c(codes, np.uint8), _c(scales, np.uint8), g, N, K, out)
+    return out
+
+
+def gemm_scaled(x, M: int, K: int, w_codes, w_scales, w_g: float, a_scales=None, a_g: float = 1.0,
+                row_idx=None, n_out=None):
+    """Two-level product: the single-level sums (W4A16 when a_scales is None,
+    else W4A4 with x the activation codes) times a_g * w_g, in fp64."""
+    if a_scales is None:
+        y = gemm_w4a16(x, M, K, w_codes, w_scales, row_idx=row_idx, n_out=n_out)
+    else:
+        y = gemm_w4a4(x, a_scales, M, K, w_codes, w_scales, row_idx=row_idx, n_out=n_out)
+    return y * (float(a_g) * float(w_g))

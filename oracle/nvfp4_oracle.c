@@ -251,6 +251,88 @@ void oracle_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, ui
 }
 
 /* ------------------------------------------------------------------------ */
+/* Two-level NVFP4: a per-tensor fp32 scale above the per-16 E4M3 scales       */
+/* ------------------------------------------------------------------------ */
+
+/* The deployed NVFP4 checkpoints come from NVFP4 quantization tools [P4
+ * section 1 and its sources: NVIDIA ModelOpt NVFP4 checkpoints]; the pages do
+ * not spell out their scaling.  Readings taken (the plainest that keeps the
+ * per-16 rule above unchanged):
+ *   - a tensor carries one positive fp32 global scale g, and an element is
+ *     e2m1(code) * e4m3(scale) * g;
+ *   - the offline quantizer picks g = fl32(amax / 2688), 2688 = 6 * 448 (the
+ *     largest e2m1 magnitude times the largest E4M3 scale), so the block
+ *     holding the tensor's amax gets scale 448; an all-zero tensor takes g = 1;
+ *   - every element is first divided by g in binary32, y = fl32(x / g), and
+ *     the single-level rule (scale from the block's max |y| / 6, codes against
+ *     it) is applied to y unchanged. */
+float oracle_global_scale(double amax)
+{
+    return amax > 0.0 ? (float)(amax / 2688.0) : 1.0f;
+}
+
+/* Quantize bf16 rows x [M][K] with a given global scale g (> 0): codes
+ * [M][K/2], scales [M][K/16] of y = fl32(x / g).  g = 1 gives exactly
+ * oracle_quantize. */
+void oracle_quantize_scaled(const uint16_t *x, int64_t M, int64_t K, float g, uint8_t *codes,
+                            uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < K / 16; ++b) {
+            double y[16], a = 0.0, s;
+            unsigned sc, cd[16];
+            for (int i = 0; i < 16; ++i) {
+                /* binary32 quotient: the double quotient rounded to binary32 */
+                y[i] = (double)(float)(oracle_bf16_value(x[m * K + b * 16 + i]) / (double)g);
+                if (fabs(y[i]) > a)
+                    a = fabs(y[i]);
+            }
+            sc = oracle_scale_code(a);
+            s = oracle_e4m3_value(sc);
+            scales[m * (K / 16) + b] = (uint8_t)sc;
+            for (int i = 0; i < 16; ++i) {
+                unsigned mag = (s == 0.0) ? 0u : oracle_e2m1_index(fabs(y[i]), s);
+                cd[i] = ((signbit(y[i]) ? 1u : 0u) << 3) | mag;
+            }
+            for (int j = 0; j < 8; ++j)
+                codes[m * (K / 2) + b * 8 + j] = (uint8_t)(cd[2 * j] | (cd[2 * j + 1] << 4));
+        }
+    }
+}
+
+/* Offline weight quantizer: bf16 weights w [N][K] -> two-level NVFP4 (codes,
+ * scales, returned g).  g comes from the whole tensor's max |w|. */
+float oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes,
+                             uint8_t *scales)
+{
+    double amax = 0.0;
+    float g;
+    for (int64_t i = 0; i < N * K; ++i) {
+        double v = fabs(oracle_bf16_value(w[i]));
+        if (v > amax)
+            amax = v;
+    }
+    g = oracle_global_scale(amax);
+    oracle_quantize_scaled(w, N, K, g, codes, scales);
+    return g;
+}
+
+/* Dequantize a two-level NVFP4 matrix to bf16: the exact value
+ * e2m1 * e4m3 * g rounded to binary32, then to bf16 (nearest even both). */
+void oracle_dequantize_scaled(const uint8_t *codes, const uint8_t *scales, float g, int64_t N,
+                              int64_t K, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_e2m1_value(code_at(codes + n * (K / 2), k)) *
+                       oracle_e4m3_value(scales[n * (K / 16) + k / 16]) * (double)g;
+            out[n * K + k] = oracle_bf16_round((double)(float)v);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Contractions                                                               */
 /* ------------------------------------------------------------------------ */
 
