@@ -347,6 +347,15 @@ def secondary(nv, torch, helpers_dev, reps=3):
     t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales))
     res["w4a4_M512_N17408_K5120_tflops"] = round(2 * 512 * 17408 * 5120 / t / 1e12, 2)
     del xd, xq, wc, ws
+    # two-level NVFP4: offline weight quantizer (amax pass + quantize pass)
+    log("secondary: offline weight quantizer")
+    wq = dev_bf16(wl.normal_bf16(np.random.default_rng(1), wl.MLP, wl.HIDDEN))
+    wqs = torch.empty(nv.lib().nvfp4_quantize_weight_workspace_size(wl.MLP, wl.HIDDEN),
+                      dtype=torch.uint8, device="cuda")
+    t = timeit(lambda: nv.quantize_weight(wq, workspace=wqs), n=10)
+    res["quantize_weight_N17408_K5120_GBs"] = round(
+        wl.MLP * wl.HIDDEN * (2 + 2 + 9 / 16) / t / 1e9, 1)   # two reads of bf16, codes + scales out
+    del wq, wqs
     # FP8 E4M3 KV-cache codec: bytes moved (bf16 in + codes out; codes in + bf16 out)
     log("secondary: KV cache store / load")
     kw = wl.kv_store(8192)

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "library_path", "dequantize", "quantize", "gemm", "gemm_workspace_size", "moe_align",
-    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3", "kv_load_e4m3", "BF16", "FP32", "NVFP4", "EPI_NONE",
+    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3", "kv_load_e4m3", "quantize_scaled", "quantize_weight",
+    "dequantize_scaled", "gemm_scaled", "BF16", "FP32", "NVFP4", "EPI_NONE",
     "EPI_SWIGLU",
 ]
 
@@ -47,6 +48,12 @@ _SIGS = {
     "nvfp4_head_topk_workspace_size": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_head_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz,
                          _vp], _int),
+    "nvfp4_quantize_scaled": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "nvfp4_quantize_weight_workspace_size": ([_i64, _i64], _sz),
+    "nvfp4_quantize_weight": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_dequantize_scaled": ([_vp, _vp, _vp, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_gemm_scaled": ([_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64,
+                           _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_kv_store_e4m3": ([_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp], _int),
     "nvfp4_kv_load_e4m3": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
                             _vp, _vp], _int),
@@ -167,6 +174,73 @@ def gemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, a_scale
     _check(lib().nvfp4_gemm(NVFP4 if w4a4 else BF16, _ptr(a), _ptr(a_scales), M, N, K,
                             _ptr(w_codes), _ptr(w_scales), _ptr(row_idx), n_out, odt, _ptr(out),
                             _ptr(ws), wsz, _stream(a.device)))
+    return out
+
+
+# ---- two-level NVFP4 (per-tensor fp32 scale on the device) ------------------------------
+
+def quantize_scaled(x: torch.Tensor, global_scale: torch.Tensor, codes=None, scales=None):
+    """bf16 [M, K] with a per-tensor scale (fp32 tensor of one element on the
+    GPU) -> (codes, scales) of fl32(x / g)."""
+    _gpu(x, global_scale, codes, scales)
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_quantize_scaled(_ptr(x), M, K, _ptr(global_scale), _ptr(codes),
+                                       _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def quantize_weight(w: torch.Tensor, workspace=None):
+    """Offline weight quantizer: bf16 [N, K] -> (codes [N, K/2], scales
+    [N, K/16], global_scale fp32 [1]), all on the GPU."""
+    _gpu(w, workspace)
+    N, K = w.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=w.device)
+    g = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws, wsz = _workspace(int(lib().nvfp4_quantize_weight_workspace_size(N, K)), w.device,
+                         workspace)
+    _check(lib().nvfp4_quantize_weight(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(g),
+                                       _ptr(ws), wsz, _stream(w.device)))
+    return codes, scales, g
+
+
+def dequantize_scaled(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                      out=None) -> torch.Tensor:
+    """Two-level NVFP4 -> bf16 [N, K]: bf16(fl32(e2m1 * e4m3 * g))."""
+    _gpu(codes, scales, global_scale, out)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().nvfp4_dequantize_scaled(_ptr(codes), _ptr(scales), _ptr(global_scale), N, K,
+                                         _ptr(out), _stream(codes.device)))
+    return out
+
+
+def gemm_scaled(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                w_global_scale=None, a_scales=None, a_global_scale=None, row_idx=None,
+                out_dtype=torch.bfloat16, out=None, workspace=None) -> torch.Tensor:
+    """gemm() of two-level operands: the output is multiplied by
+    a_global_scale * w_global_scale (fp32 device scalars; None stands for 1)."""
+    _gpu(a, w_codes, w_scales, w_global_scale, a_scales, a_global_scale, row_idx, out, workspace)
+    w4a4 = a_scales is not None
+    M = a.shape[0]
+    K = a.shape[1] * (2 if w4a4 else 1)
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise RuntimeError(f"K mismatch: activations K={K}, weights K={w_codes.shape[1] * 2}")
+    n_out = N if row_idx is None else row_idx.numel()
+    odt = {torch.bfloat16: BF16, torch.float32: FP32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, n_out), dtype=out_dtype, device=a.device)
+    ws, wsz = _workspace(gemm_workspace_size(M, N, K, n_out, w4a4), a.device, workspace)
+    _check(lib().nvfp4_gemm_scaled(NVFP4 if w4a4 else BF16, _ptr(a), _ptr(a_scales),
+                                   _ptr(a_global_scale), M, N, K, _ptr(w_codes), _ptr(w_scales),
+                                   _ptr(w_global_scale), _ptr(row_idx), n_out, odt, _ptr(out),
+                                   _ptr(ws), wsz, _stream(a.device)))
     return out
 
 

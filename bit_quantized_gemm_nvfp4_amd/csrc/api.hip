@@ -106,10 +106,14 @@ size_t nvfp4_gemm_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K, i
   return round_up(g.a_dequant_bytes, 256) + g.partial_bytes;
 }
 
-int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
-               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
-               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
-               void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+              int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+              const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+              void* workspace, size_t workspace_bytes, void* stream, Alpha alpha) {
   if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
   if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
   if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
@@ -137,7 +141,7 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
               (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16");
     void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
     return launched(launch_gemm(w4a4, a, a_scales, M, K, w_codes, w_scales, row_idx, n_out,
-                                out_dtype == NVFP4_FP32, out, partial, st));
+                                out_dtype == NVFP4_FP32, out, partial, st, alpha));
   }
   const uint16_t* x = static_cast<const uint16_t*>(a);
   if (w4a4) {
@@ -157,10 +161,87 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
     const int64_t mc = (M - m0) < g.m_chunk ? (M - m0) : g.m_chunk;
     int rc = launch_gemv(g.gemv, x + m0 * K, mc, K, w_codes, w_scales, row_idx, n_out,
                          out_dtype == NVFP4_FP32, static_cast<char*>(out) + m0 * n_out * osz,
-                         partial, st);
+                         partial, st, alpha);
     if (rc != 0) return NVFP4_ERROR_LAUNCH;
   }
   return NVFP4_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                   out, workspace, workspace_bytes, stream, Alpha{});
+}
+
+int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
+                      const float* a_global_scale, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* w_codes, const uint8_t* w_scales,
+                      const float* w_global_scale, const int32_t* row_idx, int64_t n_out,
+                      int out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (a_dtype != NVFP4_NVFP4 && a_global_scale) return NVFP4_ERROR_INVALID_VALUE;
+  if ((a_global_scale && (reinterpret_cast<uintptr_t>(a_global_scale) & 3u)) ||
+      (w_global_scale && (reinterpret_cast<uintptr_t>(w_global_scale) & 3u)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  Alpha alpha;
+  alpha.a = a_global_scale;
+  alpha.w = w_global_scale;
+  return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                   out, workspace, workspace_bytes, stream, alpha);
+}
+
+int nvfp4_quantize_scaled(const uint16_t* x, int64_t M, int64_t K, const float* global_scale,
+                          uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !global_scale || !codes || !scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(global_scale) & 3u))
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (M * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_quantize_scaled(x, M, K, global_scale, codes, scales, as_stream(stream)));
+}
+
+size_t nvfp4_quantize_weight_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return quantize_weight_workspace_bytes();
+}
+
+int nvfp4_quantize_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes,
+                          uint8_t* scales, float* global_scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!w || !codes || !scales || !global_scale) return NVFP4_ERROR_INVALID_VALUE;
+  if (N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(global_scale) & 3u))
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!workspace || workspace_bytes < quantize_weight_workspace_bytes())
+    return NVFP4_ERROR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+  return launched(launch_quantize_weight(w, N, K, codes, scales, global_scale, workspace,
+                                         as_stream(stream)));
+}
+
+int nvfp4_dequantize_scaled(const uint8_t* codes, const uint8_t* scales,
+                            const float* global_scale, int64_t N, int64_t K, uint16_t* out,
+                            void* stream) {
+  if (!codes || !scales || !global_scale || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(global_scale) & 3u))
+    return NVFP4_ERROR_INVALID_VALUE;
+  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  return launched(launch_dequantize_scaled(codes, scales, global_scale, N, K, out,
+                                           as_stream(stream)));
 }
 
 size_t nvfp4_topk_workspace_size(int64_t M, int64_t n, int64_t k) {

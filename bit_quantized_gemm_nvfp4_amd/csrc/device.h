@@ -78,6 +78,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Output multiplier of a product of two-level NVFP4 tensors: *a * *w (a null
+// pointer stands for 1).  Callers multiply only when either pointer is set.
+__device__ __forceinline__ float alpha_of(const float* a, const float* w) {
+  return (a ? *a : 1.0f) * (w ? *w : 1.0f);
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -33,6 +33,8 @@ struct GemmArgs {
   int out_f32;
   int tiles_m, tiles_n;
   int splits;               // split-K parts (1: no split)
+  const float* ga;          // two-level scales: final sums are multiplied by
+  const float* gw;          // *ga * *gw (null: 1)
 };
 
 template <bool A_NVFP4>
@@ -84,6 +86,8 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   const bool part = g.splits > 1;
   void* const dst = part ? static_cast<void*>(g.partial + (int64_t)z * g.M * g.N) : g.out;
   const bool f32 = part || g.out_f32;
+  const bool scaled = !part && (g.ga || g.gw);
+  const float alpha = scaled ? alpha_of(g.ga, g.gw) : 1.0f;
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's quarter.
@@ -98,8 +102,9 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
       for (int q = 0; q < 4; ++q) {
         const int64_t col = n0 + gemm_tile_col(j, q);
         const int64_t off = row * g.N + col;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (scaled) v0 *= alpha, v1 *= alpha, v2 *= alpha, v3 *= alpha;
         if (vec && col + 3 < g.N) {
           if (f32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + off) = f32x4{v0, v1, v2, v3};
@@ -127,15 +132,19 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
 // Split-K sum: out = sum over splits (in split order) of the fp32 partials.
 __global__ void __launch_bounds__(256) k_gemm_reduce(const float* __restrict__ partial,
                                                      int splits, int64_t count, int out_f32,
+                                                     const float* ga, const float* gw,
                                                      void* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= count) return;
+  const bool scaled = ga || gw;
+  const float alpha = scaled ? alpha_of(ga, gw) : 1.0f;
   if (i + 4 <= count) {
     f32x4 v = *reinterpret_cast<const f32x4*>(partial + i);
     for (int z = 1; z < splits; ++z) {
       const f32x4 p = *reinterpret_cast<const f32x4*>(partial + (int64_t)z * count + i);
       v[0] += p[0], v[1] += p[1], v[2] += p[2], v[3] += p[3];
     }
+    if (scaled) v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
     if (out_f32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = v;
     } else {
@@ -148,6 +157,7 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const float* __restrict__ p
   for (int64_t j = i; j < count; ++j) {
     float v = partial[j];
     for (int z = 1; z < splits; ++z) v += partial[(int64_t)z * count + j];
+    if (scaled) v *= alpha;
     if (out_f32)
       static_cast<float*>(out)[j] = v;
     else
@@ -185,10 +195,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus) {
 
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
-                bool out_f32, void* out, void* workspace, hipStream_t stream) {
+                bool out_f32, void* out, void* workspace, hipStream_t stream, Alpha alpha) {
   // activation offsets inside a 256-row tile are 32-bit byte offsets
   if (K > ((int64_t)1 << 22)) return -1;
   GemmArgs g;
+  g.ga = alpha.a;
+  g.gw = alpha.w;
   g.a = a;
   g.a_scales = a_scales;
   g.wc = wc;
@@ -219,7 +231,7 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
     const int64_t threads = (count + 3) / 4;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(workspace), g.splits, count, out_f32 ? 1 : 0,
-                       out);
+                       alpha.a, alpha.w, out);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

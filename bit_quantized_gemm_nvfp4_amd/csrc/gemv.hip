@@ -38,6 +38,8 @@ struct GemvArgs {
   int M;
   int steps;               // ceil(K / step) for the kernel's step size
   int out_f32;
+  const float* ga;         // two-level scales: the output is multiplied by
+  const float* gw;         // *ga * *gw (null: 1); applied to final sums only
 };
 
 template <int MT, int TR, int NW>
@@ -79,6 +81,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
                                   [x, K](int m) { return x + (int64_t)m * K; });
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
+  const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
+  const float alpha = scaled ? alpha_of(a.ga, a.gw) : 1.0f;
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
     const int64_t j = (tile0 + t) * 16 + ln;
@@ -90,7 +94,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
         const int m = mt * 16 + 4 * q + r;
         if (m >= a.M) continue;
         const int64_t o = (int64_t)m * a.n_out + j;
-        const float v = acc[t][mt][r];
+        const float v = scaled ? acc[t][mt][r] * alpha : acc[t][mt][r];
         if (gridDim.y > 1)
           a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
         else if (a.out_f32)
@@ -152,6 +156,8 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
 
   // acc[t][g][r] of lane (blk, cn) is block blk's part of row 4g+r, column
   // 4*tile + cn; sum the 16 blocks, then lane blk == m stores row m.
+  const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
+  const float alpha = scaled ? alpha_of(a.ga, a.gw) : 1.0f;
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
     const int64_t j = (tile0 + t) * 4 + cn;
@@ -161,7 +167,8 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * g + r;
         if (m >= a.M) continue;  // uniform
-        const float v = gemv4_reduce(acc[t][g][r]);
+        const float s4 = gemv4_reduce(acc[t][g][r]);
+        const float v = scaled ? s4 * alpha : s4;
         if (blk != m || j >= a.n_out) continue;
         const int64_t o = (int64_t)m * a.n_out + j;
         if (gridDim.y > 1)
@@ -177,11 +184,13 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
 
 __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ partial,
                                                        int splits, int64_t count, int out_f32,
+                                                       const float* ga, const float* gw,
                                                        void* __restrict__ out) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float v = 0.f;
   for (int z = 0; z < splits; ++z) v += partial[(int64_t)z * count + i];
+  if (ga || gw) v *= alpha_of(ga, gw);
   if (out_f32)
     static_cast<float*>(out)[i] = v;
   else
@@ -272,8 +281,10 @@ size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out) {
 
 int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
-                void* out, void* workspace, hipStream_t stream) {
+                void* out, void* workspace, hipStream_t stream, Alpha alpha) {
   GemvArgs a;
+  a.ga = alpha.a;
+  a.gw = alpha.w;
   a.x = x;
   a.wc = wc;
   a.ws = ws;
@@ -320,7 +331,7 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
     const int64_t count = M * n_out;
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
                        stream, static_cast<const float*>(workspace), p.z, count,
-                       out_f32 ? 1 : 0, out);
+                       out_f32 ? 1 : 0, alpha.a, alpha.w, out);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

@@ -16,6 +16,25 @@ int launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, in
 int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                     hipStream_t stream);
 
+// Two-level NVFP4 (per-tensor fp32 scale g, a device scalar).  Quantize with
+// a given g; the offline weight quantizer (g from the tensor's amax, written
+// to *g; kAbsmaxParts partial maxima in workspace); dequantize with g.
+constexpr int kAbsmaxParts = 256;
+int launch_quantize_scaled(const uint16_t* x, int64_t M, int64_t K, const float* g,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+size_t quantize_weight_workspace_bytes();
+int launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* scales, float* g, void* workspace, hipStream_t stream);
+int launch_dequantize_scaled(const uint8_t* codes, const uint8_t* scales, const float* g,
+                             int64_t N, int64_t K, uint16_t* out, hipStream_t stream);
+
+// Output multiplier of a product of two-level tensors: alpha = *a * *w, each
+// factor 1 when its pointer is null (then no multiply happens at all).
+struct Alpha {
+  const float* a = nullptr;
+  const float* w = nullptr;
+};
+
 struct GemvPlan {
   bool small;  // M <= 4: 4x4x4-block kernel (tiles of 4 rows)
   int mt;  // 16-row activation tiles (M <= 16 * mt)
@@ -28,7 +47,7 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
 int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
-                void* out, void* workspace, hipStream_t stream);
+                void* out, void* workspace, hipStream_t stream, Alpha alpha = {});
 
 // Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
 // or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  When
@@ -38,7 +57,7 @@ int gemm_splits(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
-                bool out_f32, void* out, void* workspace, hipStream_t stream);
+                bool out_f32, void* out, void* workspace, hipStream_t stream, Alpha alpha = {});
 
 // Top-k of each row of fp32 logits [M][n] (k <= kTopkMaxK), best first: larger
 // value, then smaller column; -0 below +0.  ids are ids_map[column] (or the

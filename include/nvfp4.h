@@ -128,6 +128,48 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Two-level NVFP4.  The deployed NVFP4 checkpoints come from NVFP4
+ * quantization tools ("What 350+ Experiments ...", section 1 and its
+ * sources); a tensor then carries, above its per-16 E4M3 scales, one positive
+ * fp32 global scale g, and an element is e2m1(code) * e4m3(scale) * g.  g is
+ * a DEVICE pointer to one float (4-byte aligned).
+ *
+ * nvfp4_quantize_scaled: activations with a given g (e.g. a calibrated static
+ * scale): y = fl32(x / g) (binary32 division, nearest even), then exactly the
+ * nvfp4_quantize rule on y.  g = 1 reproduces nvfp4_quantize.  Bit-exact.
+ *
+ * nvfp4_quantize_weight: offline weight quantizer, bf16 w [N][K] -> codes,
+ * scales and *global_scale = fl32(amax / 2688) (2688 = 6 * 448, so the
+ * block holding max |w| gets scale 448; 1 for an all-zero tensor), then
+ * nvfp4_quantize_scaled with that g.  Bit-exact.  workspace: >=
+ * nvfp4_quantize_weight_workspace_size(N, K) bytes.
+ *
+ * nvfp4_dequantize_scaled: out[n][k] = bf16(fl32(e2m1 * e4m3 * g)) (the first
+ * product is exact; one binary32 rounding, then bf16, nearest even).
+ *
+ * nvfp4_gemm_scaled: nvfp4_gemm of two-level operands,
+ *   out = (a . W^T) * (a_g * w_g),
+ * the factor fl32(a_g * w_g) applied once to the fp32 sums (NULL pointer: 1;
+ * a_global_scale only with NVFP4 activations).  Same shapes, workspace
+ * (nvfp4_gemm_workspace_size) and tolerance as nvfp4_gemm.  K % 32 == 0 for all.
+ */
+int nvfp4_quantize_scaled(const uint16_t *x, int64_t M, int64_t K, const float *global_scale,
+                          uint8_t *codes, uint8_t *scales, void *stream);
+size_t nvfp4_quantize_weight_workspace_size(int64_t N, int64_t K);
+int nvfp4_quantize_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes,
+                          uint8_t *scales, float *global_scale, void *workspace,
+                          size_t workspace_bytes, void *stream);
+int nvfp4_dequantize_scaled(const uint8_t *codes, const uint8_t *scales,
+                            const float *global_scale, int64_t N, int64_t K, uint16_t *out,
+                            void *stream);
+int nvfp4_gemm_scaled(int a_dtype, const void *a, const uint8_t *a_scales,
+                      const float *a_global_scale, int64_t M, int64_t N, int64_t K,
+                      const uint8_t *w_codes, const uint8_t *w_scales,
+                      const float *w_global_scale, const int32_t *row_idx, int64_t n_out,
+                      int out_dtype, void *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
  * Draft proposal from a head's logits ("Serving Qwen3.8-27B in 4-bit ...",
  * section "The masked head trick": the draft proposes tokens only from the
  * kept rows of the head).  For each row m of logits (fp32 [M][n]) the k best

@@ -177,3 +177,24 @@ def test_kv_codec_validation(L):
     assert ld(W=40) == NOT_SUPPORTED
     assert ld(out=MIS) == INVALID
     assert ld(scale=1e-40) == INVALID
+
+
+def test_two_level_validation(L):
+    G = ctypes.c_void_p(0x50000)
+    G_MIS = ctypes.c_void_p(0x50002)
+    assert L.nvfp4_quantize_scaled(P, 4, 64, NULL, P2, P3, NULL) == INVALID
+    assert L.nvfp4_quantize_scaled(P, 4, 48, G, P2, P3, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_quantize_scaled(P, 4, 64, G_MIS, P2, P3, NULL) == INVALID
+    need = L.nvfp4_quantize_weight_workspace_size(64, 64)
+    assert need > 0
+    assert L.nvfp4_quantize_weight(P, 64, 64, P2, P3, G, NULL, 0, NULL) == WORKSPACE
+    assert L.nvfp4_quantize_weight(P, 64, 64, P2, P3, G, P4, need - 1, NULL) == WORKSPACE
+    assert L.nvfp4_quantize_weight(P, 64, 64, P2, P3, NULL, P4, need, NULL) == INVALID
+    assert L.nvfp4_dequantize_scaled(P, P2, NULL, 4, 64, P3, NULL) == INVALID
+    assert L.nvfp4_dequantize_scaled(P, P2, G, 4, 40, P3, NULL) == NOT_SUPPORTED
+
+    def gs(a_dtype=0, ag=NULL, wg=G, **kw):
+        return L.nvfp4_gemm_scaled(a_dtype, P, P4 if a_dtype == 2 else NULL, ag, 4, 64, 256, P2,
+                                   P3, wg, NULL, 64, 0, P4, NULL, 0, NULL)
+    assert gs(ag=G) == INVALID                 # activation scale needs NVFP4 activations
+    assert gs(wg=G_MIS) == INVALID
