@@ -46,6 +46,9 @@ template <int MT, int TR, int NW>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
   __shared__ uint16_t win[2 * 16 * MT * kXWin];
+  // scale blocks (one-tile activations only: with two the extra registers
+  // cost more occupancy than the fetched bytes they save)
+  __shared__ uint32_t scl[MT == 1 ? NW * TR * 512 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 15, q = lane >> 4;
@@ -76,9 +79,17 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* x = a.x;
-  gemv_accumulate_win<MT, TR, XP>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
-                                  (int)(K / kGemvStep),
-                                  [x, K](int m) { return x + (int64_t)m * K; });
+  auto row_ptr = [x, K](int m) { return x + (int64_t)m * K; };
+  bool blocks = false;
+  if constexpr (MT == 1) {
+    blocks = K % 256 == 0;
+    if (blocks)
+      gemv_accumulate_win_blk<MT, TR, XP>(acc, cptr, sptr, win, scl + wave * TR * 512,
+                                          xrow_off, a.M, K, zs0, zs1, row_ptr);
+  }
+  if (!blocks)
+    gemv_accumulate_win<MT, TR, XP>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
+                                    (int)(K / kGemvStep), row_ptr);
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
   const bool scaled = gridDim.y == 1 && (a.ga || a.gw);

@@ -30,6 +30,8 @@
 // Result layout: lane holds C[m = 4*(lane/16) + r][n = lane % 16], r = 0..3.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace nvfp4 {
@@ -271,6 +273,109 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
     compute_wstep<MT, TR>(acc, bt, xl);
+  }
+}
+
+// ---- scale blocks ---------------------------------------------------------------
+// A wave reads its rows' scales 8 steps at a time instead of 4 bytes per lane
+// and step: each row's 128 scale bytes of a block are read in two bursts (the
+// block's last two steps prefetch the next block, one half each) and kept in
+// the wave's own LDS area [TR][8 steps][64 words], word n*4 + q of step j being
+// the four scale bytes lane (n, q) uses at that step.  Per-step 16-byte reads
+// let the streaming code lines evict a row's scale line between its uses (the
+// fetched bytes grew by up to a fifth); block reads fetch each line once.  The
+// wave alone writes and reads its area, and LDS operations of one wave
+// complete in order, so no barrier is needed.  Rows' scale bytes must be
+// 16-byte aligned (K % 256 == 0).
+
+template <int TR>
+__device__ __forceinline__ void load_wcodes(WStep<TR>& b, const uint8_t* const (&cptr)[TR], int s) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const int64_t k0 = (int64_t)s * kGemvStep + 64 * q;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    b.c[t][0] = *reinterpret_cast<const u32x4*>(cptr[t] + k0 / 2);
+    b.c[t][1] = *reinterpret_cast<const u32x4*>(cptr[t] + k0 / 2 + 16);
+  }
+}
+
+// 8-step scale blocks, loaded in two halves: half h of the block starting at
+// step B is, for lane (n, q), the 16-byte group of step B + 2q + h of row n;
+// it is stored to LDS rows 2q + h ([TR][8 steps][64 words: n*4 + q']).
+template <int TR>
+__device__ __forceinline__ void load_shalf(u32x4 (&p)[TR], const uint8_t* const (&sptr)[TR], int b,
+                                           int h, int last) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const int st = min(b + 2 * q + h, last);
+#pragma unroll
+  for (int t = 0; t < TR; ++t) p[t] = *reinterpret_cast<const u32x4*>(sptr[t] + 16 * st);
+}
+
+template <int TR>
+__device__ __forceinline__ void store_shalf(uint32_t* lds, const u32x4 (&p)[TR], int h) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+    *reinterpret_cast<u32x4*>(lds + t * 512 + (2 * q + h) * 64 + n * 4) = p[t];
+}
+
+template <int TR>
+__device__ __forceinline__ void read_sblock(WStep<TR>& b, const uint32_t* lds, int j) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) b.sc[t] = lds[t * 512 + j * 64 + n * 4 + q];
+}
+
+template <int MT, int TR, int XP, typename RowPtr>
+__device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
+                                                        const uint8_t* const (&cptr)[TR],
+                                                        const uint8_t* const (&sptr)[TR],
+                                                        uint16_t* win, uint32_t* my,
+                                                        const int (&xrow_off)[MT], int M,
+                                                        int64_t K, int s0, int s1,
+                                                        RowPtr row_ptr) {
+  if (s0 >= s1) return;
+  constexpr int wsz = 16 * MT * kXWin;
+  u32x4 xv[XP];
+  xwin_load<XP>(xv, M, K, s0, row_ptr);
+  xwin_store<XP>(win, xv);
+  const int e = s1;  // K % 256 == 0: every step is full
+  u32x4 ph[TR];
+  load_shalf<TR>(ph, sptr, s0, 0, e - 1);
+  store_shalf<TR>(my, ph, 0);
+  load_shalf<TR>(ph, sptr, s0, 1, e - 1);
+  store_shalf<TR>(my, ph, 1);
+  __syncthreads();
+  int s = s0, cur = 0, j = 0;  // j: position of step s in its 8-step block
+  WStep<TR> b0, b1;
+  load_wcodes<TR>(b0, cptr, s);
+  auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
+    xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+    load_wcodes<TR>(bn, cptr, min(s + 1, e - 1));
+    // the next block starts at step s + 8 - j; its two halves are loaded at
+    // the block's last two steps
+    const bool sh = j >= 6;
+    if (sh) load_shalf<TR>(ph, sptr, s + 8 - j, j - 6, e - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_sblock<TR>(bc, my, j);
+    {
+      const uint16_t* xl[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+      compute_wstep<MT, TR>(acc, bc, xl);
+    }
+    xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
+    // half 0 fills rows 0, 2, 4, 6 (row 7 is still read at the last step);
+    // half 1 fills rows 1, 3, 5, 7 after it
+    if (sh) store_shalf<TR>(my, ph, j - 6);
+    __syncthreads();
+    cur ^= 1;
+    j = (j + 1) & 7;
+    return ++s >= e;
+  };
+  while (true) {
+    if (stage(b0, b1)) break;
+    if (stage(b1, b0)) break;
   }
 }
 
