@@ -179,22 +179,25 @@ def time_decode_graph(dec, torch, steps, warmup):
 
 
 def time_decode(dec, torch, steps, warmup):
-    for _ in range(warmup):
-        for c in dec.calls:
-            c[4]()
-    torch.cuda.synchronize()
+    """Per-call pass: every call launched on its own, bracketed by HIP events on
+    the launch stream.  Warm-up and timed calls are enqueued without a
+    synchronisation between them, so the host runs ahead of the GPU and each
+    event pair brackets one kernel (plus its split-K reduce) running back to
+    back with the others, not the host's launch gaps."""
     n = len(dec.calls)
     starts = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
     ends = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    for _ in range(warmup):
+        for c in dec.calls:
+            c[4]()
     for s in range(steps):
         for i, c in enumerate(dec.calls):
             starts[s][i].record()
             c[4]()
             ends[s][i].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = starts[0][0].elapsed_time(ends[-1][-1]) / 1e3
     per_call_ms = np.array([[starts[s][i].elapsed_time(ends[s][i]) for i in range(n)]
                             for s in range(steps)])
     return wall, per_call_ms
