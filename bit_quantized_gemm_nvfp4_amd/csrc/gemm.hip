@@ -27,36 +27,66 @@ struct GemmArgs {
   const uint8_t* ws;        // weight scales [rows][K/16]
   const int32_t* row_idx;   // output column n uses weight row row_idx[n]; null: row n
   void* out;                // [M][N] bf16 or fp32
-  float* partial;           // splits > 1: fp32 [splits][M][N]
+  float* partial;           // split tiles: fp32 [tail tiles][splits][256 * 256], tile-local
   int64_t M, N, K;          // N: output columns
   int64_t k_split;          // K elements per split (a multiple of 64; the last may be shorter)
   int out_f32;
   int tiles_m, tiles_n;
-  int splits;               // split-K parts (1: no split)
+  int full;                 // tiles 0 .. full-1 of the tile order run whole (full % 8 == 0;
+                            // workgroups past the last tile exit)
+  int tail;                 // tiles full .. full+tail-1 run as `splits` K parts each
+  int splits;
   const float* ga;          // two-level scales: final sums are multiplied by
   const float* gw;          // *ga * *gw (null: 1)
 };
+
+// Tile `lin` of the launch order -> (tm, tn): n fastest within groups of 8
+// m-tiles, so the tiles one XCD holds at once share activation rows and
+// weight columns in its L2.
+__device__ __forceinline__ void gemm_tile_of(int lin, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int group = lin / (GM * tiles_n);
+  const int gm0 = group * GM;
+  const int gsz = min(GM, tiles_m - gm0);
+  const int in_group = lin - group * GM * tiles_n;
+  tm = gm0 + in_group % gsz;
+  tn = in_group / gsz;
+}
 
 template <bool A_NVFP4>
 __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   extern __shared__ char lds[];
 
-  const int tiles = g.tiles_m * g.tiles_n;
-  const int total = tiles * g.splits;
-  const int per_xcd = (total + 7) / 8;
-  const int lin_all = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (lin_all >= total) return;
-  const int z = lin_all / tiles, lin = lin_all - z * tiles;  // split z of tile `lin`
-  constexpr int GM = 8;
-  const int group = lin / (GM * g.tiles_n);
-  const int gm0 = group * GM;
-  const int gsz = min(GM, g.tiles_m - gm0);
-  const int in_group = lin - group * GM * g.tiles_n;
-  const int tm = gm0 + in_group % gsz, tn = in_group / gsz;
+  // Workgroups 0 .. full-1 take the whole-K tiles, XCD-aware: workgroups are
+  // dispatched round-robin over the 8 XCDs, and XCD x takes the contiguous
+  // band [x * full/8, (x+1) * full/8) of the tile order.  The workgroups after
+  // them (dispatched last) take the K parts of the remaining tiles, which
+  // would otherwise leave the chip half idle in the last round.
+  // The K parts are banded the same way (part slowest), so an XCD holds
+  // neighbouring tiles of the same part.
+  int lin, z = 0, tail = -1;
+  const int b = blockIdx.x;
+  if (b < g.full) {
+    const int per_xcd = g.full / 8;
+    lin = (b & 7) * per_xcd + (b >> 3);
+    if (lin >= g.tiles_m * g.tiles_n) return;
+  } else {
+    const int items = g.tail * g.splits;
+    const int per_xcd = (items + 7) / 8;
+    const int rb = b - g.full;
+    const int r = (rb & 7) * per_xcd + (rb >> 3);
+    if (r >= items) return;
+    z = r / g.tail;
+    tail = r - z * g.tail;
+    lin = g.full + tail;
+  }
+  int tm, tn;
+  gemm_tile_of(lin, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t K = g.K;
-  const int64_t k_lo = (int64_t)z * g.k_split;
-  const int64_t k_len = min(g.k_split, K - k_lo);
+  const bool part = tail >= 0 && g.splits > 1;
+  const int64_t k_lo = part ? (int64_t)z * g.k_split : 0;
+  const int64_t k_len = part ? min(g.k_split, K - k_lo) : K;
   const int t = threadIdx.x;
 
   // sources (rows past M or N are clamped to the last one; never stored)
@@ -82,15 +112,23 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   gemm_zero_acc(acc);
   gemm_mainloop<A_NVFP4>(acc, lds, src, a_tile_base, k_len);
 
-  // split z > 0 or any split of a split-K launch: fp32 partials
-  const bool part = g.splits > 1;
-  void* const dst = part ? static_cast<void*>(g.partial + (int64_t)z * g.M * g.N) : g.out;
-  const bool f32 = part || g.out_f32;
-  const bool scaled = !part && (g.ga || g.gw);
-  const float alpha = scaled ? alpha_of(g.ga, g.gw) : 1.0f;
-
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's quarter.
+  if (part) {  // fp32 partial of this K part, tile-local [256][256]
+    float* dst = g.partial + ((int64_t)tail * g.splits + z) * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(dst + gemm_tile_row(i) * BN + gemm_tile_col(j, q)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+    return;
+  }
+  const bool scaled = g.ga || g.gw;
+  const float alpha = scaled ? alpha_of(g.ga, g.gw) : 1.0f;
   const bool vec = (g.N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -106,22 +144,22 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
         float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
         if (scaled) v0 *= alpha, v1 *= alpha, v2 *= alpha, v3 *= alpha;
         if (vec && col + 3 < g.N) {
-          if (f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + off) = f32x4{v0, v1, v2, v3};
+          if (g.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + off) = f32x4{v0, v1, v2, v3};
           } else {
             const u32x2 pk = {(uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16),
                               (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16)};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + off) = pk;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = pk;
           }
         } else {
           const float v[4] = {v0, v1, v2, v3};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (col + e >= g.N) break;
-            if (f32)
-              static_cast<float*>(dst)[off + e] = v[e];
+            if (g.out_f32)
+              static_cast<float*>(g.out)[off + e] = v[e];
             else
-              static_cast<uint16_t*>(dst)[off + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+              static_cast<uint16_t*>(g.out)[off + e] = f32_to_bf16_bits(v[e]);
           }
         }
       }
@@ -129,68 +167,91 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   }
 }
 
-// Split-K sum: out = sum over splits (in split order) of the fp32 partials.
-__global__ void __launch_bounds__(256) k_gemm_reduce(const float* __restrict__ partial,
-                                                     int splits, int64_t count, int out_f32,
-                                                     const float* ga, const float* gw,
-                                                     void* __restrict__ out) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i >= count) return;
-  const bool scaled = ga || gw;
-  const float alpha = scaled ? alpha_of(ga, gw) : 1.0f;
-  if (i + 4 <= count) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(partial + i);
-    for (int z = 1; z < splits; ++z) {
-      const f32x4 p = *reinterpret_cast<const f32x4*>(partial + (int64_t)z * count + i);
-      v[0] += p[0], v[1] += p[1], v[2] += p[2], v[3] += p[3];
-    }
-    if (scaled) v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
-    if (out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = v;
+// Split tiles: out = sum over K parts (in part order) of the tile-local fp32
+// partials.  64 workgroups per tile, 4 rows of 256 columns each (4 columns per
+// thread).
+__global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
+  const int tail = blockIdx.x >> 6;
+  const int lr = (blockIdx.x & 63) * 4 + (threadIdx.x >> 6);
+  const int lc = (threadIdx.x & 63) * 4;
+  int tm, tn;
+  gemm_tile_of(g.full + tail, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t row = (int64_t)tm * BM + lr, col = (int64_t)tn * BN + lc;
+  if (row >= g.M || col >= g.N) return;
+  const float* p = g.partial + (int64_t)tail * g.splits * (BM * BN) + lr * BN + lc;
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  for (int z = 1; z < g.splits; ++z) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN));
+    v[0] += q[0], v[1] += q[1], v[2] += q[2], v[3] += q[3];
+  }
+  if (g.ga || g.gw) {
+    const float alpha = alpha_of(g.ga, g.gw);
+    v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
+  }
+  const int64_t off = row * g.N + col;
+  if ((g.N & 3) == 0 && col + 3 < g.N) {
+    if (g.out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + off) = v;
     } else {
       const u32x2 pk = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
                         (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i) = pk;
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = pk;
     }
     return;
   }
-  for (int64_t j = i; j < count; ++j) {
-    float v = partial[j];
-    for (int z = 1; z < splits; ++z) v += partial[(int64_t)z * count + j];
-    if (scaled) v *= alpha;
-    if (out_f32)
-      static_cast<float*>(out)[j] = v;
+  for (int e = 0; e < 4 && col + e < g.N; ++e) {
+    if (g.out_f32)
+      static_cast<float*>(g.out)[off + e] = v[e];
     else
-      static_cast<uint16_t*>(out)[j] = f32_to_bf16_bits(v);
+      static_cast<uint16_t*>(g.out)[off + e] = f32_to_bf16_bits(v[e]);
   }
 }
 
 }  // namespace
 
-int gemm_splits(int64_t M, int64_t n_out, int64_t K, int num_cus) {
-  // One 256 x 256 tile per CU at a time (128 KB of LDS): with z splits the
-  // compute takes rounds(z) = ceil(tiles * z / CUs) rounds of 1/z of K, and
-  // the z fp32 partials are written and read once more.  Estimate both with
-  // the measured rates (about 3.5 TFLOP/s per CU, 5 TB/s of HBM) and take the
-  // cheapest z, keeping >= 8 steps (512 elements of K) per split.
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus) {
+  // One 256 x 256 tile per CU at a time (128 KB of LDS), so a launch runs in
+  // rounds of num_cus tiles.  Whole rounds run unsplit; the tiles of a last,
+  // partly filled round (or all tiles, when there are fewer than num_cus) are
+  // split over K so that their parts fill the chip.  For the all-split case a
+  // cost model over rounds and the extra fp32 partial traffic (about 3.5
+  // TFLOP/s per CU and 5 TB/s of HBM) picks z <= 8; every part keeps >= 8
+  // K-steps (512 elements).
+  GemmSplitPlan p;
   const int64_t tiles = ((M + BM - 1) / BM) * ((n_out + BN - 1) / BN);
-  if (tiles >= num_cus) return 1;  // only a launch that cannot fill the chip once is split
   const int64_t steps = (K + BK - 1) / BK;
+  const int64_t zmax = steps / 8 < 8 ? steps / 8 : 8;
+  p.full = tiles;
+  p.tail = 0;
+  p.splits = 1;
+  if (zmax < 2) return p;
+  if (tiles >= num_cus) {
+    const int64_t rem = tiles % num_cus;
+    if (rem == 0) return p;
+    int64_t z = num_cus / rem;
+    if (z > zmax) z = zmax;
+    if (z < 2) return p;
+    p.full = tiles - rem;
+    p.tail = rem;
+    p.splits = (int)z;
+    return p;
+  }
   const double round_s = 2.0 * BM * BN * (double)K / 3.5e12;
-  const double part_s = (double)M * (double)n_out * 4.0 / 5.0e12;
+  const double part_s = (double)tiles * BM * BN * 4.0 / 5.0e12;
   auto cost = [&](int64_t z) {
     const double rounds = (double)((tiles * z + num_cus - 1) / num_cus);
     return rounds * round_s / (double)z + (z > 1 ? (double)(z + 1) * part_s : 0.0);
   };
-  int best = 1;
-  for (int64_t z = 2; z <= 8 && z <= steps / 8; ++z)
-    if (cost(z) < 0.95 * cost(best)) best = (int)z;
-  return best;
+  int64_t best = 1;
+  for (int64_t z = 2; z <= zmax; ++z)
+    if (cost(z) < 0.95 * cost(best)) best = z;
+  if (best > 1) p.full = 0, p.tail = tiles, p.splits = (int)best;
+  return p;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus) {
-  const int z = gemm_splits(M, n_out, K, num_cus);
-  return z > 1 ? (size_t)z * (size_t)M * (size_t)n_out * sizeof(float) : 0;
+  const GemmSplitPlan p = gemm_split_plan(M, n_out, K, num_cus);
+  return p.splits > 1 ? (size_t)p.tail * (size_t)p.splits * BM * BN * sizeof(float) : 0;
 }
 
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
@@ -199,8 +260,6 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
   // activation offsets inside a 256-row tile are 32-bit byte offsets
   if (K > ((int64_t)1 << 22)) return -1;
   GemmArgs g;
-  g.ga = alpha.a;
-  g.gw = alpha.w;
   g.a = a;
   g.a_scales = a_scales;
   g.wc = wc;
@@ -211,27 +270,38 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
   g.N = n_out;
   g.K = K;
   g.out_f32 = out_f32 ? 1 : 0;
+  g.ga = alpha.a;
+  g.gw = alpha.w;
   g.tiles_m = (int)((M + BM - 1) / BM);
   g.tiles_n = (int)((n_out + BN - 1) / BN);
-  g.splits = gemm_splits(M, n_out, K, kNumCUs);
+  const GemmSplitPlan p = gemm_split_plan(M, n_out, K, kNumCUs);
+  g.splits = p.splits;
+  g.tail = (int)p.tail;
+  g.full = (int)p.full;
   const int64_t steps = (K + BK - 1) / BK;
   g.k_split = ((steps + g.splits - 1) / g.splits) * BK;
-  g.splits = (int)((K + g.k_split - 1) / g.k_split);  // every split non-empty
-  g.partial = static_cast<float*>(workspace);
-  if (g.splits > 1 && !workspace) return -1;
-  const int total = g.tiles_m * g.tiles_n * g.splits;
-  const int grid = ((total + 7) / 8) * 8;
-  if (a_nvfp4)
-    hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, g);
-  else
-    hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, g);
-  if (hipGetLastError() != hipSuccess) return -1;
   if (g.splits > 1) {
-    const int64_t count = M * n_out;
-    const int64_t threads = (count + 3) / 4;
-    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(workspace), g.splits, count, out_f32 ? 1 : 0,
-                       alpha.a, alpha.w, out);
+    g.splits = (int)((K + g.k_split - 1) / g.k_split);  // every part non-empty
+    if (!workspace) return -1;
+  } else {
+    g.full = g.tiles_m * g.tiles_n;  // no split: every tile whole
+    g.tail = 0;
+  }
+  g.partial = static_cast<float*>(workspace);
+  // Both bands need a multiple of 8 workgroups: a split plan's `full` is a
+  // multiple of the CU count (or 0); an unsplit one is padded and the extra
+  // workgroups exit, as do those past the last K part.
+  if (g.full % 8 != 0) g.full = (g.full + 7) / 8 * 8;
+  const int64_t items = (int64_t)g.tail * g.splits;
+  const int64_t grid = g.full + (items + 7) / 8 * 8;
+  if (grid > INT32_MAX) return -1;
+  if (a_nvfp4)
+    hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
+  else
+    hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (g.tail > 0) {
+    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)(g.tail * 64)), dim3(256), 0, stream, g);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

@@ -50,10 +50,16 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
                 void* out, void* workspace, hipStream_t stream, Alpha alpha = {});
 
 // Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
-// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  When
-// the tiles cannot fill the chip, K is split (fp32 partials in workspace,
-// gemm_workspace_bytes of it, summed in split order by a second kernel).
-int gemm_splits(int64_t M, int64_t n_out, int64_t K, int num_cus);
+// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  The
+// tiles of a last, partly filled round (or all tiles, when they cannot fill
+// the chip once) are split over K: fp32 tile-local partials in workspace
+// (gemm_workspace_bytes of it), summed in part order by a second kernel.
+struct GemmSplitPlan {
+  int64_t full;  // tiles run whole
+  int64_t tail;  // tiles run as `splits` K parts
+  int splits;
+};
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);
 int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
                 const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,

@@ -260,6 +260,27 @@ def test_mfma_w4a4_ragged(nv, orc, M, K, N):
     _assert_close(y, orc.gemm_w4a4(rc, rs, M, K, w.codes, w.scales), what="w4a4")
 
 
+
+def test_mfma_tail_tiles_split(nv, orc):
+    """300 tiles on 256 CUs: the first 256 run whole, the last 44 (columns
+    10752 .. 12796 in the tile order) run as 5 K parts summed by the reduce
+    kernel.  Ragged M and N (N % 4 != 0); all rows, 384 columns (160 of them in
+    the split tiles, including the last) against the oracle."""
+    import torch
+    M, K, N = 1300, 2560, 12797
+    helpers.announce(f"gemm mfma tail split M={M} K={K} N={N}")
+    rng = np.random.default_rng(77)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    y = helpers.host_bits(nv.gemm(helpers.dev_bf16(x), helpers.dev_u8(w.codes),
+                                  helpers.dev_u8(w.scales)))
+    cols = np.unique(np.concatenate([rng.choice(10752, 222, replace=False),
+                                     rng.choice(np.arange(10752, N), 158, replace=False),
+                                     [0, 10751, 10752, N - 1]])).astype(np.int32)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=cols)
+    _assert_close(y[:, cols], ref, what="tail split")
+    torch.cuda.synchronize()
+
 @pytest.mark.parametrize("K,N", [(5120, 17408), (17408, 5120)])
 def test_prefill_full_size_sampled(nv, orc, K, N):
     """The prefill shapes at full size (M = 8192, outlier activations), in the
