@@ -42,32 +42,77 @@ __global__ void __launch_bounds__(256) k_align_hist(const int32_t* __restrict__ 
 
 // One workgroup of 1024 threads.  offsets = exclusive scan of the expert
 // totals; hist[b][e] is replaced by the first row of expert e owned by block b.
+// Expert offsets and, for every (block, expert), the first row that block's
+// assignments of that expert land in.  The 1024 threads split each expert's
+// column of per-block counts into `slices` contiguous ranges (slices * ep2 =
+// 1024, ep2 = E rounded up to a power of two), so every thread walks at most
+// ceil(nblocks / slices) blocks, 8 independent loads at a time.
 __global__ void __launch_bounds__(1024) k_align_scan(int32_t* __restrict__ hist, int nblocks,
-                                                     int E, int32_t* __restrict__ offsets) {
+                                                     int E, int ep2,
+                                                     int32_t* __restrict__ offsets) {
+  __shared__ int part[kMoeMaxExperts];  // [slice][expert] partial sums, then prefixes
   __shared__ int tot[kMoeMaxExperts];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) total += hist[(int64_t)b * E + e];
-  tot[e] = e < E ? total : 0;
+  const int slices = kMoeMaxExperts / ep2;
+  const int e = threadIdx.x % ep2, sl = threadIdx.x / ep2;
+  const int per = (nblocks + slices - 1) / slices;
+  const int b0 = min(sl * per, nblocks), b1 = min(b0 + per, nblocks);
+  int sum = 0;
+  if (e < E) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = hist[(int64_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += h[i];
+    }
+    for (; b < b1; ++b) sum += hist[(int64_t)b * E + e];
+  }
+  part[threadIdx.x] = sum;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 1024 slots
+  // expert totals, and each slice's exclusive prefix within its expert
+  if (sl == 0) {
+    int run = 0;
+    for (int j = 0; j < slices; ++j) {
+      const int v = part[j * ep2 + e];
+      part[j * ep2 + e] = run;
+      run += v;
+    }
+    tot[e] = e < E ? run : 0;
+  } else {
+    tot[threadIdx.x] = 0;  // slots past ep2 hold no expert
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scan of the expert totals over 1024 slots
+  const int t = threadIdx.x;
   for (int d = 1; d < kMoeMaxExperts; d <<= 1) {
-    const int v = e >= d ? tot[e - d] : 0;
+    const int v = t >= d ? tot[t - d] : 0;
     __syncthreads();
-    tot[e] += v;
+    tot[t] += v;
     __syncthreads();
   }
   if (e < E) {
-    int run = tot[e] - total;  // exclusive prefix
-    offsets[e] = run;
-    for (int b = 0; b < nblocks; ++b) {
+    const int excl = (e > 0 ? tot[e - 1] : 0);
+    if (sl == 0) offsets[e] = excl;
+    int run = excl + part[sl * ep2 + e];
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = hist[(int64_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hist[(int64_t)(b + i) * E + e] = run;
+        run += h[i];
+      }
+    }
+    for (; b < b1; ++b) {
       const int h = hist[(int64_t)b * E + e];
       hist[(int64_t)b * E + e] = run;
       run += h;
     }
   }
-  if (e == E - 1) offsets[E] = tot[e];
+  if (t == 0) offsets[E] = tot[E - 1];
 }
 
 __global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict__ ids,
@@ -371,8 +416,10 @@ int launch_moe_align(const int32_t* ids, const float* gates, int64_t T, int64_t 
   const int nb = (int)((R + kAlignBlock - 1) / kAlignBlock);
   int32_t* hist = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(k_align_hist, dim3(nb), dim3(kAlignBlock), 0, stream, ids, R, (int)E, hist);
+  int ep2 = 1;
+  while (ep2 < E) ep2 <<= 1;
   hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kMoeMaxExperts), 0, stream, hist, nb, (int)E,
-                     offsets);
+                     ep2, offsets);
   hipLaunchKernelGGL(k_align_scatter, dim3(nb), dim3(kAlignBlock), 0, stream, ids, gates, R,
                      (int)topk, (int)E, hist, gather_idx, slot_pos, row_gates);
   return hipGetLastError() == hipSuccess ? 0 : -1;
