@@ -361,6 +361,18 @@ def secondary(nv, torch, helpers_dev, reps=3):
     wc, ws = dev_u8(w.codes), dev_u8(w.scales)
     t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales))
     res["w4a4_M512_N17408_K5120_tflops"] = round(2 * 512 * 17408 * 5120 / t / 1e12, 2)
+    # W4A4 from bf16 activations with the quantizer fused in (decode shape)
+    for M in (1, 8, 32):
+        xm = dev_bf16(wl.normal_bf16(np.random.default_rng(M), M, wl.HIDDEN, 0.001))
+        om = torch.empty((M, wl.MLP), dtype=torch.bfloat16, device="cuda")
+        t_f = timeit(lambda: nv.gemm_w4a4(xm, wc, ws, out=om), n=20)
+
+        def unfused():
+            ac, as_ = nv.quantize(xm)
+            nv.gemm(ac, wc, ws, a_scales=as_, out=om)
+        t_u = timeit(unfused, n=20)
+        res[f"w4a4_fused_M{M}_K5120_N17408_us"] = round(t_f * 1e6, 2)
+        res[f"w4a4_quantize_then_gemm_M{M}_K5120_N17408_us"] = round(t_u * 1e6, 2)
     del xd, xq, wc, ws
     # two-level NVFP4: offline weight quantizer (amax pass + quantize pass)
     log("secondary: offline weight quantizer")

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "library_path", "dequantize", "quantize", "gemm", "gemm_workspace_size", "moe_align",
-    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3", "kv_load_e4m3", "quantize_scaled", "quantize_weight",
+    "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3", "kv_load_e4m3", "quantize_scaled", "quantize_weight", "gemm_w4a4",
     "dequantize_scaled", "gemm_scaled", "BF16", "FP32", "NVFP4", "EPI_NONE",
     "EPI_SWIGLU",
 ]
@@ -48,6 +48,9 @@ _SIGS = {
     "nvfp4_head_topk_workspace_size": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_head_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz,
                          _vp], _int),
+    "nvfp4_gemm_w4a4_bf16_workspace_size": ([_i64, _i64, _i64, _i64], _sz),
+    "nvfp4_gemm_w4a4_bf16": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp, _vp, _sz,
+                              _vp], _int),
     "nvfp4_quantize_scaled": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
     "nvfp4_quantize_weight_workspace_size": ([_i64, _i64], _sz),
     "nvfp4_quantize_weight": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
@@ -313,6 +316,27 @@ def kv_load_e4m3(cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch
     _check(lib().nvfp4_kv_load_e4m3(_ptr(cache), cache.shape[0], W, _ptr(block_table),
                                     _ptr(seq_lens), B, max_pages, page_size, max_len,
                                     float(scale), _ptr(out), _stream(cache.device)))
+    return out
+
+
+def gemm_w4a4(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, row_idx=None,
+              out_dtype=torch.bfloat16, out=None, workspace=None) -> torch.Tensor:
+    """W4A4 product from bf16 activations [M, K]: the activations are quantized
+    to NVFP4 inside the call (identical to quantize() then gemm())."""
+    _gpu(a, w_codes, w_scales, row_idx, out, workspace)
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise RuntimeError(f"K mismatch: activations K={K}, weights K={w_codes.shape[1] * 2}")
+    n_out = N if row_idx is None else row_idx.numel()
+    odt = {torch.bfloat16: BF16, torch.float32: FP32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, n_out), dtype=out_dtype, device=a.device)
+    ws, wsz = _workspace(int(lib().nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out)),
+                         a.device, workspace)
+    _check(lib().nvfp4_gemm_w4a4_bf16(_ptr(a), M, N, K, _ptr(w_codes), _ptr(w_scales),
+                                      _ptr(row_idx), n_out, odt, _ptr(out), _ptr(ws), wsz,
+                                      _stream(a.device)))
     return out
 
 

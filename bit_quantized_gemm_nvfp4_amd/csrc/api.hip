@@ -113,7 +113,8 @@ namespace {
 int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
-              void* workspace, size_t workspace_bytes, void* stream, Alpha alpha) {
+              void* workspace, size_t workspace_bytes, void* stream, Alpha alpha,
+              bool fakequant = false) {
   if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
   if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
   if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
@@ -135,6 +136,7 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
 
   hipStream_t st = as_stream(stream);
   if (g.mfma) {
+    if (fakequant) return NVFP4_ERROR_NOT_SUPPORTED;  // (callers quantize first)
     if (((M + 255) / 256) * ((n_out + 255) / 256) > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
     if (log_enabled())
       fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: mfma 256x256\n",
@@ -161,7 +163,7 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
     const int64_t mc = (M - m0) < g.m_chunk ? (M - m0) : g.m_chunk;
     int rc = launch_gemv(g.gemv, x + m0 * K, mc, K, w_codes, w_scales, row_idx, n_out,
                          out_dtype == NVFP4_FP32, static_cast<char*>(out) + m0 * n_out * osz,
-                         partial, st, alpha);
+                         partial, st, alpha, fakequant);
     if (rc != 0) return NVFP4_ERROR_LAUNCH;
   }
   return NVFP4_SUCCESS;
@@ -194,6 +196,63 @@ int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
   alpha.w = w_global_scale;
   return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
                    out, workspace, workspace_bytes, stream, alpha);
+}
+
+// Decode-shaped W4A4 from bf16 activations: the GEMV can quantize the
+// activations itself while staging them (no extra launch), but every
+// workgroup along N then repeats that work; otherwise one pass writes the
+// quantized-and-dequantized activations (bf16, exact) and the plain GEMV
+// reads them.  Staging wins only for very few rows and narrow layers.
+static bool w4a4_fuse_in_gemv(int64_t M, int64_t n_out) {
+  if (const char* e = getenv("NVFP4_W4A4_FUSE"))  // tuning knob: 0 never, 1 always
+    return e[0] == '1';
+  return M <= 4 && n_out <= 65536;
+}
+
+size_t nvfp4_gemm_w4a4_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return 0;
+  const GemmPlan g = plan_gemm(M, N, K, n_out, false);
+  if (!g.mfma) {
+    if (w4a4_fuse_in_gemv(M, n_out)) return g.partial_bytes;
+    return round_up((size_t)M * (size_t)K * 2, 256) + g.partial_bytes;
+  }
+  return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 16, 256) +
+         nvfp4_gemm_workspace_size(NVFP4_NVFP4, M, N, K, n_out);
+}
+
+int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (M * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  const GemmPlan g = plan_gemm(M, N, K, n_out, false);
+  const size_t need = nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
+  if ((workspace && !aligned16(workspace)) || !aligned16(a)) return NVFP4_ERROR_INVALID_VALUE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = as_stream(stream);
+  if (!g.mfma) {
+    if (w4a4_fuse_in_gemv(M, n_out))  // quantized inside the GEMV's activation staging
+      return gemm_impl(NVFP4_BF16, a, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
+                       out_dtype, out, workspace, workspace_bytes, stream, Alpha{}, true);
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
+    const size_t g_off = round_up((size_t)M * (size_t)K * 2, 256);
+    if (launch_fakequant(a, M, K, xq, st) != 0) return NVFP4_ERROR_LAUNCH;
+    return gemm_impl(NVFP4_BF16, xq, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
+                     out_dtype, out, g.partial_bytes ? ws + g_off : nullptr,
+                     workspace_bytes - g_off, stream, Alpha{});
+  }
+  // large M: quantize once, then the W4A4 MFMA GEMM
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws);
+  const size_t s_off = round_up((size_t)M * (size_t)K / 2, 256);
+  uint8_t* scales = reinterpret_cast<uint8_t*>(ws + s_off);
+  const size_t g_off = s_off + round_up((size_t)M * (size_t)K / 16, 256);
+  if (launch_quantize(a, M, K, codes, scales, st) != 0) return NVFP4_ERROR_LAUNCH;
+  return gemm_impl(NVFP4_NVFP4, codes, scales, M, N, K, w_codes, w_scales, row_idx, n_out,
+                   out_dtype, out, ws + g_off, workspace_bytes - g_off, stream, Alpha{});
 }
 
 int nvfp4_quantize_scaled(const uint16_t* x, int64_t M, int64_t K, const float* global_scale,

@@ -12,6 +12,7 @@
 // 128-bit access.  Both are HBM-bound.
 #include "device.h"
 #include "launch.h"
+#include "quant_core.h"
 
 namespace nvfp4 {
 
@@ -47,46 +48,6 @@ int launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, in
 }
 
 // ---- quantize ---------------------------------------------------------------------
-
-// Scale code for a block maximum a (finite, >= 0): a/6 rounded to the nearest
-// E4M3 value, ties to the even code, saturating at 448 (0x7E).
-//   t = a / 6 is a correctly rounded f32 division.  It cannot move the value
-//   across an E4M3 rounding boundary: a boundary t* has at most 5 significant
-//   bits, so a = 6 t* is exact and then t == t*; any other bf16 a lies at least
-//   a relative 2^-8 away from 6 t*, far beyond the 2^-24 division error.
-//   Subnormal range (t < 2^-6): the code is the integer nearest t / 2^-9
-//   (0..8; 8 is 2^-6 = code 0x08).  Normal range: round the f32 mantissa to 3
-//   bits, nearest-even, on the bit pattern, and rebias the exponent 127 -> 7.
-__device__ __forceinline__ uint32_t scale_code_from_amax(float a) {
-  float t = a / 6.0f;
-  if (t >= 448.0f) return 0x7E;
-  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
-  uint32_t b = __builtin_bit_cast(uint32_t, t);
-  uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
-  return r - (120u << 3);
-}
-
-// Magnitude index (0..7) of the e2m1 value nearest to ax / s, ties to the even
-// index, saturating at 6.  The decision points are s * {0.25, 0.75, 1.25,
-// 1.75, 2.5, 3.5, 5}; each product is exact in f32, so every comparison is
-// exact.  A tie at 0.75, 1.75, 3.5 resolves upward (to the even index 2, 4, 6)
-// and at 0.25, 1.25, 2.5, 5 downward (to 0, 2, 4, 6), hence >= vs >.
-// Three comparisons pick the index bit by bit.
-struct Thresholds {
-  float t025, t075, t125, t175, t250, t350, t500;
-};
-
-__device__ __forceinline__ Thresholds make_thresholds(float s) {
-  return {s * 0.25f, s * 0.75f, s * 1.25f, s * 1.75f, s * 2.5f, s * 3.5f, s * 5.0f};
-}
-
-__device__ __forceinline__ uint32_t e2m1_index(float ax, const Thresholds& th) {
-  bool hi = ax >= th.t175;                          // index >= 4
-  bool mid = ax >= (hi ? th.t350 : th.t075);         // next bit
-  float t3 = hi ? (mid ? th.t500 : th.t250) : (mid ? th.t125 : th.t025);
-  bool lo = ax > t3;
-  return (hi ? 4u : 0u) | (mid ? 2u : 0u) | (lo ? 1u : 0u);
-}
 
 // 16 bf16 values (8 words) -> scale code and 8 code bytes (2 words).
 __device__ __forceinline__ uint32_t quantize_block(const uint32_t (&xw)[8], u32x2& codes_out) {
@@ -144,6 +105,28 @@ int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uin
   int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, x, cpr, total,
                      codes, scales);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---- fake quantization: x -> dequantize(quantize(x)) in bf16, one pass ---------------
+
+// One thread per 16-element block: two 16-byte loads, two 16-byte stores.
+__global__ void __launch_bounds__(256) k_fakequant(const uint16_t* __restrict__ x,
+                                                   int64_t blocks, uint16_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= blocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + t * 16);
+  u32x4 v0 = src[0], v1 = src[1];
+  fakequant_block(v0, v1);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + t * 16);
+  dst[0] = v0;
+  dst[1] = v1;
+}
+
+int launch_fakequant(const uint16_t* x, int64_t M, int64_t K, uint16_t* out, hipStream_t stream) {
+  const int64_t blocks = M * (K / 16);
+  hipLaunchKernelGGL(k_fakequant, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream, x,
+                     blocks, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

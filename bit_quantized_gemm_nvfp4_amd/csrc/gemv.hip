@@ -38,11 +38,12 @@ struct GemvArgs {
   int M;
   int steps;               // ceil(K / step) for the kernel's step size
   int out_f32;
+  int fq;                  // activations quantized to NVFP4 and dequantized on staging
   const float* ga;         // two-level scales: the output is multiplied by
   const float* gw;         // *ga * *gw (null: 1); applied to final sums only
 };
 
-template <int MT, int TR, int NW>
+template <int MT, int TR, int NW, bool FQ>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
   __shared__ uint16_t win[2 * 16 * MT * kXWin];
@@ -84,11 +85,11 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   if constexpr (MT == 1) {
     blocks = K % 256 == 0;
     if (blocks)
-      gemv_accumulate_win_blk<MT, TR, XP>(acc, cptr, sptr, win, scl + wave * TR * 512,
+      gemv_accumulate_win_blk<MT, TR, XP, FQ>(acc, cptr, sptr, win, scl + wave * TR * 512,
                                           xrow_off, a.M, K, zs0, zs1, row_ptr);
   }
   if (!blocks)
-    gemv_accumulate_win<MT, TR, XP>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
+    gemv_accumulate_win<MT, TR, XP, FQ>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
                                     (int)(K / kGemvStep), row_ptr);
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
 // Very small M (<= 8): 4x4x4-block MFMA with per-block scaling of the MFMA
 // result (gemv4_core.h).  blockIdx.x picks nw*TR tiles of 4 weight rows, a wave
 // TR of them; blockIdx.y a contiguous part of K.
-template <int MG, int TR>
+template <int MG, int TR, bool FQ>
 __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
   extern __shared__ uint16_t xs[];  // [M][steps of this part * 512 + kXPad]
   const int lane = threadIdx.x & 63;
@@ -135,7 +136,7 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
   const uint16_t* x = a.x;
   const int stride = nsteps * kG4Step + kXPad;
   auto stage = [&]() {
-    stage_activations(xs, a.M, (int64_t)zs0 * kG4Step, nsteps * kG4Step, stride, K,
+    stage_activations<FQ>(xs, a.M, (int64_t)zs0 * kG4Step, nsteps * kG4Step, stride, K,
                       [x, K](int m) { return x + (int64_t)m * K; });
   };
 
@@ -208,7 +209,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
     static_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(v);
 }
 
-template <int MT, int TR>
+template <int MT, int TR, bool FQ>
 void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 15) / 16;
   const int64_t per_wg = (int64_t)nw * TR;
@@ -217,24 +218,45 @@ void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
     // 16 waves: plan_gemv asks for them only here (the window has one piece
     // per thread and the kernel fits 128 registers)
     if (nw == 16) {
-      hipLaunchKernelGGL((k_gemv<MT, TR, 16>), grid, dim3(1024), 0, stream, a);
+      hipLaunchKernelGGL((k_gemv<MT, TR, 16, FQ>), grid, dim3(1024), 0, stream, a);
       return;
     }
   }
   if (nw == 8)
-    hipLaunchKernelGGL((k_gemv<MT, TR, 8>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_gemv<MT, TR, 8, FQ>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_gemv<MT, TR, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_gemv<MT, TR, 4, FQ>), grid, dim3(256), 0, stream, a);
 }
 
-template <int MG, int TR>
+template <int MG, int TR, bool FQ>
 void launch_gemv4_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 3) / 4;
   const int64_t per_wg = (int64_t)nw * TR;
   dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
   const int max_steps = (a.steps + zsplit - 1) / zsplit;
   const size_t lds = (size_t)a.M * (max_steps * kG4Step + kXPad) * sizeof(uint16_t);
-  hipLaunchKernelGGL((k_gemv4<MG, TR>), grid, dim3(64 * nw), lds, stream, a);
+  hipLaunchKernelGGL((k_gemv4<MG, TR, FQ>), grid, dim3(64 * nw), lds, stream, a);
+}
+
+// The plan's (tiles per wave) choice as a template argument; fused W4A4
+// staging is instantiated only for the default two tiles per wave.
+template <bool SMALL, int MT, int TR>
+int launch_plan(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+  if (a.fq) {
+    if constexpr (TR == 2) {
+      if constexpr (SMALL)
+        launch_gemv4_t<MT, TR, true>(a, p.nw, p.z, stream);
+      else
+        launch_gemv_t<MT, TR, true>(a, p.nw, p.z, stream);
+      return 0;
+    }
+    return -2;
+  }
+  if constexpr (SMALL)
+    launch_gemv4_t<MT, TR, false>(a, p.nw, p.z, stream);
+  else
+    launch_gemv_t<MT, TR, false>(a, p.nw, p.z, stream);
+  return 0;
 }
 
 }  // namespace
@@ -292,8 +314,10 @@ size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out) {
 
 int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
-                void* out, void* workspace, hipStream_t stream, Alpha alpha) {
+                void* out, void* workspace, hipStream_t stream, Alpha alpha,
+                bool fakequant) {
   GemvArgs a;
+  a.fq = fakequant ? 1 : 0;
   a.ga = alpha.a;
   a.gw = alpha.w;
   a.x = x;
@@ -308,35 +332,33 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
   const int64_t step = p.small ? kG4Step : kGemvStep;
   a.steps = (int)((K + step - 1) / step);
   a.out_f32 = out_f32 ? 1 : 0;
+  int rc = -2;
   if (p.small) {
     if (p.mt == 1 && p.tr == 4)
-      launch_gemv4_t<1, 4>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 1, 4>(a, p, stream);
     else if (p.mt == 1 && p.tr == 2)
-      launch_gemv4_t<1, 2>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 1, 2>(a, p, stream);
     else if (p.mt == 1 && p.tr == 8)
-      launch_gemv4_t<1, 8>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 1, 8>(a, p, stream);
     else if (p.mt == 1 && p.tr == 1)
-      launch_gemv4_t<1, 1>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 1, 1>(a, p, stream);
     else if (p.mt == 2 && p.tr == 4)
-      launch_gemv4_t<2, 4>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 2, 4>(a, p, stream);
     else if (p.mt == 2 && p.tr == 2)
-      launch_gemv4_t<2, 2>(a, p.nw, p.z, stream);
+      rc = launch_plan<true, 2, 2>(a, p, stream);
     else if (p.mt == 2 && p.tr == 1)
-      launch_gemv4_t<2, 1>(a, p.nw, p.z, stream);
-    else
-      return -2;
+      rc = launch_plan<true, 2, 1>(a, p, stream);
   } else if (p.mt == 1 && p.tr == 2)
-    launch_gemv_t<1, 2>(a, p.nw, p.z, stream);
+    rc = launch_plan<false, 1, 2>(a, p, stream);
   else if (p.mt == 1 && p.tr == 1)
-    launch_gemv_t<1, 1>(a, p.nw, p.z, stream);
+    rc = launch_plan<false, 1, 1>(a, p, stream);
   else if (p.mt == 1 && p.tr == 4)
-    launch_gemv_t<1, 4>(a, p.nw, p.z, stream);
+    rc = launch_plan<false, 1, 4>(a, p, stream);
   else if (p.mt == 2 && p.tr == 2)
-    launch_gemv_t<2, 2>(a, p.nw, p.z, stream);
+    rc = launch_plan<false, 2, 2>(a, p, stream);
   else if (p.mt == 2 && p.tr == 1)
-    launch_gemv_t<2, 1>(a, p.nw, p.z, stream);
-  else
-    return -2;
+    rc = launch_plan<false, 2, 1>(a, p, stream);
+  if (rc != 0) return rc;
   if (hipGetLastError() != hipSuccess) return -1;
   if (p.z > 1) {
     const int64_t count = M * n_out;

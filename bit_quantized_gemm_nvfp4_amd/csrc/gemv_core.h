@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "device.h"
+#include "quant_core.h"
 
 namespace nvfp4 {
 
@@ -52,17 +53,24 @@ __host__ __device__ inline int lds_x_stride(int steps) { return steps * kGemvSte
 // [m_rows][stride] bf16; elements at or past K are zero.  row_ptr(m) gives the
 // global row (bf16, K elements).  klen % 8 == 0.  All threads of the workgroup
 // take part; ends with a barrier.
-template <typename RowPtr>
+//
+// FQ (W4A4 with bf16 activations): every 16-element block is quantized to
+// NVFP4 and dequantized on the way (fakequant_piece; a block's two pieces are
+// neighbouring lanes), so the GEMM sees exactly the activations a separate
+// nvfp4_quantize + nvfp4_dequantize would give.
+template <bool FQ = false, typename RowPtr>
 __device__ __forceinline__ void stage_activations(uint16_t* lds, int m_rows, int64_t k_lo,
                                                   int klen, int stride, int64_t K,
                                                   RowPtr row_ptr) {
   const int chunks_per_row = klen / 8;
   const int total = m_rows * chunks_per_row;
   const u32x4 z = {0u, 0u, 0u, 0u};
+  // (total and blockDim.x are even, so a block's two lanes are active together)
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
     const int m = c / chunks_per_row, c8 = c - m * chunks_per_row;
     const int64_t k = k_lo + (int64_t)c8 * 8;
-    const u32x4 v = k < K ? *reinterpret_cast<const u32x4*>(row_ptr(m) + k) : z;
+    u32x4 v = k < K ? *reinterpret_cast<const u32x4*>(row_ptr(m) + k) : z;
+    if constexpr (FQ) v = fakequant_piece(v);
     *reinterpret_cast<u32x4*>(lds + m * stride + c8 * 8) = v;
   }
   __syncthreads();
@@ -201,6 +209,18 @@ __device__ __forceinline__ void xwin_load(u32x4 (&v)[XP], int M, int64_t K, int 
   }
 }
 
+// Fused W4A4 activations: quantize and dequantize the loaded pieces in place
+// (piece c and c ^ 1 of a window row form one block; they are neighbouring
+// lanes).  Done just before the pieces are stored, so the loads stay in flight
+// over the step's compute.
+template <bool FQ, int XP>
+__device__ __forceinline__ void xwin_fakequant(u32x4 (&v)[XP]) {
+  if constexpr (FQ) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) v[i] = fakequant_piece(v[i]);
+  }
+}
+
 template <int XP>
 __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) {
 #pragma unroll
@@ -215,7 +235,7 @@ __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) 
 // 64q (rows past M hold copies, their results are never stored).  Every thread
 // of the workgroup calls this with the same arguments except the weight
 // pointers.  blockDim.x * XP == 16*MT*32.
-template <int MT, int TR, int XP, typename RowPtr>
+template <int MT, int TR, int XP, bool FQ = false, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
                                                     const uint8_t* const (&cptr)[TR],
                                                     const uint8_t* const (&sptr)[TR],
@@ -227,6 +247,7 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
   constexpr int wsz = 16 * MT * kXWin;
   u32x4 xv[XP];
   xwin_load<XP>(xv, M, K, s0, row_ptr);
+  xwin_fakequant<FQ, XP>(xv);
   xwin_store<XP>(win, xv);
   __syncthreads();
   const int e = s1 < steps_full ? s1 : steps_full;  // end of the full steps
@@ -247,6 +268,7 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
         for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
         compute_wstep<MT, TR>(acc, b0, xl);
       }
+      xwin_fakequant<FQ, XP>(xv);
       xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
       __syncthreads();
       cur ^= 1;
@@ -260,6 +282,7 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
         for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
         compute_wstep<MT, TR>(acc, b1, xl);
       }
+      xwin_fakequant<FQ, XP>(xv);
       xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
       __syncthreads();
       cur ^= 1;
@@ -326,7 +349,7 @@ __device__ __forceinline__ void read_sblock(WStep<TR>& b, const uint32_t* lds, i
   for (int t = 0; t < TR; ++t) b.sc[t] = lds[t * 512 + j * 64 + n * 4 + q];
 }
 
-template <int MT, int TR, int XP, typename RowPtr>
+template <int MT, int TR, int XP, bool FQ = false, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
                                                         const uint8_t* const (&cptr)[TR],
                                                         const uint8_t* const (&sptr)[TR],
@@ -338,6 +361,7 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
   constexpr int wsz = 16 * MT * kXWin;
   u32x4 xv[XP];
   xwin_load<XP>(xv, M, K, s0, row_ptr);
+  xwin_fakequant<FQ, XP>(xv);
   xwin_store<XP>(win, xv);
   const int e = s1;  // K % 256 == 0: every step is full
   u32x4 ph[TR];
@@ -364,6 +388,7 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
       for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
       compute_wstep<MT, TR>(acc, bc, xl);
     }
+    xwin_fakequant<FQ, XP>(xv);
     xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
     // half 0 fills rows 0, 2, 4, 6 (row 7 is still read at the last step);
     // half 1 fills rows 1, 3, 5, 7 after it

@@ -15,6 +15,8 @@ int launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, in
                       uint16_t* out, hipStream_t stream);
 int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                     hipStream_t stream);
+// out = dequantize(quantize(x)) in bf16 (exact), without the codes in memory.
+int launch_fakequant(const uint16_t* x, int64_t M, int64_t K, uint16_t* out, hipStream_t stream);
 
 // Two-level NVFP4 (per-tensor fp32 scale g, a device scalar).  Quantize with
 // a given g; the offline weight quantizer (g from the tensor's amax, written
@@ -45,9 +47,13 @@ struct GemvPlan {
 
 GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
+// fakequant: x is bf16 and every 16-element block is quantized to NVFP4 and
+// dequantized while it is staged (the W4A4 product with the activation
+// quantizer fused in; only the default two tiles per wave).
 int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
-                void* out, void* workspace, hipStream_t stream, Alpha alpha = {});
+                void* out, void* workspace, hipStream_t stream, Alpha alpha = {},
+                bool fakequant = false);
 
 // Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
 // or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  The

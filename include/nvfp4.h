@@ -128,6 +128,23 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * W4A4 linear layer from bf16 activations: the activation quantizer fused into
+ * the product ("52.6% more tokens, 1.53x less GPU time ...": NVFP4 W4A4
+ * execution).  Bit-identical to nvfp4_quantize(a) followed by nvfp4_gemm
+ * with a_dtype = NVFP4 (same arguments otherwise: row_idx, n_out, out_dtype).
+ * Decode shapes (M below the MFMA threshold) quantize every 16-element block
+ * while the GEMV stages the activations, so the codes never go to memory;
+ * large M quantizes once into the workspace and runs the W4A4 MFMA GEMM.
+ * workspace: >= nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out) bytes.
+ * K % 32 == 0.
+ */
+size_t nvfp4_gemm_w4a4_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out);
+int nvfp4_gemm_w4a4_bf16(const uint16_t *a, int64_t M, int64_t N, int64_t K,
+                         const uint8_t *w_codes, const uint8_t *w_scales,
+                         const int32_t *row_idx, int64_t n_out, int out_dtype, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Two-level NVFP4.  The deployed NVFP4 checkpoints come from NVFP4
  * quantization tools ("What 350+ Experiments ...", section 1 and its
  * sources); a tensor then carries, above its per-16 E4M3 scales, one positive

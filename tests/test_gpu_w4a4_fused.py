@@ -1,0 +1,64 @@
+"""GPU parity of the W4A4 product with the activation quantizer fused in
+(nvfp4_gemm_w4a4_bf16): bit-identical to nvfp4_quantize followed by the W4A4
+nvfp4_gemm on the GEMV (quantizer in the activation staging) and MFMA (quantize
+then GEMM) paths, and within the GEMM tolerance of the oracle."""
+import numpy as np
+import pytest
+
+import helpers
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    assert torch.cuda.is_available()
+    import bit_quantized_gemm_nvfp4_amd as m
+    m.lib()
+    return m
+
+
+def _x(rng, M, K):
+    x = workloads.normal_bf16(rng, M, K, outlier_frac=0.01)
+    x[0, :32] = 0                  # an all-zero block pair
+    x[-1, 32:48] = 0x8000          # a block of negative zeros
+    return x
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 512, 1024), (3, 800, 333), (4, 5120, 4096), (5, 512, 1000), (8, 5120, 17408),
+    (16, 800, 300), (17, 2048, 520), (32, 5120, 4000), (40, 1024, 777), (64, 512, 64),
+    (65, 512, 300), (300, 1056, 520),
+])
+def test_fused_equals_quantize_then_gemm(nv, M, K, N):
+    import torch
+    helpers.announce(f"w4a4 fused M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 131 + K + N)
+    x = helpers.dev_bf16(_x(rng, M, K))
+    w = workloads.nvfp4_weight(rng, N, K)
+    wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    for odt in (torch.float32, torch.bfloat16):
+        fused = nv.gemm_w4a4(x, wc, ws, out_dtype=odt)
+        ac, as_ = nv.quantize(x)
+        ref = nv.gemm(ac, wc, ws, a_scales=as_, out_dtype=odt)
+        assert torch.equal(fused.view(torch.int16) if odt == torch.bfloat16 else
+                           fused.view(torch.int32),
+                           ref.view(torch.int16) if odt == torch.bfloat16 else ref.view(torch.int32))
+
+
+def test_fused_masked_rows_and_oracle(nv, orc):
+    import torch
+    helpers.announce("w4a4 fused masked M=8 K=5120")
+    rng = np.random.default_rng(90)
+    M, K, N = 8, 5120, 20000
+    xb = _x(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    idx = np.sort(rng.choice(N, 3000, replace=False)).astype(np.int32)
+    y = nv.gemm_w4a4(helpers.dev_bf16(xb), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                     row_idx=helpers.dev_i32(idx), out_dtype=torch.float32)
+    ac, as_ = orc.quantize(xb, M, K)
+    ref = orc.gemm_w4a4(ac, as_, M, K, w.codes, w.scales, row_idx=idx)
+    ok, rf, worst = helpers.gemm_close(y.cpu().numpy(), ref, out_is_bf16=False)
+    assert ok, f"rel_frob={rf:.3e} worst={worst:.3f}"
