@@ -25,6 +25,21 @@ constexpr int kAlignBlock = 256;  // assignments per align workgroup
 
 // ---- align: block histograms -> per-(block, expert) bases -> ranked scatter ----
 
+// Entries of sid[base .. p) equal to e (base 16-byte aligned): 16-byte LDS
+// reads, several in flight, instead of one dependent read per entry.
+__device__ __forceinline__ int count_before(const int* sid, int base, int p, int e) {
+  const int n = p - base;
+  const int4* v = reinterpret_cast<const int4*>(sid + base);
+  int r = 0, q = 0;
+#pragma unroll 4
+  for (; q + 4 <= n; q += 4) {
+    const int4 x = v[q >> 2];
+    r += (x.x == e) + (x.y == e) + (x.z == e) + (x.w == e);
+  }
+  for (; q < n; ++q) r += sid[base + q] == e;
+  return r;
+}
+
 __global__ void __launch_bounds__(256) k_align_hist(const int32_t* __restrict__ ids, int64_t R,
                                                     int E, int32_t* __restrict__ hist) {
   __shared__ int cnt[kMoeMaxExperts];
@@ -122,7 +137,7 @@ __global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict
                                                        int32_t* __restrict__ gather_idx,
                                                        int32_t* __restrict__ slot_pos,
                                                        float* __restrict__ row_gates) {
-  __shared__ int sid[kAlignBlock];
+  __shared__ __attribute__((aligned(16))) int sid[kAlignBlock];
   const int i = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * kAlignBlock + i;
   sid[i] = p < R ? ids[p] : -1;
@@ -130,8 +145,7 @@ __global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict
   if (p >= R) return;
   const int e = sid[i];
   if (e < 0 || e >= E) return;
-  int rank = 0;
-  for (int j = 0; j < i; ++j) rank += sid[j] == e;  // earlier assignments, same expert
+  const int rank = count_before(sid, 0, i, e);  // earlier assignments, same expert
   const int dest = base[(int64_t)blockIdx.x * E + e] + rank;
   gather_idx[dest] = (int32_t)(p / topk);
   slot_pos[p] = dest;
@@ -401,6 +415,64 @@ __global__ void __launch_bounds__(256) k_moe_combine(const uint16_t* __restrict_
   *reinterpret_cast<u32x4*>(out + t * H + c8) = o;
 }
 
+// Small batches (R <= 2048 assignments, a decode step): the same three phases
+// in one workgroup of 1024 threads, through LDS, with the same result (the
+// per-(block, expert) bases and the in-block ranks define one stable order).
+constexpr int kAlignSmallMax = 2048;
+
+__global__ void __launch_bounds__(1024) k_align_small(const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ gates, int R,
+                                                      int topk, int E,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ gather_idx,
+                                                      int32_t* __restrict__ slot_pos,
+                                                      float* __restrict__ row_gates) {
+  __shared__ __attribute__((aligned(16))) int sid[kAlignSmallMax];
+  __shared__ int hist[(kAlignSmallMax / kAlignBlock) * kMoeMaxExperts];
+  __shared__ int tot[kMoeMaxExperts];
+  const int t = threadIdx.x;
+  const int nb = (R + kAlignBlock - 1) / kAlignBlock;
+  for (int i = t; i < nb * E; i += blockDim.x) hist[i] = 0;
+  for (int p = t; p < R; p += blockDim.x) sid[p] = ids[p];
+  __syncthreads();
+  for (int p = t; p < R; p += blockDim.x) {
+    const int e = sid[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[(p / kAlignBlock) * E + e], 1);
+  }
+  __syncthreads();
+  int total = 0;  // thread t < E: expert t's prefix over blocks
+  if (t < E)
+    for (int b = 0; b < nb; ++b) {
+      const int h = hist[b * E + t];
+      hist[b * E + t] = total;
+      total += h;
+    }
+  tot[t] = t < E ? total : 0;
+  __syncthreads();
+  for (int d = 1; d < kMoeMaxExperts; d <<= 1) {  // inclusive scan of the totals
+    const int v = t >= d ? tot[t - d] : 0;
+    __syncthreads();
+    tot[t] += v;
+    __syncthreads();
+  }
+  if (t < E) {
+    const int excl = tot[t] - total;
+    offsets[t] = excl;
+    for (int b = 0; b < nb; ++b) hist[b * E + t] += excl;
+  }
+  if (t == E - 1) offsets[E] = tot[t];
+  __syncthreads();
+  for (int p = t; p < R; p += blockDim.x) {
+    const int e = sid[p];
+    if (e < 0 || e >= E) continue;
+    const int b = p / kAlignBlock;
+    const int dest = hist[b * E + e] + count_before(sid, b * kAlignBlock, p, e);
+    gather_idx[dest] = p / topk;
+    slot_pos[p] = dest;
+    if (gates) row_gates[dest] = gates[p];
+  }
+}
+
 }  // namespace
 
 size_t moe_align_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -413,6 +485,11 @@ int launch_moe_align(const int32_t* ids, const float* gates, int64_t T, int64_t 
                      int32_t* offsets, int32_t* gather_idx, int32_t* slot_pos, float* row_gates,
                      void* workspace, hipStream_t stream) {
   const int64_t R = T * topk;
+  if (R <= kAlignSmallMax) {  // one launch instead of three
+    hipLaunchKernelGGL(k_align_small, dim3(1), dim3(kMoeMaxExperts), 0, stream, ids, gates,
+                       (int)R, (int)topk, (int)E, offsets, gather_idx, slot_pos, row_gates);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int nb = (int)((R + kAlignBlock - 1) / kAlignBlock);
   int32_t* hist = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(k_align_hist, dim3(nb), dim3(kAlignBlock), 0, stream, ids, R, (int)E, hist);

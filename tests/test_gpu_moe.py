@@ -20,7 +20,8 @@ def nv():
 
 
 @pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 2, 7), (32, 8, 128), (4096, 8, 128),
-                                      (300, 4, 1024), (5000, 8, 100), (20000, 2, 3)])
+                                      (300, 4, 1024), (5000, 8, 100), (20000, 2, 3),
+                                      (256, 8, 128), (2049, 1, 5)])
 def test_align_bit_exact(nv, orc, T, topk, E):
     helpers.announce(f"moe align T={T} topk={topk} E={E}")
     if E == 128 and topk == 8:
