@@ -110,23 +110,35 @@ size_t nvfp4_gemm_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K, i
 
 namespace {
 
+// Host checks of the arguments every linear-layer entry point shares (the
+// activation operand aside); the status to return, before any launch.
+int linear_args_status(const void* a, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* w_codes, const uint8_t* w_scales,
+                       const int32_t* row_idx, int64_t n_out, int out_dtype, const void* out) {
+  if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_FP32) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (row_idx ? n_out > N : n_out != N) return NVFP4_ERROR_INVALID_VALUE;
+  if (n_out > INT32_MAX || N > INT32_MAX || M > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(out) ||
+      (row_idx && !aligned16(row_idx)))
+    return NVFP4_ERROR_INVALID_VALUE;
+  return NVFP4_SUCCESS;
+}
+
 int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
               void* workspace, size_t workspace_bytes, void* stream, Alpha alpha,
               bool fakequant = false) {
-  if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
-  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
   if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
-  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_FP32) return NVFP4_ERROR_NOT_SUPPORTED;
-  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (const int rc = linear_args_status(a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                                        out))
+    return rc;
   if (a_dtype == NVFP4_BF16 && a_scales) return NVFP4_ERROR_INVALID_VALUE;
   if (a_dtype == NVFP4_NVFP4 && !a_scales) return NVFP4_ERROR_INVALID_VALUE;
-  if (row_idx ? n_out > N : n_out != N) return NVFP4_ERROR_INVALID_VALUE;
-  if (n_out > INT32_MAX || N > INT32_MAX || M > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
-  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(out) ||
-      (a_scales && !aligned16(a_scales)) || (row_idx && !aligned16(row_idx)))
-    return NVFP4_ERROR_INVALID_VALUE;
+  if (a_scales && !aligned16(a_scales)) return NVFP4_ERROR_INVALID_VALUE;
   const bool w4a4 = a_dtype == NVFP4_NVFP4;
   GemmPlan g = plan_gemm(M, N, K, n_out, w4a4);
   const size_t a_off = 0, p_off = round_up(g.a_dequant_bytes, 256);
@@ -224,14 +236,14 @@ int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                          const uint8_t* w_codes, const uint8_t* w_scales,
                          const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (!a || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
-  if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return NVFP4_ERROR_INVALID_VALUE;
-  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (const int rc = linear_args_status(a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                                        out))
+    return rc;  // (checked here, before the quantizer runs)
   if (M * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
   const GemmPlan g = plan_gemm(M, N, K, n_out, false);
   const size_t need = nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
-  if ((workspace && !aligned16(workspace)) || !aligned16(a)) return NVFP4_ERROR_INVALID_VALUE;
+  if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = as_stream(stream);
   if (!g.mfma) {

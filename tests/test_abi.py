@@ -90,6 +90,33 @@ def test_gemm_validation(L):
     assert _gemm(L, M=32, N=5120, K=17408, n_out=5120, workspace=P, wbytes=need - 1) == WORKSPACE
 
 
+
+def _w4a4(L, a=P, M=4, N=64, K=256, wc=P2, ws=P3, row_idx=NULL, n_out=64, out_dtype=0, out=P4,
+          workspace=NULL, wbytes=0):
+    return L.nvfp4_gemm_w4a4_bf16(a, M, N, K, wc, ws, row_idx, n_out, out_dtype, out, workspace,
+                                  wbytes, NULL)
+
+
+def test_gemm_w4a4_bf16_validation(L):
+    """Every argument is checked before the fused quantizer is launched."""
+    assert _w4a4(L, a=NULL) == INVALID
+    assert _w4a4(L, M=0) == INVALID
+    assert _w4a4(L, K=48) == NOT_SUPPORTED
+    assert _w4a4(L, out_dtype=2) == NOT_SUPPORTED
+    assert _w4a4(L, n_out=32) == INVALID               # no row_idx: n_out must be N
+    assert _w4a4(L, row_idx=P, n_out=65) == INVALID    # more rows than N
+    assert _w4a4(L, a=MIS) == INVALID
+    assert _w4a4(L, out=MIS) == INVALID
+    assert _w4a4(L, row_idx=MIS, n_out=32) == INVALID
+    # decode (M=8) quantizes into the workspace; prefill (M=512) too
+    for M in (8, 512):
+        need = L.nvfp4_gemm_w4a4_bf16_workspace_size(M, 5120, 17408, 5120)
+        assert need >= M * 17408 * 2 if M == 8 else need >= M * 17408 // 2 + M * 17408 // 16
+        assert _w4a4(L, M=M, N=5120, K=17408, n_out=5120) == WORKSPACE
+        assert _w4a4(L, M=M, N=5120, K=17408, n_out=5120, workspace=P, wbytes=need - 1) == WORKSPACE
+        assert _w4a4(L, M=M, N=5120, K=17408, n_out=5120, workspace=MIS, wbytes=need) == INVALID
+    assert L.nvfp4_gemm_w4a4_bf16_workspace_size(0, 64, 256, 64) == 0
+
 def test_workspace_queries_are_pure(L):
     a = L.nvfp4_gemm_workspace_size(0, 8, 17408, 5120, 17408)
     b = L.nvfp4_gemm_workspace_size(0, 8, 17408, 5120, 17408)
