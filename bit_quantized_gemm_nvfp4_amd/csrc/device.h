@@ -30,6 +30,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // E4M3 byte `sel` (0..3) of `w` -> f32 (exact).
 template <int SEL>
@@ -70,6 +72,42 @@ __device__ __forceinline__ u32x4 dequant8_bf16(uint32_t codes, float s) {
   return r;
 }
 
+// The same eight elements in fp16: e2m1 codes decoded exactly to fp16, then one
+// packed fp16 multiply per pair by the E4M3 scale s (exact in fp16: the
+// product has <= 6 significant bits within [2^-10, 2688], inside fp16's normal
+// range).  Half the vector instructions of dequant8_bf16.
+__device__ __forceinline__ u32x4 dequant8_f16(uint32_t codes, _Float16 s) {
+  const f16x2 ss = {s, s};
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss);
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss);
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss);
+  return r;
+}
+
+// E4M3 bytes 0,1 (HI = false) or 2,3 (HI = true) of w -> fp16 pair (exact).
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Eight bf16 values -> fp16.  Returns true when every value is represented
+// exactly (then an fp16 product equals the bf16 one); false for values out of
+// fp16's range, below its precision, or non-finite.
+__device__ __forceinline__ bool bf16x8_to_f16(const u32x4& v, u32x4& h) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, v[i] << 16);
+    const float hi = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+    const f16x2 p = {(_Float16)lo, (_Float16)hi};
+    ok = ok && ((float)p.x == lo) && ((float)p.y == hi);
+    h[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return ok;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
   return __builtin_bit_cast(float, h16 << 16);
 }
@@ -87,6 +125,11 @@ __device__ __forceinline__ float alpha_of(const float* a, const float* w) {
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {

@@ -46,7 +46,14 @@ struct GemvArgs {
 template <int MT, int TR, int NW, bool FQ>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
-  __shared__ uint16_t win[2 * 16 * MT * kXWin];
+  // fp16 path (plain W4A16, one activation tile): steps whose activations are
+  // exact in fp16 run the fp16 MFMA on weights decoded with packed fp16
+  // multiplies (half the vector instructions).  With two activation tiles the
+  // second path's registers cost a wave per SIMD, and the fused W4A4 staging
+  // keeps the bf16 path.
+  constexpr bool H = !FQ && MT == 1;
+  __shared__ uint16_t win[2 * 16 * MT * kXWin];  // bf16, or fp16 (H)
+  __shared__ int hflag[2];
   // scale blocks (one-tile activations only: with two the extra registers
   // cost more occupancy than the fetched bytes they save)
   __shared__ uint32_t scl[MT == 1 ? NW * TR * 512 : 1];
@@ -81,16 +88,21 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
 
   const uint16_t* x = a.x;
   auto row_ptr = [x, K](int m) { return x + (int64_t)m * K; };
+  if constexpr (H) {  // no step is marked inexact yet
+    if (threadIdx.x < 2) hflag[threadIdx.x] = -1;
+    __syncthreads();
+  }
   bool blocks = false;
   if constexpr (MT == 1) {
     blocks = K % 256 == 0;
     if (blocks)
-      gemv_accumulate_win_blk<MT, TR, XP, FQ>(acc, cptr, sptr, win, scl + wave * TR * 512,
-                                          xrow_off, a.M, K, zs0, zs1, row_ptr);
+      gemv_accumulate_win_blk<MT, TR, XP, FQ, H>(acc, cptr, sptr, win, hflag,
+                                                 scl + wave * TR * 512, xrow_off, a.M, K,
+                                                 zs0, zs1, row_ptr);
   }
   if (!blocks)
-    gemv_accumulate_win<MT, TR, XP, FQ>(acc, cptr, sptr, win, xrow_off, a.M, K, zs0, zs1,
-                                    (int)(K / kGemvStep), row_ptr);
+    gemv_accumulate_win<MT, TR, XP, FQ, H>(acc, cptr, sptr, win, hflag, xrow_off, a.M,
+                                           K, zs0, zs1, (int)(K / kGemvStep), row_ptr);
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
   const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
@@ -271,9 +283,11 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   p.small = M <= small_max;
   p.mt = p.small ? (int)((M + 3) / 4) : (M <= 16 ? 1 : 2);
   p.tr = 2;
-  // 16x16 path: wide workgroups (8 waves share one activation window) when
-  // there are rows enough to fill the chip with them; 4 waves otherwise
-  p.nw = (!p.small && n_out >= 32768) ? 8 : 4;
+  // Wide workgroups (8 waves; on the 16x16 path they share one activation
+  // window) when there are rows enough to fill the chip with them, 4 waves
+  // otherwise (measured: the 248,320-row head at M = 1 takes ~10% less time
+  // with 8 waves, the 17,408-row layers are as fast or faster with 4)
+  p.nw = n_out >= 32768 ? 8 : 4;
   int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
   // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
   // the waves per workgroup and the LDS budget of the staged activations.

@@ -18,6 +18,14 @@
 // scattered physical k; any bijection gives the same dot product as long as A
 // and B agree.
 //
+// With one activation tile (M <= 16) the plain W4A16 GEMV runs most steps in
+// fp16 instead: the window holds the activations converted to fp16, checked
+// to be exact, and the codes are decoded to fp16 with one packed fp16 multiply
+// per pair (e2m1 * E4M3 has <= 6 significant bits inside fp16's normal range),
+// for v_mfma_f32_16x16x32_f16.  Every product is the same exact value as on
+// the bf16 path, with half the vector instructions per weight; a step whose
+// activations are not all exact in fp16 runs the bf16 path.
+//
 // Code/scale loads of step s+1 are issued before step s is computed (register
 // double buffer, pinned with scheduling barriers).  Main-loop loads are
 // unconditional: weight rows past the end are clamped to a valid row and
@@ -111,33 +119,50 @@ __device__ __forceinline__ void load_wstep(WStep<TR>& b, const uint8_t* const (&
 // the step's element 64q), B operands decoded from the codes.  The A operands
 // are read one 8-element chunk at a time, one chunk ahead of their MFMAs, so
 // only two chunks per m-tile are live (fewer registers, more waves per SIMD).
-template <int MT, int TR>
+// H: the A operands are fp16 (the fp16 window copy) and the weights are
+// decoded to fp16 with packed multiplies (dequant8_f16) for the fp16 MFMA;
+// every product is the same exact value as on the bf16 path.
+template <int MT, int TR, bool H = false>
 __device__ __forceinline__ void compute_wstep(f32x4 (&acc)[TR][MT], const WStep<TR>& b,
                                               const uint16_t* const (&xl)[MT]) {
+  auto ld = [&](int mt, int j) { return *reinterpret_cast<const u32x4*>(xl[mt] + 8 * j); };
   float s[TR][4];
+  f16x2 sh[TR][2];  // fp16 scales of blocks (0, 1) and (2, 3)
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
-    s[t][0] = e4m3_to_f32<0>(b.sc[t]);
-    s[t][1] = e4m3_to_f32<1>(b.sc[t]);
-    s[t][2] = e4m3_to_f32<2>(b.sc[t]);
-    s[t][3] = e4m3_to_f32<3>(b.sc[t]);
+    if constexpr (H) {
+      sh[t][0] = e4m3x2_to_f16<false>(b.sc[t]);
+      sh[t][1] = e4m3x2_to_f16<true>(b.sc[t]);
+    } else {
+      s[t][0] = e4m3_to_f32<0>(b.sc[t]);
+      s[t][1] = e4m3_to_f32<1>(b.sc[t]);
+      s[t][2] = e4m3_to_f32<2>(b.sc[t]);
+      s[t][3] = e4m3_to_f32<3>(b.sc[t]);
+    }
   }
   u32x4 a[2][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) a[0][mt] = *reinterpret_cast<const u32x4*>(xl[mt]);
+  for (int mt = 0; mt < MT; ++mt) a[0][mt] = ld(mt, 0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j + 1 < 8) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[(j + 1) & 1][mt] = *reinterpret_cast<const u32x4*>(xl[mt] + 8 * (j + 1));
+      for (int mt = 0; mt < MT; ++mt) a[(j + 1) & 1][mt] = ld(mt, j + 1);
     }
 #pragma unroll
     for (int t = 0; t < TR; ++t) {
-      const u32x4 w = dequant8_bf16(b.c[t][j >> 2][j & 3], s[t][j >> 1]);
+      if constexpr (H) {
+        const f16x2 sp = sh[t][j >> 2];
+        const u32x4 w = dequant8_f16(b.c[t][j >> 2][j & 3], ((j >> 1) & 1) ? sp.y : sp.x);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[t][mt] = mfma_16x16x32_bf16(a[j & 1][mt], w, acc[t][mt]);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[t][mt] = mfma_16x16x32_f16(a[j & 1][mt], w, acc[t][mt]);
+      } else {
+        const u32x4 w = dequant8_bf16(b.c[t][j >> 2][j & 3], s[t][j >> 1]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[t][mt] = mfma_16x16x32_bf16(a[j & 1][mt], w, acc[t][mt]);
+      }
     }
   }
 }
@@ -230,72 +255,121 @@ __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) 
   }
 }
 
+// fp16 window (H): the window holds the steps' activations converted to fp16,
+// and a step whose activations are not all exact in fp16 is marked in the
+// workgroup's flag word of its buffer (`hflag[buffer]` = that step's index; a
+// stale index of an earlier step never matches, and the kernel sets both words
+// to -1 before the first step).  Every inexact lane writes the same value, so
+// concurrent LDS writes agree.  The flag is read after the barrier that
+// publishes the step; a marked step is staged again in bf16 (only values
+// beyond fp16's range or below 2^-17 relative precision fail, so this is rare).
+template <bool H, int XP>
+__device__ __forceinline__ void xwin_store2(uint16_t* buf, int* flag, const u32x4 (&v)[XP],
+                                            int s) {
+  if constexpr (H) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
+      u32x4 h;
+      ok = bf16x8_to_f16(v[i], h) && ok;
+      *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = h;
+    }
+    if (!ok) *flag = s;
+  } else {
+    xwin_store<XP>(buf, v);
+  }
+}
+
+// Before step s is computed from window buffer `buf` (H): true when its
+// activations are exact in fp16 (the window holds them in fp16); otherwise the
+// step is reloaded and stored in bf16 over the same buffer, with a barrier
+// (the flag is workgroup-uniform, so every wave takes this branch together).
+// `xv` is free at this point (the next step's prefetch is issued after).
+template <bool H, int XP, typename RowPtr>
+__device__ __forceinline__ bool xwin_fp16_or_restage(uint16_t* buf, const int* flag,
+                                                     u32x4 (&xv)[XP], int M, int64_t K, int s,
+                                                     RowPtr row_ptr) {
+  if constexpr (H) {
+    if (__builtin_amdgcn_readfirstlane(*flag) != s) return true;
+    xwin_load<XP>(xv, M, K, s, row_ptr);
+    xwin_store<XP>(buf, xv);
+    __syncthreads();
+  }
+  return false;
+}
+
+// One step from window buffer `cur`: fp16 MFMA path or bf16 path.
+template <int MT, int TR>
+__device__ __forceinline__ void compute_wstep_win(f32x4 (&acc)[TR][MT], const WStep<TR>& b,
+                                                  const uint16_t* win, int cur, bool f16,
+                                                  const int (&xrow_off)[MT]) {
+  constexpr int wsz = 16 * MT * kXWin;
+  const uint16_t* xl[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+  if (f16)
+    compute_wstep<MT, TR, true>(acc, b, xl);
+  else
+    compute_wstep<MT, TR, false>(acc, b, xl);
+}
+
 // Accumulate steps [s0, s1) with the activations streamed through the LDS
-// window `win` ([2][16*MT][kXWin]).  xrow_off[mt] = (16*mt + lane%16) * kXWin +
-// 64q (rows past M hold copies, their results are never stored).  Every thread
-// of the workgroup calls this with the same arguments except the weight
-// pointers.  blockDim.x * XP == 16*MT*32.
-template <int MT, int TR, int XP, bool FQ = false, typename RowPtr>
+// window `win` ([2][16*MT][kXWin]; bf16, or fp16 with `hflag` when H).
+// xrow_off[mt] = (16*mt + lane%16) * kXWin + 64q (rows past M hold copies,
+// their results are never stored).  Every thread of the workgroup calls this
+// with the same arguments except the weight pointers.  blockDim.x * XP ==
+// 16*MT*32.
+template <int MT, int TR, int XP, bool FQ = false, bool H = false, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
                                                     const uint8_t* const (&cptr)[TR],
                                                     const uint8_t* const (&sptr)[TR],
-                                                    uint16_t* win, const int (&xrow_off)[MT],
-                                                    int M, int64_t K, int s0, int s1,
-                                                    int steps_full, RowPtr row_ptr) {
+                                                    uint16_t* win, int* hflag,
+                                                    const int (&xrow_off)[MT], int M, int64_t K,
+                                                    int s0, int s1, int steps_full,
+                                                    RowPtr row_ptr) {
   if (s0 >= s1) return;
   const bool sdw = (K % 64) == 0;  // scale rows 4-byte aligned
   constexpr int wsz = 16 * MT * kXWin;
+  const int e = s1 < steps_full ? s1 : steps_full;  // end of the full steps
+  int s = s0, cur = 0;
+  // The first step's weights are requested before the activations are staged,
+  // so the two memory latencies overlap instead of adding up.
+  WStep<TR> b0, b1;
+  if (s < e) load_wstep<TR, false>(b0, cptr, sptr, K, sdw, s);
   u32x4 xv[XP];
   xwin_load<XP>(xv, M, K, s0, row_ptr);
   xwin_fakequant<FQ, XP>(xv);
-  xwin_store<XP>(win, xv);
+  xwin_store2<H, XP>(win, hflag, xv, s0);
   __syncthreads();
-  const int e = s1 < steps_full ? s1 : steps_full;  // end of the full steps
-  int s = s0, cur = 0;
+  // One step: prefetch the activations of step s+1 and the weights of step
+  // s+1 (unconditional: past the end they re-read a valid step and the data
+  // is unused), compute step s, publish the activations of step s+1.
+  auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
+                                                 row_ptr);
+    xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+    load_wstep<TR, false>(bn, cptr, sptr, K, sdw, min(s + 1, e - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
+    xwin_fakequant<FQ, XP>(xv);
+    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hflag + (cur ^ 1), xv, s + 1);
+    __syncthreads();
+    cur ^= 1;
+    return ++s >= e;
+  };
   if (s < e) {
-    // Prefetches (weights of step s+1, activations of step s+1) are issued
-    // before step s is computed and are unconditional: past the end they
-    // re-read a valid step and the data is unused.
-    WStep<TR> b0, b1;
-    load_wstep<TR, false>(b0, cptr, sptr, K, sdw, s);
     while (true) {
-      xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
-      load_wstep<TR, false>(b1, cptr, sptr, K, sdw, min(s + 1, e - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const uint16_t* xl[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
-        compute_wstep<MT, TR>(acc, b0, xl);
-      }
-      xwin_fakequant<FQ, XP>(xv);
-      xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
-      __syncthreads();
-      cur ^= 1;
-      if (++s >= e) break;
-      xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
-      load_wstep<TR, false>(b0, cptr, sptr, K, sdw, min(s + 1, e - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const uint16_t* xl[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
-        compute_wstep<MT, TR>(acc, b1, xl);
-      }
-      xwin_fakequant<FQ, XP>(xv);
-      xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
-      __syncthreads();
-      cur ^= 1;
-      if (++s >= e) break;
+      if (stage(b0, b1)) break;
+      if (stage(b1, b0)) break;
     }
   }
   if (s == steps_full && s < s1) {  // partial last step; its activations are in `cur`
     WStep<TR> bt;
     load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
-    const uint16_t* xl[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
-    compute_wstep<MT, TR>(acc, bt, xl);
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
+                                                 row_ptr);
+    compute_wstep_win<MT, TR>(acc, bt, win, cur, f16, xrow_off);
   }
 }
 
@@ -349,31 +423,35 @@ __device__ __forceinline__ void read_sblock(WStep<TR>& b, const uint32_t* lds, i
   for (int t = 0; t < TR; ++t) b.sc[t] = lds[t * 512 + j * 64 + n * 4 + q];
 }
 
-template <int MT, int TR, int XP, bool FQ = false, typename RowPtr>
+template <int MT, int TR, int XP, bool FQ = false, bool H = false, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
                                                         const uint8_t* const (&cptr)[TR],
                                                         const uint8_t* const (&sptr)[TR],
-                                                        uint16_t* win, uint32_t* my,
+                                                        uint16_t* win, int* hflag, uint32_t* my,
                                                         const int (&xrow_off)[MT], int M,
                                                         int64_t K, int s0, int s1,
                                                         RowPtr row_ptr) {
   if (s0 >= s1) return;
   constexpr int wsz = 16 * MT * kXWin;
+  const int e = s1;  // K % 256 == 0: every step is full
+  // The first step's codes and the first scale block are requested before the
+  // activations are staged, so their memory latencies overlap.
+  WStep<TR> b0, b1;
+  load_wcodes<TR>(b0, cptr, s0);
+  u32x4 ph[TR], ph1[TR];
+  load_shalf<TR>(ph, sptr, s0, 0, e - 1);
+  load_shalf<TR>(ph1, sptr, s0, 1, e - 1);
   u32x4 xv[XP];
   xwin_load<XP>(xv, M, K, s0, row_ptr);
-  xwin_fakequant<FQ, XP>(xv);
-  xwin_store<XP>(win, xv);
-  const int e = s1;  // K % 256 == 0: every step is full
-  u32x4 ph[TR];
-  load_shalf<TR>(ph, sptr, s0, 0, e - 1);
   store_shalf<TR>(my, ph, 0);
-  load_shalf<TR>(ph, sptr, s0, 1, e - 1);
-  store_shalf<TR>(my, ph, 1);
+  store_shalf<TR>(my, ph1, 1);
+  xwin_fakequant<FQ, XP>(xv);
+  xwin_store2<H, XP>(win, hflag, xv, s0);
   __syncthreads();
   int s = s0, cur = 0, j = 0;  // j: position of step s in its 8-step block
-  WStep<TR> b0, b1;
-  load_wcodes<TR>(b0, cptr, s);
   auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
+                                                 row_ptr);
     xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
     load_wcodes<TR>(bn, cptr, min(s + 1, e - 1));
     // the next block starts at step s + 8 - j; its two halves are loaded at
@@ -382,14 +460,9 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
     if (sh) load_shalf<TR>(ph, sptr, s + 8 - j, j - 6, e - 1);
     __builtin_amdgcn_sched_barrier(0);
     read_sblock<TR>(bc, my, j);
-    {
-      const uint16_t* xl[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
-      compute_wstep<MT, TR>(acc, bc, xl);
-    }
+    compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
     xwin_fakequant<FQ, XP>(xv);
-    xwin_store<XP>(win + (cur ^ 1) * wsz, xv);
+    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hflag + (cur ^ 1), xv, s + 1);
     // half 0 fills rows 0, 2, 4, 6 (row 7 is still read at the last step);
     // half 1 fills rows 1, 3, 5, 7 after it
     if (sh) store_shalf<TR>(my, ph, j - 6);

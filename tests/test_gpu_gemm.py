@@ -47,7 +47,8 @@ def test_tiny_config(nv, orc):
 
 @pytest.mark.parametrize("M,K,N", [
     (1, 32, 16), (1, 64, 5), (3, 288, 33), (8, 1024, 560), (16, 2080, 100), (17, 512, 48),
-    (32, 1536, 272), (33, 768, 64), (70, 256, 40), (5, 8192, 24),
+    (32, 1536, 272), (33, 768, 64), (70, 256, 40), (5, 8192, 24), (6, 1312, 300),
+    (7, 544, 33000),
 ])
 def test_ragged_shapes(nv, orc, M, K, N):
     """Shapes spanning several tiles with ragged tails in M (16-row MFMA tiles),
@@ -111,6 +112,26 @@ def test_zero_and_extreme_weights(nv, orc):
     w = workloads.NF4W(np.full((N, K // 2), 0xF7, np.uint8), np.full((N, K // 16), 0x7E, np.uint8))
     ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
     _assert_close(_run(nv, x, w), ref, what="extreme")
+
+
+@pytest.mark.parametrize("M", [8, 32])
+def test_activations_outside_fp16(nv, orc, M):
+    """Steps whose activations are not all exact in fp16 (values beyond its
+    range, below its precision, or bf16 subnormals) take the bf16 path of the
+    16x16 GEMV, the other steps the fp16 path: the product stays within the
+    GEMM tolerance either way, with both K layouts (scale blocks and K tail)."""
+    helpers.announce(f"gemm activations outside fp16 M={M}")
+    rng = np.random.default_rng(40 + M)
+    for K, N in ((2048, 700), (1312, 260)):
+        x = workloads.normal_bf16(rng, M, K)
+        x[0, 300] = 0x4880          # 2^18: beyond fp16's range
+        x[M - 1, 1000] = 0x3380     # 2^-24 * 1.0: below fp16's precision for 8 bits
+        x[M // 2, 1030] = 0x0005    # a bf16 subnormal
+        x[1, 5] = 0xC780            # -65536: rounds to fp16 infinity
+        w = workloads.nvfp4_weight(rng, N, K)
+        ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+        _assert_close(_run(nv, x, w), ref, what=f"{M}x{K}x{N} bf16 steps")
+        _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
 
 
 @pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
