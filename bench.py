@@ -312,9 +312,12 @@ def secondary(nv, torch, helpers_dev, reps=3):
     dev_u8, dev_bf16, dev_i32 = helpers_dev
     res = {}
 
-    def timeit(fn, n=reps):
+    def timeit(fn, n=reps, warm_s=0.03, timed_s=0.03):
         """Seconds per call: n calls captured in one HIP graph (so the host-side
-        cost of the binding is not measured), replayed twice after a warm-up."""
+        cost of the binding is not measured), replayed for ~warm_s of GPU time
+        (the clocks settle under sustained load: a lone first call of the
+        prefill GEMM runs ~15% slower), then timed over >= 2 replays and
+        ~timed_s."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -324,17 +327,23 @@ def secondary(nv, torch, helpers_dev, reps=3):
         with torch.cuda.graph(g, stream=side):
             for _ in range(n):
                 fn()
-        g.replay()
-        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(2):
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t_replay = max(a.elapsed_time(b) / 1e3, 1e-6)
+        for _ in range(int(warm_s / t_replay)):
+            g.replay()
+        reps_t = max(2, int(timed_s / t_replay))
+        a.record()
+        for _ in range(reps_t):
             g.replay()
         b.record()
         torch.cuda.synchronize()
         del g
-        return a.elapsed_time(b) / (2 * n) / 1e3
+        return a.elapsed_time(b) / (reps_t * n) / 1e3
 
     # prefill GEMM, M = 8192
     for (K, N) in [(wl.HIDDEN, wl.MLP), (wl.MLP, wl.HIDDEN)]:
@@ -448,6 +457,13 @@ def main():
     hd = (dev_u8, dev_bf16, dev_i32)
     log("generating decode workload")
     dec = Decode(nv, torch, hd)
+    # the clocks settle only after some sustained load: run the step for ~0.2 s
+    # first (untimed), so the timed passes see the steady state
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for c in dec.calls:
+            c[4]()
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps x {len(dec.calls)} calls (warmup {args.warmup}): "
         "eager with per-call events, then as a replayed graph")
     wall_eager, per_call = time_decode(dec, torch, args.steps, args.warmup)

@@ -261,40 +261,57 @@ __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) 
 // stale index of an earlier step never matches, and the kernel sets both words
 // to -1 before the first step).  Every inexact lane writes the same value, so
 // concurrent LDS writes agree.  The flag is read after the barrier that
-// publishes the step; a marked step is staged again in bf16 (only values
-// beyond fp16's range or below 2^-17 relative precision fail, so this is rare).
+// publishes the step; a marked step is staged again in bf16.  Only values
+// beyond fp16's range (|x| > 65504) or too small to keep bf16's 8 significant
+// bits as fp16 subnormals (|x| < 2^-17) fail: for N(0,1) activations about 1%
+// of the steps at M = 8.
+//
+// A workgroup whose activations fail twice stops converting (`hw.on` false)
+// and streams the rest of its K range in bf16, so data full of such values
+// costs at most two restaged steps per workgroup.
+struct HWin {
+  int* flag;  // [2] flag words of the two buffers
+  int fails;  // steps restaged so far (workgroup-uniform)
+  bool on;    // the window is being filled in fp16
+};
+
 template <bool H, int XP>
-__device__ __forceinline__ void xwin_store2(uint16_t* buf, int* flag, const u32x4 (&v)[XP],
-                                            int s) {
+__device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int bufidx,
+                                            const u32x4 (&v)[XP], int s) {
   if constexpr (H) {
-    bool ok = true;
+    if (hw.on) {
+      bool ok = true;
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int c = threadIdx.x + i * blockDim.x;
-      u32x4 h;
-      ok = bf16x8_to_f16(v[i], h) && ok;
-      *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = h;
+      for (int i = 0; i < XP; ++i) {
+        const int c = threadIdx.x + i * blockDim.x;
+        u32x4 h;
+        ok = bf16x8_to_f16(v[i], h) && ok;
+        *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = h;
+      }
+      if (!ok) hw.flag[bufidx] = s;
+      return;
     }
-    if (!ok) *flag = s;
-  } else {
-    xwin_store<XP>(buf, v);
   }
+  xwin_store<XP>(buf, v);
 }
 
-// Before step s is computed from window buffer `buf` (H): true when its
-// activations are exact in fp16 (the window holds them in fp16); otherwise the
-// step is reloaded and stored in bf16 over the same buffer, with a barrier
-// (the flag is workgroup-uniform, so every wave takes this branch together).
-// `xv` is free at this point (the next step's prefetch is issued after).
+// Before step s is computed from window buffer `buf` (H): true when the
+// buffer holds the step in fp16 and its activations are exact there;
+// otherwise (marked step) the step is reloaded and stored in bf16 over the
+// same buffer, with a barrier (the flag is workgroup-uniform, so every wave
+// takes this branch together), and false.  `xv` is free at this point (the next
+// step's prefetch is issued after).
 template <bool H, int XP, typename RowPtr>
-__device__ __forceinline__ bool xwin_fp16_or_restage(uint16_t* buf, const int* flag,
+__device__ __forceinline__ bool xwin_fp16_or_restage(uint16_t* buf, HWin& hw, int bufidx,
                                                      u32x4 (&xv)[XP], int M, int64_t K, int s,
                                                      RowPtr row_ptr) {
   if constexpr (H) {
-    if (__builtin_amdgcn_readfirstlane(*flag) != s) return true;
+    if (!hw.on) return false;
+    if (__builtin_amdgcn_readfirstlane(hw.flag[bufidx]) != s) return true;
     xwin_load<XP>(xv, M, K, s, row_ptr);
     xwin_store<XP>(buf, xv);
     __syncthreads();
+    hw.on = ++hw.fails < 2;
   }
   return false;
 }
@@ -340,20 +357,20 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
   u32x4 xv[XP];
   xwin_load<XP>(xv, M, K, s0, row_ptr);
   xwin_fakequant<FQ, XP>(xv);
-  xwin_store2<H, XP>(win, hflag, xv, s0);
+  HWin hw{hflag, 0, true};
+  xwin_store2<H, XP>(win, hw, 0, xv, s0);
   __syncthreads();
   // One step: prefetch the activations of step s+1 and the weights of step
   // s+1 (unconditional: past the end they re-read a valid step and the data
   // is unused), compute step s, publish the activations of step s+1.
   auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
-    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
-                                                 row_ptr);
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
     xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
     load_wstep<TR, false>(bn, cptr, sptr, K, sdw, min(s + 1, e - 1));
     __builtin_amdgcn_sched_barrier(0);
     compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
     xwin_fakequant<FQ, XP>(xv);
-    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hflag + (cur ^ 1), xv, s + 1);
+    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hw, cur ^ 1, xv, s + 1);
     __syncthreads();
     cur ^= 1;
     return ++s >= e;
@@ -367,8 +384,7 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
   if (s == steps_full && s < s1) {  // partial last step; its activations are in `cur`
     WStep<TR> bt;
     load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
-    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
-                                                 row_ptr);
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
     compute_wstep_win<MT, TR>(acc, bt, win, cur, f16, xrow_off);
   }
 }
@@ -446,12 +462,12 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
   store_shalf<TR>(my, ph, 0);
   store_shalf<TR>(my, ph1, 1);
   xwin_fakequant<FQ, XP>(xv);
-  xwin_store2<H, XP>(win, hflag, xv, s0);
+  HWin hw{hflag, 0, true};
+  xwin_store2<H, XP>(win, hw, 0, xv, s0);
   __syncthreads();
   int s = s0, cur = 0, j = 0;  // j: position of step s in its 8-step block
   auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
-    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hflag + cur, xv, M, K, s,
-                                                 row_ptr);
+    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
     xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
     load_wcodes<TR>(bn, cptr, min(s + 1, e - 1));
     // the next block starts at step s + 8 - j; its two halves are loaded at
@@ -462,7 +478,7 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
     read_sblock<TR>(bc, my, j);
     compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
     xwin_fakequant<FQ, XP>(xv);
-    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hflag + (cur ^ 1), xv, s + 1);
+    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hw, cur ^ 1, xv, s + 1);
     // half 0 fills rows 0, 2, 4, 6 (row 7 is still read at the last step);
     // half 1 fills rows 1, 3, 5, 7 after it
     if (sh) store_shalf<TR>(my, ph, j - 6);

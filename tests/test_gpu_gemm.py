@@ -118,8 +118,10 @@ def test_zero_and_extreme_weights(nv, orc):
 def test_activations_outside_fp16(nv, orc, M):
     """Steps whose activations are not all exact in fp16 (values beyond its
     range, below its precision, or bf16 subnormals) take the bf16 path of the
-    16x16 GEMV, the other steps the fp16 path: the product stays within the
-    GEMM tolerance either way, with both K layouts (scale blocks and K tail)."""
+    16x16 GEMV, the other steps the fp16 path; with a failing value in every
+    step the workgroups stop converting after two.  The product stays within
+    the GEMM tolerance either way, with both K layouts (scale blocks and K
+    tail)."""
     helpers.announce(f"gemm activations outside fp16 M={M}")
     rng = np.random.default_rng(40 + M)
     for K, N in ((2048, 700), (1312, 260)):
@@ -128,6 +130,8 @@ def test_activations_outside_fp16(nv, orc, M):
         x[M - 1, 1000] = 0x3380     # 2^-24 * 1.0: below fp16's precision for 8 bits
         x[M // 2, 1030] = 0x0005    # a bf16 subnormal
         x[1, 5] = 0xC780            # -65536: rounds to fp16 infinity
+        if K == 2048:               # every step fails: workgroups switch to bf16 for good
+            x[2, ::256] = 0x3380
         w = workloads.nvfp4_weight(rng, N, K)
         ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
         _assert_close(_run(nv, x, w), ref, what=f"{M}x{K}x{N} bf16 steps")

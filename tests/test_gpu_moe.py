@@ -41,17 +41,22 @@ def test_align_bit_exact(nv, orc, T, topk, E):
     assert np.array_equal(rg.cpu().numpy(), want_rg)
 
 
-@pytest.mark.parametrize("epi", [0, 1])
-def test_grouped_gemm_matches_oracle(nv, orc, epi):
+@pytest.mark.parametrize("epi,outside", [(0, False), (1, False), (0, True), (1, True)])
+def test_grouped_gemm_matches_oracle(nv, orc, epi, outside):
     """Uneven groups (empty experts, one row, > 32 rows -> several chunks), with
-    gather and row scale."""
-    helpers.announce(f"moe grouped gemm epi={epi}")
-    rng = np.random.default_rng(30 + epi)
+    gather and row scale.  `outside`: some gathered rows also hold values far
+    from the N(0,1) bulk (2^18, 2^-24, a bf16 subnormal)."""
+    helpers.announce(f"moe grouped gemm epi={epi} outside_fp16={outside}")
+    rng = np.random.default_rng(30 + epi + 2 * outside)
     E, K, N, rows = 6, 512, 96, 50
     counts = np.array([0, 1, 40, 0, 70, 9])
     R = int(counts.sum())
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     a = workloads.normal_bf16(rng, rows, K)
+    if outside:
+        a[3, 7] = 0x4880
+        a[11, 500] = 0x3380
+        a[20, 64] = 0x0005
     w = workloads.nvfp4_weight(rng, E, N, K)
     gather = rng.integers(0, rows, R).astype(np.int32)
     rs = (rng.random(R) + 0.5).astype(np.float32)
