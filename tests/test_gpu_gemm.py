@@ -48,7 +48,7 @@ def test_tiny_config(nv, orc):
 @pytest.mark.parametrize("M,K,N", [
     (1, 32, 16), (1, 64, 5), (3, 288, 33), (8, 1024, 560), (16, 2080, 100), (17, 512, 48),
     (32, 1536, 272), (33, 768, 64), (70, 256, 40), (5, 8192, 24), (6, 1312, 300),
-    (7, 544, 33000),
+    (7, 544, 33000), (4, 8192, 24), (4, 8224, 40), (1, 17440, 200),
 ])
 def test_ragged_shapes(nv, orc, M, K, N):
     """Shapes spanning several tiles with ragged tails in M (16-row MFMA tiles),
