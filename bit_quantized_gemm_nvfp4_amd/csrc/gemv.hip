@@ -46,17 +46,19 @@ struct GemvArgs {
 template <int MT, int TR, int NW, bool FQ>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
-  // fp16 path (plain W4A16, one activation tile): steps whose activations are
-  // exact in fp16 run the fp16 MFMA on weights decoded with packed fp16
-  // multiplies (half the vector instructions).  With two activation tiles the
-  // second path's registers cost a wave per SIMD, and the fused W4A4 staging
-  // keeps the bf16 path.
-  constexpr bool H = !FQ && MT == 1;
+  // Scale blocks and the fp16 path fit the register budget of 4 waves per SIMD
+  // with one activation tile, and with two tiles in 16-wave workgroups (one
+  // window piece per thread); with two tiles in smaller workgroups they cost a
+  // wave per SIMD, more than the fetched bytes and vector instructions they
+  // save.
+  constexpr bool BLK = MT == 1 || NW == 16;
+  // fp16 path (plain W4A16): steps whose activations are exact in fp16 run
+  // the fp16 MFMA on weights decoded with packed fp16 multiplies (half the
+  // vector instructions).  The fused W4A4 staging keeps the bf16 path.
+  constexpr bool H = !FQ && BLK;
   __shared__ uint16_t win[2 * 16 * MT * kXWin];  // bf16, or fp16 (H)
   __shared__ int hflag[2];
-  // scale blocks (one-tile activations only: with two the extra registers
-  // cost more occupancy than the fetched bytes they save)
-  __shared__ uint32_t scl[MT == 1 ? NW * TR * 512 : 1];
+  __shared__ uint32_t scl[BLK ? NW * TR * 512 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 15, q = lane >> 4;
@@ -93,7 +95,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
     __syncthreads();
   }
   bool blocks = false;
-  if constexpr (MT == 1) {
+  if constexpr (BLK) {
     blocks = K % 256 == 0;
     if (blocks)
       gemv_accumulate_win_blk<MT, TR, XP, FQ, H>(acc, cptr, sptr, win, hflag,
@@ -286,8 +288,13 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   // Wide workgroups (8 waves; on the 16x16 path they share one activation
   // window) when there are rows enough to fill the chip with them, 4 waves
   // otherwise (measured: the 248,320-row head at M = 1 takes ~10% less time
-  // with 8 waves, the 17,408-row layers are as fast or faster with 4)
+  // with 8 waves, the 17,408-row layers are as fast or faster with 4).  With
+  // two activation tiles, 16 waves (scale blocks and the fp16 path, one
+  // 99 KB workgroup per CU) once there are at least 256 such workgroups: the
+  // 248,320-row head at M = 32 takes ~10% less time than with 8 waves, while
+  // the 32,768-row masked head would fill only half the CUs.
   p.nw = n_out >= 32768 ? 8 : 4;
+  if (!p.small && p.mt == 2 && n_out >= 256 * 512) p.nw = 16;
   int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
   // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
   // the waves per workgroup and the LDS budget of the staged activations.

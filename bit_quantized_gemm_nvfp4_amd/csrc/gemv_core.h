@@ -18,11 +18,11 @@
 // scattered physical k; any bijection gives the same dot product as long as A
 // and B agree.
 //
-// With one activation tile (M <= 16) the plain W4A16 GEMV runs most steps in
-// fp16 instead: the window holds the activations converted to fp16, checked
-// to be exact, and the codes are decoded to fp16 with one packed fp16 multiply
-// per pair (e2m1 * E4M3 has <= 6 significant bits inside fp16's normal range),
-// for v_mfma_f32_16x16x32_f16.  Every product is the same exact value as on
+// With one activation tile (M <= 16), and with two in 16-wave workgroups, the
+// plain W4A16 GEMV runs most steps in fp16 instead: the window holds the
+// activations converted to fp16, checked to be exact, and the codes are
+// decoded to fp16 with one packed fp16 multiply per pair (e2m1 * E4M3 has <= 6
+// significant bits inside fp16's normal range), for v_mfma_f32_16x16x32_f16.  Every product is the same exact value as on
 // the bf16 path, with half the vector instructions per weight; a step whose
 // activations are not all exact in fp16 runs the bf16 path.
 //

@@ -64,25 +64,31 @@ def test_fused_masked_rows_and_oracle(nv, orc):
     assert ok, f"rel_frob={rf:.3e} worst={worst:.3f}"
 
 
-@pytest.mark.parametrize("M,K,N", [(3, 1056, 700), (5, 512, 1000), (8, 5120, 4000),
-                                   (6, 1312, 90000), (17, 2048, 520)])
-def test_fused_in_staging_forced(nv, M, K, N):
+@pytest.mark.parametrize("M,K,N,plan", [(3, 1056, 700, None), (5, 512, 1000, None),
+                                        (8, 5120, 4000, None), (6, 1312, 90000, None),
+                                        (17, 2048, 520, None), (17, 2048, 520, "2,16"),
+                                        (30, 1312, 700, "2,16")])
+def test_fused_in_staging_forced(nv, M, K, N, plan):
     """The quantizer inside the GEMV's activation staging (whole-K staging for
     M <= 4, the streamed window for 5 <= M <= 8 and M > 8), forced for every
     shape (NVFP4_W4A4_FUSE is read per call): bit-identical to quantize then
-    the W4A4 GEMM, including ragged K steps and split-K."""
+    the W4A4 GEMM, including ragged K steps and split-K.  plan "2,16": two
+    activation tiles in 16-wave workgroups (scale blocks when K % 256 == 0)."""
     import os
     import torch
-    helpers.announce(f"w4a4 fused in staging M={M} K={K} N={N}")
+    helpers.announce(f"w4a4 fused in staging M={M} K={K} N={N} plan={plan}")
     rng = np.random.default_rng(M * 17 + K + N)
     x = helpers.dev_bf16(_x(rng, M, K))
     w = workloads.nvfp4_weight(rng, N, K)
     wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
     os.environ["NVFP4_W4A4_FUSE"] = "1"
+    if plan:
+        os.environ["NVFP4_GEMV_PLAN"] = plan
     try:
         fused = nv.gemm_w4a4(x, wc, ws, out_dtype=torch.float32)
     finally:
         del os.environ["NVFP4_W4A4_FUSE"]
+        os.environ.pop("NVFP4_GEMV_PLAN", None)
     ac, as_ = nv.quantize(x)
     ref = nv.gemm(ac, wc, ws, a_scales=as_, out_dtype=torch.float32)
     assert torch.equal(fused.view(torch.int32), ref.view(torch.int32))
