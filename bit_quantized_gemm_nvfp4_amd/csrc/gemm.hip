@@ -18,6 +18,8 @@
 
 namespace nvfp4 {
 
+constexpr int kMaxGemmSplits = 8;  // K parts of a split tile at most
+
 namespace {
 
 struct GemmArgs {
@@ -170,6 +172,9 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
 // Split tiles: out = sum over K parts (in part order) of the tile-local fp32
 // partials.  64 workgroups per tile, 4 rows of 256 columns each (4 columns per
 // thread).
+// Z = g.splits (a template argument: all Z loads are issued before the adds,
+// which run in part order, so the sum waits one memory latency, not Z).
+template <int Z>
 __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
   const int tail = blockIdx.x >> 6;
   const int lr = (blockIdx.x & 63) * 4 + (threadIdx.x >> 6);
@@ -178,12 +183,13 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
   gemm_tile_of(g.full + tail, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t row = (int64_t)tm * BM + lr, col = (int64_t)tn * BN + lc;
   if (row >= g.M || col >= g.N) return;
-  const float* p = g.partial + (int64_t)tail * g.splits * (BM * BN) + lr * BN + lc;
-  f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  for (int z = 1; z < g.splits; ++z) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN));
-    v[0] += q[0], v[1] += q[1], v[2] += q[2], v[3] += q[3];
-  }
+  const float* p = g.partial + (int64_t)tail * Z * (BM * BN) + lr * BN + lc;
+  f32x4 q[Z];
+#pragma unroll
+  for (int z = 0; z < Z; ++z) q[z] = *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN));
+  f32x4 v = q[0];
+#pragma unroll
+  for (int z = 1; z < Z; ++z) v[0] += q[z][0], v[1] += q[z][1], v[2] += q[z][2], v[3] += q[z][3];
   if (g.ga || g.gw) {
     const float alpha = alpha_of(g.ga, g.gw);
     v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
@@ -220,7 +226,7 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus) 
   GemmSplitPlan p;
   const int64_t tiles = ((M + BM - 1) / BM) * ((n_out + BN - 1) / BN);
   const int64_t steps = (K + BK - 1) / BK;
-  const int64_t zmax = steps / 8 < 8 ? steps / 8 : 8;
+  const int64_t zmax = steps / 8 < kMaxGemmSplits ? steps / 8 : kMaxGemmSplits;
   p.full = tiles;
   p.tail = 0;
   p.splits = 1;
@@ -301,7 +307,18 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
     hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
   if (hipGetLastError() != hipSuccess) return -1;
   if (g.tail > 0) {
-    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)(g.tail * 64)), dim3(256), 0, stream, g);
+    const dim3 rg((unsigned)(g.tail * 64));
+    switch (g.splits) {
+      case 1: hipLaunchKernelGGL(k_gemm_reduce<1>, rg, dim3(256), 0, stream, g); break;
+      case 2: hipLaunchKernelGGL(k_gemm_reduce<2>, rg, dim3(256), 0, stream, g); break;
+      case 3: hipLaunchKernelGGL(k_gemm_reduce<3>, rg, dim3(256), 0, stream, g); break;
+      case 4: hipLaunchKernelGGL(k_gemm_reduce<4>, rg, dim3(256), 0, stream, g); break;
+      case 5: hipLaunchKernelGGL(k_gemm_reduce<5>, rg, dim3(256), 0, stream, g); break;
+      case 6: hipLaunchKernelGGL(k_gemm_reduce<6>, rg, dim3(256), 0, stream, g); break;
+      case 7: hipLaunchKernelGGL(k_gemm_reduce<7>, rg, dim3(256), 0, stream, g); break;
+      case 8: hipLaunchKernelGGL(k_gemm_reduce<8>, rg, dim3(256), 0, stream, g); break;
+      default: return -2;
+    }
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

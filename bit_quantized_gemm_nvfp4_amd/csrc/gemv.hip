@@ -208,19 +208,75 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
   }
 }
 
+// Sum of the K parts of a split-K launch, in part order (bit-identical from
+// run to run).  A thread owns V consecutive outputs (V = 4 when count % 4 ==
+// 0 and the output is aligned for 4-element stores).  The parts are loaded in
+// batches of up to eight whose loads are all in flight before the adds, so the
+// sum waits about one memory latency per eight parts instead of one per part.
+template <int V>
+__device__ __forceinline__ void load_part(float (&d)[V], const float* p) {
+  if constexpr (V == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    d[0] = t[0], d[1] = t[1], d[2] = t[2], d[3] = t[3];
+  } else {
+    d[0] = *p;
+  }
+}
+
+// v += parts z0 .. z0+B-1 (in that order) at p = partial + i.
+template <int B, int V>
+__device__ __forceinline__ void add_parts(float (&v)[V], const float* p, int64_t count, int z0) {
+  float q[B][V];
+#pragma unroll
+  for (int j = 0; j < B; ++j) load_part<V>(q[j], p + (int64_t)(z0 + j) * count);
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] += q[j][e];
+}
+
+template <int V>
 __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ partial,
                                                        int splits, int64_t count, int out_f32,
                                                        const float* ga, const float* gw,
                                                        void* __restrict__ out) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= count) return;
-  float v = 0.f;
-  for (int z = 0; z < splits; ++z) v += partial[(int64_t)z * count + i];
-  if (ga || gw) v *= alpha_of(ga, gw);
-  if (out_f32)
-    static_cast<float*>(out)[i] = v;
-  else
-    static_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(v);
+  const float* p = partial + i;
+  float v[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) v[e] = 0.f;
+  int z = 0;
+  for (; z + 8 <= splits; z += 8) add_parts<8, V>(v, p, count, z);
+  switch (splits - z) {  // the last batch (uniform)
+    case 1: add_parts<1, V>(v, p, count, z); break;
+    case 2: add_parts<2, V>(v, p, count, z); break;
+    case 3: add_parts<3, V>(v, p, count, z); break;
+    case 4: add_parts<4, V>(v, p, count, z); break;
+    case 5: add_parts<5, V>(v, p, count, z); break;
+    case 6: add_parts<6, V>(v, p, count, z); break;
+    case 7: add_parts<7, V>(v, p, count, z); break;
+    default: break;
+  }
+  if (ga || gw) {
+    const float alpha = alpha_of(ga, gw);
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] *= alpha;
+  }
+  if constexpr (V == 4) {
+    if (out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      const u32x2 pk = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                        (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i) = pk;
+    }
+  } else {
+    if (out_f32)
+      static_cast<float*>(out)[i] = v[0];
+    else
+      static_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(v[0]);
+  }
 }
 
 template <int MT, int TR, bool FQ>
@@ -253,11 +309,11 @@ void launch_gemv4_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
 }
 
 // The plan's (tiles per wave) choice as a template argument; fused W4A4
-// staging is instantiated only for the default two tiles per wave.
+// staging is instantiated for the plan's defaults (one or two tiles per wave).
 template <bool SMALL, int MT, int TR>
 int launch_plan(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
   if (a.fq) {
-    if constexpr (TR == 2) {
+    if constexpr (TR <= 2) {
       if constexpr (SMALL)
         launch_gemv4_t<MT, TR, true>(a, p.nw, p.z, stream);
       else
@@ -289,24 +345,32 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   // window) when there are rows enough to fill the chip with them, 4 waves
   // otherwise (measured: the 248,320-row head at M = 1 takes ~10% less time
   // with 8 waves, the 17,408-row layers are as fast or faster with 4).  With
-  // two activation tiles, 16 waves (scale blocks and the fp16 path, one
-  // 99 KB workgroup per CU) once there are at least 256 such workgroups: the
-  // 248,320-row head at M = 32 takes ~10% less time than with 8 waves, while
-  // the 32,768-row masked head would fill only half the CUs.
+  // two activation tiles, 16 waves (scale blocks and the fp16 path; one
+  // workgroup per CU, 99 KB of LDS with two weight tiles per wave, 66 KB with
+  // one): two tiles per wave once they give at least 256 workgroups, one
+  // below (measured at M = 32 against 8 and 4 waves: the 248,320-row head
+  // 204 -> 177 us, the 32,768-row masked head 38 -> 33 us, the 17,408-row
+  // layers 33-34 -> 28-29 us).
   p.nw = n_out >= 32768 ? 8 : 4;
-  if (!p.small && p.mt == 2 && n_out >= 256 * 512) p.nw = 16;
+  if (!p.small && p.mt == 2) {
+    p.nw = 16;
+    p.tr = n_out >= 256 * 512 ? 2 : 1;
+  }
   int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
-  // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib]" overrides the tiles per wave,
-  // the waves per workgroup and the LDS budget of the staged activations.
+  // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib[,z]]" overrides the tiles per
+  // wave, the waves per workgroup, the LDS budget of the staged activations
+  // (0: default) and the number of K parts (0: default).
+  int z_force = 0;
   if (const char* e = getenv("NVFP4_GEMV_PLAN")) {
     int tr = 0, nw = 0, kib = 0;
-    const int n = sscanf(e, "%d,%d,%d", &tr, &nw, &kib);
+    const int n = sscanf(e, "%d,%d,%d,%d", &tr, &nw, &kib, &z_force);
     const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || (tr == 8 && p.mt == 1))
                                : (tr == 1 || tr == 2 || (tr == 4 && p.mt == 1));
     const bool nw_ok = p.small ? (nw >= 1 && nw <= 8)
                                : (nw == 4 || nw == 8 || (nw == 16 && p.mt == 2 && tr <= 2));
     if (n >= 2 && tr_ok && nw_ok) p.tr = tr, p.nw = nw;
-    if (n == 3 && kib >= 8 && kib <= 160) lds_budget = (int64_t)kib * 1024;
+    if (n >= 3 && kib >= 8 && kib <= 160) lds_budget = (int64_t)kib * 1024;
+    if (n < 4) z_force = 0;
   }
   const int64_t step = p.small ? kG4Step : kGemvStep;
   const int64_t rows_per_tile = p.small ? 4 : 16;
@@ -317,12 +381,23 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
     if (max_steps < 1) max_steps = 1;
     z = (steps + max_steps - 1) / max_steps;
   }
+  const int64_t z_lds = z;
   // enough waves to fill the chip
   const int64_t tiles = (n_out + rows_per_tile - 1) / rows_per_tile;
   const int64_t wgs = (tiles + (int64_t)p.nw * p.tr - 1) / ((int64_t)p.nw * p.tr);
-  const int64_t want_waves = (int64_t)num_cus * 8;
-  const int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
-  if (zw > z) z = zw;
+  if (p.nw == 16) {
+    // one workgroup per CU (LDS, registers): as many K parts as keep every
+    // workgroup in one round (measured at M = 32: the 17,408 x 5,120 layer
+    // 44 / 36 / 28 us with 4 / 6 / 9 parts, the masked head 48 -> 35 us with
+    // 2 parts instead of 1, a second round costing more than it splits)
+    const int64_t zc = num_cus / wgs;
+    if (zc > z) z = zc;
+  } else {
+    const int64_t want_waves = (int64_t)num_cus * 8;
+    const int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
+    if (zw > z) z = zw;
+  }
+  if (z_force > 0) z = z_force > z_lds ? z_force : z_lds;
   if (z > steps) z = steps;
   if (z < 1) z = 1;
   p.z = (int)z;
@@ -383,9 +458,15 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
   if (hipGetLastError() != hipSuccess) return -1;
   if (p.z > 1) {
     const int64_t count = M * n_out;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const float*>(workspace), p.z, count,
-                       out_f32 ? 1 : 0, alpha.a, alpha.w, out);
+    const float* part = static_cast<const float*>(workspace);
+    const uintptr_t oa = reinterpret_cast<uintptr_t>(out) % (out_f32 ? 16 : 8);
+    if (count % 4 == 0 && oa == 0)
+      hipLaunchKernelGGL(k_splitk_reduce<4>, dim3((unsigned)((count / 4 + 255) / 256)),
+                         dim3(256), 0, stream, part, p.z, count, out_f32 ? 1 : 0, alpha.a,
+                         alpha.w, out);
+    else
+      hipLaunchKernelGGL(k_splitk_reduce<1>, dim3((unsigned)((count + 255) / 256)), dim3(256),
+                         0, stream, part, p.z, count, out_f32 ? 1 : 0, alpha.a, alpha.w, out);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

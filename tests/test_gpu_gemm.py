@@ -62,14 +62,15 @@ def test_ragged_shapes(nv, orc, M, K, N):
     _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
 
 
-@pytest.mark.parametrize("plan", ["2,16", "1,16"])
+@pytest.mark.parametrize("plan", ["2,16", "1,16", "2,8", "1,4"])
 @pytest.mark.parametrize("M,K,N", [(17, 2048, 700), (32, 1312, 1000), (24, 4096, 1100),
                                    (32, 256, 33)])
-def test_two_tiles_wide_workgroups(nv, orc, M, K, N, plan):
-    """Two activation tiles (16 < M <= 32) in 16-wave workgroups, one and two
-    weight tiles per wave (the fp16 path and scale blocks for K % 256 == 0),
-    forced through NVFP4_GEMV_PLAN at sizes the oracle checks whole: ragged
-    M, N and K, workgroups with padding rows only."""
+def test_two_tiles_plans(nv, orc, M, K, N, plan):
+    """Two activation tiles (16 < M <= 32) in every workgroup layout, forced
+    through NVFP4_GEMV_PLAN ("tiles per wave, waves") at sizes the oracle
+    checks whole: 16-wave workgroups (the fp16 path, scale blocks for K % 256
+    == 0) and the 8- and 4-wave bf16 layouts; ragged M, N and K, waves with
+    padding rows only."""
     import os
     helpers.announce(f"gemm two tiles 16 waves M={M} K={K} N={N} plan={plan}")
     rng = np.random.default_rng(M * 7 + K + N)
@@ -138,15 +139,16 @@ def test_zero_and_extreme_weights(nv, orc):
     _assert_close(_run(nv, x, w), ref, what="extreme")
 
 
-@pytest.mark.parametrize("M,plan", [(8, None), (32, None), (32, "2,16"), (20, "2,16")])
+@pytest.mark.parametrize("M,plan", [(8, None), (32, None), (32, "2,16"), (20, "2,8")])
 def test_activations_outside_fp16(nv, orc, M, plan):
     """Steps whose activations are not all exact in fp16 (values beyond its
     range, below its precision, or bf16 subnormals) take the bf16 path of the
     16x16 GEMV, the other steps the fp16 path; with a failing value in every
     step the workgroups stop converting after two.  The product stays within
     the GEMM tolerance either way, with both K layouts (scale blocks and K
-    tail).  plan "2,16" (NVFP4_GEMV_PLAN, read per call): two activation
-    tiles in 16-wave workgroups, the layout of the widest layers at M > 16."""
+    tail).  plan (NVFP4_GEMV_PLAN, read per call): "2,16" two weight tiles
+    per wave in 16-wave workgroups (the widest layers at M > 16), "2,8" the
+    8-wave bf16 layout."""
     import os
     helpers.announce(f"gemm activations outside fp16 M={M} plan={plan}")
     if plan:
