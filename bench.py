@@ -171,6 +171,13 @@ def time_decode_graph(dec, torch, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    # the GPU idled while the graph was captured: replay it (untimed) for
+    # ~0.2 s more, so the timed replays see the clocks settled under load again
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         g.replay()
