@@ -290,7 +290,7 @@ struct GroupedMfmaArgs {
   int E;
   int swiglu;
   int n_tiles;  // tiles per chunk: ceil(N / 256), or ceil(N/2 / 128) with SWIGLU
-  int total;    // upper bound of chunks * n_tiles
+  int chunks;   // upper bound of the 256-row chunks
 };
 
 // One workgroup: one 256-row chunk of one expert's gathered rows against one
@@ -302,10 +302,14 @@ struct GroupedMfmaArgs {
 // and j + 2 of the wave), so the epilogue needs no exchange.
 __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g) {
   extern __shared__ char lds[];
-  const int per_xcd = (g.total + 7) / 8;
-  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);  // XCD-aware order
-  if (lin >= g.total) return;
-  const int chunk = lin / g.n_tiles, tn = lin - chunk * g.n_tiles;
+  // Consecutive workgroups go to consecutive XCDs.  Chunk c runs on XCD c % 8,
+  // its n_tiles tiles one after another there, so they share its activation
+  // rows in one L2; and the chunks that exist (the host knows only an upper
+  // bound) spread evenly over the XCDs, the surplus workgroups at the end of
+  // every XCD's sequence.
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int chunk = (k / g.n_tiles) * 8 + xcd, tn = k % g.n_tiles;
+  if (chunk >= g.chunks) return;
   int e, c;
   if (!find_chunk(g.offsets, g.E, chunk, BM, e, c)) return;  // uniform over the workgroup
   const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * BM;
@@ -535,8 +539,8 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
     m.swiglu = swiglu ? 1 : 0;
     m.n_tiles = (int)(swiglu ? (N / 2 + 127) / 128 : (N + BN - 1) / BN);
     const int64_t chunks = (R + BM - 1) / BM + E;  // upper bound
-    m.total = (int)(chunks * m.n_tiles);
-    const int grid = ((m.total + 7) / 8) * 8;
+    m.chunks = (int)chunks;
+    const int grid = (int)(((chunks + 7) / 8) * 8 * m.n_tiles);
     hipLaunchKernelGGL(k_grouped_mfma, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, m);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
