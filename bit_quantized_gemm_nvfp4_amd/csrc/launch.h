@@ -41,7 +41,7 @@ struct GemvPlan {
   bool small;  // M <= 4: 4x4x4-block kernel (tiles of 4 rows)
   int mt;  // 16-row activation tiles (M <= 16 * mt)
   int tr;  // 16-row weight tiles per wave
-  int nw;  // waves per workgroup (split-K inside the workgroup)
+  int nw;  // waves per workgroup (each streams its own weight tiles)
   int z;   // split-K across workgroups (fp32 partials + reduce kernel)
 };
 
@@ -49,7 +49,7 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
 // fakequant: x is bf16 and every 16-element block is quantized to NVFP4 and
 // dequantized while it is staged (the W4A4 product with the activation
-// quantizer fused in; only the default two tiles per wave).
+// quantizer fused in; one or two weight tiles per wave).
 int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
                 void* out, void* workspace, hipStream_t stream, Alpha alpha = {},
