@@ -57,7 +57,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4) {
   g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs);
   g.partial_bytes = g.mfma ? gemm_workspace_bytes(M, n_out, K, kNumCUs)
                            : gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
-  g.a_dequant_bytes = (w4a4 && !g.mfma) ? (size_t)M * (size_t)K * 2 : 0;
+  // W4A4: the activations are dequantized once (exact in bf16) and the bf16
+  // kernels run; on the MFMA path that replaces a decode of the activation
+  // tile by every workgroup of its row band (tuning knob NVFP4_W4A4_MFMA_DEQ=0:
+  // decode inside the GEMM)
+  bool deq = w4a4;
+  if (g.mfma) {
+    const char* e = getenv("NVFP4_W4A4_MFMA_DEQ");
+    deq = w4a4 && !(e && e[0] == '0');
+  }
+  g.a_dequant_bytes = deq ? (size_t)M * (size_t)K * 2 : 0;
   return g;
 }
 
@@ -154,6 +163,13 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
       fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: mfma 256x256\n",
               (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16");
     void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
+    if (w4a4 && g.a_dequant_bytes) {
+      uint16_t* xa = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + a_off);
+      if (launch_dequantize(static_cast<const uint8_t*>(a), a_scales, M, K, xa, st) != 0)
+        return NVFP4_ERROR_LAUNCH;
+      return launched(launch_gemm(false, xa, nullptr, M, K, w_codes, w_scales, row_idx, n_out,
+                                  out_dtype == NVFP4_FP32, out, partial, st, alpha));
+    }
     return launched(launch_gemm(w4a4, a, a_scales, M, K, w_codes, w_scales, row_idx, n_out,
                                 out_dtype == NVFP4_FP32, out, partial, st, alpha));
   }
