@@ -240,12 +240,8 @@ static bool w4a4_fuse_in_gemv(int64_t M, int64_t n_out) {
 size_t nvfp4_gemm_w4a4_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out) {
   if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return 0;
   const GemmPlan g = plan_gemm(M, N, K, n_out, false);
-  if (!g.mfma) {
-    if (w4a4_fuse_in_gemv(M, n_out)) return g.partial_bytes;
-    return round_up((size_t)M * (size_t)K * 2, 256) + g.partial_bytes;
-  }
-  return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 16, 256) +
-         nvfp4_gemm_workspace_size(NVFP4_NVFP4, M, N, K, n_out);
+  if (!g.mfma && w4a4_fuse_in_gemv(M, n_out)) return g.partial_bytes;
+  return round_up((size_t)M * (size_t)K * 2, 256) + g.partial_bytes;
 }
 
 int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
@@ -262,25 +258,17 @@ int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
   if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = as_stream(stream);
-  if (!g.mfma) {
-    if (w4a4_fuse_in_gemv(M, n_out))  // quantized inside the GEMV's activation staging
-      return gemm_impl(NVFP4_BF16, a, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
-                       out_dtype, out, workspace, workspace_bytes, stream, Alpha{}, true);
-    uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
-    const size_t g_off = round_up((size_t)M * (size_t)K * 2, 256);
-    if (launch_fakequant(a, M, K, xq, st) != 0) return NVFP4_ERROR_LAUNCH;
-    return gemm_impl(NVFP4_BF16, xq, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
-                     out_dtype, out, g.partial_bytes ? ws + g_off : nullptr,
-                     workspace_bytes - g_off, stream, Alpha{});
-  }
-  // large M: quantize once, then the W4A4 MFMA GEMM
-  uint8_t* codes = reinterpret_cast<uint8_t*>(ws);
-  const size_t s_off = round_up((size_t)M * (size_t)K / 2, 256);
-  uint8_t* scales = reinterpret_cast<uint8_t*>(ws + s_off);
-  const size_t g_off = s_off + round_up((size_t)M * (size_t)K / 16, 256);
-  if (launch_quantize(a, M, K, codes, scales, st) != 0) return NVFP4_ERROR_LAUNCH;
-  return gemm_impl(NVFP4_NVFP4, codes, scales, M, N, K, w_codes, w_scales, row_idx, n_out,
-                   out_dtype, out, ws + g_off, workspace_bytes - g_off, stream, Alpha{});
+  if (!g.mfma && w4a4_fuse_in_gemv(M, n_out))  // quantized inside the GEMV's activation staging
+    return gemm_impl(NVFP4_BF16, a, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
+                     out_dtype, out, workspace, workspace_bytes, stream, Alpha{}, true);
+  // one pass writes the activations quantized to NVFP4 and dequantized (bf16,
+  // exact), then the bf16-activation GEMV or MFMA GEMM runs on them
+  uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
+  const size_t g_off = round_up((size_t)M * (size_t)K * 2, 256);
+  if (launch_fakequant(a, M, K, xq, st) != 0) return NVFP4_ERROR_LAUNCH;
+  return gemm_impl(NVFP4_BF16, xq, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
+                   out_dtype, out, g.partial_bytes ? ws + g_off : nullptr,
+                   workspace_bytes - g_off, stream, Alpha{});
 }
 
 int nvfp4_quantize_scaled(const uint16_t* x, int64_t M, int64_t K, const float* global_scale,

@@ -132,9 +132,10 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
  * the product ("52.6% more tokens, 1.53x less GPU time ...": NVFP4 W4A4
  * execution).  Bit-identical to nvfp4_quantize(a) followed by nvfp4_gemm
  * with a_dtype = NVFP4 (same arguments otherwise: row_idx, n_out, out_dtype).
- * Decode shapes (M below the MFMA threshold) quantize every 16-element block
- * while the GEMV stages the activations, so the codes never go to memory;
- * large M quantizes once into the workspace and runs the W4A4 MFMA GEMM.
+ * Very small M quantizes every 16-element block while the GEMV stages the
+ * activations, so the codes never go to memory; otherwise one pass writes the
+ * activations quantized and dequantized (bf16, exact) into the workspace and
+ * the bf16-activation GEMV or MFMA GEMM runs on them.
  * workspace: >= nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out) bytes.
  * K % 32 == 0.
  */
