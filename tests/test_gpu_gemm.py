@@ -361,3 +361,27 @@ def test_prefill_full_size_sampled(nv, orc, K, N):
     ref = orc.gemm_w4a16(xs, len(rows), K, w.codes, w.scales, row_idx=cols)
     _assert_close(y[np.ix_(rows, cols)], ref, what=f"prefill K={K} N={N}")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,plan", [(1, "2,4,0,8"), (1, "2,4,0,11"), (8, "2,4,0,8"),
+                                    (8, "2,8,0,16"), (32, "1,16,0,11"), (32, "2,16,0,16"),
+                                    (3, "1,4,0,13")])
+def test_split_k_part_counts(nv, orc, M, plan):
+    """K split into 8, 11, 13 and 16 parts (NVFP4_GEMV_PLAN "tr,nw,lds,z"): the
+    reduce adds full batches of eight parts and every remainder; bf16 and
+    fp32 outputs within the GEMM tolerance of the oracle."""
+    import os
+    helpers.announce(f"gemm split-K part counts M={M} plan={plan}")
+    rng = np.random.default_rng(M * 11 + len(plan))
+    K, N = 8192, 300
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    os.environ["NVFP4_GEMV_PLAN"] = plan
+    try:
+        got = _run(nv, x, w)
+        got32 = _run(nv, x, w, out_f32=True)
+    finally:
+        del os.environ["NVFP4_GEMV_PLAN"]
+    _assert_close(got, ref, what=f"{M}x{K}x{N} {plan}")
+    _assert_close(got32, ref, out_f32=True, what=f"{M}x{K}x{N} {plan} fp32")
