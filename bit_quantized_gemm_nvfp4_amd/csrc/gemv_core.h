@@ -73,13 +73,27 @@ __device__ __forceinline__ void stage_activations(uint16_t* lds, int m_rows, int
   const int chunks_per_row = klen / 8;
   const int total = m_rows * chunks_per_row;
   const u32x4 z = {0u, 0u, 0u, 0u};
+  // Four pieces per thread are loaded before any is stored, so the staging
+  // waits about one memory latency per four rounds instead of one per round.
   // (total and blockDim.x are even, so a block's two lanes are active together)
-  for (int c = threadIdx.x; c < total; c += blockDim.x) {
-    const int m = c / chunks_per_row, c8 = c - m * chunks_per_row;
-    const int64_t k = k_lo + (int64_t)c8 * 8;
-    u32x4 v = k < K ? *reinterpret_cast<const u32x4*>(row_ptr(m) + k) : z;
-    if constexpr (FQ) v = fakequant_piece(v);
-    *reinterpret_cast<u32x4*>(lds + m * stride + c8 * 8) = v;
+  for (int c0 = threadIdx.x; c0 < total; c0 += 4 * blockDim.x) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * blockDim.x;
+      const int m = c / chunks_per_row, c8 = c - m * chunks_per_row;
+      const int64_t k = k_lo + (int64_t)c8 * 8;
+      v[u] = (c < total && k < K) ? *reinterpret_cast<const u32x4*>(row_ptr(m) + k) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * blockDim.x;
+      if (c >= total) break;
+      const int m = c / chunks_per_row, c8 = c - m * chunks_per_row;
+      u32x4 w = v[u];
+      if constexpr (FQ) w = fakequant_piece(w);
+      *reinterpret_cast<u32x4*>(lds + m * stride + c8 * 8) = w;
+    }
   }
   __syncthreads();
 }
