@@ -403,15 +403,28 @@ __global__ void __launch_bounds__(256) k_moe_combine(const uint16_t* __restrict_
   if (i >= T * per_row) return;
   const int64_t t = i / per_row, c8 = (i - t * per_row) * 8;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int64_t row = slot_pos[t * topk + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(y + row * H + c8);
+  auto add = [&](const u32x4& v) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       s[2 * w] += bf16_bits_to_f32(v[w] & 0xFFFFu);
       s[2 * w + 1] += bf16_bits_to_f32(v[w] >> 16);
     }
+  };
+  int j = 0;
+  // eight slots at a time: their rows, then all eight row loads in flight,
+  // then the adds in slot order
+  for (; j + 8 <= topk; j += 8) {
+    int64_t rows[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rows[u] = slot_pos[t * topk + j + u];
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const u32x4*>(y + rows[u] * H + c8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(v[u]);
   }
+  for (; j < topk; ++j)
+    add(*reinterpret_cast<const u32x4*>(y + (int64_t)slot_pos[t * topk + j] * H + c8));
   u32x4 o;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
