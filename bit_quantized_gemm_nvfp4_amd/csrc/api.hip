@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include "../../include/nvfp4.h"
+#include "../../include/nvfp4_plan.h"
 #include "launch.h"
 #include "moe.h"
 
@@ -36,41 +37,63 @@ constexpr int64_t kGemvMaxM = 32;
 // 32-row chunk).
 constexpr int64_t kGemmMinM = 65;
 
+// Largest K of the MFMA GEMM: its activation offsets inside a 256-row tile are
+// 32-bit byte offsets.
+constexpr int64_t kGemmMaxK = (int64_t)1 << 22;
+
 struct GemmPlan {
   bool mfma;             // large-M MFMA GEMM
   GemvPlan gemv;
   int64_t m_chunk;       // activation rows per GEMV launch
-  size_t a_dequant_bytes;  // W4A4 GEMV: bf16 copy of the dequantized activations
+  size_t a_dequant_bytes;  // W4A4: bf16 copy of the dequantized activations
   size_t partial_bytes;
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t n_out, bool w4a4,
+                   const PlanOverride& ov) {
   (void)N;
   GemmPlan g;
-  int64_t min_m = kGemmMinM;
-  if (const char* e = getenv("NVFP4_GEMM_MIN_M")) {  // tuning knob
-    const long v = atol(e);
-    if (v >= 1) min_m = v;
-  }
+  const int64_t min_m = ov.gemm_min_m >= 1 ? ov.gemm_min_m : kGemmMinM;
   g.mfma = M >= min_m;
   g.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
-  g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs);
+  g.gemv = plan_gemv(g.m_chunk, n_out, K, kNumCUs, ov);
   g.partial_bytes = g.mfma ? gemm_workspace_bytes(M, n_out, K, kNumCUs)
                            : gemv_workspace_bytes(g.gemv, g.m_chunk, n_out);
-  // W4A4: the activations are dequantized once (exact in bf16) and the bf16
-  // kernels run; on the MFMA path that replaces a decode of the activation
-  // tile by every workgroup of its row band (tuning knob NVFP4_W4A4_MFMA_DEQ=0:
-  // decode inside the GEMM)
-  bool deq = w4a4;
-  if (g.mfma) {
-    const char* e = getenv("NVFP4_W4A4_MFMA_DEQ");
-    deq = w4a4 && !(e && e[0] == '0');
-  }
-  g.a_dequant_bytes = deq ? (size_t)M * (size_t)K * 2 : 0;
+  // W4A4 (NVFP4 activations): the activations are dequantized once (exact in
+  // bf16) and the bf16-activation kernels run on them
+  g.a_dequant_bytes = w4a4 ? (size_t)M * (size_t)K * 2 : 0;
   return g;
 }
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// The caller's plan as the internal override; false if it names a layout the
+// library does not build (then nothing is launched).
+bool to_override(const nvfp4_plan_t* plan, PlanOverride& ov) {
+  ov = PlanOverride{};
+  if (!plan) return true;
+  ov.gemm_min_m = plan->gemm_min_m;
+  ov.gemv_small_max = plan->gemv_small_max;
+  ov.gemv_tiles = plan->gemv_tiles;
+  ov.gemv_waves = plan->gemv_waves;
+  ov.gemv_lds_kib = plan->gemv_lds_kib;
+  ov.gemv_splits = plan->gemv_splits;
+  ov.w4a4_fuse = plan->w4a4_fuse;
+  ov.grouped_mfma_min_rows = plan->grouped_mfma_min_rows;
+  if (ov.gemm_min_m == 0 || ov.w4a4_fuse > 1) return false;
+  return true;
+}
+
+// Whether the GEMV layout of a plan exists for activation chunks of M rows
+// (the fused W4A4 staging is built for 1 or 2 tiles per wave).
+bool gemv_plan_ok(const PlanOverride& ov, int64_t M, bool fused) {
+  if (!gemv_override_valid(M, ov)) return false;
+  if (fused) {
+    const GemvPlan p = plan_gemv(M, 1, 32, kNumCUs, ov);
+    if (p.tr > 2) return false;
+  }
+  return true;
+}
 
 }  // namespace
 
@@ -110,8 +133,21 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint
 }
 
 size_t nvfp4_gemm_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K, int64_t n_out) {
+  return nvfp4_gemm_workspace_size_planned(nullptr, a_dtype, M, N, K, n_out);
+}
+
+void nvfp4_plan_default(nvfp4_plan_t* plan) {
+  if (!plan) return;
+  plan->gemm_min_m = plan->gemv_small_max = plan->gemv_tiles = plan->gemv_waves = -1;
+  plan->gemv_lds_kib = plan->gemv_splits = plan->w4a4_fuse = plan->grouped_mfma_min_rows = -1;
+}
+
+size_t nvfp4_gemm_workspace_size_planned(const nvfp4_plan_t* plan, int a_dtype, int64_t M,
+                                         int64_t N, int64_t K, int64_t n_out) {
   if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return 0;
-  GemmPlan g = plan_gemm(M, N, K, n_out, a_dtype == NVFP4_NVFP4);
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return 0;
+  GemmPlan g = plan_gemm(M, N, K, n_out, a_dtype == NVFP4_NVFP4, ov);
   return round_up(g.a_dequant_bytes, 256) + g.partial_bytes;
 }
 
@@ -140,7 +176,7 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
               int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
               const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
               void* workspace, size_t workspace_bytes, void* stream, Alpha alpha,
-              bool fakequant = false) {
+              const PlanOverride& ov, bool fakequant = false) {
   if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
   if (const int rc = linear_args_status(a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
                                         out))
@@ -149,7 +185,8 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
   if (a_dtype == NVFP4_NVFP4 && !a_scales) return NVFP4_ERROR_INVALID_VALUE;
   if (a_scales && !aligned16(a_scales)) return NVFP4_ERROR_INVALID_VALUE;
   const bool w4a4 = a_dtype == NVFP4_NVFP4;
-  GemmPlan g = plan_gemm(M, N, K, n_out, w4a4);
+  GemmPlan g = plan_gemm(M, N, K, n_out, w4a4, ov);
+  if (g.mfma && K > kGemmMaxK) return NVFP4_ERROR_NOT_SUPPORTED;
   const size_t a_off = 0, p_off = round_up(g.a_dequant_bytes, 256);
   const size_t need = p_off + g.partial_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
@@ -157,20 +194,20 @@ int gemm_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, in
 
   hipStream_t st = as_stream(stream);
   if (g.mfma) {
-    if (fakequant) return NVFP4_ERROR_NOT_SUPPORTED;  // (callers quantize first)
     if (((M + 255) / 256) * ((n_out + 255) / 256) > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
     if (log_enabled())
       fprintf(stderr, "[nvfp4] gemm M=%lld N=%lld K=%lld n_out=%lld %s: mfma 256x256\n",
               (long long)M, (long long)N, (long long)K, (long long)n_out, w4a4 ? "w4a4" : "w4a16");
     void* partial = g.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
-    if (w4a4 && g.a_dequant_bytes) {
-      uint16_t* xa = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + a_off);
-      if (launch_dequantize(static_cast<const uint8_t*>(a), a_scales, M, K, xa, st) != 0)
+    const void* xa = a;
+    if (w4a4) {
+      uint16_t* xd = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + a_off);
+      if (launch_dequantize(static_cast<const uint8_t*>(a), a_scales, M, K, xd, st) != 0)
         return NVFP4_ERROR_LAUNCH;
-      return launched(launch_gemm(false, xa, nullptr, M, K, w_codes, w_scales, row_idx, n_out,
-                                  out_dtype == NVFP4_FP32, out, partial, st, alpha));
+      xa = xd;
     }
-    return launched(launch_gemm(w4a4, a, a_scales, M, K, w_codes, w_scales, row_idx, n_out,
+    return launched(launch_gemm(fakequant ? GemmA::kFakeQuant : GemmA::kBf16, xa, M, K,
+                                w_codes, w_scales, row_idx, n_out,
                                 out_dtype == NVFP4_FP32, out, partial, st, alpha));
   }
   const uint16_t* x = static_cast<const uint16_t*>(a);
@@ -206,7 +243,19 @@ int nvfp4_gemm(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, i
                const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
                void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
-                   out, workspace, workspace_bytes, stream, Alpha{});
+                   out, workspace, workspace_bytes, stream, Alpha{}, PlanOverride{});
+}
+
+int nvfp4_gemm_planned(const nvfp4_plan_t* plan, int a_dtype, const void* a,
+                       const uint8_t* a_scales, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const int32_t* row_idx,
+                       int64_t n_out, int out_dtype, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, false)) return NVFP4_ERROR_INVALID_VALUE;
+  return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                   out, workspace, workspace_bytes, stream, Alpha{}, ov);
 }
 
 int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
@@ -223,44 +272,47 @@ int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
   alpha.a = a_global_scale;
   alpha.w = w_global_scale;
   return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
-                   out, workspace, workspace_bytes, stream, alpha);
+                   out, workspace, workspace_bytes, stream, alpha, PlanOverride{});
 }
 
-// Decode-shaped W4A4 from bf16 activations: the GEMV can quantize the
-// activations itself while staging them (no extra launch), but every
-// workgroup along N then repeats that work; otherwise one pass writes the
-// quantized-and-dequantized activations (bf16, exact) and the plain GEMV
-// reads them.  Staging wins only for very few rows and narrow layers.
-static bool w4a4_fuse_in_gemv(int64_t M, int64_t n_out) {
-  if (const char* e = getenv("NVFP4_W4A4_FUSE"))  // tuning knob: 0 never, 1 always
-    return e[0] == '1';
-  return M <= 4 && n_out <= 65536;
+// W4A4 from bf16 activations.  The kernel can quantize the activations
+// itself as it loads them (no extra launch and no activation copy in memory),
+// but every workgroup along N then repeats that work; otherwise one pass
+// writes the quantized-and-dequantized activations (bf16, exact) and the
+// plain bf16-activation kernel reads them.  In the GEMV staging wins only for
+// very few rows on narrow layers; in the MFMA GEMM's tile loads it does not
+// win (measured: DESIGN notes), so large M takes the pass.
+static bool w4a4_fuse(const GemmPlan& g, int64_t M, int64_t n_out, const PlanOverride& ov) {
+  if (ov.w4a4_fuse >= 0) return ov.w4a4_fuse == 1;
+  return !g.mfma && M <= 4 && n_out <= 65536;
 }
 
-size_t nvfp4_gemm_w4a4_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out) {
+static size_t w4a4_bf16_workspace(const PlanOverride& ov, int64_t M, int64_t N, int64_t K,
+                                  int64_t n_out) {
   if (M <= 0 || N <= 0 || K <= 0 || n_out <= 0) return 0;
-  const GemmPlan g = plan_gemm(M, N, K, n_out, false);
-  if (!g.mfma && w4a4_fuse_in_gemv(M, n_out)) return g.partial_bytes;
+  const GemmPlan g = plan_gemm(M, N, K, n_out, false, ov);
+  if (w4a4_fuse(g, M, n_out, ov)) return g.partial_bytes;
   return round_up((size_t)M * (size_t)K * 2, 256) + g.partial_bytes;
 }
 
-int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
-                         const uint8_t* w_codes, const uint8_t* w_scales,
-                         const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+static int w4a4_bf16_impl(const PlanOverride& ov, const uint16_t* a, int64_t M, int64_t N,
+                          int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   if (const int rc = linear_args_status(a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
                                         out))
     return rc;  // (checked here, before the quantizer runs)
   if (M * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
-  const GemmPlan g = plan_gemm(M, N, K, n_out, false);
-  const size_t need = nvfp4_gemm_w4a4_bf16_workspace_size(M, N, K, n_out);
+  const GemmPlan g = plan_gemm(M, N, K, n_out, false, ov);
+  if (g.mfma && K > kGemmMaxK) return NVFP4_ERROR_NOT_SUPPORTED;
+  const size_t need = w4a4_bf16_workspace(ov, M, N, K, n_out);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = as_stream(stream);
-  if (!g.mfma && w4a4_fuse_in_gemv(M, n_out))  // quantized inside the GEMV's activation staging
+  if (w4a4_fuse(g, M, n_out, ov))  // quantized inside the kernel's activation loads
     return gemm_impl(NVFP4_BF16, a, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
-                     out_dtype, out, workspace, workspace_bytes, stream, Alpha{}, true);
+                     out_dtype, out, workspace, workspace_bytes, stream, Alpha{}, ov, true);
   // one pass writes the activations quantized to NVFP4 and dequantized (bf16,
   // exact), then the bf16-activation GEMV or MFMA GEMM runs on them
   uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
@@ -268,7 +320,39 @@ int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
   if (launch_fakequant(a, M, K, xq, st) != 0) return NVFP4_ERROR_LAUNCH;
   return gemm_impl(NVFP4_BF16, xq, nullptr, M, N, K, w_codes, w_scales, row_idx, n_out,
                    out_dtype, out, g.partial_bytes ? ws + g_off : nullptr,
-                   workspace_bytes - g_off, stream, Alpha{});
+                   workspace_bytes - g_off, stream, Alpha{}, ov);
+}
+
+size_t nvfp4_gemm_w4a4_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int64_t n_out) {
+  return w4a4_bf16_workspace(PlanOverride{}, M, N, K, n_out);
+}
+
+int nvfp4_gemm_w4a4_bf16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return w4a4_bf16_impl(PlanOverride{}, a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                        out, workspace, workspace_bytes, stream);
+}
+
+size_t nvfp4_gemm_w4a4_bf16_workspace_size_planned(const nvfp4_plan_t* plan, int64_t M,
+                                                   int64_t N, int64_t K, int64_t n_out) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return 0;
+  return w4a4_bf16_workspace(ov, M, N, K, n_out);
+}
+
+int nvfp4_gemm_w4a4_bf16_planned(const nvfp4_plan_t* plan, const uint16_t* a, int64_t M,
+                                 int64_t N, int64_t K, const uint8_t* w_codes,
+                                 const uint8_t* w_scales, const int32_t* row_idx, int64_t n_out,
+                                 int out_dtype, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, ov.w4a4_fuse == 1))
+    return NVFP4_ERROR_INVALID_VALUE;
+  return w4a4_bf16_impl(ov, a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype, out,
+                        workspace, workspace_bytes, stream);
 }
 
 int nvfp4_quantize_scaled(const uint16_t* x, int64_t M, int64_t K, const float* global_scale,
@@ -437,11 +521,13 @@ size_t nvfp4_grouped_gemm_workspace_size(int64_t R, int64_t E, int64_t N, int64_
   return moe_grouped_workspace_bytes(R, E, N, K);
 }
 
-int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather_idx,
-                       const int32_t* expert_offsets, int64_t E, int64_t R, int64_t N,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const float* row_scale,
-                       int epilogue, uint16_t* out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+}  // extern "C"
+
+static int grouped_impl(const PlanOverride& ov, const uint16_t* a, int64_t a_rows, int64_t K,
+                        const int32_t* gather_idx, const int32_t* expert_offsets, int64_t E,
+                        int64_t R, int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* row_scale, int epilogue, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (!a || !expert_offsets || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
   if (a_rows <= 0 || K <= 0 || E <= 0 || R <= 0 || N <= 0) return NVFP4_ERROR_INVALID_VALUE;
   if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
@@ -454,11 +540,35 @@ int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32
       !aligned16(w_scales) || !aligned16(out) || (gather_idx && !aligned16(gather_idx)) ||
       (row_scale && !aligned16(row_scale)))
     return NVFP4_ERROR_INVALID_VALUE;
+  if (grouped_path(a_rows, K, E, R, ov) == GroupedPath::kNone) return NVFP4_ERROR_NOT_SUPPORTED;
   const size_t need = moe_grouped_workspace_bytes(R, E, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
   return launched(launch_grouped_gemm(a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
                                       w_scales, row_scale, epilogue == NVFP4_EPI_SWIGLU, out,
-                                      workspace, as_stream(stream)));
+                                      workspace, as_stream(stream), ov));
+}
+
+extern "C" {
+
+int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather_idx,
+                       const int32_t* expert_offsets, int64_t E, int64_t R, int64_t N,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* row_scale,
+                       int epilogue, uint16_t* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return grouped_impl(PlanOverride{}, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
+                      w_scales, row_scale, epilogue, out, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_grouped_gemm_planned(const nvfp4_plan_t* plan, const uint16_t* a, int64_t a_rows,
+                               int64_t K, const int32_t* gather_idx,
+                               const int32_t* expert_offsets, int64_t E, int64_t R, int64_t N,
+                               const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* row_scale, int epilogue, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  return grouped_impl(ov, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes, w_scales,
+                      row_scale, epilogue, out, workspace, workspace_bytes, stream);
 }
 
 int nvfp4_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,

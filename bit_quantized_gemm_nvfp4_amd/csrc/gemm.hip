@@ -3,11 +3,11 @@
 // y = a . W^T with W = e2m1(code) * e4m3(scale) (NVFP4: "Serving Qwen3.8-27B in
 // 4-bit with a masked speculative decoding head", section "What the artifact
 // is"), bf16 activations (W4A16: "What 350+ Experiments Taught Us About Serving
-// Qwen 3.6 35B-A3B", section 1) or NVFP4 activations (W4A4: "52.6% more
-// tokens, 1.53x less GPU time: production inference with Minima and Rafay"),
-// fp32 accumulation.  At M in the thousands every weight is reused M times, so
-// the kernel is bound by the bf16 MFMA rate, not by HBM.  The 256 x 256 tile
-// is gemm_core.h.
+// Qwen 3.6 35B-A3B", section 1) or bf16 activations quantized to NVFP4 as the
+// tiles load them (W4A4: "52.6% more tokens, 1.53x less GPU time: production
+// inference with Minima and Rafay"), fp32 accumulation.  At M in the thousands
+// every weight is reused M times, so the kernel is bound by the bf16 MFMA rate,
+// not by HBM.  The 256 x 256 tile is gemm_core.h.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
 // XCDs, so each XCD is given a contiguous band of the tile sequence, which runs
@@ -23,8 +23,7 @@ constexpr int kMaxGemmSplits = 8;  // K parts of a split tile at most
 namespace {
 
 struct GemmArgs {
-  const void* a;            // bf16 [M][K], or NVFP4 codes [M][K/2]
-  const uint8_t* a_scales;  // NVFP4 activations: [M][K/16]
+  const uint16_t* a;        // bf16 [M][K]
   const uint8_t* wc;        // weight codes [rows][K/2]
   const uint8_t* ws;        // weight scales [rows][K/16]
   const int32_t* row_idx;   // output column n uses weight row row_idx[n]; null: row n
@@ -55,7 +54,9 @@ __device__ __forceinline__ void gemm_tile_of(int lin, int tiles_m, int tiles_n, 
   tn = in_group / gsz;
 }
 
-template <bool A_NVFP4>
+// A_FQ: the activations are quantized to NVFP4 and dequantized (exactly the
+// W4A4 operand nvfp4_quantize would give) while their tiles are loaded.
+template <bool A_FQ>
 __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   extern __shared__ char lds[];
 
@@ -94,25 +95,23 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   // sources (rows past M or N are clamped to the last one; never stored)
   GemmSrc src;
   // (K ranges of a split start at k_lo: a multiple of 64, so pointers stay aligned)
-  const uint8_t* a_tile_base =
-      static_cast<const uint8_t*>(g.a) + (A_NVFP4 ? 0 : m0 * K * 2 + 2 * k_lo);
+  const uint8_t* a_tile_base = reinterpret_cast<const uint8_t*>(g.a + m0 * K + k_lo);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t n = min(n0 + (t >> 1) + 128 * q, g.N - 1);
     const int64_t wr = g.row_idx ? (int64_t)g.row_idx[n] : n;
     gemm_src_nvfp4_row(src.wc[q], src.ws[q], g.wc + k_lo / 2, g.ws + k_lo / 16, wr, K);
-    if constexpr (A_NVFP4) {
+    if constexpr (A_FQ) {
       const int64_t ar = min(m0 + (t >> 1) + 128 * q, g.M - 1);
-      gemm_src_nvfp4_row(src.ac[q], src.as[q], static_cast<const uint8_t*>(g.a) + k_lo / 2,
-                         g.a_scales + k_lo / 16, ar, K);
+      src.ar[q] = g.a + ar * K + k_lo + 32 * (t & 1);
     }
   }
-  if constexpr (!A_NVFP4)
+  if constexpr (!A_FQ)
     gemm_src_bf16(src, [&](int r) { return min(m0 + r, g.M - 1) - m0; }, K);
 
   f32x16 acc[4][4];
   gemm_zero_acc(acc);
-  gemm_mainloop<A_NVFP4>(acc, lds, src, a_tile_base, k_len);
+  gemm_mainloop<A_FQ>(acc, lds, src, a_tile_base, k_len);
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's quarter.
@@ -260,14 +259,14 @@ size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   return p.splits > 1 ? (size_t)p.tail * (size_t)p.splits * BM * BN * sizeof(float) : 0;
 }
 
-int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
-                const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
-                bool out_f32, void* out, void* workspace, hipStream_t stream, Alpha alpha) {
-  // activation offsets inside a 256-row tile are 32-bit byte offsets
+int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* wc,
+                const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32, void* out,
+                void* workspace, hipStream_t stream, Alpha alpha) {
+  // activation offsets inside a 256-row tile are 32-bit byte offsets (the
+  // entry points reject a longer K before launching)
   if (K > ((int64_t)1 << 22)) return -1;
   GemmArgs g;
-  g.a = a;
-  g.a_scales = a_scales;
+  g.a = static_cast<const uint16_t*>(a);
   g.wc = wc;
   g.ws = ws;
   g.row_idx = row_idx;
@@ -301,7 +300,7 @@ int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M,
   const int64_t items = (int64_t)g.tail * g.splits;
   const int64_t grid = g.full + (items + 7) / 8 * 8;
   if (grid > INT32_MAX) return -1;
-  if (a_nvfp4)
+  if (mode == GemmA::kFakeQuant)
     hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
   else
     hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);

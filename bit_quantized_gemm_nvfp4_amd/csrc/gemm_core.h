@@ -5,7 +5,9 @@
 // 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (accumulators
 // in AGPRs).  K advances 64 elements per step through a double buffer in LDS:
 //   A tile  [256 rows][64] bf16 (32 KB): bf16 activations copied global->LDS
-//           (global_load_lds_dwordx4), or NVFP4 activations decoded exactly;
+//           (global_load_lds_dwordx4), or (A_FQ: the W4A4 product from bf16
+//           activations) loaded through registers, quantized to NVFP4 and
+//           dequantized exactly on the way;
 //   B tile  [256 cols][64] bf16 (32 KB): NVFP4 weight rows decoded exactly to
 //           bf16 as they are written (once per tile, not per use).
 // LDS layout: [A buffer 0][A buffer 1][B buffer 0][B buffer 1], so every LDS
@@ -18,9 +20,11 @@
 // instruction; NVFP4 rows are loaded cooperatively, two lanes per row (one
 // 16-byte half each), so a load instruction touches 32 cache lines and every
 // line is looked up once per step -- the line count per instruction, not
-// bandwidth, is what these loads cost.
+// bandwidth, is what these loads cost.  A_FQ activation rows are loaded the
+// same way, two lanes per row, each lane 64 bytes (two whole 16-element
+// blocks), so a block's maximum needs no exchange between lanes.
 //
-// Pipeline: the weight (and NVFP4 activation) loads of step s+2 are issued at
+// Pipeline: the weight (and A_FQ activation) loads of step s+2 are issued at
 // the start of step s into one of two register sets, the bf16 activation copy
 // of step s+1 straight into the idle LDS buffer; the other register set (step
 // s+1) is decoded into the idle buffer while step s is computed.  A step is 16
@@ -35,6 +39,7 @@
 #pragma once
 
 #include "device.h"
+#include "quant_core.h"
 
 namespace nvfp4 {
 
@@ -56,10 +61,10 @@ __device__ __forceinline__ T& lds_ref(char* lds, uint32_t off) {
 // g = h ^ f(r): fragment (substep kk, block i) of the wave's activation rows
 // wm*128 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
 // it is rd_x[kk ^ 2(i&1)] + 32 KB * buffer + 4096 i (likewise rd_w for the
-// weight rows wn*128 + ...).  An NVFP4 row
-// write (row t/2 + 128 q, piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j]
-// (NVFP4 activations) + 32 KB * buffer + 16384 q.  (Immediate offsets of LDS
-// instructions stop at 64 KB, so the B-tile base is part of the registers.)
+// weight rows wn*128 + ...).  A row write of a thread's half (row t/2 + 128 q,
+// piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j] (A_FQ activations) +
+// 32 KB * buffer + 16384 q.  (Immediate offsets of LDS instructions stop at
+// 64 KB, so the B-tile base is part of the registers.)
 struct LdsOffsets {
   uint32_t rd_x[4], rd_w[4];
   uint32_t wr_w[4], wr_na[4];
@@ -91,7 +96,10 @@ struct Nvfp4Rows {
   u32x4 c[2];     // codes of half (t & 1) of tile rows t/2 and 128 + t/2
   uint32_t s[2];  // their two E4M3 scale bytes (one 16-bit load each)
 };
-template <bool A_NVFP4>
+struct Bf16Rows {
+  u32x4 v[2][4];  // half (t & 1) of tile rows t/2 and 128 + t/2: 32 bf16 each
+};
+template <bool A_FQ>
 struct GemmLoad;
 template <>
 struct GemmLoad<false> {
@@ -99,18 +107,18 @@ struct GemmLoad<false> {
 };
 template <>
 struct GemmLoad<true> {
-  Nvfp4Rows a;
+  Bf16Rows a;
   Nvfp4Rows w;
 };
 
 // Where a thread loads from: bf16 activations as byte offsets (32-bit) from a
-// base pointer at k = 0 (see dma_a_tile); NVFP4 rows as pointers to this
-// lane's half of rows t/2 and 128 + t/2 at k = 0 (gemm_src_nvfp4_row).
+// base pointer at k = 0 (see dma_a_tile); NVFP4 weight rows as pointers to
+// this lane's half of rows t/2 and 128 + t/2 at k = 0 (gemm_src_nvfp4_row);
+// A_FQ activation rows as pointers to this lane's half of those rows.
 struct GemmSrc {
   uint32_t a_off[8];
   uint32_t a_back[2];
-  const uint8_t* ac[2];
-  const uint8_t* as[2];
+  const uint16_t* ar[2];
   const uint8_t* wc[2];
   const uint8_t* ws[2];
 };
@@ -128,11 +136,23 @@ __device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* con
   }
 }
 
-template <bool A_NVFP4>
-__device__ __forceinline__ void gemm_load(GemmLoad<A_NVFP4>& L, const GemmSrc& src,
+// A_FQ: 32 bf16 activations of this lane's half of each of its two rows (a
+// partial last step re-reads the first half, as load_nvfp4_rows does).
+__device__ __forceinline__ void load_bf16_rows(Bf16Rows& R, const uint16_t* const (&a)[2],
+                                               int64_t k0, bool kfull) {
+  const int hh = threadIdx.x & 1;
+  const int64_t off = k0 - (kfull ? 0 : 32 * hh);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.v[q][j] = *reinterpret_cast<const u32x4*>(a[q] + off + 8 * j);
+}
+
+template <bool A_FQ>
+__device__ __forceinline__ void gemm_load(GemmLoad<A_FQ>& L, const GemmSrc& src,
                                           const uint8_t* a_tile_base, int64_t K, int64_t k0) {
   const bool kfull = k0 + BK <= K;
-  if constexpr (A_NVFP4) load_nvfp4_rows(L.a, src.ac, src.as, k0, kfull);
+  if constexpr (A_FQ) load_bf16_rows(L.a, src.ar, k0, kfull);
   load_nvfp4_rows(L.w, src.wc, src.ws, k0, kfull);
 }
 
@@ -167,16 +187,33 @@ __device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const
   lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
 }
 
+// A_FQ: piece j (0..3) of this thread's half of activation tile row t/2 + 128 q,
+// quantized to NVFP4 with its 16-element block (pieces j and j ^ 1, both in
+// this lane) and dequantized: exactly nvfp4_quantize then nvfp4_dequantize.  A
+// block at or past `kval` is written as zeros.
+__device__ __forceinline__ void store_fq_piece(char* lds, uint32_t off, const Bf16Rows& R, int q,
+                                               int j, int kval) {
+  const int p = 4 * (threadIdx.x & 1) + j;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if (16 * (p >> 1) >= kval) {
+    lds_ref<u32x4>(lds, off) = z;
+    return;
+  }
+  const uint32_t amax = max(piece_amax_bits(R.v[q][j]), piece_amax_bits(R.v[q][j ^ 1]));
+  lds_ref<u32x4>(lds, off) =
+      fakequant_with(R.v[q][j], scale_code_from_amax(bf16_bits_to_f32(amax)));
+}
+
 // Piece c of writing a loaded set to LDS buffer `buf`: weight pieces 0..7,
-// then (NVFP4 activations only) activation pieces 8..15.
-template <bool A_NVFP4>
+// then (A_FQ only) activation pieces 8..15.
+template <bool A_FQ>
 __device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
-                                                 const GemmLoad<A_NVFP4>& L, int c, int kval) {
+                                                 const GemmLoad<A_FQ>& L, int c, int kval) {
   const int q = (c & 7) >> 2, j = c & 3;
   if (c < 8) {
     store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
-  } else if constexpr (A_NVFP4) {
-    store_nvfp4_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
+  } else if constexpr (A_FQ) {
+    store_fq_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
   }
 }
 
@@ -200,14 +237,14 @@ __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets&
 // tile; then the workgroup barrier publishes `nxt`, and substep 3 reads the
 // next step's substep-0 fragments from it into f[0] while its MFMAs run, so no
 // fragment read is left exposed behind the barrier.
-template <bool A_NVFP4>
+template <bool A_FQ>
 __device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], char* lds,
                                           const LdsOffsets& o, uint32_t cur, uint32_t nxt,
-                                          const GemmLoad<A_NVFP4>& L, int kval) {
-  constexpr int kPieces = A_NVFP4 ? 16 : 8;
+                                          const GemmLoad<A_FQ>& L, int kval) {
+  constexpr int kPieces = A_FQ ? 16 : 8;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk == 3) lds_barrier<A_NVFP4 ? -1 : 0>();
+    if (kk == 3) lds_barrier<A_FQ ? -1 : 0>();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (kk < 3)
@@ -216,8 +253,8 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], ch
         read_frag(f[0], lds, o, nxt, 0, i);
       const int c = 4 * kk + i;  // chunk 0..11 carries pieces c and c + 12
       if (kk < 3) {
-        if (c < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c, kval);
-        if (c + 12 < kPieces) gemm_store_piece<A_NVFP4>(lds, o, nxt, L, c + 12, kval);
+        if (c < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c, kval);
+        if (c + 12 < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c + 12, kval);
       }
       const Frags& fc = f[kk & 1];
 #pragma unroll
@@ -265,7 +302,7 @@ __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[4][4]) {
 
 // The whole K loop of one tile: acc += a_tile . w_tile^T.  `lds` is the
 // kLdsBytes of dynamic LDS; every thread of the workgroup calls it.
-template <bool A_NVFP4>
+template <bool A_FQ>
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, const GemmSrc& src,
                                               const uint8_t* a_tile_base, int64_t K) {
   const int wave = threadIdx.x >> 6;
@@ -286,18 +323,18 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, co
   // the step before; each wave waits for its own copies before the barrier
   // that publishes the buffer.
   auto dma = [&](int s, uint32_t buf) {
-    if constexpr (!A_NVFP4)
+    if constexpr (!A_FQ)
       dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
   };
 
-  GemmLoad<A_NVFP4> L0, L1;
+  GemmLoad<A_FQ> L0, L1;
   Frags f[2];
   dma(0, 0);
-  gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(0));
-  gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(1));
+  gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(0));
+  gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
-  for (int c = 0; c < 16; ++c) gemm_store_piece<A_NVFP4>(lds, o, 0, L0, c, kval(0));
-  lds_barrier<A_NVFP4 ? -1 : 0>();
+  for (int c = 0; c < 16; ++c) gemm_store_piece<A_FQ>(lds, o, 0, L0, c, kval(0));
+  lds_barrier<A_FQ ? -1 : 0>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, 0, 0, i);
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
@@ -307,14 +344,14 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, co
   for (int s = 0; s < steps2; s += 2) {
     dma(s + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load<A_NVFP4>(L0, src, a_tile_base, K, kstep(s + 2));
+    gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
+    gemm_step<A_FQ>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
     dma(s + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load<A_NVFP4>(L1, src, a_tile_base, K, kstep(s + 3));
+    gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_NVFP4>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
+    gemm_step<A_FQ>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
   }
 
 }

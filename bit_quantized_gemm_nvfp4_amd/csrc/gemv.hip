@@ -15,9 +15,6 @@
 // bf16/fp32 results directly; otherwise it stores fp32 partials and
 // k_splitk_reduce adds them in part order, so results are bit-identical from
 // run to run.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "gemv4_core.h"
 #include "gemv_core.h"
 #include "launch.h"
@@ -331,13 +328,10 @@ int launch_plan(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
 
 }  // namespace
 
-GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
+GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanOverride& ov) {
   GemvPlan p;
-  int64_t small_max = 4;  // largest M for the 4x4x4-block kernel with per-block scaling
-  if (const char* e = getenv("NVFP4_GEMV_SMALL_MAX")) {
-    const int v = atoi(e);
-    if (v >= 0 && v <= 8) small_max = v;
-  }
+  // largest M for the 4x4x4-block kernel with per-block scaling
+  const int64_t small_max = ov.gemv_small_max >= 0 ? ov.gemv_small_max : 4;
   p.small = M <= small_max;
   p.mt = p.small ? (int)((M + 3) / 4) : (M <= 16 ? 1 : 2);
   p.tr = 2;
@@ -356,22 +350,11 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
     p.nw = 16;
     p.tr = n_out >= 256 * 512 ? 2 : 1;
   }
-  int64_t lds_budget = 64 * 1024;  // staged activations of the 4x4x4 kernel
-  // Tuning knob: NVFP4_GEMV_PLAN="tr,nw[,lds_kib[,z]]" overrides the tiles per
-  // wave, the waves per workgroup, the LDS budget of the staged activations
-  // (0: default) and the number of K parts (0: default).
-  int z_force = 0;
-  if (const char* e = getenv("NVFP4_GEMV_PLAN")) {
-    int tr = 0, nw = 0, kib = 0;
-    const int n = sscanf(e, "%d,%d,%d,%d", &tr, &nw, &kib, &z_force);
-    const bool tr_ok = p.small ? (tr == 1 || tr == 2 || tr == 4 || (tr == 8 && p.mt == 1))
-                               : (tr == 1 || tr == 2 || (tr == 4 && p.mt == 1));
-    const bool nw_ok = p.small ? (nw >= 1 && nw <= 8)
-                               : (nw == 4 || nw == 8 || (nw == 16 && p.mt == 2 && tr <= 2));
-    if (n >= 2 && tr_ok && nw_ok) p.tr = tr, p.nw = nw;
-    if (n >= 3 && kib >= 8 && kib <= 160) lds_budget = (int64_t)kib * 1024;
-    if (n < 4) z_force = 0;
-  }
+  // overrides (tuning entry points): tiles per wave, waves per workgroup, the
+  // LDS budget of the staged activations, the number of K parts
+  if (ov.gemv_tiles >= 0) p.tr = ov.gemv_tiles;
+  if (ov.gemv_waves >= 0) p.nw = ov.gemv_waves;
+  const int64_t lds_budget = ov.gemv_lds_kib >= 0 ? (int64_t)ov.gemv_lds_kib * 1024 : 64 * 1024;
   const int64_t step = p.small ? kG4Step : kGemvStep;
   const int64_t rows_per_tile = p.small ? 4 : 16;
   const int64_t steps = (K + step - 1) / step;
@@ -397,11 +380,22 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus) {
     const int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
     if (zw > z) z = zw;
   }
-  if (z_force > 0) z = z_force > z_lds ? z_force : z_lds;
+  if (ov.gemv_splits > 0) z = ov.gemv_splits > z_lds ? ov.gemv_splits : z_lds;
   if (z > steps) z = steps;
   if (z < 1) z = 1;
   p.z = (int)z;
   return p;
+}
+
+bool gemv_override_valid(int64_t M, const PlanOverride& ov) {
+  if (ov.gemv_small_max > 8) return false;
+  if (ov.gemv_lds_kib >= 0 && (ov.gemv_lds_kib < 8 || ov.gemv_lds_kib > 160)) return false;
+  const GemvPlan p = plan_gemv(M, 1, 32, kNumCUs, ov);
+  const bool tr_ok = p.small ? (p.tr == 1 || p.tr == 2 || p.tr == 4 || (p.tr == 8 && p.mt == 1))
+                             : (p.tr == 1 || p.tr == 2 || (p.tr == 4 && p.mt == 1));
+  const bool nw_ok = p.small ? (p.nw >= 1 && p.nw <= 8)
+                             : (p.nw == 4 || p.nw == 8 || (p.nw == 16 && p.mt == 2 && p.tr <= 2));
+  return tr_ok && nw_ok;
 }
 
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out) {

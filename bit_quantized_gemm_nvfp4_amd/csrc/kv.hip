@@ -20,7 +20,8 @@ namespace nvfp4 {
 namespace {
 
 // E4M3 code of a binary32 value: nearest, ties to the even code, magnitudes
-// at or above 448 saturate to 448 (0x7E), the sign is kept (zero included).
+// at or above 448 saturate to 448 (0x7E), the sign is kept (zero included);
+// a NaN gives the NaN code of its sign (0x7F / 0xFF).
 //   Below 2^-6 (subnormal E4M3, spacing 2^-9): the magnitude is the integer
 //   nearest |q| * 512 (exact scaling), 0..8, and 8 is the code of 2^-6.
 //   Normal range: round the binary32 mantissa to 3 bits, nearest even, on
@@ -31,7 +32,9 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
   const uint32_t a = b & 0x7FFFFFFFu;
   const float af = __uint_as_float(a);
   uint32_t c;
-  if (af >= 448.0f)
+  if (af != af)
+    c = 0x7Fu;
+  else if (af >= 448.0f)
     c = 0x7Eu;
   else if (af < 0.015625f)
     c = (uint32_t)__builtin_rintf(af * 512.0f);

@@ -37,6 +37,20 @@ struct Alpha {
   const float* w = nullptr;
 };
 
+// Launch-plan overrides of the tuning entry points (include/nvfp4_plan.h):
+// every field < 0 keeps the plan's own choice.  The product entry points pass
+// the all-default value, so their plans stay a pure function of the shape.
+struct PlanOverride {
+  int gemm_min_m = -1;             // rows of M from which the MFMA GEMM runs
+  int gemv_small_max = -1;         // largest M of the 4x4x4-block GEMV (0..8)
+  int gemv_tiles = -1;             // weight tiles per wave
+  int gemv_waves = -1;             // waves per workgroup
+  int gemv_lds_kib = -1;           // LDS budget of the 4x4x4 kernel's staged activations
+  int gemv_splits = -1;            // K parts across workgroups
+  int w4a4_fuse = -1;              // W4A4 from bf16: quantize inside the kernel (1) or in a pass (0)
+  int grouped_mfma_min_rows = -1;  // average rows per expert from which the grouped MFMA runs
+};
+
 struct GemvPlan {
   bool small;  // M <= 4: 4x4x4-block kernel (tiles of 4 rows)
   int mt;  // 16-row activation tiles (M <= 16 * mt)
@@ -45,7 +59,10 @@ struct GemvPlan {
   int z;   // split-K across workgroups (fp32 partials + reduce kernel)
 };
 
-GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus);
+GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus,
+                   const PlanOverride& ov = PlanOverride{});
+// Whether the override's GEMV fields name a layout that exists for this M.
+bool gemv_override_valid(int64_t M, const PlanOverride& ov);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
 // fakequant: x is bf16 and every 16-element block is quantized to NVFP4 and
 // dequantized while it is staged (the W4A4 product with the activation
@@ -55,10 +72,11 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
                 void* out, void* workspace, hipStream_t stream, Alpha alpha = {},
                 bool fakequant = false);
 
-// Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K]
-// or, with a_nvfp4, NVFP4 codes [M][K/2] with scales a_scales [M][K/16].  The
-// tiles of a last, partly filled round (or all tiles, when they cannot fill
-// the chip once) are split over K: fp32 tile-local partials in workspace
+// Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K];
+// with GemmA::kFakeQuant its tiles are quantized to NVFP4 and dequantized as
+// they are loaded (the W4A4 product from bf16 activations).  The tiles of a
+// last, partly filled round (or all tiles, when they cannot fill the chip
+// once) are split over K: fp32 tile-local partials in workspace
 // (gemm_workspace_bytes of it), summed in part order by a second kernel.
 struct GemmSplitPlan {
   int64_t full;  // tiles run whole
@@ -67,9 +85,10 @@ struct GemmSplitPlan {
 };
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);
-int launch_gemm(bool a_nvfp4, const void* a, const uint8_t* a_scales, int64_t M, int64_t K,
-                const uint8_t* wc, const uint8_t* ws, const int32_t* row_idx, int64_t n_out,
-                bool out_f32, void* out, void* workspace, hipStream_t stream, Alpha alpha = {});
+enum class GemmA { kBf16, kFakeQuant };
+int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* wc,
+                const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32, void* out,
+                void* workspace, hipStream_t stream, Alpha alpha = {});
 
 // Top-k of each row of fp32 logits [M][n] (k <= kTopkMaxK), best first: larger
 // value, then smaller column; -0 below +0.  ids are ids_map[column] (or the

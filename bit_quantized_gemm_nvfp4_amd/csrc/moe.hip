@@ -11,8 +11,6 @@
 //               workgroup) when experts get few rows, the 256 x 256 MFMA tile
 //               of gemm_core.h when they get many;
 //   combine  -- per-token sum of its slots' outputs.
-#include <stdlib.h>
-
 #include "gemm_core.h"
 #include "gemv_core.h"
 #include "moe.h"
@@ -527,17 +525,35 @@ size_t moe_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
   return 0;
 }
 
+// LDS of the grouped GEMV: kGroupRows activation rows of the whole K range.
+static size_t grouped_gemv_lds_bytes(int64_t K) {
+  const int steps = (int)((K + kGemvStep - 1) / kGemvStep);
+  return (size_t)kGroupRows * lds_x_stride(steps) * sizeof(uint16_t);
+}
+
+GroupedPath grouped_path(int64_t a_rows, int64_t K, int64_t E, int64_t R,
+                         const PlanOverride& ov) {
+  // MFMA tiles once experts average enough rows to fill them (32 by default);
+  // the GEMV stages the rows' whole K range in LDS, so a K past what LDS holds
+  // (above 4,864) runs the MFMA kernel at any row count.  The MFMA kernel's
+  // activation offsets are 32-bit.
+  const int64_t min_avg = ov.grouped_mfma_min_rows >= 0 ? ov.grouped_mfma_min_rows : 32;
+  const bool mfma_fits = a_rows * K * 2 < ((int64_t)1 << 32);
+  const bool gemv_fits = grouped_gemv_lds_bytes(K) <= kGroupedGemvMaxLds;
+  if (mfma_fits && (R >= min_avg * E || !gemv_fits)) return GroupedPath::kMfma;
+  if (gemv_fits) return GroupedPath::kGemv;
+  return GroupedPath::kNone;
+}
+
 int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather,
                         const int32_t* offsets, int64_t E, int64_t R, int64_t N,
                         const uint8_t* wc, const uint8_t* ws, const float* row_scale,
-                        bool swiglu, uint16_t* out, void* workspace, hipStream_t stream) {
+                        bool swiglu, uint16_t* out, void* workspace, hipStream_t stream,
+                        const PlanOverride& ov) {
   (void)workspace;
-  // MFMA tiles once experts average enough rows to fill them (tuning knob:
-  // NVFP4_GROUPED_MFMA_MIN_ROWS, the average rows per expert from which the
-  // MFMA kernel is used); its activation offsets are 32-bit.
-  int64_t min_avg = 32;
-  if (const char* env = getenv("NVFP4_GROUPED_MFMA_MIN_ROWS")) min_avg = atol(env);
-  if (R >= min_avg * E && a_rows * K * 2 < ((int64_t)1 << 32)) {
+  const GroupedPath path = grouped_path(a_rows, K, E, R, ov);
+  if (path == GroupedPath::kNone) return -2;
+  if (path == GroupedPath::kMfma) {
     GroupedMfmaArgs m;
     m.a = a;
     m.gather = gather;
@@ -573,7 +589,7 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
   const int64_t chunks = (R + kGroupRows - 1) / kGroupRows + E;  // upper bound
   const int64_t tiles_y = swiglu ? (N / 2 + 15) / 16 : (N + 31) / 32;  // gate tiles or tile pairs
   const int64_t ytiles = (tiles_y + kGroupWaves - 1) / kGroupWaves;
-  const size_t lds = (size_t)kGroupRows * lds_x_stride(g.steps) * sizeof(uint16_t);
+  const size_t lds = grouped_gemv_lds_bytes(K);
   hipLaunchKernelGGL(k_grouped_gemv<2>, dim3((unsigned)chunks, (unsigned)ytiles),
                      dim3(64 * kGroupWaves), lds, stream, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;

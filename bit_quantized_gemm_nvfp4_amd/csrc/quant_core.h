@@ -24,8 +24,11 @@ namespace nvfp4 {
 //   Subnormal range (t < 2^-6): the code is the integer nearest t / 2^-9
 //   (0..8; 8 is 2^-6 = code 0x08).  Normal range: round the f32 mantissa to 3
 //   bits, nearest-even, on the bit pattern, and rebias the exponent 127 -> 7.
+//   A NaN maximum (the block holds a NaN) gives the NaN code 0x7F, so the
+//   block decodes to NaN and the code never spills past its 8 bits.
 __device__ __forceinline__ uint32_t scale_code_from_amax(float a) {
   float t = a / 6.0f;
+  if (t != t) return 0x7F;
   if (t >= 448.0f) return 0x7E;
   if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
   uint32_t b = __builtin_bit_cast(uint32_t, t);

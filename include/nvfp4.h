@@ -94,7 +94,9 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t N, int
  *           a zero scale gives magnitude 0.
  * Outputs: codes[M][K/2], scales[M][K/16] (the NF4W(M, K) layout).  The
  * result is unique and bit-exact.  Non-finite inputs are outside the
- * contract.  K % 32 == 0.
+ * contract, but they stay inside their block: a block holding a NaN gets the
+ * E4M3 NaN scale code 0x7F (it decodes to NaN) and codes that keep only their
+ * sign bits; an infinity saturates like any value above 6*448.  K % 32 == 0.
  */
 int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
                    void *stream);
@@ -237,7 +239,8 @@ int nvfp4_head_topk(const uint16_t *a, int64_t M, int64_t N, int64_t K, const ui
  * even code, saturating to +-448, sign kept.  The result is bit-exact.  The
  * cache is updated in place (the one exception to "outputs are fully
  * overwritten"): slot_mapping[t] < 0 (padding) or >= num_slots leaves it
- * untouched; slots must be distinct.  W % 16 == 0.
+ * untouched; slots must be distinct.  A NaN element is stored as the NaN code
+ * of its sign (0x7F / 0xFF); infinities saturate to +-448.  W % 16 == 0.
  *
  * nvfp4_kv_load_e4m3: B sequences back to bf16 out [B][max_len][W],
  *   out[b][i][w] = bf16(fl32(e4m3(cache[s][w]) * scale)),
@@ -304,7 +307,10 @@ int nvfp4_grouped_gemm(const uint16_t *a, int64_t a_rows, int64_t K, const int32
                        void *stream);
 
 /*
- * Combine the per-slot expert outputs of a routed layer:
+ * Combine the per-slot expert outputs of a routed layer ("What 350+
+ * Experiments ...", section 1: each token's output is the gate-weighted sum
+ * over the experts it was routed to; the gate weights are applied by the
+ * down projection's row_scale, so this step only adds):
  *   out[t][c] = bf16( sum_{j < topk} y[slot_pos[t*topk + j]][c] )
  * summed in fp32 in slot order.  y is bf16 [R][H] with R = T*topk, out is
  * bf16 [T][H].  H % 8 == 0.

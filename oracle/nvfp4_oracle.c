@@ -159,11 +159,16 @@ void oracle_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t N, i
  * a/6 is never formed: with v(c) the candidate values, "v(c) <= a/6" is tested
  * as 6*v(c) <= a and "a/6 against the midpoint of v(c), v(c+1)" as a against
  * 3*(v(c)+v(c+1)).  Both right-hand sides carry at most 8 significant bits, so
- * every comparison is exact in double. */
+ * every comparison is exact in double.  Non-finite inputs are outside the
+ * quantizer's contract; the reading that keeps the damage inside the block is
+ * that a NaN maximum takes the E4M3 NaN code 0x7F (the block then decodes to
+ * NaN) and an infinite one saturates to 0x7E like any value above 448*6. */
 unsigned oracle_scale_code(double a)
 {
     unsigned c = 0, next;
     double mid6;
+    if (isnan(a))
+        return 0x7F;                       /* a block holding a NaN: the NaN code */
     for (unsigned cand = 1; cand <= 0x7E; ++cand)
         if (6.0 * oracle_e4m3_value(cand) <= a)
             c = cand;
@@ -226,7 +231,10 @@ void oracle_e2m1_encode_array(const uint16_t *x, int64_t n, unsigned scale_code,
  * block of 16 consecutive elements, (1) a = max |x|, (2) scale code from a,
  * (3) each element's code against the decoded scale, (4) two codes per byte,
  * element 2j in the low nibble.  x is bf16 [M][K]; codes [M][K/2]; scales
- * [M][K/16].  Non-finite inputs are outside the contract. */
+ * [M][K/16].  Non-finite inputs are outside the contract, but a block holding
+ * a NaN is confined to itself: its scale code is 0x7F (oracle_scale_code) and
+ * every code keeps only its sign bit (no magnitude compares true against a
+ * NaN scale). */
 void oracle_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales)
 {
 #pragma omp parallel for schedule(static)
@@ -237,7 +245,7 @@ void oracle_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, ui
             unsigned sc, cd[16];
             for (int i = 0; i < 16; ++i) {
                 double v = fabs(oracle_bf16_value(blk[i]));
-                if (v > a)
+                if (v > a || isnan(v))   /* a NaN stays the maximum */
                     a = v;
             }
             sc = oracle_scale_code(a);
@@ -285,7 +293,7 @@ void oracle_quantize_scaled(const uint16_t *x, int64_t M, int64_t K, float g, ui
             for (int i = 0; i < 16; ++i) {
                 /* binary32 quotient: the double quotient rounded to binary32 */
                 y[i] = (double)(float)(oracle_bf16_value(x[m * K + b * 16 + i]) / (double)g);
-                if (fabs(y[i]) > a)
+                if (fabs(y[i]) > a || isnan(y[i]))   /* a NaN stays the maximum */
                     a = fabs(y[i]);
             }
             sc = oracle_scale_code(a);
@@ -606,8 +614,10 @@ void oracle_topk(const double *v, int64_t M, int64_t n, int64_t k, const int32_t
 /* E4M3 code of a real value v [P4 section 3: the KV cache stored as FP8
  * E4M3].  Readings: round to the nearest E4M3 value, ties to the even code;
  * magnitudes at or above 448 saturate to 448 (satfinite: there is no
- * infinity); the sign is kept, zero included.  Written as the plain nearest
- * search over the 127 non-negative finite values; every comparison is exact
+ * infinity); the sign is kept, zero included; a NaN becomes the NaN code of
+ * its sign (the format's only non-finite codes, 0x7F and 0xFF).  Written as
+ * the plain nearest search over the 127 non-negative finite values; every
+ * comparison is exact
  * in double (E4M3 values and their midpoints have at most 5 significant
  * bits). */
 unsigned oracle_e4m3_encode(double v)
@@ -615,6 +625,8 @@ unsigned oracle_e4m3_encode(double v)
     unsigned sign = signbit(v) ? 0x80u : 0u;
     double a = fabs(v);
     unsigned c = 0;
+    if (isnan(v))
+        return sign | 0x7Fu;              /* NaN keeps its sign: code 0x7F / 0xFF */
     for (unsigned cand = 1; cand <= 0x7E; ++cand)
         if (oracle_e4m3_value(cand) <= a)
             c = cand;

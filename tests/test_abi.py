@@ -10,7 +10,8 @@ import pytest
 import bit_quantized_gemm_nvfp4_amd as nv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 SUCCESS, INVALID, NOT_SUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
 
@@ -24,9 +25,11 @@ NULL = None
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -225,3 +228,121 @@ def test_two_level_validation(L):
                                    P3, wg, NULL, 64, 0, P4, NULL, 0, NULL)
     assert gs(ag=G) == INVALID                 # activation scale needs NVFP4 activations
     assert gs(wg=G_MIS) == INVALID
+
+
+def test_mfma_k_limit_is_not_supported(L):
+    """The MFMA GEMM's 32-bit activation offsets cap K at 2^22: a longer K at a
+    large M is refused on the host (NOT_SUPPORTED), not at launch."""
+    K = (1 << 22) + 32
+    assert _gemm(L, M=128, N=64, K=K, n_out=64, workspace=P, wbytes=1 << 40) == NOT_SUPPORTED
+    assert _w4a4(L, M=128, N=64, K=K, n_out=64, workspace=P, wbytes=1 << 40) == NOT_SUPPORTED
+
+
+def test_grouped_shape_no_kernel_takes(L):
+    """A K past the grouped GEMV's LDS staging runs the MFMA kernel; with 32-bit
+    MFMA activation offsets exceeded as well no kernel takes the shape and the
+    call returns NOT_SUPPORTED before any launch."""
+    g = L.nvfp4_grouped_gemm
+    assert g(P, 32768, 65536, NULL, P2, 4, 32768, 64, P3, P4, NULL, 0, P, NULL, 0,
+             NULL) == NOT_SUPPORTED
+
+
+def _plan(**kw):
+    return ctypes.byref(nv.make_plan(**kw))
+
+
+def test_plan_default_is_all_minus_one(L):
+    p = nv.Plan()
+    L.nvfp4_plan_default(ctypes.byref(p))
+    assert all(getattr(p, n) == -1 for n, _ in nv.Plan._fields_)
+
+
+def test_planned_entry_points_validate_the_plan(L):
+    """A plan naming a layout the library does not build is refused with
+    INVALID before any HIP call; a default plan behaves as the plain entry
+    point (same workspace, same argument checks)."""
+    def gp(plan, M=4, **kw):
+        return L.nvfp4_gemm_planned(plan, 0, P, NULL, M, 64, 256, P2, P3, NULL, 64, 0, P4, NULL,
+                                    0, NULL)
+    assert gp(_plan(gemv_tiles=3)) == INVALID            # no 3-tile layout
+    assert gp(_plan(gemv_waves=16), M=8) == INVALID       # 16 waves need two activation tiles
+    assert gp(_plan(gemv_small_max=9)) == INVALID
+    assert gp(_plan(gemv_lds_kib=4)) == INVALID
+    assert gp(_plan(gemm_min_m=0)) == INVALID
+    assert L.nvfp4_gemm_planned(_plan(), 0, NULL, NULL, 4, 64, 256, P2, P3, NULL, 64, 0, P4,
+                                NULL, 0, NULL) == INVALID
+    for args in ((0, 8, 17408, 5120, 17408), (0, 32, 5120, 17408, 5120), (2, 512, 17408, 5120,
+                                                                          17408)):
+        assert (L.nvfp4_gemm_workspace_size_planned(None, *args) ==
+                L.nvfp4_gemm_workspace_size(*args))
+        assert (L.nvfp4_gemm_workspace_size_planned(_plan(), *args) ==
+                L.nvfp4_gemm_workspace_size(*args))
+    # the K parts of the plan size the partial workspace
+    base = L.nvfp4_gemm_workspace_size(0, 8, 1024, 4096, 1024)
+    assert base == 16 * 8 * 1024 * 4
+    assert L.nvfp4_gemm_workspace_size_planned(_plan(gemv_splits=2), 0, 8, 1024, 4096,
+                                               1024) == 2 * 8 * 1024 * 4
+    # the fused W4A4 staging is built for one or two weight tiles per wave
+    assert L.nvfp4_gemm_w4a4_bf16_planned(_plan(w4a4_fuse=1, gemv_tiles=4), P, 8, 64, 256, P2, P3,
+                                          NULL, 64, 0, P4, NULL, 0, NULL) == INVALID
+    assert L.nvfp4_gemm_w4a4_bf16_planned(_plan(w4a4_fuse=2), P, 8, 64, 256, P2, P3, NULL, 64, 0,
+                                          P4, NULL, 0, NULL) == INVALID
+    # fused W4A4 needs no activation copy in the workspace; the one-pass form does
+    fused = L.nvfp4_gemm_w4a4_bf16_workspace_size_planned(_plan(w4a4_fuse=1), 512, 17408, 5120,
+                                                          17408)
+    pas = L.nvfp4_gemm_w4a4_bf16_workspace_size_planned(_plan(w4a4_fuse=0), 512, 17408, 5120,
+                                                        17408)
+    assert pas >= fused + 512 * 5120 * 2
+    g = L.nvfp4_grouped_gemm_planned
+    assert g(_plan(gemm_min_m=0), P, 32, 256, P, P2, 4, 32, 64, P3, P4, NULL, 0, P, NULL, 0,
+             NULL) == INVALID
+    assert g(_plan(grouped_mfma_min_rows=1), NULL, 32, 256, P, P2, 4, 32, 64, P3, P4, NULL, 0, P,
+             NULL, 0, NULL) == INVALID
+
+
+def test_binding_checks_shapes_before_the_gpu(L):
+    """The binding checks every tensor's dtype and exact shape (caller-supplied
+    outputs, scales, indices, workspace) before any GPU work: a wrong one is a
+    ValueError naming the argument (CPU tensors reach this check first)."""
+    import torch
+    bf = torch.bfloat16
+    u8 = torch.uint8
+    x = torch.zeros(4, 256, dtype=bf)
+    wc = torch.zeros(64, 128, dtype=u8)
+    ws = torch.zeros(64, 16, dtype=u8)
+
+    def raises(match, fn, *a, **k):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **k)
+    raises("w_scales", nv.gemm, x, wc, torch.zeros(64, 15, dtype=u8))
+    raises("K mismatch", nv.gemm, torch.zeros(4, 512, dtype=bf), wc, ws)
+    raises("out", nv.gemm, x, wc, ws, out=torch.zeros(4, 64, dtype=bf), out_dtype=torch.float32)
+    raises("out", nv.gemm, x, wc, ws, out=torch.zeros(4, 63, dtype=bf))
+    raises("row_idx", nv.gemm, x, wc, ws, row_idx=torch.zeros(8, dtype=torch.int64))
+    raises("row_idx", nv.gemm, x, wc, ws, row_idx=torch.zeros(65, dtype=torch.int32))
+    raises("a_scales", nv.gemm, torch.zeros(4, 128, dtype=u8), wc, ws,
+           a_scales=torch.zeros(4, 8, dtype=u8))
+    raises("out_dtype", nv.gemm, x, wc, ws, out_dtype=torch.float16)
+    raises("codes", nv.quantize, x, codes=torch.zeros(4, 64, dtype=u8))
+    raises("x", nv.quantize, torch.zeros(4, 256, dtype=torch.float32))
+    raises("out", nv.dequantize, wc, ws, out=torch.zeros(64, 128, dtype=bf))
+    raises("global_scale", nv.gemm_scaled, x, wc, ws, w_global_scale=torch.zeros(2))
+    raises("out", nv.gemm_w4a4, x, wc, ws, out=torch.zeros(3, 64, dtype=bf))
+    w3c = torch.zeros(4, 64, 128, dtype=u8)
+    w3s = torch.zeros(4, 64, 16, dtype=u8)
+    off = torch.zeros(5, dtype=torch.int32)
+    raises("expert_offsets", nv.grouped_gemm, x, None, torch.zeros(4, dtype=torch.int32), w3c,
+           w3s, 4)
+    raises("row_scale", nv.grouped_gemm, x, None, off, w3c, w3s, 4,
+           row_scale=torch.zeros(3, dtype=torch.float32))
+    raises("gather_idx", nv.grouped_gemm, x, torch.zeros(4, dtype=torch.int64), off, w3c, w3s, 4)
+    raises("out", nv.grouped_gemm, x, None, off, w3c, w3s, 4, epilogue=nv.EPI_SWIGLU,
+           out=torch.zeros(4, 64, dtype=bf))
+    raises("rows", nv.moe_combine, torch.zeros(7, 64, dtype=bf), torch.zeros(2, 4, dtype=torch.int32))
+    raises("cache", nv.kv_store_e4m3, torch.zeros(4, 64, dtype=bf),
+           torch.zeros(4, dtype=torch.int32), 1.0, torch.zeros(8, 32, dtype=u8))
+    raises("seq_lens", nv.kv_load_e4m3, torch.zeros(8, 64, dtype=u8),
+           torch.zeros(2, 3, dtype=torch.int32), torch.zeros(3, dtype=torch.int32), 16, 48, 1.0)
+    raises("ids_map", nv.topk, torch.zeros(2, 100), 4, ids_map=torch.zeros(99, dtype=torch.int32))
+    with pytest.raises(RuntimeError, match="GPU"):   # shapes right, tensors on the CPU
+        nv.gemm(x, wc, ws)

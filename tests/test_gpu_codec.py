@@ -113,3 +113,23 @@ def test_quantize_w4a4_workload(nv, orc):
     rc, rs = orc.quantize(xb, M, K)
     assert np.array_equal(gs.cpu().numpy(), rs)
     assert np.array_equal(gc.cpu().numpy(), rc)
+
+
+def test_quantize_nan_blocks_confined(nv, orc):
+    """Blocks holding a NaN (outside the contract) take the NaN scale code and
+    sign-only codes; every neighbouring block, scale byte and code byte is
+    bit-exact against the oracle (nothing spills into the next byte)."""
+    helpers.announce("quantize: NaN blocks confined")
+    rng = np.random.default_rng(90)
+    M, K = 6, 256
+    x = workloads.normal_bf16(rng, M, K)
+    x[0, 17] = 0x7FC0
+    x[1, 0] = 0xFFC0
+    x[2, 255] = 0x7F81          # a signalling-NaN pattern
+    x[3, 40] = 0x7F80           # +inf: saturates
+    x[4, 15], x[4, 16] = 0x7FC0, 0xFFC0   # NaNs in two neighbouring blocks
+    gc, gs = nv.quantize(helpers.dev_bf16(x))
+    rc, rs = orc.quantize(x, M, K)
+    assert rs[0, 1] == 0x7F and rs[4, 0] == 0x7F and rs[4, 1] == 0x7F
+    assert np.array_equal(gs.cpu().numpy(), rs)
+    assert np.array_equal(gc.cpu().numpy(), rc)

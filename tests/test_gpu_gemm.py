@@ -20,12 +20,26 @@ def nv():
     return m
 
 
-def _run(nv, x, w, row_idx=None, out_f32=False):
+def _plan(spec):
+    """"tiles,waves[,lds_kib[,splits]]" -> a GEMV plan override (None: default)."""
+    if spec is None:
+        return None
+    keys = ("gemv_tiles", "gemv_waves", "gemv_lds_kib", "gemv_splits")
+    return {k: int(v) for k, v in zip(keys, spec.split(",")) if int(v) > 0}
+
+
+def _run(nv, x, w, row_idx=None, out_f32=False, plan=None):
+    """The product on the GPU into a guard-padded output (a write outside the
+    output fails the case)."""
     import torch
     xd = helpers.dev_bf16(x)
     ri = None if row_idx is None else helpers.dev_i32(row_idx)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    n_out = w.codes.shape[0] if row_idx is None else len(row_idx)
+    g = helpers.Guarded((x.shape[0], n_out), dt)
     y = nv.gemm(xd, helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), row_idx=ri,
-                out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+                out_dtype=dt, plan=plan, out=g.t)
+    g.check()
     return y.cpu().numpy() if out_f32 else helpers.host_bits(y)
 
 
@@ -67,22 +81,17 @@ def test_ragged_shapes(nv, orc, M, K, N):
                                    (32, 256, 33)])
 def test_two_tiles_plans(nv, orc, M, K, N, plan):
     """Two activation tiles (16 < M <= 32) in every workgroup layout, forced
-    through NVFP4_GEMV_PLAN ("tiles per wave, waves") at sizes the oracle
-    checks whole: 16-wave workgroups (the fp16 path, scale blocks for K % 256
-    == 0) and the 8- and 4-wave bf16 layouts; ragged M, N and K, waves with
-    padding rows only."""
-    import os
+    through a plan ("tiles per wave, waves") at sizes the oracle checks whole:
+    16-wave workgroups (the fp16 path, scale blocks for K % 256 == 0) and the
+    8- and 4-wave bf16 layouts; ragged M, N and K, waves with padding rows
+    only."""
     helpers.announce(f"gemm two tiles 16 waves M={M} K={K} N={N} plan={plan}")
     rng = np.random.default_rng(M * 7 + K + N)
     x = workloads.normal_bf16(rng, M, K)
     w = workloads.nvfp4_weight(rng, N, K)
     ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
-    os.environ["NVFP4_GEMV_PLAN"] = plan
-    try:
-        got = _run(nv, x, w)
-        got32 = _run(nv, x, w, out_f32=True)
-    finally:
-        del os.environ["NVFP4_GEMV_PLAN"]
+    got = _run(nv, x, w, plan=_plan(plan))
+    got32 = _run(nv, x, w, out_f32=True, plan=_plan(plan))
     _assert_close(got, ref, what=f"{M}x{K}x{N}")
     _assert_close(got32, ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
 
@@ -146,20 +155,14 @@ def test_activations_outside_fp16(nv, orc, M, plan):
     16x16 GEMV, the other steps the fp16 path; with a failing value in every
     step the workgroups stop converting after two.  The product stays within
     the GEMM tolerance either way, with both K layouts (scale blocks and K
-    tail).  plan (NVFP4_GEMV_PLAN, read per call): "2,16" two weight tiles
+    tail).  plan ("tiles,waves" of the GEMV plan): "2,16" two weight tiles
     per wave in 16-wave workgroups (the widest layers at M > 16), "2,8" the
     8-wave bf16 layout."""
-    import os
     helpers.announce(f"gemm activations outside fp16 M={M} plan={plan}")
-    if plan:
-        os.environ["NVFP4_GEMV_PLAN"] = plan
-    try:
-        _outside_fp16_cases(nv, orc, M)
-    finally:
-        os.environ.pop("NVFP4_GEMV_PLAN", None)
+    _outside_fp16_cases(nv, orc, M, _plan(plan))
 
 
-def _outside_fp16_cases(nv, orc, M):
+def _outside_fp16_cases(nv, orc, M, plan):
     rng = np.random.default_rng(40 + M)
     for K, N in ((2048, 700), (1312, 260)):
         x = workloads.normal_bf16(rng, M, K)
@@ -171,8 +174,9 @@ def _outside_fp16_cases(nv, orc, M):
             x[2, ::256] = 0x3380
         w = workloads.nvfp4_weight(rng, N, K)
         ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
-        _assert_close(_run(nv, x, w), ref, what=f"{M}x{K}x{N} bf16 steps")
-        _assert_close(_run(nv, x, w, out_f32=True), ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
+        _assert_close(_run(nv, x, w, plan=plan), ref, what=f"{M}x{K}x{N} bf16 steps")
+        _assert_close(_run(nv, x, w, out_f32=True, plan=plan), ref, out_f32=True,
+                      what=f"{M}x{K}x{N} fp32")
 
 
 @pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
@@ -291,20 +295,16 @@ def test_mfma_masked_rows(nv, orc):
 
 
 def test_mfma_matches_gemv_chunks(nv):
-    """The same product through both paths (NVFP4_GEMM_MIN_M is read per call):
-    both are fp32 sums of exact products, so they agree to fp32 rounding."""
-    import os
+    """The same product through both paths (the plan's gemm_min_m forces the
+    GEMV at M = 96): both are fp32 sums of exact products, so they agree to
+    fp32 rounding."""
     helpers.announce("gemm mfma vs gemv")
     rng = np.random.default_rng(22)
     M, K, N = 96, 2048, 512
     x = workloads.normal_bf16(rng, M, K)
     w = workloads.nvfp4_weight(rng, N, K)
     a = _run(nv, x, w, out_f32=True)
-    os.environ["NVFP4_GEMM_MIN_M"] = "100000"
-    try:
-        b = _run(nv, x, w, out_f32=True)
-    finally:
-        del os.environ["NVFP4_GEMM_MIN_M"]
+    b = _run(nv, x, w, out_f32=True, plan={"gemm_min_m": 100000})
     scale = np.abs(a).max() + 1.0
     assert np.max(np.abs(a - b)) <= 1e-5 * scale
 
@@ -367,21 +367,16 @@ def test_prefill_full_size_sampled(nv, orc, K, N):
                                     (8, "2,8,0,16"), (32, "1,16,0,11"), (32, "2,16,0,16"),
                                     (3, "1,4,0,13")])
 def test_split_k_part_counts(nv, orc, M, plan):
-    """K split into 8, 11, 13 and 16 parts (NVFP4_GEMV_PLAN "tr,nw,lds,z"): the
+    """K split into 8, 11, 13 and 16 parts (plan "tiles,waves,lds,splits"): the
     reduce adds full batches of eight parts and every remainder; bf16 and
     fp32 outputs within the GEMM tolerance of the oracle."""
-    import os
     helpers.announce(f"gemm split-K part counts M={M} plan={plan}")
     rng = np.random.default_rng(M * 11 + len(plan))
     K, N = 8192, 300
     x = workloads.normal_bf16(rng, M, K)
     w = workloads.nvfp4_weight(rng, N, K)
     ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
-    os.environ["NVFP4_GEMV_PLAN"] = plan
-    try:
-        got = _run(nv, x, w)
-        got32 = _run(nv, x, w, out_f32=True)
-    finally:
-        del os.environ["NVFP4_GEMV_PLAN"]
+    got = _run(nv, x, w, plan=_plan(plan))
+    got32 = _run(nv, x, w, out_f32=True, plan=_plan(plan))
     _assert_close(got, ref, what=f"{M}x{K}x{N} {plan}")
     _assert_close(got32, ref, out_f32=True, what=f"{M}x{K}x{N} {plan} fp32")

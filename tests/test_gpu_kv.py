@@ -122,3 +122,20 @@ def test_store_then_load_round_trip(nv, orc):
                               np.zeros((w.num_slots, 256), dtype=np.uint8))
     ref = orc.kv_load_e4m3(c_ref, bt, lens, 16, 304, w.scale)
     assert np.array_equal(out, ref)
+
+
+def test_store_nan_elements_confined(nv, orc):
+    """NaN elements (both signs) become the NaN codes 0x7F / 0xFF; every other
+    code of the cache is bit-exact against the oracle (no spill into the next
+    code of the packed word)."""
+    helpers.announce("kv store NaN elements")
+    rng = np.random.default_rng(71)
+    T, W, slots = 8, 64, 12
+    x = workloads.normal_bf16(rng, T, W)
+    x[0, 3], x[0, 4], x[5, 63], x[7, 0] = 0x7FC0, 0xFFC0, 0x7F81, 0xFFFF
+    slot = rng.permutation(slots)[:T].astype(np.int32)
+    cache0 = rng.integers(0, 256, size=(slots, W), dtype=np.uint8)
+    got = _store_gpu(nv, x, slot, 0.03, cache0)
+    ref = orc.kv_store_e4m3(x, slot, 0.03, cache0.copy())
+    assert ref[slot[0], 3] == 0x7F and ref[slot[0], 4] == 0xFF
+    assert np.array_equal(got, ref)

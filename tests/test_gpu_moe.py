@@ -3,6 +3,7 @@ grouped GEMM (per expert, both epilogues), combine, and the whole layer
 against the oracle's token-by-token definition."""
 import numpy as np
 import pytest
+import torch
 
 import helpers
 import workloads
@@ -60,9 +61,11 @@ def test_grouped_gemm_matches_oracle(nv, orc, epi, outside):
     w = workloads.nvfp4_weight(rng, E, N, K)
     gather = rng.integers(0, rows, R).astype(np.int32)
     rs = (rng.random(R) + 0.5).astype(np.float32)
+    g = helpers.Guarded((R, N // 2 if epi else N), torch.bfloat16)
     y = nv.grouped_gemm(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
                         helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), R,
-                        row_scale=helpers.dev_f32(rs), epilogue=epi)
+                        row_scale=helpers.dev_f32(rs), epilogue=epi, out=g.t)
+    g.check()
     ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
                            epilogue=epi)
     ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
@@ -72,11 +75,10 @@ def test_grouped_gemm_matches_oracle(nv, orc, epi, outside):
 @pytest.mark.parametrize("epi,gathered,scaled", [(0, True, True), (1, True, False), (1, False, True),
                                                 (0, False, False)])
 def test_grouped_mfma_matches_oracle(nv, orc, epi, gathered, scaled):
-    """The MFMA grouped kernel (forced for these sizes through
-    NVFP4_GROUPED_MFMA_MIN_ROWS): experts with 0 rows, 1 row, a partial
+    """The MFMA grouped kernel (forced for these sizes through the plan's
+    grouped_mfma_min_rows): experts with 0 rows, 1 row, a partial
     256-row chunk, exactly 256 rows and several chunks; N and N/2 not multiples
     of the 256 / 128 output tile; K % 64 == 32 (a partial last K step)."""
-    import os
     helpers.announce(f"moe grouped mfma epi={epi} gather={gathered} scale={scaled}")
     rng = np.random.default_rng(50 + 2 * epi + gathered + 4 * scaled)
     E, K, N = 7, 416, 352
@@ -88,13 +90,12 @@ def test_grouped_mfma_matches_oracle(nv, orc, epi, gathered, scaled):
     w = workloads.nvfp4_weight(rng, E, N, K)
     gather = rng.integers(0, rows, R).astype(np.int32) if gathered else None
     rs = (rng.random(R) + 0.5).astype(np.float32) if scaled else None
-    os.environ["NVFP4_GROUPED_MFMA_MIN_ROWS"] = "1"
-    try:
-        y = nv.grouped_gemm(helpers.dev_bf16(a), None if gather is None else helpers.dev_i32(gather),
-                            helpers.dev_i32(off), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
-                            R, row_scale=None if rs is None else helpers.dev_f32(rs), epilogue=epi)
-    finally:
-        del os.environ["NVFP4_GROUPED_MFMA_MIN_ROWS"]
+    g = helpers.Guarded((R, N // 2 if epi else N), torch.bfloat16)
+    y = nv.grouped_gemm(helpers.dev_bf16(a), None if gather is None else helpers.dev_i32(gather),
+                        helpers.dev_i32(off), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                        R, row_scale=None if rs is None else helpers.dev_f32(rs), epilogue=epi,
+                        plan={"grouped_mfma_min_rows": 1}, out=g.t)
+    g.check()
     ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
                            epilogue=epi)
     ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
@@ -107,7 +108,9 @@ def test_combine_matches_oracle(nv, orc):
     T, topk, H = 33, 8, 2048
     y = workloads.normal_bf16(rng, T * topk, H)
     slot = rng.permutation(T * topk).astype(np.int32).reshape(T, topk)
-    got = helpers.host_bits(nv.moe_combine(helpers.dev_bf16(y), helpers.dev_i32(slot)))
+    g = helpers.Guarded((T, H), torch.bfloat16)
+    got = helpers.host_bits(nv.moe_combine(helpers.dev_bf16(y), helpers.dev_i32(slot), out=g.t))
+    g.check()
     ref = orc.moe_combine(y, slot, T, topk, H)
     ok, rf, worst = helpers.gemm_close(got, ref)
     assert ok, (rf, worst)
@@ -206,3 +209,108 @@ def test_moe_layer_prefill_sampled(nv, orc):
                         wl.w1.scales, wl.w2.codes, wl.w2.scales)
     ok, rf, worst = _layer_close(got[toks], ref, _slot_magnitude(orc, wl, toks))
     assert ok, (rf, worst)
+
+
+def _sub_problem(rows, off_h, E):
+    """Offsets of a grouped problem holding only the grouped rows `rows`
+    (sorted), each still with its expert: the expert of row r is the e with
+    off[e] <= r < off[e+1]."""
+    ex = np.searchsorted(off_h, rows, side="right") - 1
+    counts = np.bincount(ex, minlength=E)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False):
+    """Every GPU step of the layer against the oracle fed the GPU's own inputs
+    to that step, at the GEMM tolerance element by element: align bit-exact,
+    then the gate/up grouped GEMM with SwiGLU, the down grouped GEMM with the
+    gate weights and the combine, each on all rows (n_rows None) or on a
+    seeded sample of grouped rows / tokens (the oracle recomputes a grouped
+    problem of just those rows, each with its own expert).  down_fp32_bound:
+    the down projection's element bound also admits the fp32 summation error
+    bound I * 2^-24 * sum_k |a_k w_k g_r| of each output."""
+    E = wl.w1.codes.shape[0]
+    H = wl.x.shape[1]
+    I = wl.w2.codes.shape[2] * 2
+    T, topk = wl.ids.shape
+    R = T * topk
+    w1c, w1s = helpers.dev_u8(wl.w1.codes), helpers.dev_u8(wl.w1.scales)
+    w2c, w2s = helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales)
+    off, gather, slot, rg = nv.moe_align(helpers.dev_i32(wl.ids), E, helpers.dev_f32(wl.gates))
+    act = nv.grouped_gemm(helpers.dev_bf16(wl.x), gather, off, w1c, w1s, R, epilogue=1)
+    y = nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg)
+    out = nv.moe_combine(y, slot)
+    torch.cuda.synchronize()
+    off_h, gather_h, slot_h = off.cpu().numpy(), gather.cpu().numpy(), slot.cpu().numpy()
+    rg_h, act_h, y_h = rg.cpu().numpy(), helpers.host_bits(act), helpers.host_bits(y)
+    ro, rgat, rslot = orc.moe_align(wl.ids, E)
+    assert np.array_equal(off_h, ro) and np.array_equal(gather_h, rgat)
+    assert np.array_equal(slot_h, rslot)
+    rng = np.random.default_rng(seed)
+    rows = np.arange(R) if n_rows is None else np.sort(rng.choice(R, n_rows, replace=False))
+    toks = np.arange(T) if n_tok is None else np.sort(rng.choice(T, n_tok, replace=False))
+    so = _sub_problem(rows, off_h, E)
+    ref_act = orc.grouped_gemm(wl.x, H, gather_h[rows], so, E, len(rows), 2 * I, wl.w1.codes,
+                               wl.w1.scales, epilogue=1)
+    ok, rf, worst = helpers.gemm_close(act_h[rows], ref_act)
+    assert ok, ("gate/up", rf, worst)
+    ref_y = orc.grouped_gemm(np.ascontiguousarray(act_h[rows]), I, None, so, E, len(rows), H,
+                             wl.w2.codes, wl.w2.scales, row_scale=rg_h[rows])
+    extra = None
+    if down_fp32_bound:
+        a_abs = np.ascontiguousarray(act_h[rows] & 0x7FFF)
+        mag = orc.grouped_gemm(a_abs, I, None, so, E, len(rows), H, wl.w2.codes & 0x77,
+                               wl.w2.scales, row_scale=np.abs(rg_h[rows]))
+        extra = I * 2.0 ** -24 * mag
+        ok_bj, _, worst_bj = helpers.gemm_close(y_h[rows], ref_y)
+        print(f"[down] BJ element bound alone: ok={ok_bj} worst ratio {worst_bj:.2f}", flush=True)
+    ok, rf, worst = helpers.gemm_close(y_h[rows], ref_y, abs_extra=extra)
+    assert ok, ("down", rf, worst)
+    ref_out = orc.moe_combine(y_h, np.ascontiguousarray(slot_h[toks]), len(toks), topk, H)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(out)[toks], ref_out)
+    assert ok, ("combine", rf, worst)
+
+
+def test_moe_layer_prefill_steps_chained_sampled(nv, orc):
+    """T = 4096 at full size (the MFMA grouped kernel): every step held to the
+    GEMM tolerance element by element on 96 sampled grouped rows (experts of
+    every popularity) and 64 sampled tokens, the oracle fed the GPU's own
+    inputs to each step."""
+    helpers.announce("moe layer T=4096 chained steps, sampled rows")
+    _chained(nv, orc, workloads.moe(4096), n_rows=96, n_tok=64, seed=43)
+
+
+def test_moe_layer_steps_chained_dense_scales(nv, orc):
+    """T = 32 with the dense layers' scale distribution (exponent fields 3..9,
+    2^-4 .. 2^2 before the mantissa) instead of the checkpoint-like expert
+    scales: the SwiGLU outputs grow to ~10^5 and the down projection's 768-term
+    sums cancel far below their terms, so its element bound 1e-2*(|ref|+1)
+    cannot hold for fp32 accumulation; that step is held to it plus the fp32
+    summation error bound of each output (relative Frobenius <= 1e-3 as
+    always).  Align, gate/up and combine meet the plain GEMM tolerance."""
+    helpers.announce("moe layer T=32 chained steps, dense-layer scales")
+    _chained(nv, orc, workloads.moe(32, exp_field=(3, 9)), down_fp32_bound=True)
+
+
+def test_grouped_long_k_few_rows(nv, orc):
+    """A K past the grouped GEMV's LDS staging (5,120 > 4,864) with decode-like
+    row counts runs the MFMA kernel; every row against the oracle, both
+    epilogues, guarded outputs."""
+    rng = np.random.default_rng(60)
+    E, K, N = 5, 5120, 96
+    counts = np.array([1, 3, 0, 5, 2])
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, 7, K)
+    w = workloads.nvfp4_weight(rng, E, N, K)
+    gather = rng.integers(0, 7, R).astype(np.int32)
+    for epi in (0, 1):
+        helpers.announce(f"moe grouped long K={K} epi={epi}")
+        g = helpers.Guarded((R, N // 2 if epi else N), torch.bfloat16)
+        y = nv.grouped_gemm(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+                            helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), R, epilogue=epi,
+                            out=g.t)
+        g.check()
+        ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, epilogue=epi)
+        ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+        assert ok, (epi, rf, worst)

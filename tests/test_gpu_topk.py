@@ -44,7 +44,11 @@ def _check_exact(nv, orc, v, k, ids_map=None):
     import torch
     ld = torch.from_numpy(v).cuda()
     im = None if ids_map is None else helpers.dev_i32(ids_map)
-    gv, gi = nv.topk(ld, k, ids_map=im)
+    gval = helpers.Guarded((v.shape[0], k), torch.float32)
+    gids = helpers.Guarded((v.shape[0], k), torch.int32)
+    gv, gi = nv.topk(ld, k, ids_map=im, values=gval.t, ids=gids.t)
+    gval.check()
+    gids.check()
     gv, gi = gv.cpu().numpy(), gi.cpu().numpy()
     ov, oi = orc.topk(v, k, ids_map=ids_map)
     assert np.array_equal(gi, oi)
@@ -95,8 +99,13 @@ def test_head_topk_one_hot_exact(nv, orc, M):
     x = np.zeros((M, K))
     x[np.arange(M), rng.integers(0, K, size=M)] = rng.choice([1.0, -2.0, 0.5], size=M)
     xb = helpers.f64_to_bf16_bits_exact(x)
+    import torch
+    gval = helpers.Guarded((M, k), torch.float32)
+    gids = helpers.Guarded((M, k), torch.int32)
     gv, gi = nv.head_topk(helpers.dev_bf16(xb), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
-                          k, row_idx=helpers.dev_i32(idx))
+                          k, row_idx=helpers.dev_i32(idx), values=gval.t, ids=gids.t)
+    gval.check()
+    gids.check()
     ov, oi, _ = orc.head_topk(xb, M, K, w.codes, w.scales, k, row_idx=idx)
     assert np.array_equal(gi.cpu().numpy(), oi)
     assert np.array_equal(gv.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))

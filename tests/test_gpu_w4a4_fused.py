@@ -71,24 +71,47 @@ def test_fused_masked_rows_and_oracle(nv, orc):
 def test_fused_in_staging_forced(nv, M, K, N, plan):
     """The quantizer inside the GEMV's activation staging (whole-K staging for
     M <= 4, the streamed window for 5 <= M <= 8 and M > 8), forced for every
-    shape (NVFP4_W4A4_FUSE is read per call): bit-identical to quantize then
-    the W4A4 GEMM, including ragged K steps and split-K.  plan "2,16": two
-    activation tiles in 16-wave workgroups (scale blocks when K % 256 == 0)."""
-    import os
+    shape (plan w4a4_fuse = 1): bit-identical to quantize then the W4A4 GEMM,
+    including ragged K steps and split-K.  plan "2,16": two activation tiles
+    in 16-wave workgroups (scale blocks when K % 256 == 0)."""
     import torch
     helpers.announce(f"w4a4 fused in staging M={M} K={K} N={N} plan={plan}")
     rng = np.random.default_rng(M * 17 + K + N)
     x = helpers.dev_bf16(_x(rng, M, K))
     w = workloads.nvfp4_weight(rng, N, K)
     wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
-    os.environ["NVFP4_W4A4_FUSE"] = "1"
+    pl = {"w4a4_fuse": 1}
     if plan:
-        os.environ["NVFP4_GEMV_PLAN"] = plan
-    try:
-        fused = nv.gemm_w4a4(x, wc, ws, out_dtype=torch.float32)
-    finally:
-        del os.environ["NVFP4_W4A4_FUSE"]
-        os.environ.pop("NVFP4_GEMV_PLAN", None)
+        pl.update(gemv_tiles=int(plan.split(",")[0]), gemv_waves=int(plan.split(",")[1]))
+    fused = nv.gemm_w4a4(x, wc, ws, out_dtype=torch.float32, plan=pl)
     ac, as_ = nv.quantize(x)
     ref = nv.gemm(ac, wc, ws, a_scales=as_, out_dtype=torch.float32)
     assert torch.equal(fused.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,K,N,fuse", [(65, 64, 16, 1), (300, 160, 520, 1), (300, 160, 520, 0),
+                                        (700, 2048, 1000, 1), (512, 5120, 1100, 1),
+                                        (1000, 2080, 300, 1)])
+def test_mfma_fused_quantizer_tile_loads(nv, orc, M, K, N, fuse):
+    """Large M: the quantizer inside the MFMA GEMM's activation tile loads
+    (plan w4a4_fuse = 1), and the one-pass variant (0), against quantize then
+    the W4A4 GEMM -- bit-identical (the same exact operands summed in the same
+    order) -- and against the oracle within the GEMM tolerance.  Shapes with a
+    partial last K step (K % 64 == 32), ragged M and N, outlier activations,
+    and split-K tail tiles."""
+    import torch
+    helpers.announce(f"w4a4 mfma fused tile loads M={M} K={K} N={N} fuse={fuse}")
+    rng = np.random.default_rng(M + 3 * K + N)
+    xb = _x(rng, M, K)
+    x = helpers.dev_bf16(xb)
+    w = workloads.nvfp4_weight(rng, N, K)
+    wc, ws = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    got = nv.gemm_w4a4(x, wc, ws, out_dtype=torch.float32, plan={"w4a4_fuse": fuse})
+    ac, as_ = nv.quantize(x)
+    ref = nv.gemm(ac, wc, ws, a_scales=as_, out_dtype=torch.float32)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    rc, rs = orc.quantize(xb, M, K)
+    ok, rf, worst = helpers.gemm_close(got.cpu().numpy(),
+                                       orc.gemm_w4a4(rc, rs, M, K, w.codes, w.scales),
+                                       out_is_bf16=False)
+    assert ok, f"rel_frob={rf:.3e} worst={worst:.3f}"

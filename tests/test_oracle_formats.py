@@ -254,3 +254,37 @@ def test_quantize_error_bound(orc):
     assert ok.all()
     # with a zero scale every element is below 6 * 2^-10 and is stored as zero
     assert np.all(ax[s == 0] <= 6 * 2.0**-10)
+
+
+def test_nan_block_is_confined(orc):
+    """Non-finite inputs are outside the quantizer's contract, but a block that
+    holds a NaN stays confined to itself: its scale is the E4M3 NaN code 0x7F
+    and its codes keep only their sign bits; every other block of the row is
+    exactly what it is without the NaN block.  An infinite element saturates
+    (scale 0x7E, magnitude index 7)."""
+    assert orc.scale_code(float("nan")) == 0x7F
+    assert orc.scale_code(float("inf")) == 0x7E
+    rng = np.random.default_rng(5)
+    x = helpers.f64_to_bf16_bits_exact(
+        helpers.bf16_bits_to_f64(((rng.standard_normal((2, 64)).astype(np.float32).view(np.uint32)
+                                   + 0x8000) >> 16).astype(np.uint16)))
+    qc0, qs0 = orc.quantize(x, 2, 64)
+    xn = x.copy()
+    xn[0, 20] = 0x7FC0      # NaN in block 1 of row 0
+    xn[1, 63] = 0xFFC0      # -NaN in block 3 of row 1
+    qc, qs = orc.quantize(xn, 2, 64)
+    assert qs[0, 1] == 0x7F and qs[1, 3] == 0x7F
+    keep = np.ones((2, 4), bool)
+    keep[0, 1] = keep[1, 3] = False
+    assert np.array_equal(qs[keep], qs0[keep])
+    nib = np.stack([qc & 15, qc >> 4], axis=-1).reshape(2, 64)
+    nib0 = np.stack([qc0 & 15, qc0 >> 4], axis=-1).reshape(2, 64)
+    sign = ((xn >> 15) & 1).astype(np.uint8) << 3
+    for r, b in ((0, 1), (1, 3)):
+        assert np.array_equal(nib[r, 16 * b:16 * b + 16], sign[r, 16 * b:16 * b + 16])
+    other = np.repeat(keep, 16, axis=1)
+    assert np.array_equal(nib[other], nib0[other])
+    xi = x.copy()
+    xi[0, 0] = 0x7F80       # +inf
+    qc, qs = orc.quantize(xi, 2, 64)
+    assert qs[0, 0] == 0x7E and (qc[0, 0] & 15) == 7

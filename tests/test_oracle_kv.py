@@ -119,3 +119,34 @@ def test_store_then_load_is_identity_on_e4m3_values(orc):
         assert np.array_equal(got & 0x7FFF, x & 0x7FFF)
         nz = (x & 0x7FFF) != 0
         assert np.array_equal(got[nz], x[nz])
+
+
+def test_encode_nan_is_the_nan_code_of_its_sign(orc):
+    """A NaN quotient becomes the format's NaN code with its sign (0x7F / 0xFF),
+    as torch's float8_e4m3fn cast gives (a library routine); infinities keep the
+    satfinite reading (448), where torch's cast would give NaN."""
+    for bits in (0x7FC0, 0x7F81, 0xFFC0, 0xFFFF):
+        v = float(helpers.bf16_bits_to_f64(np.array([bits], np.uint16))[0])
+        want = int(_torch_e4m3(np.array([v], np.float32))[0])
+        assert want == (0xFF if bits & 0x8000 else 0x7F)
+        assert orc.e4m3_encode(v) == want
+    assert orc.e4m3_encode(float("inf")) == 0x7E and orc.e4m3_encode(-float("inf")) == 0xFE
+
+
+def test_store_nan_leaves_neighbours_exact(orc):
+    """A NaN element of a token row gets its NaN code; every other element of the
+    row and of the cache is what the store gives without it (nothing spills
+    into the next code)."""
+    rng = np.random.default_rng(12)
+    T, W, slots = 4, 32, 8
+    x = helpers.f64_to_bf16_bits_exact(
+        helpers.bf16_bits_to_f64(((rng.standard_normal((T, W)).astype(np.float32).view(np.uint32)
+                                   + 0x8000) >> 16).astype(np.uint16)))
+    sm = np.array([5, 0, 7, 2], np.int32)
+    base = orc.kv_store_e4m3(x, sm, 0.05, np.zeros((slots, W), np.uint8))
+    xn = x.copy()
+    xn[1, 9], xn[2, 0], xn[2, 31] = 0x7FC0, 0xFFC0, 0x7FC0
+    got = orc.kv_store_e4m3(xn, sm, 0.05, np.zeros((slots, W), np.uint8))
+    want = base.copy()
+    want[0, 9], want[7, 0], want[7, 31] = 0x7F, 0xFF, 0x7F
+    assert np.array_equal(got, want)

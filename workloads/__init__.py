@@ -179,14 +179,15 @@ MOE_SCALE_EXP_FIELD = (0, 2)
 
 
 def moe(T: int, E: int = MOE_EXPERTS, topk: int = MOE_TOPK, H: int = MOE_HIDDEN,
-        I: int = MOE_INTER, seed: int = 0) -> MoEWorkload:
+        I: int = MOE_INTER, seed: int = 0, exp_field=MOE_SCALE_EXP_FIELD) -> MoEWorkload:
     """Routed MoE layer.  Draws: x [T, H] N(0,1), routing, W1 NF4W(E x 2I, H),
-    W2 NF4W(E x H, I), both with scale exponent fields MOE_SCALE_EXP_FIELD."""
+    W2 NF4W(E x H, I), both with scale exponent fields exp_field (default
+    MOE_SCALE_EXP_FIELD; (3, 9) gives the dense layers' 2^-4 .. 2^2 scales)."""
     rng = np.random.default_rng(seed)
     x = normal_bf16(rng, T, H)
     ids, gates = zipf_routing(rng, T, E, topk)
-    w1 = nvfp4_weight(rng, E, 2 * I, H, exp_field=MOE_SCALE_EXP_FIELD)
-    w2 = nvfp4_weight(rng, E, H, I, exp_field=MOE_SCALE_EXP_FIELD)
+    w1 = nvfp4_weight(rng, E, 2 * I, H, exp_field=exp_field)
+    w2 = nvfp4_weight(rng, E, H, I, exp_field=exp_field)
     return MoEWorkload(x, ids, gates, w1, w2)
 
 
