@@ -66,6 +66,9 @@ _SIGS = {
     "nvfp4_grouped_gemm": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _int,
                             _vp, _vp, _sz, _vp], _int),
     "nvfp4_moe_combine": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_noalloc_scratch_bytes": ([], _sz),
+    "nvfp4_gemm_noalloc": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp,
+                            _vp], _int),
 }
 
 

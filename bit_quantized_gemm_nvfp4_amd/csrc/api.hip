@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4.h"
 #include "../../include/nvfp4_plan.h"
 #include "launch.h"
@@ -578,6 +580,68 @@ int nvfp4_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int
   if (H % 8 != 0 || topk > 32 || T * topk > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
   if (!aligned16(y) || !aligned16(slot_pos) || !aligned16(out)) return NVFP4_ERROR_INVALID_VALUE;
   return launched(launch_moe_combine(y, slot_pos, T, topk, H, out, as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing ---------------------------------------
+//
+// nvfp4_gemm_noalloc keeps its workspace in `scratch`, a file-scope device
+// array: every GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory,
+// so its address on each device is looked up once with hipGetSymbolAddress
+// (with that device current) and only that address is passed to the kernels.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+// This device's address of `scratch` (looked up on the first call on the
+// device); nullptr if the lookup fails.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int nvfp4_gemm_noalloc(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+                       int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                       const int32_t* row_idx, int64_t n_out, int out_dtype, void* out,
+                       void* stream) {
+  // the host checks of nvfp4_gemm first, so an invalid call makes no HIP call
+  if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (const int rc = linear_args_status(a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                                        out))
+    return rc;
+  if ((a_dtype == NVFP4_BF16) != (a_scales == nullptr)) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_scales && !aligned16(a_scales)) return NVFP4_ERROR_INVALID_VALUE;
+  const size_t need = nvfp4_gemm_workspace_size(a_dtype, M, N, K, n_out);
+  if (need > kScratchBytes) return NVFP4_ERROR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_for_current_device();
+    if (!ws) return NVFP4_ERROR_LAUNCH;
+  }
+  return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
+                   out, ws, need > 0 ? kScratchBytes : 0, stream, Alpha{}, PlanOverride{});
 }
 
 }  // extern "C"

@@ -130,6 +130,27 @@ int nvfp4_gemm(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, i
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same operation, arguments, results (bit-identical
+ * to nvfp4_gemm) and status codes otherwise.  The workspace nvfp4_gemm would
+ * take lives in a device array inside the library, nvfp4_noalloc_scratch_bytes()
+ * = 64 MiB on each GPU, held until the process ends: a call whose
+ * nvfp4_gemm_workspace_size exceeds it returns NVFP4_ERROR_WORKSPACE before
+ * any launch.  The call allocates nothing (no hipMalloc, no library
+ * allocator); its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress).  Every call on one GPU shares its array: calls
+ * that overlap in time on one GPU (different streams, or host threads) race
+ * and must be serialised by the caller.  Nothing in the array needs to start
+ * at zero: each call writes every workspace byte it reads.
+ */
+size_t nvfp4_noalloc_scratch_bytes(void);
+int nvfp4_gemm_noalloc(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, int64_t N,
+                       int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                       const int32_t *row_idx, int64_t n_out, int out_dtype, void *out,
+                       void *stream);
+
+/*
  * W4A4 linear layer from bf16 activations: the activation quantizer fused into
  * the product ("52.6% more tokens, 1.53x less GPU time ...": NVFP4 W4A4
  * execution).  Bit-identical to nvfp4_quantize(a) followed by nvfp4_gemm

@@ -346,3 +346,20 @@ def test_binding_checks_shapes_before_the_gpu(L):
     raises("ids_map", nv.topk, torch.zeros(2, 100), 4, ids_map=torch.zeros(99, dtype=torch.int32))
     with pytest.raises(RuntimeError, match="GPU"):   # shapes right, tensors on the CPU
         nv.gemm(x, wc, ws)
+
+
+def test_noalloc_validation(L):
+    """nvfp4_gemm_noalloc checks its arguments as nvfp4_gemm does and refuses a
+    call that needs more than its device array, all before any HIP call."""
+    def na(a_dtype=0, a=P, a_scales=NULL, M=4, N=64, K=256, out=P4, n_out=64):
+        return L.nvfp4_gemm_noalloc(a_dtype, a, a_scales, M, N, K, P2, P3, NULL, n_out, 0, out,
+                                    NULL)
+    assert L.nvfp4_noalloc_scratch_bytes() == 64 << 20
+    assert na(a=NULL) == INVALID
+    assert na(K=48) == NOT_SUPPORTED
+    assert na(a_scales=P) == INVALID
+    assert na(a_dtype=2) == INVALID
+    assert na(out=MIS) == INVALID
+    assert na(n_out=32) == INVALID
+    # W4A4 at M = 8192: 80 MiB of dequantized activations alone
+    assert na(a_dtype=2, a_scales=P, M=8192, N=256, K=5120, n_out=256) == WORKSPACE
