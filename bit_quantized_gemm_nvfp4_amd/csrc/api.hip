@@ -82,17 +82,19 @@ bool to_override(const nvfp4_plan_t* plan, PlanOverride& ov) {
   ov.gemv_splits = plan->gemv_splits;
   ov.w4a4_fuse = plan->w4a4_fuse;
   ov.grouped_mfma_min_rows = plan->grouped_mfma_min_rows;
+  ov.gemv_kparts = plan->gemv_kparts;
   if (ov.gemm_min_m == 0 || ov.w4a4_fuse > 1) return false;
   return true;
 }
 
 // Whether the GEMV layout of a plan exists for activation chunks of M rows
 // (the fused W4A4 staging is built for 1 or 2 tiles per wave).
-bool gemv_plan_ok(const PlanOverride& ov, int64_t M, bool fused) {
-  if (!gemv_override_valid(M, ov)) return false;
+bool gemv_plan_ok(const PlanOverride& ov, int64_t M, int64_t K, bool fused) {
+  if (K <= 0 || K % 32 != 0) return true;  // (the entry point reports the shape)
+  if (!gemv_override_valid(M, K, ov)) return false;
   if (fused) {
-    const GemvPlan p = plan_gemv(M, 1, 32, kNumCUs, ov);
-    if (p.tr > 2) return false;
+    const GemvPlan p = plan_gemv(M, 1, K, kNumCUs, ov);
+    if (p.tr > 2 || ov.gemv_kparts > 1) return false;
   }
   return true;
 }
@@ -142,6 +144,7 @@ void nvfp4_plan_default(nvfp4_plan_t* plan) {
   if (!plan) return;
   plan->gemm_min_m = plan->gemv_small_max = plan->gemv_tiles = plan->gemv_waves = -1;
   plan->gemv_lds_kib = plan->gemv_splits = plan->w4a4_fuse = plan->grouped_mfma_min_rows = -1;
+  plan->gemv_kparts = -1;
 }
 
 size_t nvfp4_gemm_workspace_size_planned(const nvfp4_plan_t* plan, int a_dtype, int64_t M,
@@ -255,7 +258,7 @@ int nvfp4_gemm_planned(const nvfp4_plan_t* plan, int a_dtype, const void* a,
                        size_t workspace_bytes, void* stream) {
   PlanOverride ov;
   if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
-  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, false)) return NVFP4_ERROR_INVALID_VALUE;
+  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, K, false)) return NVFP4_ERROR_INVALID_VALUE;
   return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
                    out, workspace, workspace_bytes, stream, Alpha{}, ov);
 }
@@ -351,7 +354,7 @@ int nvfp4_gemm_w4a4_bf16_planned(const nvfp4_plan_t* plan, const uint16_t* a, in
                                  size_t workspace_bytes, void* stream) {
   PlanOverride ov;
   if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
-  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, ov.w4a4_fuse == 1))
+  if (M > 0 && !gemv_plan_ok(ov, M < 32 ? M : 32, K, ov.w4a4_fuse == 1))
     return NVFP4_ERROR_INVALID_VALUE;
   return w4a4_bf16_impl(ov, a, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype, out,
                         workspace, workspace_bytes, stream);

@@ -129,6 +129,83 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   }
 }
 
+// K parts inside the workgroup (gemv_accumulate_kp): G groups of TR weight
+// tiles x KP parts of the workgroup's K steps, summed in LDS in part order,
+// so a K range too long for the rows alone to fill the chip needs neither a
+// second kernel nor fp32 partials in memory.  Plain W4A16, one or two
+// activation tiles, K % 256 == 0.  blockIdx.x picks G*TR tiles, blockIdx.y a
+// K range (z > 1: fp32 partials summed by k_splitk_reduce, as k_gemv).
+template <int MT, int TR, int G, int KP, int WR>
+__global__ void __launch_bounds__(64 * G * KP) k_gemv_kp(GemvArgs a) {
+  constexpr int NW = G * KP;
+  constexpr int RPP = WR * MT;
+  constexpr int XP = KP * RPP * 32 / (64 * NW);  // window pieces per thread and step
+  static_assert(XP * 64 * NW == KP * RPP * 32, "window pieces must divide the workgroup");
+  static_assert((KP - 1) * G * TR * MT * 64 * 16 <= 2 * KP * RPP * kXWin * 2,
+                "the parts' sums must fit the window");
+  __shared__ __attribute__((aligned(16))) uint16_t win[2 * KP * RPP * kXWin];
+  __shared__ int hflag[2 * KP];
+  __shared__ uint32_t scl[NW * TR * 512];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = wave % G, part = wave / G;
+  const int ln = lane & 15, q = lane >> 4;
+  const int64_t K = a.K;
+  const int zs0 = (int)(((int64_t)a.steps * blockIdx.y) / gridDim.y);
+  const int zs1 = (int)(((int64_t)a.steps * (blockIdx.y + 1)) / gridDim.y);
+
+  const int64_t tile0 = ((int64_t)blockIdx.x * G + g) * TR;
+  const uint8_t* cptr[TR];
+  const uint8_t* sptr[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    int64_t j = (tile0 + t) * 16 + ln;
+    if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
+    const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
+    cptr[t] = a.wc + row * (K / 2);
+    sptr[t] = a.ws + row * (K / 16);
+  }
+  f32x4 acc[TR][MT];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (threadIdx.x < 2 * KP) hflag[threadIdx.x] = -1;  // no step is marked inexact yet
+  __syncthreads();
+  const uint16_t* x = a.x;
+  gemv_accumulate_kp<MT, TR, XP, KP, WR, true>(acc, cptr, sptr, win, hflag,
+                                               scl + wave * TR * 512, part, a.M, K, zs0,
+                                               zs1 - zs0,
+                                               [x, K](int m) { return x + (int64_t)m * K; });
+  gemv_kp_reduce<MT, TR, KP>(acc, reinterpret_cast<f32x4*>(win), part, g, G);
+  if (part != 0) return;
+
+  // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
+  const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
+  const float alpha = scaled ? alpha_of(a.ga, a.gw) : 1.0f;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const int64_t j = (tile0 + t) * 16 + ln;
+    if (j >= a.n_out) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + 4 * q + r;
+        if (m >= a.M) continue;
+        const int64_t o = (int64_t)m * a.n_out + j;
+        const float v = scaled ? acc[t][mt][r] * alpha : acc[t][mt][r];
+        if (gridDim.y > 1)
+          a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
+        else if (a.out_f32)
+          static_cast<float*>(a.out)[o] = v;
+        else
+          static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
 // Very small M (<= 8): 4x4x4-block MFMA with per-block scaling of the MFMA
 // result (gemv4_core.h).  blockIdx.x picks nw*TR tiles of 4 weight rows, a wave
 // TR of them; blockIdx.y a contiguous part of K.
@@ -295,6 +372,32 @@ void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
     hipLaunchKernelGGL((k_gemv<MT, TR, 4, FQ>), grid, dim3(256), 0, stream, a);
 }
 
+// The K-parts layouts that are built: (tiles per wave, tile groups, parts).
+struct KpLayout {
+  int tr, g, kp;
+};
+constexpr KpLayout kKpLayouts[] = {{2, 2, 4}, {2, 4, 2}, {1, 4, 4}, {2, 2, 8}, {1, 2, 8},
+                                   {2, 1, 8}, {1, 4, 2}};
+
+template <int MT, int WR, int TR, int G, int KP>
+bool try_kp(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+  if (p.tr != TR || p.nw != G * KP || p.kp != KP) return false;
+  const int64_t tiles = (a.n_out + 15) / 16;
+  dim3 grid((unsigned)((tiles + G * TR - 1) / (G * TR)), (unsigned)p.z);
+  hipLaunchKernelGGL((k_gemv_kp<MT, TR, G, KP, WR>), grid, dim3(64 * G * KP), 0, stream, a);
+  return true;
+}
+
+template <int MT, int WR>
+int launch_gemv_kp_t(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+  bool ok = try_kp<MT, WR, 2, 2, 4>(a, p, stream) || try_kp<MT, WR, 2, 4, 2>(a, p, stream) ||
+            try_kp<MT, WR, 1, 4, 4>(a, p, stream) || try_kp<MT, WR, 1, 4, 2>(a, p, stream);
+  if constexpr (WR == 8)  // eight parts fit LDS with 8-row windows only
+    ok = ok || try_kp<MT, WR, 2, 2, 8>(a, p, stream) || try_kp<MT, WR, 1, 2, 8>(a, p, stream) ||
+         try_kp<MT, WR, 2, 1, 8>(a, p, stream);
+  return ok ? 0 : -2;
+}
+
 template <int MG, int TR, bool FQ>
 void launch_gemv4_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 3) / 4;
@@ -384,13 +487,43 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
   if (z > steps) z = steps;
   if (z < 1) z = 1;
   p.z = (int)z;
+  // K parts inside the workgroup (override only, for now): the workgroup's
+  // waves are tile groups x parts
+  p.kp = 1;
+  // K parts inside the workgroup instead of across workgroups, for M <= 8 on
+  // layers wide enough for 1.5 workgroups of 4 tiles per CU (measured at M = 8:
+  // the 32,768-row masked head 27.7 -> 23.8 us; on the 17,408-row layer the
+  // 272 workgroups leave some CUs with two and the split-K launch is as fast)
+  const bool kp_default = ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
+                          ov.gemv_splits < 0 && !p.small && M <= 8 && K % kGemvStep == 0 &&
+                          p.z >= 2 && steps >= 2 && (tiles + 3) / 4 >= (int64_t)num_cus * 3 / 2;
+  if (kp_default) {
+    p.tr = 1;
+    p.nw = 8;
+    p.kp = 2;
+    p.z = 1;
+  }
+  if (ov.gemv_kparts > 1 && !p.small && K % kGemvStep == 0) {
+    p.kp = ov.gemv_kparts;
+    if (ov.gemv_splits <= 0) p.z = 1;
+    if ((int64_t)p.z * p.kp > steps) p.z = (int)(steps / p.kp);  // every part >= 1 step
+  }
   return p;
 }
 
-bool gemv_override_valid(int64_t M, const PlanOverride& ov) {
+bool gemv_override_valid(int64_t M, int64_t K, const PlanOverride& ov) {
   if (ov.gemv_small_max > 8) return false;
   if (ov.gemv_lds_kib >= 0 && (ov.gemv_lds_kib < 8 || ov.gemv_lds_kib > 160)) return false;
-  const GemvPlan p = plan_gemv(M, 1, 32, kNumCUs, ov);
+  const GemvPlan p = plan_gemv(M, 1, K, kNumCUs, ov);
+  if (ov.gemv_kparts > 1) {  // a built K-parts layout: full steps, one activation tile
+                             // (two: 1 tile per wave, 16 waves, 2 parts)
+    if (p.small || K % kGemvStep != 0 || K / kGemvStep < ov.gemv_kparts) return false;
+    if (p.mt == 2) return p.tr == 1 && p.nw == 16 && ov.gemv_kparts == 2;
+    if (ov.gemv_kparts == 8 && M > 8) return false;  // 16-row windows: at most 4 parts
+    for (const KpLayout& l : kKpLayouts)
+      if (l.tr == p.tr && l.g * l.kp == p.nw && l.kp == ov.gemv_kparts) return true;
+    return false;
+  }
   const bool tr_ok = p.small ? (p.tr == 1 || p.tr == 2 || p.tr == 4 || (p.tr == 8 && p.mt == 1))
                              : (p.tr == 1 || p.tr == 2 || (p.tr == 4 && p.mt == 1));
   const bool nw_ok = p.small ? (p.nw >= 1 && p.nw <= 8)
@@ -423,7 +556,14 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
   a.steps = (int)((K + step - 1) / step);
   a.out_f32 = out_f32 ? 1 : 0;
   int rc = -2;
-  if (p.small) {
+  if (p.kp > 1 && !fakequant) {
+    if (p.mt == 1 && M <= 8)
+      rc = launch_gemv_kp_t<1, 8>(a, p, stream);
+    else if (p.mt == 1)
+      rc = launch_gemv_kp_t<1, 16>(a, p, stream);
+    else if (p.mt == 2 && try_kp<2, 16, 1, 8, 2>(a, p, stream))
+      rc = 0;
+  } else if (p.small) {
     if (p.mt == 1 && p.tr == 4)
       rc = launch_plan<true, 1, 4>(a, p, stream);
     else if (p.mt == 1 && p.tr == 2)

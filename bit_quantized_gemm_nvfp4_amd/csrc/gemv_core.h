@@ -507,4 +507,169 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
   }
 }
 
+// ---- K parts inside the workgroup -------------------------------------------------
+// A workgroup of G x KP waves: G groups of TR weight tiles, and KP contiguous
+// parts of the workgroup's K steps; wave w streams the tiles of group w % G over
+// part w / G.  At iteration i every part p processes its step start_p + i, so
+// the activation window holds one step per part ([2][KP][WR*MT][kXWin]) and the
+// workgroup still meets once per iteration.  The parts' sums are added in LDS
+// at the end, in part order (gemv_kp_reduce), so no second kernel and no fp32
+// partials in memory are needed.  WR is the number of window rows per
+// activation tile: 8 when M <= 8 (rows 8..15 of the MFMA operand read row 7),
+// else 16.  Full 256-element steps only (K % 256 == 0), scale blocks, fp16
+// path as gemv_accumulate_win_blk.
+
+struct KParts {
+  int start;  // first step of the wave's part
+  int len;    // its steps (>= 1)
+};
+
+__device__ __forceinline__ KParts kpart(int s0, int S, int p, int KP) {
+  const int a = (S * p) / KP, b = (S * (p + 1)) / KP;
+  return KParts{s0 + a, b - a};
+}
+
+// Window pieces of iteration i: piece c of the buffer is row (c >> 5) % (WR*MT)
+// of part (c >> 5) / (WR*MT), 8 elements at (c & 31) * 8 of that part's step
+// (clamped to the part's last step); rows past M repeat row M-1.
+template <int XP, int KP, int RPP, typename RowPtr>
+__device__ __forceinline__ void xwin_load_kp(u32x4 (&v)[XP], int M, int64_t K, int s0, int S,
+                                             int i, RowPtr row_ptr) {
+#pragma unroll
+  for (int u = 0; u < XP; ++u) {
+    const int c = threadIdx.x + u * blockDim.x;
+    const int p = (c >> 5) / RPP, r = (c >> 5) - p * RPP;
+    const KParts kp = kpart(s0, S, p, KP);
+    const int s = kp.start + min(i, kp.len - 1);
+    const int m = min(r, M - 1);
+    v[u] = *reinterpret_cast<const u32x4*>(row_ptr(m) + (int64_t)s * kGemvStep + (c & 31) * 8);
+  }
+}
+
+// Stores the pieces (fp16 when hw.on, marking a part whose values are not all
+// exact in fp16 with tag `i` in hflag[buffer][part]; bf16 otherwise).
+template <bool H, int XP, int RPP>
+__device__ __forceinline__ void xwin_store_kp(uint16_t* buf, int* hflag_buf, bool on,
+                                              const u32x4 (&v)[XP], int tag) {
+#pragma unroll
+  for (int u = 0; u < XP; ++u) {
+    const int c = threadIdx.x + u * blockDim.x;
+    uint16_t* dst = buf + (c >> 5) * kXWin + (c & 31) * 8;
+    if (H && on) {
+      u32x4 h;
+      if (!bf16x8_to_f16(v[u], h)) hflag_buf[(c >> 5) / RPP] = tag;
+      *reinterpret_cast<u32x4*>(dst) = h;
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = v[u];
+    }
+  }
+}
+
+template <int MT, int TR, int XP, int KP, int WR, bool H, typename RowPtr>
+__device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
+                                                   const uint8_t* const (&cptr)[TR],
+                                                   const uint8_t* const (&sptr)[TR],
+                                                   uint16_t* win, int* hflag, uint32_t* my,
+                                                   int part, int M, int64_t K, int s0, int S,
+                                                   RowPtr row_ptr) {
+  constexpr int RPP = WR * MT;              // window rows per part
+  constexpr int psz = RPP * kXWin;          // one part's rows
+  constexpr int wsz = KP * psz;             // one buffer
+  const int lane = threadIdx.x & 63, ln = lane & 15, q = lane >> 4;
+  const KParts me = kpart(s0, S, part, KP);
+  int xrow_off[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    xrow_off[mt] = part * psz + (WR == 8 ? min(ln, 7) : 16 * mt + ln) * kXWin + 64 * q;
+  const int L = (S + KP - 1) / KP;          // iterations (the longest part)
+  const int last = me.start + me.len - 1;
+  WStep<TR> b0, b1;
+  load_wcodes<TR>(b0, cptr, me.start);
+  u32x4 ph[TR], ph1[TR];
+  load_shalf<TR>(ph, sptr, me.start, 0, last);
+  load_shalf<TR>(ph1, sptr, me.start, 1, last);
+  u32x4 xv[XP];
+  xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, 0, row_ptr);
+  store_shalf<TR>(my, ph, 0);
+  store_shalf<TR>(my, ph1, 1);
+  bool on = true;
+  int fails = 0;
+  xwin_store_kp<H, XP, RPP>(win, hflag, on, xv, 0);
+  __syncthreads();
+  int i = 0, cur = 0;
+  auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
+    // fp16 unless a part of this buffer was marked at tag i: then the whole
+    // buffer is staged again in bf16 (workgroup-uniform, with a barrier)
+    bool f16 = false;
+    if (H && on) {
+      bool marked = false;
+#pragma unroll
+      for (int p = 0; p < KP; ++p)
+        marked = marked || __builtin_amdgcn_readfirstlane(hflag[cur * KP + p]) == i;
+      f16 = !marked;
+      if (marked) {
+        xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, i, row_ptr);
+        xwin_store_kp<false, XP, RPP>(win + cur * wsz, nullptr, false, xv, 0);
+        __syncthreads();
+        on = ++fails < 2;
+      }
+    }
+    xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, min(i + 1, L - 1), row_ptr);
+    load_wcodes<TR>(bn, cptr, min(me.start + i + 1, last));
+    const int j = i & 7;
+    const bool sh = j >= 6;
+    if (sh) load_shalf<TR>(ph, sptr, me.start + i + 8 - j, j - 6, last);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < me.len) {
+      read_sblock<TR>(bc, my, j);
+      const uint16_t* xl[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
+      if (f16)
+        compute_wstep<MT, TR, true>(acc, bc, xl);
+      else
+        compute_wstep<MT, TR, false>(acc, bc, xl);
+    }
+    xwin_store_kp<H, XP, RPP>(win + (cur ^ 1) * wsz, hflag + (cur ^ 1) * KP, on, xv, i + 1);
+    if (sh) store_shalf<TR>(my, ph, j - 6);
+    __syncthreads();
+    cur ^= 1;
+    return ++i >= L;
+  };
+  while (true) {
+    if (stage(b0, b1)) break;
+    if (stage(b1, b0)) break;
+  }
+}
+
+// Sum of the KP parts' accumulators in part order, through LDS `red` (every
+// wave of the workgroup calls it after the last barrier of the main loop).
+// On return the waves of part 0 hold the sums; the other waves' values are
+// undefined.  red holds (KP - 1) * G * TR * MT * 64 f32x4.
+template <int MT, int TR, int KP>
+__device__ __forceinline__ void gemv_kp_reduce(f32x4 (&acc)[TR][MT], f32x4* red, int part, int g,
+                                               int G) {
+  const int lane = threadIdx.x & 63;
+  auto slot = [&](int p, int t, int mt) { return (((p - 1) * G + g) * TR + t) * MT + mt; };
+  if (part > 0) {
+#pragma unroll
+    for (int t = 0; t < TR; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[slot(part, t, mt) * 64 + lane] = acc[t][mt];
+  }
+  __syncthreads();
+  if (part == 0) {
+    for (int p = 1; p < KP; ++p) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 v = red[slot(p, t, mt) * 64 + lane];
+          acc[t][mt][0] += v[0], acc[t][mt][1] += v[1], acc[t][mt][2] += v[2],
+              acc[t][mt][3] += v[3];
+        }
+    }
+  }
+}
+
 }  // namespace nvfp4

@@ -47,6 +47,7 @@ struct PlanOverride {
   int gemv_waves = -1;             // waves per workgroup
   int gemv_lds_kib = -1;           // LDS budget of the 4x4x4 kernel's staged activations
   int gemv_splits = -1;            // K parts across workgroups
+  int gemv_kparts = -1;            // K parts inside a workgroup (16x16 GEMV, K % 256 == 0)
   int w4a4_fuse = -1;              // W4A4 from bf16: quantize inside the kernel (1) or in a pass (0)
   int grouped_mfma_min_rows = -1;  // average rows per expert from which the grouped MFMA runs
 };
@@ -57,12 +58,13 @@ struct GemvPlan {
   int tr;  // 16-row weight tiles per wave
   int nw;  // waves per workgroup (each streams its own weight tiles)
   int z;   // split-K across workgroups (fp32 partials + reduce kernel)
+  int kp;  // K parts inside a workgroup (nw = tile groups * kp), summed in LDS
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus,
                    const PlanOverride& ov = PlanOverride{});
 // Whether the override's GEMV fields name a layout that exists for this M.
-bool gemv_override_valid(int64_t M, const PlanOverride& ov);
+bool gemv_override_valid(int64_t M, int64_t K, const PlanOverride& ov);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
 // fakequant: x is bf16 and every 16-element block is quantized to NVFP4 and
 // dequantized while it is staged (the W4A4 product with the activation

@@ -47,6 +47,12 @@ typedef struct {
     /* nvfp4_grouped_gemm: average rows per expert from which the MFMA tile
      * kernel replaces the weight-streaming grouped GEMV (default 32; >= 0). */
     int grouped_mfma_min_rows;
+    /* GEMV K parts inside one workgroup, summed in LDS (16x16 GEMV, K % 256
+     * == 0; gemv_waves = tile groups * parts).  Built layouts (tiles, waves,
+     * parts): one activation tile (M <= 16) (2,8,4) (2,8,2) (1,16,4) (1,8,2),
+     * and for M <= 8 also (2,16,8) (1,16,8) (2,8,8); two activation tiles
+     * (16 < M <= 32) (1,16,2). */
+    int gemv_kparts;
 } nvfp4_plan_t;
 
 /* Every field set to -1 (the library's own choice). */

@@ -363,3 +363,20 @@ def test_noalloc_validation(L):
     assert na(n_out=32) == INVALID
     # W4A4 at M = 8192: 80 MiB of dequantized activations alone
     assert na(a_dtype=2, a_scales=P, M=8192, N=256, K=5120, n_out=256) == WORKSPACE
+
+
+def test_kparts_plan_validation(L):
+    """A K-parts plan names a built layout, one activation tile, full 256-element
+    steps and at least one step per part; anything else is INVALID before any
+    HIP call."""
+    def gp(M=8, K=4096, **kw):
+        return L.nvfp4_gemm_planned(_plan(**kw), 0, P, NULL, M, 64, K, P2, P3, NULL, 64, 0, P4,
+                                    NULL, 0, NULL)
+    ok = dict(gemv_tiles=2, gemv_waves=8, gemv_kparts=4)
+    assert gp(K=4128, **ok) == INVALID           # K % 256 != 0
+    assert gp(K=768, **ok) == INVALID            # 3 steps, 4 parts
+    assert gp(M=3, **ok) == INVALID              # the 4x4x4-block GEMV takes M <= 4
+    assert gp(M=20, **ok) == INVALID             # two activation tiles
+    assert gp(gemv_tiles=2, gemv_waves=16, gemv_kparts=4) == INVALID   # no (2, 16, 4)
+    assert gp(M=12, gemv_tiles=2, gemv_waves=16, gemv_kparts=8) == INVALID  # 8 parts need M <= 8
+    assert (L.nvfp4_gemm_workspace_size_planned(_plan(**ok), 0, 8, 64, 4096, 64) == 0)

@@ -380,3 +380,71 @@ def test_split_k_part_counts(nv, orc, M, plan):
     got32 = _run(nv, x, w, out_f32=True, plan=_plan(plan))
     _assert_close(got, ref, what=f"{M}x{K}x{N} {plan}")
     _assert_close(got32, ref, out_f32=True, what=f"{M}x{K}x{N} {plan} fp32")
+
+
+KP_LAYOUTS = [(2, 8, 4), (2, 8, 2), (1, 16, 4), (1, 8, 2), (2, 16, 8), (1, 16, 8), (2, 8, 8)]
+
+
+@pytest.mark.parametrize("tiles,waves,parts", KP_LAYOUTS)
+@pytest.mark.parametrize("M,K,N", [(8, 2304, 700), (5, 4352, 333), (16, 1280, 1000),
+                                   (7, 5120, 40)])
+def test_kparts_layouts(nv, orc, M, K, N, tiles, waves, parts):
+    """K parts inside the workgroup (plan gemv_kparts): every built layout, part
+    lengths that do not divide the K steps evenly, ragged N (padding columns),
+    one to sixteen activation rows; bf16 and fp32 outputs within the GEMM
+    tolerance of the oracle, guarded outputs."""
+    if parts == 8 and M > 8:
+        pytest.skip("eight parts are built for 8-row windows (M <= 8) only")
+    helpers.announce(f"gemm kparts M={M} K={K} N={N} layout={tiles},{waves},{parts}")
+    rng = np.random.default_rng(M * 3 + K + N + parts)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    plan = {"gemv_tiles": tiles, "gemv_waves": waves, "gemv_kparts": parts}
+    _assert_close(_run(nv, x, w, plan=plan), ref, what=f"{M}x{K}x{N}")
+    _assert_close(_run(nv, x, w, out_f32=True, plan=plan), ref, out_f32=True,
+                  what=f"{M}x{K}x{N} fp32")
+
+
+@pytest.mark.parametrize("M,K,N", [(32, 2304, 700), (17, 4352, 333), (24, 512, 40)])
+def test_kparts_two_tiles(nv, orc, M, K, N):
+    """K parts with two activation tiles (1 tile per wave, 16 waves, 2 parts):
+    ragged M, N and part lengths; bf16 and fp32 outputs against the oracle."""
+    helpers.announce(f"gemm kparts two tiles M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + 5 * N)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    plan = {"gemv_tiles": 1, "gemv_waves": 16, "gemv_kparts": 2}
+    _assert_close(_run(nv, x, w, plan=plan), ref, what=f"{M}x{K}x{N}")
+    _assert_close(_run(nv, x, w, out_f32=True, plan=plan), ref, out_f32=True,
+                  what=f"{M}x{K}x{N} fp32")
+
+
+@pytest.mark.parametrize("tiles,waves,parts", [(2, 8, 4), (1, 16, 8)])
+def test_kparts_masked_outside_fp16_and_splits(nv, orc, tiles, waves, parts):
+    """K parts with a row mask, activations outside fp16 in some steps (the
+    whole window buffer is restaged in bf16 and the workgroup stops converting
+    after two), and K parts across workgroups as well (plan gemv_splits): the
+    fp32 partials of each workgroup are its parts' sum."""
+    helpers.announce(f"gemm kparts masked/outside fp16/splits layout={tiles},{waves},{parts}")
+    rng = np.random.default_rng(77 + parts)
+    M, K, N = 8, 4096, 3000
+    x = workloads.normal_bf16(rng, M, K)
+    x[0, 300] = 0x4880          # 2^18: beyond fp16's range
+    x[3, 1500] = 0x3380         # below fp16's precision for 8 bits
+    x[7, 4000] = 0x0005         # a bf16 subnormal
+    w = workloads.nvfp4_weight(rng, N, K)
+    idx = np.sort(rng.choice(N, 777, replace=False)).astype(np.int32)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx)
+    for z in (None, 2):
+        plan = {"gemv_tiles": tiles, "gemv_waves": waves, "gemv_kparts": parts}
+        if z:
+            plan["gemv_splits"] = z
+        _assert_close(_run(nv, x, w, row_idx=idx, plan=plan), ref, what=f"masked z={z}")
+    x2 = x.copy()
+    x2[1, ::256] = 0x3380       # every step: workgroups switch to bf16 for good
+    ref2 = orc.gemm_w4a16(x2, M, K, w.codes, w.scales)
+    _assert_close(_run(nv, x2, w, out_f32=True,
+                       plan={"gemv_tiles": tiles, "gemv_waves": waves, "gemv_kparts": parts}),
+                  ref2, out_f32=True, what="every step restaged")
