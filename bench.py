@@ -11,10 +11,11 @@ step is captured once as a HIP graph and replayed (as a serving engine replays
 its decode step); the same calls launched one by one give config.eager_GBs and
 the per-call event times of the roofline.
 
-Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies and
-the head in two copies; calls alternate copies and the masked head always
-reads the copy the full head did not just read, so no call re-reads weights
-that are still cached.
+Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies that
+calls alternate, and the head in three: the full-head calls alternate copies 0
+and 1, and the masked-head calls read copy 2, which no full-head call reads.
+Between two reads of one copy the step streams at least one other full head
+(715 MB, far more than the cache), so no call re-reads weights still cached.
 
 Also reported on the same JSON line:
   roofline      -- the decode GEMV kernel: algorithmic weight bytes per launch
@@ -104,7 +105,9 @@ class Decode:
         for (K, N) in shapes:
             w = wl.decode_weights(K, N)
             copies = [(dev_u8(w.codes), dev_u8(w.scales))]
-            copies.append((copies[0][0].clone(), copies[0][1].clone()))
+            n_copies = 3 if (K, N) == (wl.HIDDEN, wl.VOCAB) else 2
+            for _ in range(n_copies - 1):
+                copies.append((copies[0][0].clone(), copies[0][1].clone()))
             self.weights[(K, N)] = copies
             del w
         self.idx = dev_i32(wl.decode_masked_rows())
@@ -118,10 +121,9 @@ class Decode:
                 c = call_no % 2
                 self._add(f"M{M}_K{K}_N{N}", M, K, N, self.weights[(K, N)][c], None, N)
                 call_no += 1
-            # masked head: the copy the full head call of this M did not read
+            # masked head: its own copy, which no full-head call reads
             K, N = head
-            c_full = (call_no - 1) % 2
-            self._add(f"M{M}_masked_head", M, K, N, self.weights[head][1 - c_full], self.idx,
+            self._add(f"M{M}_masked_head", M, K, N, self.weights[head][2], self.idx,
                       self.idx.numel())
         torch.cuda.synchronize()
 
@@ -313,13 +315,8 @@ def cpu_baseline(target_s=15.0):
     }
 
 
-def secondary(nv, torch, helpers_dev, reps=3):
-    """Single-GPU timings of the other rows of the layer (GPU events)."""
-    import workloads as wl
-    dev_u8, dev_bf16, dev_i32 = helpers_dev
-    res = {}
-
-    def timeit(fn, n=reps, warm_s=0.03, timed_s=0.03):
+def _graph_timer(torch):
+    def timeit(fn, n=3, warm_s=0.03, timed_s=0.03):
         """Seconds per call: n calls captured in one HIP graph (so the host-side
         cost of the binding is not measured), replayed for ~warm_s of GPU time
         (the clocks settle under sustained load: a lone first call of the
@@ -351,9 +348,37 @@ def secondary(nv, torch, helpers_dev, reps=3):
         torch.cuda.synchronize()
         del g
         return a.elapsed_time(b) / (reps_t * n) / 1e3
+    return timeit
 
-    # prefill GEMM, M = 8192
-    for (K, N) in [(wl.HIDDEN, wl.MLP), (wl.MLP, wl.HIDDEN)]:
+
+def _row(value, unit, peak):
+    """A secondary row: the figure, its unit and its fraction of the MI355X
+    peak that bounds it (HBM 8 TB/s, or dense bf16 MFMA 2.5 PFLOP/s)."""
+    return {"value": round(value, 2), "unit": unit, "frac": round(value / peak, 4)}
+
+
+def _tf(flop, t):
+    return _row(flop / t / 1e12, "TFLOP/s", BF16_MFMA_PEAK_TFLOPS)
+
+
+def _gb(nbytes, t):
+    return _row(nbytes / t / 1e9, "GB/s", HBM_PEAK_GBS)
+
+
+SECONDARY_CASES = ["prefill_K5120", "prefill_K17408", "quantize", "w4a4", "w4a4_decode",
+                   "quantize_weight", "kv", "moe_T32", "moe_T4096"]
+
+
+def secondary(nv, torch, helpers_dev, cases=None):
+    """Single-GPU timings of the other rows of the layer, graph-replayed; each
+    with its roofline fraction.  `cases` selects a subset (profiling)."""
+    import workloads as wl
+    dev_u8, dev_bf16, dev_i32 = helpers_dev
+    timeit = _graph_timer(torch)
+    res = {}
+    cases = SECONDARY_CASES if cases is None else cases
+
+    def prefill(K, N):
         log(f"secondary: prefill K={K} N={N}")
         x, w = wl.prefill(K, N)
         xd, wc, ws = dev_bf16(x), dev_u8(w.codes), dev_u8(w.scales)
@@ -362,71 +387,179 @@ def secondary(nv, torch, helpers_dev, reps=3):
         wsz = nv.gemm_workspace_size(8192, N, K, N)
         wsb = torch.empty(max(wsz, 1), dtype=torch.uint8, device="cuda")
         t = timeit(lambda: nv.gemm(xd, wc, ws, out=out, workspace=wsb), n=1)
-        res[f"prefill_M8192_K{K}_N{N}_tflops"] = round(2 * 8192 * N * K / t / 1e12, 2)
-        del xd, wc, ws, out, wsb
-    # quantizer and W4A4 GEMM
-    log("secondary: quantize + W4A4")
-    x, w = wl.w4a4()
-    xd = dev_bf16(x)
-    t = timeit(lambda: nv.quantize(xd), n=20)
-    res["quantize_M512_K5120_GBs"] = round(512 * 5120 * (2 + 9 / 16) / t / 1e9, 2)
-    xq = dev_bf16(wl.normal_bf16(np.random.default_rng(0), 8192, 5120, 0.001))
-    t = timeit(lambda: nv.quantize(xq), n=20)
-    res["quantize_M8192_K5120_GBs"] = round(8192 * 5120 * (2 + 9 / 16) / t / 1e9, 2)
-    codes, scales = nv.quantize(xd)
-    wc, ws = dev_u8(w.codes), dev_u8(w.scales)
-    t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales))
-    res["w4a4_M512_N17408_K5120_tflops"] = round(2 * 512 * 17408 * 5120 / t / 1e12, 2)
-    # W4A4 from bf16 activations with the quantizer fused in (decode shape)
-    for M in (1, 8, 32):
-        xm = dev_bf16(wl.normal_bf16(np.random.default_rng(M), M, wl.HIDDEN, 0.001))
-        om = torch.empty((M, wl.MLP), dtype=torch.bfloat16, device="cuda")
-        t_f = timeit(lambda: nv.gemm_w4a4(xm, wc, ws, out=om), n=20)
+        res[f"prefill_M8192_K{K}_N{N}"] = _tf(2 * 8192 * N * K, t)
 
-        def unfused():
-            ac, as_ = nv.quantize(xm)
-            nv.gemm(ac, wc, ws, a_scales=as_, out=om)
-        t_u = timeit(unfused, n=20)
-        res[f"w4a4_fused_M{M}_K5120_N17408_us"] = round(t_f * 1e6, 2)
-        res[f"w4a4_quantize_then_gemm_M{M}_K5120_N17408_us"] = round(t_u * 1e6, 2)
-    del xd, xq, wc, ws
-    # two-level NVFP4: offline weight quantizer (amax pass + quantize pass)
-    log("secondary: offline weight quantizer")
-    wq = dev_bf16(wl.normal_bf16(np.random.default_rng(1), wl.MLP, wl.HIDDEN))
-    wqs = torch.empty(nv.lib().nvfp4_quantize_weight_workspace_size(wl.MLP, wl.HIDDEN),
-                      dtype=torch.uint8, device="cuda")
-    t = timeit(lambda: nv.quantize_weight(wq, workspace=wqs), n=10)
-    res["quantize_weight_N17408_K5120_GBs"] = round(
-        wl.MLP * wl.HIDDEN * (2 + 2 + 9 / 16) / t / 1e9, 1)   # two reads of bf16, codes + scales out
-    del wq, wqs
-    # FP8 E4M3 KV-cache codec: bytes moved (bf16 in + codes out; codes in + bf16 out)
-    log("secondary: KV cache store / load")
-    kw = wl.kv_store(8192)
-    kx, ksm = dev_bf16(kw.x), dev_i32(kw.slot_mapping)
-    kc = torch.zeros((kw.num_slots, wl.KV_W), dtype=torch.uint8, device="cuda")
-    t = timeit(lambda: nv.kv_store_e4m3(kx, ksm, kw.scale, kc), n=20)
-    res["kv_store_T8192_W1024_GBs"] = round(8192 * wl.KV_W * 3 / t / 1e9, 1)
-    cache, bt, lens, kscale = wl.kv_load(32, 4096)
-    kc2, kbt, kl = dev_u8(cache), dev_i32(bt), dev_i32(lens)
-    kout = torch.empty((32, 4096, wl.KV_W), dtype=torch.bfloat16, device="cuda")
-    t = timeit(lambda: nv.kv_load_e4m3(kc2, kbt, kl, wl.KV_PAGE, 4096, kscale, out=kout), n=10)
-    used = int(lens.sum()) * wl.KV_W
-    res["kv_load_B32_L4096_W1024_GBs"] = round((used * 3 + (32 * 4096 * wl.KV_W - used) * 2)
-                                               / t / 1e9, 1)
-    del kx, ksm, kc, kc2, kbt, kl, kout, cache
-    # MoE layer
+    if "prefill_K5120" in cases:
+        prefill(wl.HIDDEN, wl.MLP)
+    if "prefill_K17408" in cases:
+        prefill(wl.MLP, wl.HIDDEN)
+    if "quantize" in cases:
+        log("secondary: quantize")
+        for M in (512, 8192):
+            xq = dev_bf16(wl.normal_bf16(np.random.default_rng(0), M, wl.HIDDEN, 0.001))
+            t = timeit(lambda: nv.quantize(xq), n=20)
+            res[f"quantize_M{M}_K5120"] = _gb(M * wl.HIDDEN * (2 + 9 / 16), t)
+    if "w4a4" in cases:
+        # W4A4 from NVFP4 codes (dequantize pass + bf16 MFMA GEMM), and from bf16
+        # activations with the quantizer fused into the MFMA tile loads (fuse=1)
+        # or in one pass before the bf16-activation GEMM (fuse=0, the default)
+        log("secondary: W4A4")
+        _, w = wl.w4a4()
+        wc, ws = dev_u8(w.codes), dev_u8(w.scales)
+        for M in (512, 8192):
+            x = wl.normal_bf16(np.random.default_rng(0), M, wl.HIDDEN, 0.001)
+            xd = dev_bf16(x)
+            codes, scales = nv.quantize(xd)
+            out = torch.empty((M, wl.MLP), dtype=torch.bfloat16, device="cuda")
+            fl = 2 * M * wl.MLP * wl.HIDDEN
+            n = 3 if M == 512 else 1
+            t = timeit(lambda: nv.gemm(codes, wc, ws, a_scales=scales, out=out), n=n)
+            res[f"w4a4_codes_M{M}_N17408_K5120"] = _tf(fl, t)
+            for fuse in (0, 1):
+                pl = {"w4a4_fuse": fuse}
+                wsb = torch.empty(max(1, int(nv.lib().nvfp4_gemm_w4a4_bf16_workspace_size_planned(
+                    nv._plan_ref(pl), M, wl.MLP, wl.HIDDEN, wl.MLP))), dtype=torch.uint8,
+                    device="cuda")
+                t = timeit(lambda: nv.gemm_w4a4(xd, wc, ws, out=out, workspace=wsb, plan=pl), n=n)
+                res[f"w4a4_bf16_fuse{fuse}_M{M}_N17408_K5120"] = _tf(fl, t)
+            del xd, codes, scales, out
+    if "w4a4_decode" in cases:
+        log("secondary: W4A4 decode shapes")
+        _, w = wl.w4a4()
+        wc, ws = dev_u8(w.codes), dev_u8(w.scales)
+        wb = wl.MLP * wl.HIDDEN * 9 / 16
+        for M in (1, 8, 32):
+            xm = dev_bf16(wl.normal_bf16(np.random.default_rng(M), M, wl.HIDDEN, 0.001))
+            om = torch.empty((M, wl.MLP), dtype=torch.bfloat16, device="cuda")
+            t_f = timeit(lambda: nv.gemm_w4a4(xm, wc, ws, out=om), n=20)
+
+            def unfused():
+                ac, as_ = nv.quantize(xm)
+                nv.gemm(ac, wc, ws, a_scales=as_, out=om)
+            t_u = timeit(unfused, n=20)
+            res[f"w4a4_fused_M{M}_K5120_N17408"] = dict(_gb(wb, t_f), us=round(t_f * 1e6, 2))
+            res[f"w4a4_quantize_then_gemm_M{M}_K5120_N17408"] = dict(_gb(wb, t_u),
+                                                                    us=round(t_u * 1e6, 2))
+    if "quantize_weight" in cases:
+        log("secondary: offline weight quantizer")
+        wq = dev_bf16(wl.normal_bf16(np.random.default_rng(1), wl.MLP, wl.HIDDEN))
+        wqs = torch.empty(nv.lib().nvfp4_quantize_weight_workspace_size(wl.MLP, wl.HIDDEN),
+                          dtype=torch.uint8, device="cuda")
+        t = timeit(lambda: nv.quantize_weight(wq, workspace=wqs), n=10)
+        # two reads of the bf16 weights (amax pass, quantize pass), codes + scales out
+        res["quantize_weight_N17408_K5120"] = _gb(wl.MLP * wl.HIDDEN * (2 + 2 + 9 / 16), t)
+        del wq, wqs
+    if "kv" in cases:
+        log("secondary: KV cache store / load")
+        kw = wl.kv_store(8192)
+        kx, ksm = dev_bf16(kw.x), dev_i32(kw.slot_mapping)
+        kc = torch.zeros((kw.num_slots, wl.KV_W), dtype=torch.uint8, device="cuda")
+        t = timeit(lambda: nv.kv_store_e4m3(kx, ksm, kw.scale, kc), n=20)
+        res["kv_store_T8192_W1024"] = _gb(8192 * wl.KV_W * 3, t)
+        cache, bt, lens, kscale = wl.kv_load(32, 4096)
+        kc2, kbt, kl = dev_u8(cache), dev_i32(bt), dev_i32(lens)
+        kout = torch.empty((32, 4096, wl.KV_W), dtype=torch.bfloat16, device="cuda")
+        t = timeit(lambda: nv.kv_load_e4m3(kc2, kbt, kl, wl.KV_PAGE, 4096, kscale, out=kout),
+                   n=10)
+        used = int(lens.sum()) * wl.KV_W
+        res["kv_load_B32_L4096_W1024"] = _gb(used * 3 + (32 * 4096 * wl.KV_W - used) * 2, t)
+        del kx, ksm, kc, kc2, kbt, kl, kout, cache
     for T in (32, 4096):
+        if f"moe_T{T}" not in cases:
+            continue
         log(f"secondary: MoE T={T}")
         m = wl.moe(T)
-        args = (dev_bf16(m.x), dev_i32(m.ids), torch.from_numpy(m.gates).cuda(),
-                dev_u8(m.w1.codes), dev_u8(m.w1.scales), dev_u8(m.w2.codes), dev_u8(m.w2.scales))
-        t = timeit(lambda: nv.moe_layer(*args))
+        E, topk = 128, 8
+        R = T * topk
+        x, ids = dev_bf16(m.x), dev_i32(m.ids)
+        gates = torch.from_numpy(m.gates).cuda()
+        w1c, w1s = dev_u8(m.w1.codes), dev_u8(m.w1.scales)
+        w2c, w2s = dev_u8(m.w2.codes), dev_u8(m.w2.scales)
+        t = timeit(lambda: nv.moe_layer(x, ids, gates, w1c, w1s, w2c, w2s))
         touched = len(np.unique(m.ids))
-        if T == 32:
-            b = touched * (1536 * 2048 + 2048 * 768) * 9 // 16
-            res["moe_T32_weight_GBs"] = round(b / t / 1e9, 2)
-        res[f"moe_T{T}_tflops"] = round(2 * T * 8 * (1536 * 2048 + 2048 * 768) / t / 1e12, 3)
-        res[f"moe_T{T}_ms"] = round(t * 1e3, 3)
+        flop = 2 * R * (1536 * 2048 + 2048 * 768)
+        wbytes = touched * (1536 * 2048 + 2048 * 768) * 9 // 16
+        res[f"moe_T{T}_layer"] = dict(_tf(flop, t) if T > 32 else _gb(wbytes, t),
+                                      ms=round(t * 1e3, 4))
+        # the layer's steps one by one (each graph-replayed)
+        off, gat, slot, rg = nv.moe_align(ids, E, gates)
+        act = nv.grouped_gemm(x, gat, off, w1c, w1s, R, epilogue=nv.EPI_SWIGLU)
+        y = nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg)
+        steps = {
+            "align": (lambda: nv.moe_align(ids, E, gates), None),
+            "gate_up": (lambda: nv.grouped_gemm(x, gat, off, w1c, w1s, R, epilogue=nv.EPI_SWIGLU,
+                                                out=act), 2 * R * 1536 * 2048),
+            "down": (lambda: nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg, out=y),
+                     2 * R * 2048 * 768),
+            "combine": (lambda: nv.moe_combine(y, slot), None),
+        }
+        for name, (fn, fl) in steps.items():
+            ts = timeit(fn)
+            res[f"moe_T{T}_{name}_us"] = round(ts * 1e6, 2)
+            if fl and T > 32:
+                res[f"moe_T{T}_{name}"] = _tf(fl, ts)
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_configs(budget_s=4.0):
+    """The oracle (as it stands) beside the GPU on the other configurations, each
+    on a bounded, evenly spaced sample of its rows, scaled to the config's unit:
+    prefill and W4A4 on 256 of 8192 / 512 activation rows (all weight rows),
+    the quantizer on 512 rows, the MoE layer on 32 tokens (T = 32) and on 64 of
+    4096 tokens (T = 4096)."""
+    import oracle
+    import workloads as wl
+    res = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    for (K, N) in [(wl.HIDDEN, wl.MLP), (wl.MLP, wl.HIDDEN)]:
+        x, w = wl.prefill(K, N)
+        rows = np.linspace(0, 8191, 256).astype(np.int64)
+        # calibrate on 8 rows, then as many rows as fit the budget (<= 256)
+        t8 = timed(lambda: oracle.gemm_w4a16(np.ascontiguousarray(x[rows[:8]]), 8, K, w.codes,
+                                             w.scales))
+        n = int(min(256, max(8, 8 * budget_s / max(t8, 1e-3))))
+        sel = np.ascontiguousarray(x[rows[:n]])
+        t = timed(lambda: oracle.gemm_w4a16(sel, n, K, w.codes, w.scales))
+        res[f"prefill_M8192_K{K}_N{N}"] = {
+            "value": round(2 * n * N * K / t / 1e9, 3), "unit": "GFLOP/s",
+            "sample": f"{n} of 8192 rows (evenly spaced), all {N} weight rows: {t:.2f} s"}
+        del x, w
+    x, w = wl.w4a4()
+    t = timed(lambda: oracle.quantize(x, 512, wl.HIDDEN))
+    res["quantize_M512_K5120"] = {"value": round(512 * wl.HIDDEN * (2 + 9 / 16) / t / 1e9, 4),
+                                  "unit": "GB/s", "sample": f"all 512 rows: {t:.2f} s"}
+    ac, as_ = oracle.quantize(x, 512, wl.HIDDEN)
+    n = 32
+    t = timed(lambda: oracle.gemm_w4a4(np.ascontiguousarray(ac[:n]), np.ascontiguousarray(as_[:n]),
+                                       n, wl.HIDDEN, w.codes, w.scales))
+    res["w4a4_M512_N17408_K5120"] = {"value": round(2 * n * wl.MLP * wl.HIDDEN / t / 1e9, 3),
+                                     "unit": "GFLOP/s",
+                                     "sample": f"{n} of 512 rows, all weight rows: {t:.2f} s"}
+    for T, n_tok in ((32, 32), (4096, 64)):
+        m = wl.moe(T)
+        toks = np.linspace(0, T - 1, n_tok).astype(np.int64)
+        t = timed(lambda: oracle.moe_layer(np.ascontiguousarray(m.x[toks]),
+                                           np.ascontiguousarray(m.ids[toks]),
+                                           np.ascontiguousarray(m.gates[toks]), 128, 768,
+                                           m.w1.codes, m.w1.scales, m.w2.codes, m.w2.scales))
+        res[f"moe_T{T}_layer"] = {
+            "value": round(2 * n_tok * 8 * (1536 * 2048 + 2048 * 768) / t / 1e9, 3),
+            "unit": "GFLOP/s", "sample": f"{n_tok} of {T} tokens: {t:.2f} s"}
     return res
 
 
@@ -440,6 +573,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--case", action="append", choices=SECONDARY_CASES,
+                    help="run only these secondary rows (no decode set); for profiling one "
+                         "kernel at a time")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: the NVFP4 layer is built for a single GPU "
@@ -462,6 +598,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
     hd = (dev_u8, dev_bf16, dev_i32)
+    if args.case:
+        print(json.dumps({"cases": secondary(nv, torch, hd, cases=args.case)}), flush=True)
+        return
     log("generating decode workload")
     dec = Decode(nv, torch, hd)
     # the clocks settle only after some sustained load: run the step for ~0.2 s
@@ -506,7 +645,13 @@ def main():
     sec = None
     if not args.no_secondary:
         sec = secondary(nv, torch, hd)
-    cpu = None if args.no_cpu else cpu_baseline()
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline()
+        cpu["cpu_model"] = cpu_model()
+        if not args.no_secondary:
+            log("oracle on the other configurations (bounded samples)")
+            cpu["configs"] = cpu_configs()
 
     line = {
         "metric": METRIC,

@@ -96,31 +96,30 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   GemmSrc src;
   // (K ranges of a split start at k_lo: a multiple of 64, so pointers stay aligned)
   const uint8_t* a_tile_base = reinterpret_cast<const uint8_t*>(g.a + m0 * K + k_lo);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t n = min(n0 + (t >> 1) + 128 * q, g.N - 1);
+  {
+    const int64_t n = min(n0 + (t >> 1), g.N - 1);
     const int64_t wr = g.row_idx ? (int64_t)g.row_idx[n] : n;
-    gemm_src_nvfp4_row(src.wc[q], src.ws[q], g.wc + k_lo / 2, g.ws + k_lo / 16, wr, K);
+    gemm_src_nvfp4_row(src.wc, src.ws, g.wc + k_lo / 2, g.ws + k_lo / 16, wr, K);
     if constexpr (A_FQ) {
-      const int64_t ar = min(m0 + (t >> 1) + 128 * q, g.M - 1);
-      src.ar[q] = g.a + ar * K + k_lo + 32 * (t & 1);
+      const int64_t ar = min(m0 + (t >> 1), g.M - 1);
+      src.ar = g.a + ar * K + k_lo + 32 * (t & 1);
     }
   }
   if constexpr (!A_FQ)
     gemm_src_bf16(src, [&](int r) { return min(m0 + r, g.M - 1) - m0; }, K);
 
-  f32x16 acc[4][4];
+  f32x16 acc[kXBlocks][kWBlocks];
   gemm_zero_acc(acc);
   gemm_mainloop<A_FQ>(acc, lds, src, a_tile_base, k_len);
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
-  // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's quarter.
+  // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's part.
   if (part) {  // fp32 partial of this K part, tile-local [256][256]
     float* dst = g.partial + ((int64_t)tail * g.splits + z) * (BM * BN);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kXBlocks; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kWBlocks; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<f32x4*>(dst + gemm_tile_row(i) * BN + gemm_tile_col(j, q)) =
@@ -132,11 +131,11 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   const float alpha = scaled ? alpha_of(g.ga, g.gw) : 1.0f;
   const bool vec = (g.N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kXBlocks; ++i) {
     const int64_t row = m0 + gemm_tile_row(i);
     if (row >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kWBlocks; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t col = n0 + gemm_tile_col(j, q);

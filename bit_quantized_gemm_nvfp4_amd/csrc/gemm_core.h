@@ -1,9 +1,13 @@
 // gemm_core.h -- the 256 x 256 MFMA tile of the NVFP4 GEMM kernels (internal):
 // the large-M linear layer (gemm.hip) and the grouped expert GEMM (moe.hip).
 //
-// A workgroup of 4 waves computes a 256 x 256 tile of y = a . W^T; each wave a
-// 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (accumulators
-// in AGPRs).  K advances 64 elements per step through a double buffer in LDS:
+// A workgroup of 8 waves (two per SIMD) computes a 256 x 256 tile of
+// y = a . W^T; wave w a 128 (weight rows, wn = w & 1) x 64 (activation rows,
+// wm = w >> 1) part as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (accumulators
+// in AGPRs).  Two waves share each SIMD, so one wave's MFMAs keep the matrix
+// core busy while the other waits on LDS, global loads or the barrier (with
+// one 128 x 128 wave per SIMD, measured: MFMA busy 51%, 39% of wave cycles
+// waiting).  K advances 64 elements per step through a double buffer in LDS:
 //   A tile  [256 rows][64] bf16 (32 KB): bf16 activations copied global->LDS
 //           (global_load_lds_dwordx4), or (A_FQ: the W4A4 product from bf16
 //           activations) loaded through registers, quantized to NVFP4 and
@@ -27,15 +31,15 @@
 // Pipeline: the weight (and A_FQ activation) loads of step s+2 are issued at
 // the start of step s into one of two register sets, the bf16 activation copy
 // of step s+1 straight into the idle LDS buffer; the other register set (step
-// s+1) is decoded into the idle buffer while step s is computed.  A step is 16
-// chunks (substep kk = 0..3, accumulator row i = 0..3): chunk (kk, i) issues
-// the 4 MFMAs of row i, reads fragments x[i], w[i] of substep kk+1 and writes
-// pieces of the next tile; scheduling barriers keep that interleave.  One
-// LDS-only workgroup barrier per step, between substeps 2 and 3.
+// s+1) is decoded into the idle buffer while step s is computed.  A step is 8
+// chunks (substep kk = 0..3, activation block i = 0..1): chunk (kk, i) issues
+// the 4 MFMAs of block i, reads fragments of substep kk+1 and writes pieces of
+// the next tile; scheduling barriers keep that interleave.  One LDS-only
+// workgroup barrier per step, between substeps 2 and 3.
 //
 // The weight tile is the MFMA's A operand and the activation tile its B
 // operand, so an accumulator block holds y^T: lane l has output row l % 32 and
-// 4 consecutive output columns per register group (gemm_tile_acc).
+// 4 consecutive output columns per register group (gemm_tile_row/col).
 #pragma once
 
 #include "device.h"
@@ -44,7 +48,9 @@
 namespace nvfp4 {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;
+constexpr int kXBlocks = 2;  // 32-row activation blocks per wave
+constexpr int kWBlocks = 4;  // 32-row weight blocks per wave
 constexpr uint32_t kTileBytes = BM * BK * 2;  // one bf16 operand tile (32 KB)
 constexpr uint32_t kBOffset = 2 * kTileBytes;  // B buffers follow both A buffers
 constexpr uint32_t kLdsBytes = 4 * kTileBytes;
@@ -59,12 +65,12 @@ __device__ __forceinline__ T& lds_ref(char* lds, uint32_t off) {
 
 // Per-lane LDS byte offsets.  With r = lane % 32, h = lane / 32 and
 // g = h ^ f(r): fragment (substep kk, block i) of the wave's activation rows
-// wm*128 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
+// wm*64 + 32 i + r sits at piece (2kk + h) ^ f(row) = 2 (kk ^ 2(i&1)) ^ g, so
 // it is rd_x[kk ^ 2(i&1)] + 32 KB * buffer + 4096 i (likewise rd_w for the
-// weight rows wn*128 + ...).  A row write of a thread's half (row t/2 + 128 q,
+// weight rows wn*128 + 32 j + r).  The row write of a thread's half (row t/2,
 // piece 4 (t&1) + j) is wr_w[j] (weights) or wr_na[j] (A_FQ activations) +
-// 32 KB * buffer + 16384 q.  (Immediate offsets of LDS instructions stop at
-// 64 KB, so the B-tile base is part of the registers.)
+// 32 KB * buffer.  (Immediate offsets of LDS instructions stop at 64 KB, so
+// the B-tile base is part of the registers.)
 struct LdsOffsets {
   uint32_t rd_x[4], rd_w[4];
   uint32_t wr_w[4], wr_na[4];
@@ -76,7 +82,7 @@ __device__ __forceinline__ LdsOffsets lds_offsets(int wm, int wn) {
   const uint32_t g = (h ^ swz_f(r)) & 7u;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    o.rd_x[kk] = (wm * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
+    o.rd_x[kk] = (wm * 64 + r) * 128 + (((2u * kk) ^ g) << 4);
     o.rd_w[kk] = kBOffset + (wn * 128 + r) * 128 + (((2u * kk) ^ g) << 4);
   }
   const uint32_t fw = ((t >> 1) ^ (t >> 4)) & 7u, hh = t & 1;
@@ -93,11 +99,11 @@ __device__ __forceinline__ LdsOffsets lds_offsets(int wm, int wn) {
 // re-read from inside the row and zeroed when the set is written to LDS, so no
 // wait for the loads is needed before then.
 struct Nvfp4Rows {
-  u32x4 c[2];     // codes of half (t & 1) of tile rows t/2 and 128 + t/2
-  uint32_t s[2];  // their two E4M3 scale bytes (one 16-bit load each)
+  u32x4 c;     // codes of half (t & 1) of tile row t/2
+  uint32_t s;  // its two E4M3 scale bytes (one 16-bit load)
 };
 struct Bf16Rows {
-  u32x4 v[2][4];  // half (t & 1) of tile rows t/2 and 128 + t/2: 32 bf16 each
+  u32x4 v[4];  // half (t & 1) of tile row t/2: 32 bf16
 };
 template <bool A_FQ>
 struct GemmLoad;
@@ -112,40 +118,34 @@ struct GemmLoad<true> {
 };
 
 // Where a thread loads from: bf16 activations as byte offsets (32-bit) from a
-// base pointer at k = 0 (see dma_a_tile); NVFP4 weight rows as pointers to
-// this lane's half of rows t/2 and 128 + t/2 at k = 0 (gemm_src_nvfp4_row);
-// A_FQ activation rows as pointers to this lane's half of those rows.
+// base pointer at k = 0 (see dma_a_tile); its NVFP4 weight row as pointers to
+// this lane's half of row t/2 at k = 0 (gemm_src_nvfp4_row); an A_FQ
+// activation row as a pointer to this lane's half of row t/2.
 struct GemmSrc {
-  uint32_t a_off[8];
-  uint32_t a_back[2];
-  const uint16_t* ar[2];
-  const uint8_t* wc[2];
-  const uint8_t* ws[2];
+  uint32_t a_off[4];
+  uint32_t a_back[4];
+  const uint16_t* ar;
+  const uint8_t* wc;
+  const uint8_t* ws;
 };
 
-__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* const (&c)[2],
-                                                const uint8_t* const (&s)[2], int64_t k0,
-                                                bool kfull) {
+__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* c, const uint8_t* s,
+                                                int64_t k0, bool kfull) {
   const int hh = threadIdx.x & 1;
   const int64_t coff = k0 / 2 - (kfull ? 0 : 16 * hh);
   const int64_t soff = k0 / 16 - (kfull ? 0 : 2 * hh);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    R.c[q] = *reinterpret_cast<const u32x4*>(c[q] + coff);
-    R.s[q] = *reinterpret_cast<const uint16_t*>(s[q] + soff);
-  }
+  R.c = *reinterpret_cast<const u32x4*>(c + coff);
+  R.s = *reinterpret_cast<const uint16_t*>(s + soff);
 }
 
-// A_FQ: 32 bf16 activations of this lane's half of each of its two rows (a
-// partial last step re-reads the first half, as load_nvfp4_rows does).
-__device__ __forceinline__ void load_bf16_rows(Bf16Rows& R, const uint16_t* const (&a)[2],
-                                               int64_t k0, bool kfull) {
+// A_FQ: 32 bf16 activations of this lane's half of its row (a partial last
+// step re-reads the first half, as load_nvfp4_rows does).
+__device__ __forceinline__ void load_bf16_rows(Bf16Rows& R, const uint16_t* a, int64_t k0,
+                                               bool kfull) {
   const int hh = threadIdx.x & 1;
   const int64_t off = k0 - (kfull ? 0 : 32 * hh);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) R.v[q][j] = *reinterpret_cast<const u32x4*>(a[q] + off + 8 * j);
+  for (int j = 0; j < 4; ++j) R.v[j] = *reinterpret_cast<const u32x4*>(a + off + 8 * j);
 }
 
 template <bool A_FQ>
@@ -158,9 +158,9 @@ __device__ __forceinline__ void gemm_load(GemmLoad<A_FQ>& L, const GemmSrc& src,
 
 // bf16 activation tile of the step at k0 -> LDS A buffer at `dst`, straight
 // from global memory (global_load_lds_dwordx4: lane l of a load lands at the
-// wave's LDS base + 16 l).  Wave w fills rows 64 w .. 64 w + 63, eight rows
-// (1 KB of LDS) per load; lane l takes row 8 i + l/8 of its band and physical
-// piece l % 8, i.e. logical piece (l % 8) ^ f(row) = (l % 8) ^ (l / 8) ^ i.
+// wave's LDS base + 16 l).  Wave w fills rows 32 w .. 32 w + 31, eight rows
+// (1 KB of LDS) per load; lane l takes row 32 w + 8 i + l/8 and physical piece
+// l % 8, i.e. logical piece (l % 8) ^ f(row) = (l % 8) ^ (l / 8) ^ ((4w + i) & 7).
 // On a partial last step (K % 64 == 32) logical pieces 4..7 re-read pieces
 // 0..3: those k have zero weights, so the products vanish.
 __device__ __forceinline__ void dma_a_tile(char* dst, const GemmSrc& src,
@@ -169,66 +169,75 @@ __device__ __forceinline__ void dma_a_tile(char* dst, const GemmSrc& src,
   const int wave = threadIdx.x >> 6;
   const uint32_t keep = kfull ? 0u : ~0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint8_t* gp = base + (src.a_off[i] - (src.a_back[(i >> 2) & 1] & keep));
-    __builtin_amdgcn_global_load_lds(gp, dst + (64 * wave + 8 * i) * 128, 16, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* gp = base + (src.a_off[i] - (src.a_back[i] & keep));
+    __builtin_amdgcn_global_load_lds(gp, dst + (32 * wave + 8 * i) * 128, 16, 0, 0);
   }
 }
 
-// Piece j (0..3) of this thread's half of NVFP4 tile row t/2 + 128 q -> 8
-// exact bf16 values.  A block at or past `kval` (the valid elements of the
-// step, 0..64, a multiple of 32) gets scale 0; its codes are finite, so it is
-// written as zeros.
+// Piece j (0..3) of this thread's half of NVFP4 tile row t/2 -> 8 exact bf16
+// values.  A block at or past `kval` (the valid elements of the step, 0..64, a
+// multiple of 32) gets scale 0; its codes are finite, so it is written as
+// zeros.
 __device__ __forceinline__ void store_nvfp4_piece(char* lds, uint32_t off, const Nvfp4Rows& R,
-                                                  int q, int j, int kval) {
+                                                  int j, int kval) {
   const int p = 4 * (threadIdx.x & 1) + j;
-  const float s_blk = (j >> 1) ? e4m3_to_f32<1>(R.s[q]) : e4m3_to_f32<0>(R.s[q]);
+  const float s_blk = (j >> 1) ? e4m3_to_f32<1>(R.s) : e4m3_to_f32<0>(R.s);
   const float s = 16 * (p >> 1) < kval ? s_blk : 0.f;
-  lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[q][j], s);
+  lds_ref<u32x4>(lds, off) = dequant8_bf16(R.c[j], s);
 }
 
-// A_FQ: piece j (0..3) of this thread's half of activation tile row t/2 + 128 q,
+// A_FQ: piece j (0..3) of this thread's half of activation tile row t/2,
 // quantized to NVFP4 with its 16-element block (pieces j and j ^ 1, both in
 // this lane) and dequantized: exactly nvfp4_quantize then nvfp4_dequantize.  A
 // block at or past `kval` is written as zeros.
-__device__ __forceinline__ void store_fq_piece(char* lds, uint32_t off, const Bf16Rows& R, int q,
-                                               int j, int kval) {
+__device__ __forceinline__ void store_fq_piece(char* lds, uint32_t off, const Bf16Rows& R, int j,
+                                               int kval) {
   const int p = 4 * (threadIdx.x & 1) + j;
   const u32x4 z = {0u, 0u, 0u, 0u};
   if (16 * (p >> 1) >= kval) {
     lds_ref<u32x4>(lds, off) = z;
     return;
   }
-  const uint32_t amax = max(piece_amax_bits(R.v[q][j]), piece_amax_bits(R.v[q][j ^ 1]));
-  lds_ref<u32x4>(lds, off) =
-      fakequant_with(R.v[q][j], scale_code_from_amax(bf16_bits_to_f32(amax)));
+  const uint32_t amax = max(piece_amax_bits(R.v[j]), piece_amax_bits(R.v[j ^ 1]));
+  lds_ref<u32x4>(lds, off) = fakequant_with(R.v[j], scale_code_from_amax(bf16_bits_to_f32(amax)));
 }
 
-// Piece c of writing a loaded set to LDS buffer `buf`: weight pieces 0..7,
-// then (A_FQ only) activation pieces 8..15.
+// Piece c of writing a loaded set to LDS buffer `buf`: weight pieces 0..3,
+// then (A_FQ only) activation pieces 4..7.
 template <bool A_FQ>
 __device__ __forceinline__ void gemm_store_piece(char* lds, const LdsOffsets& o, uint32_t buf,
                                                  const GemmLoad<A_FQ>& L, int c, int kval) {
-  const int q = (c & 7) >> 2, j = c & 3;
-  if (c < 8) {
-    store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes + q * 16384, L.w, q, j, kval);
+  const int j = c & 3;
+  if (c < 4) {
+    store_nvfp4_piece(lds, o.wr_w[j] + buf * kTileBytes, L.w, j, kval);
   } else if constexpr (A_FQ) {
-    store_fq_piece(lds, o.wr_na[j] + buf * kTileBytes + q * 16384, L.a, q, j, kval);
+    store_fq_piece(lds, o.wr_na[j] + buf * kTileBytes, L.a, j, kval);
   }
 }
 
 struct Frags {
-  u32x4 w[4];  // weight rows (MFMA A operand), 4 blocks of 32
-  u32x4 x[4];  // activation rows (MFMA B operand), 4 blocks of 32
+  u32x4 w[kWBlocks];  // weight rows (MFMA A operand), 4 blocks of 32
+  u32x4 x[kXBlocks];  // activation rows (MFMA B operand), 2 blocks of 32
 };
 
 // Operand layout (lane l): A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32],
 // i.e. both read row l%32 of their tile block, piece 2*kk + l/32 (substep kk).
+__device__ __forceinline__ void read_x(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
+                                       int kk, int i) {
+  f.x[i] = lds_ref<const u32x4>(lds, o.rd_x[kk ^ (2 * (i & 1))] + buf * kTileBytes + i * 4096);
+}
+__device__ __forceinline__ void read_w(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
+                                       int kk, int j) {
+  f.w[j] = lds_ref<const u32x4>(lds, o.rd_w[kk ^ (2 * (j & 1))] + buf * kTileBytes + j * 4096);
+}
+// The fragments chunk i (0, 1) of a substep reads for its successor: x[i],
+// w[2i], w[2i+1].
 __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
                                           int kk, int i) {
-  const int kq = kk ^ (2 * (i & 1));
-  f.x[i] = lds_ref<const u32x4>(lds, o.rd_x[kq] + buf * kTileBytes + i * 4096);
-  f.w[i] = lds_ref<const u32x4>(lds, o.rd_w[kq] + buf * kTileBytes + i * 4096);
+  read_x(f, lds, o, buf, kk, i);
+  read_w(f, lds, o, buf, kk, 2 * i);
+  read_w(f, lds, o, buf, kk, 2 * i + 1);
 }
 
 // One 64-element step on LDS buffer `cur` while set L is decoded into buffer
@@ -236,29 +245,32 @@ __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets&
 // read the fragments of the next substep and write the pieces of the next
 // tile; then the workgroup barrier publishes `nxt`, and substep 3 reads the
 // next step's substep-0 fragments from it into f[0] while its MFMAs run, so no
-// fragment read is left exposed behind the barrier.
+// fragment read is left exposed behind the barrier.  (Chunk i of a substep
+// uses all four weight fragments of the substep: its successor's fragments
+// go to the other set.)
 template <bool A_FQ>
-__device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], char* lds,
-                                          const LdsOffsets& o, uint32_t cur, uint32_t nxt,
-                                          const GemmLoad<A_FQ>& L, int kval) {
-  constexpr int kPieces = A_FQ ? 16 : 8;
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[kXBlocks][kWBlocks], Frags (&f)[2],
+                                          char* lds, const LdsOffsets& o, uint32_t cur,
+                                          uint32_t nxt, const GemmLoad<A_FQ>& L, int kval) {
+  constexpr int kPieces = A_FQ ? 8 : 4;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk == 3) lds_barrier<A_FQ ? -1 : 0>();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kXBlocks; ++i) {
       if (kk < 3)
         read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
       else
         read_frag(f[0], lds, o, nxt, 0, i);
-      const int c = 4 * kk + i;  // chunk 0..11 carries pieces c and c + 12
+      const int c = 2 * kk + i;  // chunk 0..5 carries pieces c and c + 6
       if (kk < 3) {
         if (c < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c, kval);
-        if (c + 12 < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c + 12, kval);
+        if (c + 6 < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c + 6, kval);
       }
       const Frags& fc = f[kk & 1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
+      for (int j = 0; j < kWBlocks; ++j)
+        acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -266,21 +278,21 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[4][4], Frags (&f)[2], ch
 
 // Sources of the tile's rows for this thread.  Activation rows: abs_row(t)
 // gives the global row (clamped to a valid one) of tile row t for t < 256;
-// bf16 offsets are relative to `a_base`.  Weight and NVFP4 activation rows:
-// the pointer to this lane's half of the row at k = 0.
+// bf16 offsets are relative to `a_base`.  Weight and A_FQ activation rows: the
+// pointer to this lane's half of the row at k = 0.
 template <typename ARow>
 __device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_t K) {
   const int t = threadIdx.x;
-  const int lw = t & 63, band = 64 * (t >> 6);
+  const int lw = t & 63, wave = t >> 6, band = 32 * wave;
   const uint32_t lp = (uint32_t)((lw & 7) ^ (lw >> 3));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int64_t r = abs_row(band + 8 * i + (lw >> 3));
-    src.a_off[i] = (uint32_t)((r * K + 8 * ((lp ^ i) & 7)) * 2);
+    const uint32_t piece = (lp ^ (uint32_t)(4 * wave + i)) & 7u;  // logical piece
+    src.a_off[i] = (uint32_t)((r * K + 8 * piece) * 2);
+    // partial step: logical pieces 4..7 step back 32 elements
+    src.a_back[i] = (piece & 4) ? 64u : 0u;
   }
-  // partial step: logical pieces 4..7 step back 32 elements (bit 2 of lp ^ i)
-  src.a_back[0] = (lp & 4) ? 64u : 0u;
-  src.a_back[1] = (lp & 4) ? 0u : 64u;
 }
 
 __device__ __forceinline__ void gemm_src_nvfp4_row(const uint8_t*& c, const uint8_t*& s,
@@ -291,11 +303,11 @@ __device__ __forceinline__ void gemm_src_nvfp4_row(const uint8_t*& c, const uint
   s = scales + row * (K / 16) + 2 * hh;
 }
 
-__device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[kXBlocks][kWBlocks]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kXBlocks; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWBlocks; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
@@ -303,8 +315,9 @@ __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[4][4]) {
 // The whole K loop of one tile: acc += a_tile . w_tile^T.  `lds` is the
 // kLdsBytes of dynamic LDS; every thread of the workgroup calls it.
 template <bool A_FQ>
-__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, const GemmSrc& src,
-                                              const uint8_t* a_tile_base, int64_t K) {
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
+                                              const GemmSrc& src, const uint8_t* a_tile_base,
+                                              int64_t K) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int steps = (int)((K + BK - 1) / BK);
@@ -333,10 +346,10 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, co
   gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(0));
   gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(1));
 #pragma unroll
-  for (int c = 0; c < 16; ++c) gemm_store_piece<A_FQ>(lds, o, 0, L0, c, kval(0));
+  for (int c = 0; c < 8; ++c) gemm_store_piece<A_FQ>(lds, o, 0, L0, c, kval(0));
   lds_barrier<A_FQ ? -1 : 0>();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) read_frag(f[0], lds, o, 0, 0, i);
+  for (int i = 0; i < kXBlocks; ++i) read_frag(f[0], lds, o, 0, 0, i);
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
   // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
   // written during the last step is not read.  The scheduling barriers keep
@@ -353,14 +366,13 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], char* lds, co
     __builtin_amdgcn_sched_barrier(0);
     gemm_step<A_FQ>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
   }
-
 }
 
 // Output coordinates of accumulator register e of acc[i][j] in this lane:
-// tile row wm*128 + i*32 + l%32, tile column wn*128 + j*32 + 8*(e/4) +
+// tile row wm*64 + i*32 + l%32, tile column wn*128 + j*32 + 8*(e/4) +
 // 4*(l/32) + e%4 (registers 4q .. 4q+3 are 4 consecutive columns).
 __device__ __forceinline__ int gemm_tile_row(int i) {
-  return ((threadIdx.x >> 6) >> 1) * 128 + i * 32 + (threadIdx.x & 31);
+  return ((threadIdx.x >> 6) >> 1) * 64 + i * 32 + (threadIdx.x & 31);
 }
 __device__ __forceinline__ int gemm_tile_col(int j, int q) {
   return ((threadIdx.x >> 6) & 1) * 128 + j * 32 + 8 * q + 4 * ((threadIdx.x & 63) >> 5);

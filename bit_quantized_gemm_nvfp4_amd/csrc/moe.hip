@@ -323,26 +323,26 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   }, K);
   const uint8_t* we_c = g.wc + (int64_t)e * N * (K / 2);
   const uint8_t* we_s = g.ws + (int64_t)e * N * (K / 16);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int u = t >> 1;  // tile row u + 128 q
+  {
+    const int row = t >> 1;  // tile row u + 128 q
+    const int q = row >> 7, u = row & 127;
     int64_t n;
     if (g.swiglu) {
       const int64_t o = min((int64_t)tn * 128 + q * 64 + (u & 63), half_n - 1);
       n = u < 64 ? o : half_n + o;
     } else {
-      n = min((int64_t)tn * BN + u + 128 * q, N - 1);
+      n = min((int64_t)tn * BN + row, N - 1);
     }
-    gemm_src_nvfp4_row(src.wc[q], src.ws[q], we_c, we_s, n, K);
+    gemm_src_nvfp4_row(src.wc, src.ws, we_c, we_s, n, K);
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[kXBlocks][kWBlocks];
   gemm_zero_acc(acc);
   gemm_mainloop<false>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K);
 
   const int wn = (t >> 6) & 1, h = (t & 63) >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kXBlocks; ++i) {
     const int tr = gemm_tile_row(i);
     if (tr >= rows) continue;
     const int64_t row = r0 + tr;
