@@ -93,12 +93,14 @@ def lib():
         L.oracle_moe_align.argtypes = [_I32, _i64, _i64, _i64, _I32, _I32, _I32]
         L.oracle_moe_align.restype = ctypes.c_int
         L.oracle_grouped_gemm.argtypes = [_U16, _i64, _nullable(_I32), _I32, _i64, _i64, _i64,
-                                          _U8, _U8, _nullable(_F32), ctypes.c_int, _F64]
+                                          _U8, _U8, _nullable(_F32), _nullable(_F32),
+                                          ctypes.c_int, _F64]
         L.oracle_grouped_gemm.restype = None
         L.oracle_moe_combine.argtypes = [_U16, _I32, _i64, _i64, _i64, _F64]
         L.oracle_moe_combine.restype = None
         L.oracle_moe_layer.argtypes = [_U16, _i64, _i64, _I32, _F32, _i64, _i64, _i64,
-                                       _U8, _U8, _U8, _U8, _F64]
+                                       _U8, _U8, _U8, _U8, _nullable(_F32), _nullable(_F32),
+                                       _F64]
         L.oracle_moe_layer.restype = None
         L.oracle_topk.argtypes = [_F64, _i64, _i64, _i64, _nullable(_I32), _F64, _I32]
         L.oracle_topk.restype = None
@@ -231,13 +233,19 @@ def moe_align(topk_ids, E: int):
 
 
 def grouped_gemm(a_bits, K: int, gather_idx, offsets, E: int, R: int, N: int, w_codes,
-                 w_scales, row_scale=None, epilogue: int = 0):
+                 w_scales, row_scale=None, epilogue: int = 0, w_global=None):
+    """Grouped GEMM over experts; w_global (fp32 [E]) is the per-expert global
+    scale of two-level weights (None: 1)."""
     width = N // 2 if epilogue == 1 else N
     out = np.empty((R, width), dtype=np.float64)
     gi = None if gather_idx is None else _c(gather_idx, np.int32)
     rs = None if row_scale is None else _c(row_scale, np.float32)
+    wg = None if w_global is None else _c(w_global, np.float32)
+    if wg is not None and wg.shape != (E,):
+        raise ValueError("w_global must hold one scale per expert")
     lib().oracle_grouped_gemm(_c(a_bits, np.uint16), K, gi, _c(offsets, np.int32), E, R, N,
-                              _c(w_codes, np.uint8), _c(w_scales, np.uint8), rs, epilogue, out)
+                              _c(w_codes, np.uint8), _c(w_scales, np.uint8), wg, rs, epilogue,
+                              out)
     return out
 
 
@@ -247,14 +255,22 @@ def moe_combine(y_bits, slot_pos, T: int, topk: int, H: int):
     return out
 
 
-def moe_layer(x_bits, ids, gates, E: int, I: int, w1_codes, w1_scales, w2_codes, w2_scales):
+def moe_layer(x_bits, ids, gates, E: int, I: int, w1_codes, w1_scales, w2_codes, w2_scales,
+              w1_global=None, w2_global=None):
+    """The routed-expert layer token by token; w1_global / w2_global (fp32 [E])
+    are the per-expert global scales of two-level weights (None: 1)."""
     x = _c(x_bits, np.uint16)
     T, H = x.shape
     topk = np.asarray(ids).shape[1]
     out = np.empty((T, H), dtype=np.float64)
+    g1 = None if w1_global is None else _c(w1_global, np.float32)
+    g2 = None if w2_global is None else _c(w2_global, np.float32)
+    for g in (g1, g2):
+        if g is not None and g.shape != (E,):
+            raise ValueError("global scales must hold one scale per expert")
     lib().oracle_moe_layer(x, T, H, _c(ids, np.int32), _c(gates, np.float32), topk, E, I,
                            _c(w1_codes, np.uint8), _c(w1_scales, np.uint8),
-                           _c(w2_codes, np.uint8), _c(w2_scales, np.uint8), out)
+                           _c(w2_codes, np.uint8), _c(w2_scales, np.uint8), g1, g2, out)
     return out
 
 

@@ -443,12 +443,17 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  *   epi == 1 (gated, reading of a fused gate+up weight: first half of the
  *            rows is the gate, second half the up projection):
  *            out[r][i] = silu(h[i]) * h[i + N/2],  i < N/2
- * then, if row_scale, out[r][.] *= row_scale[r].  out is fp64 (unrounded),
+ * Two-level weights (reading of [P4] section 1: the deployed MoE checkpoints
+ * come from NVFP4 quantization tools, whose tensors carry one fp32 global
+ * scale each): if w_global (fp32 [E]) is given, every h[n] of expert e is
+ * multiplied by w_global[e] before the epilogue (the gate and up halves of a
+ * fused W1 share their expert's scale).
+ * Then, if row_scale, out[r][.] *= row_scale[r].  out is fp64 (unrounded),
  * width N or N/2. */
 void oracle_grouped_gemm(const uint16_t *a, int64_t K, const int32_t *gather_idx,
                          const int32_t *offsets, int64_t E, int64_t R, int64_t N,
-                         const uint8_t *w_codes, const uint8_t *w_scales, const float *row_scale,
-                         int epi, double *out)
+                         const uint8_t *w_codes, const uint8_t *w_scales, const float *w_global,
+                         const float *row_scale, int epi, double *out)
 {
     int64_t width = (epi == 1) ? N / 2 : N;
 #pragma omp parallel
@@ -459,6 +464,7 @@ void oracle_grouped_gemm(const uint16_t *a, int64_t K, const int32_t *gather_idx
         for (int64_t e = 0; e < E; ++e) {
             const uint8_t *ce = w_codes + e * N * (K / 2);
             const uint8_t *se = w_scales + e * N * (K / 16);
+            double ge = w_global ? (double)w_global[e] : 1.0;
             for (int64_t r = offsets[e]; r < offsets[e + 1] && r < R; ++r) {
                 int64_t src = gather_idx ? (int64_t)gather_idx[r] : r;
                 for (int64_t n = 0; n < N; ++n) {
@@ -466,7 +472,7 @@ void oracle_grouped_gemm(const uint16_t *a, int64_t K, const int32_t *gather_idx
                     dequant_row_f64(ce, se, K, n, w);
                     for (int64_t k = 0; k < K; ++k)
                         acc += oracle_bf16_value(a[src * K + k]) * w[k];
-                    h[n] = acc;
+                    h[n] = acc * ge;
                 }
                 for (int64_t i = 0; i < width; ++i) {
                     double v = (epi == 1) ? silu(h[i]) * h[i + N / 2] : h[i];
@@ -502,12 +508,15 @@ void oracle_moe_combine(const uint16_t *y, const int32_t *slot_pos, int64_t T, i
  *   y_j = bf16( g * (act . W2_e^T) )         (stored per slot)
  *   out[t] = sum_j y_j                       (fp64, slot order; unrounded)
  * W1: codes [E][2I][H/2], scales [E][2I][H/16]; W2: codes [E][H][I/2], scales
- * [E][H][I/16].  The bf16 rounding points are where this library stores
- * intermediates in bf16. */
+ * [E][H][I/16].  Two-level weights: w1_global / w2_global (fp32 [E], or NULL
+ * for 1) multiply h and act . W2_e^T of expert e (as in oracle_grouped_gemm).
+ * The bf16 rounding points are where this library stores intermediates in
+ * bf16. */
 void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, const int32_t *ids,
                       const float *gates, int64_t topk, int64_t E, int64_t I,
                       const uint8_t *w1_codes, const uint8_t *w1_scales,
-                      const uint8_t *w2_codes, const uint8_t *w2_scales, double *out)
+                      const uint8_t *w2_codes, const uint8_t *w2_scales,
+                      const float *w1_global, const float *w2_global, double *out)
 {
     (void)E;
 #pragma omp parallel
@@ -523,6 +532,8 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, const int32_t *id
             for (int64_t j = 0; j < topk; ++j) {
                 int64_t e = ids[t * topk + j];
                 double g = (double)gates[t * topk + j];
+                double g1 = w1_global ? (double)w1_global[e] : 1.0;
+                double g2 = w2_global ? (double)w2_global[e] : 1.0;
                 const uint8_t *c1 = w1_codes + e * (2 * I) * (H / 2);
                 const uint8_t *s1 = w1_scales + e * (2 * I) * (H / 16);
                 const uint8_t *c2 = w2_codes + e * H * (I / 2);
@@ -532,7 +543,7 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, const int32_t *id
                     dequant_row_f64(c1, s1, H, n, w);
                     for (int64_t k = 0; k < H; ++k)
                         s += oracle_bf16_value(x[t * H + k]) * w[k];
-                    h[n] = s;
+                    h[n] = s * g1;
                 }
                 for (int64_t i = 0; i < I; ++i)
                     act[i] = oracle_bf16_value(oracle_bf16_round(silu(h[i]) * h[i + I]));
@@ -541,7 +552,7 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, const int32_t *id
                     dequant_row_f64(c2, s2, I, c, w);
                     for (int64_t k = 0; k < I; ++k)
                         s += act[k] * w[k];
-                    acc[c] += oracle_bf16_value(oracle_bf16_round(g * s));
+                    acc[c] += oracle_bf16_value(oracle_bf16_round(g * (s * g2)));
                 }
             }
             for (int64_t c = 0; c < H; ++c)

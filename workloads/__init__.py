@@ -71,12 +71,13 @@ def nvfp4_weight(rng: np.random.Generator, *shape_rows_k, exp_field=(3, 9)) -> N
     over all 16 e2m1 codes, negative zero included).  Scales: E4M3 with the
     biased exponent field uniform over exp_field (inclusive; the default 3..9
     gives 2^-4 .. 2^2 before the mantissa) and the 3-bit mantissa uniform;
-    sign 0."""
+    sign 0.  A drawn 0x7F (exponent field 15, mantissa 7: the NaN code) is
+    replaced by 0x7E (448)."""
     *lead, R, K = shape_rows_k
     codes = rng.integers(0, 256, size=(*lead, R, K // 2), dtype=np.uint8)
     e = rng.integers(exp_field[0], exp_field[1] + 1, size=(*lead, R, K // 16), dtype=np.uint8)
     m = rng.integers(0, 8, size=(*lead, R, K // 16), dtype=np.uint8)
-    return NF4W(codes, (e << 3) | m)
+    return NF4W(codes, np.minimum((e << 3) | m, 0x7E).astype(np.uint8))
 
 
 def normal_bf16(rng: np.random.Generator, M: int, K: int, outlier_frac: float = 0.0) -> np.ndarray:
@@ -189,6 +190,32 @@ def moe(T: int, E: int = MOE_EXPERTS, topk: int = MOE_TOPK, H: int = MOE_HIDDEN,
     w1 = nvfp4_weight(rng, E, 2 * I, H, exp_field=exp_field)
     w2 = nvfp4_weight(rng, E, H, I, exp_field=exp_field)
     return MoEWorkload(x, ids, gates, w1, w2)
+
+
+# Two-level expert weights (a per-expert fp32 global scale above the E4M3 block
+# scales), as a quantizer that puts each expert's largest block at scale 448
+# would leave them: block scales near the top of the E4M3 range (exponent fields
+# 11..15, 2^4 .. 448) and global scales around 2^-14 .. 2^-12, so that the
+# products scale * g fall near the single-level expert scales above.
+MOE_TWO_LEVEL_EXP_FIELD = (11, 15)
+
+
+def expert_global_scales(rng: np.random.Generator, E: int, exp_range=(-14, -13)) -> np.ndarray:
+    """Per-expert fp32 global scales 2^u * (1 + f): u an integer uniform over
+    exp_range (inclusive), f uniform in [0, 1); one draw of u, then one of f."""
+    u = rng.integers(exp_range[0], exp_range[1] + 1, size=E)
+    f = rng.random(E)
+    return (np.ldexp(1.0 + f, u)).astype(np.float32)
+
+
+def moe_two_level(T: int, E: int = MOE_EXPERTS, topk: int = MOE_TOPK, H: int = MOE_HIDDEN,
+                  I: int = MOE_INTER, seed: int = 0):
+    """Routed MoE layer with two-level expert weights: moe(..., exp_field =
+    MOE_TWO_LEVEL_EXP_FIELD), then the W1 and W2 global scales [E] (fp32) from
+    the same generator.  Returns (workload, w1_global, w2_global)."""
+    wl = moe(T, E=E, topk=topk, H=H, I=I, seed=seed, exp_field=MOE_TWO_LEVEL_EXP_FIELD)
+    rng = np.random.default_rng(seed + 7919)
+    return wl, expert_global_scales(rng, E), expert_global_scales(rng, E)
 
 
 # ---- FP8 E4M3 KV cache ------------------------------------------------------------
