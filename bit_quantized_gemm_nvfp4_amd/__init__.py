@@ -65,6 +65,8 @@ _SIGS = {
     "nvfp4_grouped_gemm_workspace_size": ([_i64, _i64, _i64, _i64], _sz),
     "nvfp4_grouped_gemm": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _int,
                             _vp, _vp, _sz, _vp], _int),
+    "nvfp4_grouped_gemm_scaled": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                   _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_moe_combine": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
     "nvfp4_noalloc_scratch_bytes": ([], _sz),
     "nvfp4_gemm_noalloc": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp,
@@ -91,6 +93,8 @@ _SIGS.update({
                                       _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                     _vp, _int, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_grouped_gemm_scaled_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp,
+                                           _vp, _vp, _vp, _int, _vp, _vp, _sz, _vp], _int),
 })
 
 
@@ -537,9 +541,11 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, gates=None):
 
 def grouped_gemm(a: torch.Tensor, gather_idx, expert_offsets: torch.Tensor,
                  w_codes: torch.Tensor, w_scales: torch.Tensor, rows: int, row_scale=None,
-                 epilogue: int = EPI_NONE, out=None, plan=None) -> torch.Tensor:
+                 epilogue: int = EPI_NONE, out=None, plan=None, w_global=None) -> torch.Tensor:
     """Per-expert W4A16 GEMM over `rows` grouped rows (see nvfp4_grouped_gemm).
-    plan (dict or Plan) forces the kernel choice (same results)."""
+    w_global (fp32 [E]) holds the experts' global scales of two-level weights
+    (nvfp4_grouped_gemm_scaled).  plan (dict or Plan) forces the kernel choice
+    (same results)."""
     a_rows, K = _dims(a, "a", 2)
     _arg(a, "a", torch.bfloat16)
     E, N, half = _dims(w_codes, "w_codes", 3)
@@ -550,20 +556,27 @@ def grouped_gemm(a: torch.Tensor, gather_idx, expert_offsets: torch.Tensor,
     _arg(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
     _arg(gather_idx, "gather_idx", torch.int32, (rows,), optional=True)
     _arg(row_scale, "row_scale", torch.float32, (rows,), optional=True)
+    _arg(w_global, "w_global", torch.float32, (E,), optional=True)
     width = N // 2 if epilogue == EPI_SWIGLU else N
     _arg(out, "out", torch.bfloat16, (rows, width), optional=True)
-    _gpu(a, gather_idx, expert_offsets, w_codes, w_scales, row_scale, out)
+    _gpu(a, gather_idx, expert_offsets, w_codes, w_scales, row_scale, w_global, out)
     if out is None:
         out = torch.empty((rows, width), dtype=torch.bfloat16, device=a.device)
     nbytes = int(lib().nvfp4_grouped_gemm_workspace_size(rows, E, N, K))
     ws, wsz = _workspace(nbytes, a.device)
-    args = (_ptr(a), a_rows, K, _ptr(gather_idx), _ptr(expert_offsets), E, rows, N,
-            _ptr(w_codes), _ptr(w_scales), _ptr(row_scale), epilogue, _ptr(out), _ptr(ws), wsz,
-            _stream(a.device))
-    if plan is not None:
-        _check(lib().nvfp4_grouped_gemm_planned(_plan_ref(plan), *args))
+    head = (_ptr(a), a_rows, K, _ptr(gather_idx), _ptr(expert_offsets), E, rows, N,
+            _ptr(w_codes), _ptr(w_scales))
+    tail = (_ptr(row_scale), epilogue, _ptr(out), _ptr(ws), wsz, _stream(a.device))
+    if w_global is not None:
+        args = head + (_ptr(w_global),) + tail
+        if plan is not None:
+            _check(lib().nvfp4_grouped_gemm_scaled_planned(_plan_ref(plan), *args))
+        else:
+            _check(lib().nvfp4_grouped_gemm_scaled(*args))
+    elif plan is not None:
+        _check(lib().nvfp4_grouped_gemm_planned(_plan_ref(plan), *head, *tail))
     else:
-        _check(lib().nvfp4_grouped_gemm(*args))
+        _check(lib().nvfp4_grouped_gemm(*head, *tail))
     return out
 
 
@@ -583,13 +596,18 @@ def moe_combine(y: torch.Tensor, slot_pos: torch.Tensor, out=None) -> torch.Tens
     return out
 
 
-def moe_layer(x, topk_ids, gates, w1_codes, w1_scales, w2_codes, w2_scales):
+def moe_layer(x, topk_ids, gates, w1_codes, w1_scales, w2_codes, w2_scales, w1_global=None,
+              w2_global=None):
     """Routed MoE layer: align -> grouped gate+up GEMM with SwiGLU -> grouped down
-    GEMM scaled by the gate weights -> combine.  All on the current stream."""
+    GEMM scaled by the gate weights -> combine.  All on the current stream.
+    w1_global / w2_global (fp32 [E]): per-expert global scales of two-level
+    weights."""
     E = w1_codes.shape[0]
     T, topk = _dims(topk_ids, "topk_ids", 2)
     R = T * topk
     offsets, gather, slot, row_gate = moe_align(topk_ids, E, gates)
-    act = grouped_gemm(x, gather, offsets, w1_codes, w1_scales, R, epilogue=EPI_SWIGLU)
-    y = grouped_gemm(act, None, offsets, w2_codes, w2_scales, R, row_scale=row_gate)
+    act = grouped_gemm(x, gather, offsets, w1_codes, w1_scales, R, epilogue=EPI_SWIGLU,
+                       w_global=w1_global)
+    y = grouped_gemm(act, None, offsets, w2_codes, w2_scales, R, row_scale=row_gate,
+                     w_global=w2_global)
     return moe_combine(y, slot)

@@ -531,9 +531,11 @@ size_t nvfp4_grouped_gemm_workspace_size(int64_t R, int64_t E, int64_t N, int64_
 static int grouped_impl(const PlanOverride& ov, const uint16_t* a, int64_t a_rows, int64_t K,
                         const int32_t* gather_idx, const int32_t* expert_offsets, int64_t E,
                         int64_t R, int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
-                        const float* row_scale, int epilogue, uint16_t* out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        const float* w_global, const float* row_scale, int epilogue,
+                        uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!a || !expert_offsets || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (w_global && reinterpret_cast<uintptr_t>(w_global) % alignof(float) != 0)
+    return NVFP4_ERROR_INVALID_VALUE;
   if (a_rows <= 0 || K <= 0 || E <= 0 || R <= 0 || N <= 0) return NVFP4_ERROR_INVALID_VALUE;
   if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
   if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_SWIGLU) return NVFP4_ERROR_NOT_SUPPORTED;
@@ -549,8 +551,9 @@ static int grouped_impl(const PlanOverride& ov, const uint16_t* a, int64_t a_row
   const size_t need = moe_grouped_workspace_bytes(R, E, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
   return launched(launch_grouped_gemm(a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
-                                      w_scales, row_scale, epilogue == NVFP4_EPI_SWIGLU, out,
-                                      workspace, as_stream(stream), ov));
+                                      w_scales, w_global, row_scale,
+                                      epilogue == NVFP4_EPI_SWIGLU, out, workspace,
+                                      as_stream(stream), ov));
 }
 
 extern "C" {
@@ -561,7 +564,19 @@ int nvfp4_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32
                        int epilogue, uint16_t* out, void* workspace, size_t workspace_bytes,
                        void* stream) {
   return grouped_impl(PlanOverride{}, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
-                      w_scales, row_scale, epilogue, out, workspace, workspace_bytes, stream);
+                      w_scales, nullptr, row_scale, epilogue, out, workspace, workspace_bytes,
+                      stream);
+}
+
+int nvfp4_grouped_gemm_scaled(const uint16_t* a, int64_t a_rows, int64_t K,
+                              const int32_t* gather_idx, const int32_t* expert_offsets, int64_t E,
+                              int64_t R, int64_t N, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* w_global_scales,
+                              const float* row_scale, int epilogue, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_impl(PlanOverride{}, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
+                      w_scales, w_global_scales, row_scale, epilogue, out, workspace,
+                      workspace_bytes, stream);
 }
 
 int nvfp4_grouped_gemm_planned(const nvfp4_plan_t* plan, const uint16_t* a, int64_t a_rows,
@@ -573,7 +588,21 @@ int nvfp4_grouped_gemm_planned(const nvfp4_plan_t* plan, const uint16_t* a, int6
   PlanOverride ov;
   if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
   return grouped_impl(ov, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes, w_scales,
-                      row_scale, epilogue, out, workspace, workspace_bytes, stream);
+                      nullptr, row_scale, epilogue, out, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_grouped_gemm_scaled_planned(const nvfp4_plan_t* plan, const uint16_t* a,
+                                      int64_t a_rows, int64_t K, const int32_t* gather_idx,
+                                      const int32_t* expert_offsets, int64_t E, int64_t R,
+                                      int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
+                                      const float* w_global_scales, const float* row_scale,
+                                      int epilogue, uint16_t* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  return grouped_impl(ov, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes, w_scales,
+                      w_global_scales, row_scale, epilogue, out, workspace, workspace_bytes,
+                      stream);
 }
 
 int nvfp4_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,

@@ -161,6 +161,7 @@ struct GroupedArgs {
   const int32_t* offsets;
   const uint8_t* wc;
   const uint8_t* ws;
+  const float* wg;  // per-expert global scales [E] of two-level weights, or NULL
   const float* row_scale;
   uint16_t* out;
   int64_t K;
@@ -243,7 +244,8 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
 
   gemv_accumulate<1, TR>(acc, cptr, sptr, xl, K, 0, g.steps, (int)(K / kGemvStep));
 
-  // lane holds C[m = 4*q + r][column 16*tile + ln]
+  // lane holds C[m = 4*q + r][column 16*tile + ln]; the sums are h / g_e
+  const float ge = g.wg ? g.wg[e] : 1.0f;
   const int64_t width = g.swiglu ? g.N / 2 : g.N;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
     if (g.swiglu) {
       const int64_t col = gt * 16 + ln;
       if (col < width) {
-        const float hg = acc[0][0][r], hu = acc[TR - 1][0][r];
+        const float hg = acc[0][0][r] * ge, hu = acc[TR - 1][0][r] * ge;
         float v = hg / (1.0f + expf(-hg)) * hu;
         if (g.row_scale) v *= rs;
         g.out[row * width + col] = f32_to_bf16_bits(v);
@@ -264,7 +266,7 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
       for (int t = 0; t < TR; ++t) {
         const int64_t col = (gt * TR + t) * 16 + ln;
         if (col < width) {
-          float v = acc[t][0][r];
+          float v = acc[t][0][r] * ge;
           if (g.row_scale) v *= rs;
           g.out[row * width + col] = f32_to_bf16_bits(v);
         }
@@ -281,6 +283,7 @@ struct GroupedMfmaArgs {
   const int32_t* offsets;
   const uint8_t* wc;
   const uint8_t* ws;
+  const float* wg;  // per-expert global scales [E] of two-level weights, or NULL
   const float* row_scale;
   uint16_t* out;
   int64_t K;
@@ -341,6 +344,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   gemm_mainloop<false>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K);
 
   const int wn = (t >> 6) & 1, h = (t & 63) >> 5;
+  const float ge = g.wg ? g.wg[e] : 1.0f;  // the sums are h / g_e
 #pragma unroll
   for (int i = 0; i < kXBlocks; ++i) {
     const int tr = gemm_tile_row(i);
@@ -360,7 +364,8 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
             float v[2];
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
-              const float hg = acc[i][j][4 * q + 2 * p + w], hu = acc[i][j + 2][4 * q + 2 * p + w];
+              const float hg = acc[i][j][4 * q + 2 * p + w] * ge;
+              const float hu = acc[i][j + 2][4 * q + 2 * p + w] * ge;
               v[w] = hg / (1.0f + expf(-hg)) * hu;
               if (g.row_scale) v[w] *= rs;
             }
@@ -379,7 +384,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
           uint32_t pk[2];
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            float v0 = acc[i][j][4 * q + 2 * p], v1 = acc[i][j][4 * q + 2 * p + 1];
+            float v0 = acc[i][j][4 * q + 2 * p] * ge, v1 = acc[i][j][4 * q + 2 * p + 1] * ge;
             if (g.row_scale) v0 *= rs, v1 *= rs;
             pk[p] = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
           }
@@ -547,9 +552,9 @@ GroupedPath grouped_path(int64_t a_rows, int64_t K, int64_t E, int64_t R,
 
 int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int32_t* gather,
                         const int32_t* offsets, int64_t E, int64_t R, int64_t N,
-                        const uint8_t* wc, const uint8_t* ws, const float* row_scale,
-                        bool swiglu, uint16_t* out, void* workspace, hipStream_t stream,
-                        const PlanOverride& ov) {
+                        const uint8_t* wc, const uint8_t* ws, const float* wg,
+                        const float* row_scale, bool swiglu, uint16_t* out, void* workspace,
+                        hipStream_t stream, const PlanOverride& ov) {
   (void)workspace;
   const GroupedPath path = grouped_path(a_rows, K, E, R, ov);
   if (path == GroupedPath::kNone) return -2;
@@ -560,6 +565,7 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
     m.offsets = offsets;
     m.wc = wc;
     m.ws = ws;
+    m.wg = wg;
     m.row_scale = row_scale;
     m.out = out;
     m.K = K;
@@ -579,6 +585,7 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
   g.offsets = offsets;
   g.wc = wc;
   g.ws = ws;
+  g.wg = wg;
   g.row_scale = row_scale;
   g.out = out;
   g.K = K;

@@ -328,6 +328,28 @@ int nvfp4_grouped_gemm(const uint16_t *a, int64_t a_rows, int64_t K, const int32
                        void *stream);
 
 /*
+ * nvfp4_grouped_gemm of two-level expert weights.  The MoE checkpoints the
+ * pages deploy come from NVFP4 quantization tools ("What 350+ Experiments
+ * ...", section 1); each expert tensor then carries one positive fp32 global
+ * scale above its per-16 E4M3 scales (see the two-level functions above;
+ * nvfp4_quantize_weight run per expert writes them).  w_global_scales is a
+ * DEVICE fp32 array [E] (4-byte aligned; NULL means 1 for every expert).  The
+ * fp32 sums of expert e are multiplied by w_global_scales[e] before the
+ * epilogue:
+ *   h[n] = fl32( w_global_scales[e] * sum_k a[src][k] * w_e[n][k] ),
+ * then SwiGLU (the gate and up halves of a fused W1 share their expert's
+ * scale), row_scale and the bf16 rounding exactly as nvfp4_grouped_gemm.
+ * All scales 1 (or NULL) gives nvfp4_grouped_gemm's output bit for bit.
+ * Other arguments, errors and workspace as nvfp4_grouped_gemm.
+ */
+int nvfp4_grouped_gemm_scaled(const uint16_t *a, int64_t a_rows, int64_t K,
+                              const int32_t *gather_idx, const int32_t *expert_offsets, int64_t E,
+                              int64_t R, int64_t N, const uint8_t *w_codes,
+                              const uint8_t *w_scales, const float *w_global_scales,
+                              const float *row_scale, int epilogue, uint16_t *out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Combine the per-slot expert outputs of a routed layer ("What 350+
  * Experiments ...", section 1: each token's output is the gate-weighted sum
  * over the experts it was routed to; the gate weights are applied by the

@@ -143,6 +143,15 @@ def test_moe_validation(L):
     assert g(P, 32, 256, P, P2, 4, 32, 48, P3, P4, NULL, 1, P, NULL, 0, NULL) == NOT_SUPPORTED
     assert g(P, 32, 256, P, P2, 4, 32, 64, P3, P4, NULL, 5, P, NULL, 0, NULL) == NOT_SUPPORTED
     assert g(P, 8, 256, NULL, P2, 4, 32, 64, P3, P4, NULL, 0, P, NULL, 0, NULL) == INVALID
+    gs = L.nvfp4_grouped_gemm_scaled  # the same checks, plus a float-aligned scale array
+    assert gs(NULL, 32, 256, P, P2, 4, 32, 64, P3, P4, P, NULL, 0, P, NULL, 0, NULL) == INVALID
+    assert gs(P, 32, 240, P, P2, 4, 32, 64, P3, P4, P, NULL, 0, P, NULL, 0,
+              NULL) == NOT_SUPPORTED
+    assert gs(P, 32, 256, P, P2, 4, 32, 64, P3, P4, ctypes.c_void_p(0x10002), NULL, 0, P, NULL,
+              0, NULL) == INVALID
+    gsp = L.nvfp4_grouped_gemm_scaled_planned
+    assert gsp(_plan(gemm_min_m=0), P, 32, 256, P, P2, 4, 32, 64, P3, P4, P, NULL, 0, P, NULL, 0,
+               NULL) == INVALID
     c = L.nvfp4_moe_combine
     assert c(P, NULL, 4, 8, 64, P2, NULL) == INVALID
     assert c(P, P2, 4, 8, 60, P3, NULL) == NOT_SUPPORTED
@@ -338,6 +347,10 @@ def test_binding_checks_shapes_before_the_gpu(L):
     raises("gather_idx", nv.grouped_gemm, x, torch.zeros(4, dtype=torch.int64), off, w3c, w3s, 4)
     raises("out", nv.grouped_gemm, x, None, off, w3c, w3s, 4, epilogue=nv.EPI_SWIGLU,
            out=torch.zeros(4, 64, dtype=bf))
+    raises("w_global", nv.grouped_gemm, x, None, off, w3c, w3s, 4,
+           w_global=torch.zeros(5, dtype=torch.float32))
+    raises("w_global", nv.grouped_gemm, x, None, off, w3c, w3s, 4,
+           w_global=torch.zeros(4, dtype=torch.float64))
     raises("rows", nv.moe_combine, torch.zeros(7, 64, dtype=bf), torch.zeros(2, 4, dtype=torch.int32))
     raises("cache", nv.kv_store_e4m3, torch.zeros(4, 64, dtype=bf),
            torch.zeros(4, dtype=torch.int32), 1.0, torch.zeros(8, 32, dtype=u8))

@@ -116,18 +116,24 @@ def test_combine_matches_oracle(nv, orc):
     assert ok, (rf, worst)
 
 
-def _layer(nv, wl):
+def _dev_g(g):
+    return None if g is None else helpers.dev_f32(g)
+
+
+def _layer(nv, wl, g1=None, g2=None):
     import torch
     out = nv.moe_layer(helpers.dev_bf16(wl.x), helpers.dev_i32(wl.ids), helpers.dev_f32(wl.gates),
                        helpers.dev_u8(wl.w1.codes), helpers.dev_u8(wl.w1.scales),
-                       helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales))
+                       helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales),
+                       w1_global=_dev_g(g1), w2_global=_dev_g(g2))
     torch.cuda.synchronize()
     return helpers.host_bits(out)
 
 
-def _slot_magnitude(orc, wl, toks):
+def _slot_magnitude(orc, wl, toks, g1=None, g2=None):
     """sum_j |y_j| per output element, from the oracle's own grouped steps: the
-    scale of the terms the combine adds (each stored in bf16)."""
+    scale of the terms the combine adds (each stored in bf16).  g1 / g2: the
+    experts' global scales of two-level weights."""
     ids, gates = wl.ids[toks], wl.gates[toks]
     T, topk = ids.shape
     E = wl.w1.codes.shape[0]
@@ -136,11 +142,11 @@ def _slot_magnitude(orc, wl, toks):
     off, gather, slot = orc.moe_align(ids, E)
     R = T * topk
     act = orc.bf16_round(orc.grouped_gemm(wl.x[toks], H, gather, off, E, R, 2 * I, wl.w1.codes,
-                                          wl.w1.scales, epilogue=1))
+                                          wl.w1.scales, epilogue=1, w_global=g1))
     rg = np.empty(R, np.float32)
     rg[slot.reshape(-1)] = gates.reshape(-1)
     y = helpers.bf16_bits_to_f64(orc.bf16_round(orc.grouped_gemm(
-        act, I, None, off, E, R, H, wl.w2.codes, wl.w2.scales, row_scale=rg)))
+        act, I, None, off, E, R, H, wl.w2.codes, wl.w2.scales, row_scale=rg, w_global=g2)))
     return np.abs(y)[slot].sum(axis=1)
 
 
@@ -220,7 +226,8 @@ def _sub_problem(rows, off_h, E):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
-def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False):
+def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False, g1=None,
+             g2=None):
     """Every GPU step of the layer against the oracle fed the GPU's own inputs
     to that step, at the GEMM tolerance element by element: align bit-exact,
     then the gate/up grouped GEMM with SwiGLU, the down grouped GEMM with the
@@ -228,7 +235,8 @@ def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False
     seeded sample of grouped rows / tokens (the oracle recomputes a grouped
     problem of just those rows, each with its own expert).  down_fp32_bound:
     the down projection's element bound also admits the fp32 summation error
-    bound I * 2^-24 * sum_k |a_k w_k g_r| of each output."""
+    bound I * 2^-24 * sum_k |a_k w_k g_r| of each output.  g1 / g2: the
+    experts' global scales of two-level weights (fp32 [E])."""
     E = wl.w1.codes.shape[0]
     H = wl.x.shape[1]
     I = wl.w2.codes.shape[2] * 2
@@ -237,8 +245,9 @@ def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False
     w1c, w1s = helpers.dev_u8(wl.w1.codes), helpers.dev_u8(wl.w1.scales)
     w2c, w2s = helpers.dev_u8(wl.w2.codes), helpers.dev_u8(wl.w2.scales)
     off, gather, slot, rg = nv.moe_align(helpers.dev_i32(wl.ids), E, helpers.dev_f32(wl.gates))
-    act = nv.grouped_gemm(helpers.dev_bf16(wl.x), gather, off, w1c, w1s, R, epilogue=1)
-    y = nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg)
+    act = nv.grouped_gemm(helpers.dev_bf16(wl.x), gather, off, w1c, w1s, R, epilogue=1,
+                          w_global=_dev_g(g1))
+    y = nv.grouped_gemm(act, None, off, w2c, w2s, R, row_scale=rg, w_global=_dev_g(g2))
     out = nv.moe_combine(y, slot)
     torch.cuda.synchronize()
     off_h, gather_h, slot_h = off.cpu().numpy(), gather.cpu().numpy(), slot.cpu().numpy()
@@ -251,16 +260,16 @@ def _chained(nv, orc, wl, n_rows=None, n_tok=None, seed=0, down_fp32_bound=False
     toks = np.arange(T) if n_tok is None else np.sort(rng.choice(T, n_tok, replace=False))
     so = _sub_problem(rows, off_h, E)
     ref_act = orc.grouped_gemm(wl.x, H, gather_h[rows], so, E, len(rows), 2 * I, wl.w1.codes,
-                               wl.w1.scales, epilogue=1)
+                               wl.w1.scales, epilogue=1, w_global=g1)
     ok, rf, worst = helpers.gemm_close(act_h[rows], ref_act)
     assert ok, ("gate/up", rf, worst)
     ref_y = orc.grouped_gemm(np.ascontiguousarray(act_h[rows]), I, None, so, E, len(rows), H,
-                             wl.w2.codes, wl.w2.scales, row_scale=rg_h[rows])
+                             wl.w2.codes, wl.w2.scales, row_scale=rg_h[rows], w_global=g2)
     extra = None
     if down_fp32_bound:
         a_abs = np.ascontiguousarray(act_h[rows] & 0x7FFF)
         mag = orc.grouped_gemm(a_abs, I, None, so, E, len(rows), H, wl.w2.codes & 0x77,
-                               wl.w2.scales, row_scale=np.abs(rg_h[rows]))
+                               wl.w2.scales, row_scale=np.abs(rg_h[rows]), w_global=g2)
         extra = I * 2.0 ** -24 * mag
         ok_bj, _, worst_bj = helpers.gemm_close(y_h[rows], ref_y)
         print(f"[down] BJ element bound alone: ok={ok_bj} worst ratio {worst_bj:.2f}", flush=True)
@@ -314,3 +323,73 @@ def test_grouped_long_k_few_rows(nv, orc):
         ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, epilogue=epi)
         ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
         assert ok, (epi, rf, worst)
+
+
+# ---- two-level expert weights (one fp32 global scale per expert) ---------------
+
+@pytest.mark.parametrize("kernel,epi", [("gemv", 0), ("gemv", 1), ("mfma", 0), ("mfma", 1)])
+def test_grouped_two_level_matches_oracle(nv, orc, kernel, epi):
+    """nvfp4_grouped_gemm_scaled on both grouped kernels: block scales near the
+    top of E4M3 (up to 448) and per-expert global scales 2^-14 .. 2^-12 (one
+    expert's exactly 1); uneven experts (empty, one row, several chunks), with
+    gather and row scale, guarded output.  Unit global scales reproduce
+    nvfp4_grouped_gemm bit for bit."""
+    helpers.announce(f"moe grouped two-level kernel={kernel} epi={epi}")
+    rng = np.random.default_rng(70 + epi + 2 * (kernel == "mfma"))
+    if kernel == "gemv":
+        E, K, N, rows = 6, 512, 96, 50
+        counts = np.array([0, 1, 40, 0, 70, 9])
+        plan = {"grouped_mfma_min_rows": 1 << 20}
+    else:
+        E, K, N, rows = 5, 416, 352, 129
+        counts = np.array([1, 300, 0, 256, 37])
+        plan = {"grouped_mfma_min_rows": 1}
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, rows, K)
+    w = workloads.nvfp4_weight(rng, E, N, K, exp_field=workloads.MOE_TWO_LEVEL_EXP_FIELD)
+    wg = workloads.expert_global_scales(rng, E)
+    wg[2] = 1.0
+    gather = rng.integers(0, rows, R).astype(np.int32)
+    rs = (rng.random(R) + 0.5).astype(np.float32)
+    width = N // 2 if epi else N
+    args = (helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+            helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), R)
+    g = helpers.Guarded((R, width), torch.bfloat16)
+    y = nv.grouped_gemm(*args, row_scale=helpers.dev_f32(rs), epilogue=epi, plan=plan,
+                        w_global=helpers.dev_f32(wg), out=g.t)
+    g.check()
+    ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
+                           epilogue=epi, w_global=wg)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+    assert ok, (rf, worst)
+    ones = nv.grouped_gemm(*args, row_scale=helpers.dev_f32(rs), epilogue=epi, plan=plan,
+                           w_global=helpers.dev_f32(np.ones(E, np.float32)))
+    plain = nv.grouped_gemm(*args, row_scale=helpers.dev_f32(rs), epilogue=epi, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(ones, plain)
+
+
+def test_moe_layer_two_level_decode_full(nv, orc):
+    """T = 32 decode batch with two-level expert weights through the binding's
+    layer (both global-scale arrays): every token against the oracle's
+    token-by-token layer."""
+    helpers.announce("moe layer two-level T=32 full")
+    wl, g1, g2 = workloads.moe_two_level(32)
+    got = _layer(nv, wl, g1, g2)
+    ref = orc.moe_layer(wl.x, wl.ids, wl.gates, 128, 768, wl.w1.codes, wl.w1.scales,
+                        wl.w2.codes, wl.w2.scales, w1_global=g1, w2_global=g2)
+    ok, rf, worst = _layer_close(got, ref, _slot_magnitude(orc, wl, np.arange(32), g1, g2))
+    assert ok, (rf, worst)
+
+
+def test_moe_layer_two_level_steps_chained(nv, orc):
+    """Every step of the two-level layer at T = 32 (grouped GEMV) on all rows and
+    at T = 4096 (MFMA grouped kernel) on sampled rows and tokens, the oracle fed
+    the GPU's own inputs to each step."""
+    helpers.announce("moe layer two-level T=32 chained steps")
+    wl, g1, g2 = workloads.moe_two_level(32, seed=5)
+    _chained(nv, orc, wl, g1=g1, g2=g2)
+    helpers.announce("moe layer two-level T=4096 chained steps, sampled rows")
+    wl, g1, g2 = workloads.moe_two_level(4096, seed=6)
+    _chained(nv, orc, wl, n_rows=96, n_tok=64, seed=44, g1=g1, g2=g2)
