@@ -480,7 +480,13 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
     if (zc > z) z = zc;
   } else {
     const int64_t want_waves = (int64_t)num_cus * 8;
-    const int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
+    int64_t zw = (want_waves + wgs * p.nw - 1) / (wgs * p.nw);
+    // a layer that needs K parts to fill the chip takes parts of at most 4
+    // steps on the 16x16 path: a workgroup's steps run one after another, each
+    // about one memory latency (measured at M = 8: the 17,408 x 5,120 layer
+    // 21.5 -> 19.4 us with 5 parts instead of 4, the 5,120 x 17,408 layer
+    // 22.4 -> 19.5 us with 17 instead of 13)
+    if (!p.small && zw >= 2 && (steps + 3) / 4 > zw) zw = (steps + 3) / 4;
     if (zw > z) z = zw;
   }
   if (ov.gemv_splits > 0) z = ov.gemv_splits > z_lds ? ov.gemv_splits : z_lds;

@@ -482,12 +482,14 @@ __device__ __forceinline__ void gemv_accumulate_win_blk(f32x4 (&acc)[TR][MT],
   int s = s0, cur = 0, j = 0;  // j: position of step s in its 8-step block
   auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
     const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
-    xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
-    load_wcodes<TR>(bn, cptr, min(s + 1, e - 1));
     // the next block starts at step s + 8 - j; its two halves are loaded at
-    // the block's last two steps
+    // the block's last two steps, ahead of the window and code prefetches, so
+    // the scale store below waits for the scale and window loads only and the
+    // codes of step s + 1 stay in flight over the barrier
     const bool sh = j >= 6;
     if (sh) load_shalf<TR>(ph, sptr, s + 8 - j, j - 6, e - 1);
+    xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+    load_wcodes<TR>(bn, cptr, min(s + 1, e - 1));
     __builtin_amdgcn_sched_barrier(0);
     read_sblock<TR>(bc, my, j);
     compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
@@ -614,11 +616,11 @@ __device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
         on = ++fails < 2;
       }
     }
+    const int j = i & 7;
+    const bool sh = j >= 6;  // scale halves first, as in gemv_accumulate_win_blk
+    if (sh) load_shalf<TR>(ph, sptr, me.start + i + 8 - j, j - 6, last);
     xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, min(i + 1, L - 1), row_ptr);
     load_wcodes<TR>(bn, cptr, min(me.start + i + 1, last));
-    const int j = i & 7;
-    const bool sh = j >= 6;
-    if (sh) load_shalf<TR>(ph, sptr, me.start + i + 8 - j, j - 6, last);
     __builtin_amdgcn_sched_barrier(0);
     if (i < me.len) {
       read_sblock<TR>(bc, my, j);
