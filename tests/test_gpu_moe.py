@@ -102,6 +102,33 @@ def test_grouped_mfma_matches_oracle(nv, orc, epi, gathered, scaled):
     assert ok, (rf, worst)
 
 
+@pytest.mark.parametrize("epi", [0, 1])
+def test_grouped_mfma_partial_chunks(nv, orc, epi):
+    """Experts whose last 256-row chunk holds 127, 128, 129, 255, 1 and 0 rows,
+    with and without whole chunks before it: every row against the oracle,
+    guarded output."""
+    helpers.announce(f"moe grouped mfma partial chunks epi={epi}")
+    rng = np.random.default_rng(80 + epi)
+    E, K, N = 9, 320, 288
+    counts = np.array([128, 129, 255, 257, 384, 385, 127, 0, 513])
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, 700, K)
+    w = workloads.nvfp4_weight(rng, E, N, K)
+    gather = rng.integers(0, 700, R).astype(np.int32)
+    rs = (rng.random(R) + 0.5).astype(np.float32)
+    g = helpers.Guarded((R, N // 2 if epi else N), torch.bfloat16)
+    y = nv.grouped_gemm(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+                        helpers.dev_u8(w.codes), helpers.dev_u8(w.scales), R,
+                        row_scale=helpers.dev_f32(rs), epilogue=epi,
+                        plan={"grouped_mfma_min_rows": 1}, out=g.t)
+    g.check()
+    ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
+                           epilogue=epi)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+    assert ok, (rf, worst)
+
+
 def test_combine_matches_oracle(nv, orc):
     helpers.announce("moe combine")
     rng = np.random.default_rng(40)
