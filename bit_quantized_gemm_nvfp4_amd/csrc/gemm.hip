@@ -13,12 +13,15 @@
 // XCDs, so each XCD is given a contiguous band of the tile sequence, which runs
 // over n fastest within groups of 8 m-tiles; the tiles an XCD holds at once
 // share activation rows and weight columns in its L2.
+#include <algorithm>
+
 #include "gemm_core.h"
 #include "launch.h"
 
 namespace nvfp4 {
 
-constexpr int kMaxGemmSplits = 8;  // K parts of a split tile at most
+constexpr int kMaxGemmSegs = 8;  // partial slots per shared tile at most
+constexpr int kMinSegSteps = 8;  // K steps per workgroup of a shared round at least
 
 namespace {
 
@@ -28,18 +31,25 @@ struct GemmArgs {
   const uint8_t* ws;        // weight scales [rows][K/16]
   const int32_t* row_idx;   // output column n uses weight row row_idx[n]; null: row n
   void* out;                // [M][N] bf16 or fp32
-  float* partial;           // split tiles: fp32 [tail tiles][splits][256 * 256], tile-local
+  float* partial;           // shared tiles: fp32 [tail][max_seg][256 * 256], tile-local
   int64_t M, N, K;          // N: output columns
-  int64_t k_split;          // K elements per split (a multiple of 64; the last may be shorter)
   int out_f32;
   int tiles_m, tiles_n;
   int full;                 // tiles 0 .. full-1 of the tile order run whole (full % 8 == 0;
                             // workgroups past the last tile exit)
-  int tail;                 // tiles full .. full+tail-1 run as `splits` K parts each
-  int splits;
+  int tail;                 // tiles full .. full+tail-1 are shared by `parts` workgroups
+  int parts;
+  int max_seg;
+  int steps;                // K steps of 64 (the last may be partial)
   const float* ga;          // two-level scales: final sums are multiplied by
   const float* gw;          // *ga * *gw (null: 1)
 };
+
+// The shared round: flattened step f = tail tile * steps + K step, F of them;
+// workgroup w takes [w F / P, (w + 1) F / P).  The workgroup holding step f:
+__host__ __device__ inline int sk_owner(int64_t f, int64_t F, int P) {
+  return (int)(((f + 1) * P - 1) / F);
+}
 
 // Tile `lin` of the launch order -> (tm, tn): n fastest within groups of 8
 // m-tiles, so the tiles one XCD holds at once share activation rows and
@@ -54,47 +64,22 @@ __device__ __forceinline__ void gemm_tile_of(int lin, int tiles_m, int tiles_n, 
   tn = in_group / gsz;
 }
 
-// A_FQ: the activations are quantized to NVFP4 and dequantized (exactly the
-// W4A4 operand nvfp4_quantize would give) while their tiles are loaded.
+// Tile `lin` over K steps [s0, s1): the output (dst null, whole K) or the
+// tile-local fp32 partial at dst.
 template <bool A_FQ>
-__global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
-  extern __shared__ char lds[];
-
-  // Workgroups 0 .. full-1 take the whole-K tiles, XCD-aware: workgroups are
-  // dispatched round-robin over the 8 XCDs, and XCD x takes the contiguous
-  // band [x * full/8, (x+1) * full/8) of the tile order.  The workgroups after
-  // them (dispatched last) take the K parts of the remaining tiles, which
-  // would otherwise leave the chip half idle in the last round.
-  // The K parts are banded the same way (part slowest), so an XCD holds
-  // neighbouring tiles of the same part.
-  int lin, z = 0, tail = -1;
-  const int b = blockIdx.x;
-  if (b < g.full) {
-    const int per_xcd = g.full / 8;
-    lin = (b & 7) * per_xcd + (b >> 3);
-    if (lin >= g.tiles_m * g.tiles_n) return;
-  } else {
-    const int items = g.tail * g.splits;
-    const int per_xcd = (items + 7) / 8;
-    const int rb = b - g.full;
-    const int r = (rb & 7) * per_xcd + (rb >> 3);
-    if (r >= items) return;
-    z = r / g.tail;
-    tail = r - z * g.tail;
-    lin = g.full + tail;
-  }
+__device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int lin, int s0,
+                                              int s1, float* dst) {
   int tm, tn;
   gemm_tile_of(lin, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t K = g.K;
-  const bool part = tail >= 0 && g.splits > 1;
-  const int64_t k_lo = part ? (int64_t)z * g.k_split : 0;
-  const int64_t k_len = part ? min(g.k_split, K - k_lo) : K;
+  const int64_t k_lo = (int64_t)s0 * BK;
+  const int64_t k_len = min((int64_t)s1 * BK, K) - k_lo;
   const int t = threadIdx.x;
 
   // sources (rows past M or N are clamped to the last one; never stored)
   GemmSrc src;
-  // (K ranges of a split start at k_lo: a multiple of 64, so pointers stay aligned)
+  // (K ranges start at multiples of 64, so pointers stay aligned)
   const uint8_t* a_tile_base = reinterpret_cast<const uint8_t*>(g.a + m0 * K + k_lo);
   {
     const int64_t n = min(n0 + (t >> 1), g.N - 1);
@@ -114,8 +99,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's part.
-  if (part) {  // fp32 partial of this K part, tile-local [256][256]
-    float* dst = g.partial + ((int64_t)tail * g.splits + z) * (BM * BN);
+  if (dst) {  // fp32 partial of this segment, tile-local [256][256]
 #pragma unroll
     for (int i = 0; i < kXBlocks; ++i)
 #pragma unroll
@@ -167,11 +151,77 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   }
 }
 
-// Split tiles: out = sum over K parts (in part order) of the tile-local fp32
-// partials.  64 workgroups per tile, 4 rows of 256 columns each (4 columns per
-// thread).
-// Z = g.splits (a template argument: all Z loads are issued before the adds,
-// which run in part order, so the sum waits one memory latency, not Z).
+// A_FQ: the activations are quantized to NVFP4 and dequantized (exactly the
+// W4A4 operand nvfp4_quantize would give) while their tiles are loaded.
+//
+// Workgroups 0 .. full-1 take the whole-K tiles, XCD-aware: workgroups are
+// dispatched round-robin over the 8 XCDs, and XCD x takes the contiguous band
+// [x * full/8, (x+1) * full/8) of the tile order.  The workgroups after them
+// (dispatched last) share the remaining tiles, which would otherwise leave
+// the chip partly idle in a last round: workgroup w of that band takes the
+// flattened steps [w F / P, (w + 1) F / P) of those tiles, F = tail * steps,
+// banded per XCD the same way, so neighbouring ranges -- pieces of the same
+// tiles -- run on one XCD.  SEGS = false: every range lies in one tile (the
+// shared round of a launch that also has whole tiles: P = tail * z).
+// SEGS = true (a launch of its own, every tile shared): a range may cover
+// the end of one tile and the start of the next, run one after the other.
+// (The loop over segments would raise the registers of the whole-tile
+// kernel, hence two instantiations.)
+template <bool A_FQ, bool SEGS>
+__global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
+  extern __shared__ char lds[];
+  const int b = blockIdx.x;
+  if constexpr (!SEGS) {
+    // One call site for both kinds of workgroup (one inlined copy of the tile).
+    int lin, s0 = 0, s1 = g.steps;
+    float* dst = nullptr;
+    if (b < g.full) {
+      const int per_xcd = g.full / 8;
+      lin = (b & 7) * per_xcd + (b >> 3);
+      if (lin >= g.tiles_m * g.tiles_n) return;
+    } else {
+      // P = tail * z: range w is part w % z of tile w / z, steps
+      // [seg S / z, (seg + 1) S / z) -- the partition below in 32-bit arithmetic
+      const int per_xcd = (g.parts + 7) / 8;
+      const int rb = b - g.full;
+      const int w = (rb & 7) * per_xcd + (rb >> 3);
+      if (w >= g.parts) return;
+      const int z = g.max_seg;
+      const int tt = w / z, seg = w - tt * z;
+      lin = g.full + tt;
+      s0 = seg * g.steps / z;
+      s1 = (seg + 1) * g.steps / z;
+      dst = g.partial + ((int64_t)tt * z + seg) * (BM * BN);
+    }
+    gemm_tile_run<A_FQ>(g, lds, lin, s0, s1, dst);
+    return;
+  }
+  const int per_xcd = (g.parts + 7) / 8;
+  const int w = (b & 7) * per_xcd + (b >> 3);
+  if (w >= g.parts) return;
+  // Workgroup-uniform and < 2^24 (tail <= 256 tiles, steps <= 2^16).
+  const int64_t F = (int64_t)g.tail * g.steps;
+  int f = (int)((int64_t)w * F / g.parts);
+  const int f1 = (int)((int64_t)(w + 1) * F / g.parts);
+  bool first = true;
+  while (f < f1) {
+    const int tt = f / g.steps;
+    const int s0 = f - tt * g.steps;
+    const int s1 = min(g.steps, s0 + (f1 - f));
+    const int seg = w - sk_owner((int64_t)tt * g.steps, F, g.parts);
+    if (!first) __syncthreads();  // every wave is done with the last segment's LDS
+    first = false;
+    gemm_tile_run<A_FQ>(g, lds, g.full + tt, s0, s1,
+                        g.partial + ((int64_t)tt * g.max_seg + seg) * (BM * BN));
+    f += s1 - s0;
+  }
+}
+
+// Shared tiles: out = sum over the tile's segments (in K order) of its
+// tile-local fp32 partials.  64 workgroups per tile, 4 rows of 256 columns each
+// (4 columns per thread).  Z = max_seg (a template argument: all loads are
+// issued before the adds, which run in K order, so the sum waits one memory
+// latency, not Z).
 template <int Z>
 __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
   const int tail = blockIdx.x >> 6;
@@ -181,13 +231,19 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
   gemm_tile_of(g.full + tail, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t row = (int64_t)tm * BM + lr, col = (int64_t)tn * BN + lc;
   if (row >= g.M || col >= g.N) return;
-  const float* p = g.partial + (int64_t)tail * Z * (BM * BN) + lr * BN + lc;
+  const int64_t F = (int64_t)g.tail * g.steps;
+  const int nseg = sk_owner((int64_t)(tail + 1) * g.steps - 1, F, g.parts) -
+                   sk_owner((int64_t)tail * g.steps, F, g.parts) + 1;
+  const float* p = g.partial + (int64_t)tail * g.max_seg * (BM * BN) + lr * BN + lc;
   f32x4 q[Z];
 #pragma unroll
-  for (int z = 0; z < Z; ++z) q[z] = *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN));
+  for (int z = 0; z < Z; ++z)
+    q[z] = z < nseg ? *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 v = q[0];
 #pragma unroll
-  for (int z = 1; z < Z; ++z) v[0] += q[z][0], v[1] += q[z][1], v[2] += q[z][2], v[3] += q[z][3];
+  for (int z = 1; z < Z; ++z)
+    if (z < nseg) v[0] += q[z][0], v[1] += q[z][1], v[2] += q[z][2], v[3] += q[z][3];
   if (g.ga || g.gw) {
     const float alpha = alpha_of(g.ga, g.gw);
     v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
@@ -211,51 +267,81 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
   }
 }
 
+// Most segments of one tile when T tiles of S steps are shared by P workgroups.
+int max_segments(int64_t T, int64_t S, int P) {
+  const int64_t F = T * S;
+  int m = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    const int n = sk_owner((t + 1) * S - 1, F, P) - sk_owner(t * S, F, P) + 1;
+    if (n > m) m = n;
+  }
+  return m;
+}
+
 }  // namespace
 
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   // One 256 x 256 tile per CU at a time (128 KB of LDS), so a launch runs in
-  // rounds of num_cus tiles.  Whole rounds run unsplit; the tiles of a last,
-  // partly filled round (or all tiles, when there are fewer than num_cus) are
-  // split over K so that their parts fill the chip.  For the all-split case a
-  // cost model over rounds and the extra fp32 partial traffic (about 3.5
-  // TFLOP/s per CU and 5 TB/s of HBM) picks z <= 8; every part keeps >= 8
-  // K-steps (512 elements).
+  // rounds of num_cus tiles.  Whole rounds run unsplit.  The rem tiles of a
+  // last, partly filled round are split over K into z = num_cus / rem equal
+  // parts (<= 8, >= 8 steps each), so their parts fill that round; their
+  // workgroups follow the whole tiles' in the same launch and start as CUs
+  // free up.  When there are fewer tiles than CUs, every tile is shared: P
+  // workgroups each take an equal contiguous range of all the tiles' K steps
+  // (>= 8 steps, <= 8 segments per tile), P from a cost model -- the longest
+  // range at about 3.5 TFLOP/s per CU plus the fp32 partials written and read
+  // back at about 5 TB/s -- against the unsplit launch.
   GemmSplitPlan p;
   const int64_t tiles = ((M + BM - 1) / BM) * ((n_out + BN - 1) / BN);
   const int64_t steps = (K + BK - 1) / BK;
-  const int64_t zmax = steps / 8 < kMaxGemmSplits ? steps / 8 : kMaxGemmSplits;
   p.full = tiles;
   p.tail = 0;
-  p.splits = 1;
-  if (zmax < 2) return p;
+  p.parts = 0;
+  p.max_seg = 0;
+  p.own_launch = false;
   if (tiles >= num_cus) {
     const int64_t rem = tiles % num_cus;
     if (rem == 0) return p;
     int64_t z = num_cus / rem;
-    if (z > zmax) z = zmax;
+    if (z > steps / kMinSegSteps) z = steps / kMinSegSteps;
+    if (z > kMaxGemmSegs) z = kMaxGemmSegs;
     if (z < 2) return p;
     p.full = tiles - rem;
     p.tail = rem;
-    p.splits = (int)z;
+    p.parts = (int)(rem * z);
+    p.max_seg = (int)z;
     return p;
   }
-  const double round_s = 2.0 * BM * BN * (double)K / 3.5e12;
-  const double part_s = (double)tiles * BM * BN * 4.0 / 5.0e12;
-  auto cost = [&](int64_t z) {
-    const double rounds = (double)((tiles * z + num_cus - 1) / num_cus);
-    return rounds * round_s / (double)z + (z > 1 ? (double)(z + 1) * part_s : 0.0);
+  const double step_s = 2.0 * BM * BN * BK / 3.5e12;
+  const double seg_s = 2.0 * BM * BN * 4.0 / 5.0e12;
+  const int64_t F = tiles * steps;
+  auto cost = [&](int64_t P) {
+    const double span = (double)((F + P - 1) / P) * step_s;
+    return P > tiles ? span + (double)(P + tiles) * seg_s : span;
   };
-  int64_t best = 1;
-  for (int64_t z = 2; z <= zmax; ++z)
-    if (cost(z) < 0.95 * cost(best)) best = z;
-  if (best > 1) p.full = 0, p.tail = tiles, p.splits = (int)best;
+  int64_t best = tiles;
+  double best_cost = 0.95 * cost(tiles);  // splitting must gain 5%
+  const int64_t pmax = std::min<int64_t>(num_cus, F / kMinSegSteps);
+  for (int64_t P = tiles + 1; P <= pmax; ++P) {
+    const double c = cost(P);
+    if (c < best_cost && max_segments(tiles, steps, (int)P) <= kMaxGemmSegs) {
+      best = P;
+      best_cost = c;
+    }
+  }
+  if (best > tiles) {
+    p.full = 0;
+    p.tail = tiles;
+    p.parts = (int)best;
+    p.max_seg = max_segments(tiles, steps, (int)best);
+    p.own_launch = true;
+  }
   return p;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus) {
   const GemmSplitPlan p = gemm_split_plan(M, n_out, K, num_cus);
-  return p.splits > 1 ? (size_t)p.tail * (size_t)p.splits * BM * BN * sizeof(float) : 0;
+  return p.parts > 0 ? (size_t)p.tail * (size_t)p.max_seg * BM * BN * sizeof(float) : 0;
 }
 
 int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* wc,
@@ -278,35 +364,46 @@ int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* 
   g.gw = alpha.w;
   g.tiles_m = (int)((M + BM - 1) / BM);
   g.tiles_n = (int)((n_out + BN - 1) / BN);
+  g.steps = (int)((K + BK - 1) / BK);
   const GemmSplitPlan p = gemm_split_plan(M, n_out, K, kNumCUs);
-  g.splits = p.splits;
-  g.tail = (int)p.tail;
   g.full = (int)p.full;
-  const int64_t steps = (K + BK - 1) / BK;
-  g.k_split = ((steps + g.splits - 1) / g.splits) * BK;
-  if (g.splits > 1) {
-    g.splits = (int)((K + g.k_split - 1) / g.k_split);  // every part non-empty
-    if (!workspace) return -1;
-  } else {
-    g.full = g.tiles_m * g.tiles_n;  // no split: every tile whole
+  g.tail = (int)p.tail;
+  g.parts = p.parts;
+  g.max_seg = p.max_seg;
+  if (g.parts > 0 && !workspace) return -1;
+  if (g.parts == 0) {
+    g.full = g.tiles_m * g.tiles_n;  // every tile whole
     g.tail = 0;
   }
   g.partial = static_cast<float*>(workspace);
-  // Both bands need a multiple of 8 workgroups: a split plan's `full` is a
-  // multiple of the CU count (or 0); an unsplit one is padded and the extra
-  // workgroups exit, as do those past the last K part.
+  // The bands need a multiple of 8 workgroups (the XCD banding): a split
+  // plan's `full` is a multiple of the CU count (or 0); an unsplit one is
+  // padded and the extra workgroups exit, as do those past the last range.
   if (g.full % 8 != 0) g.full = (g.full + 7) / 8 * 8;
-  const int64_t items = (int64_t)g.tail * g.splits;
-  const int64_t grid = g.full + (items + 7) / 8 * 8;
+  const bool fq = mode == GemmA::kFakeQuant;
+  const int64_t grid = g.full + ((int64_t)g.parts + 7) / 8 * 8;
   if (grid > INT32_MAX) return -1;
-  if (mode == GemmA::kFakeQuant)
-    hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
-  else
-    hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)grid), dim3(kGemmThreads), kLdsBytes, stream, g);
+  // (Both activation modes take the same partition, so the fused-quantizer
+  // product stays bit-identical to quantize + the W4A4 GEMM.)
+  if (p.own_launch) {
+    if (fq)
+      hipLaunchKernelGGL((k_gemm<true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                         kLdsBytes, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm<false, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                         kLdsBytes, stream, g);
+  } else {
+    if (fq)
+      hipLaunchKernelGGL((k_gemm<true, false>), dim3((unsigned)grid), dim3(kGemmThreads),
+                         kLdsBytes, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm<false, false>), dim3((unsigned)grid), dim3(kGemmThreads),
+                         kLdsBytes, stream, g);
+  }
   if (hipGetLastError() != hipSuccess) return -1;
-  if (g.tail > 0) {
+  if (g.parts > 0) {
     const dim3 rg((unsigned)(g.tail * 64));
-    switch (g.splits) {
+    switch (g.max_seg) {
       case 1: hipLaunchKernelGGL(k_gemm_reduce<1>, rg, dim3(256), 0, stream, g); break;
       case 2: hipLaunchKernelGGL(k_gemm_reduce<2>, rg, dim3(256), 0, stream, g); break;
       case 3: hipLaunchKernelGGL(k_gemm_reduce<3>, rg, dim3(256), 0, stream, g); break;

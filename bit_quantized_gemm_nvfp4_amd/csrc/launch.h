@@ -78,12 +78,18 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
 // with GemmA::kFakeQuant its tiles are quantized to NVFP4 and dequantized as
 // they are loaded (the W4A4 product from bf16 activations).  The tiles of a
 // last, partly filled round (or all tiles, when they cannot fill the chip
-// once) are split over K: fp32 tile-local partials in workspace
-// (gemm_workspace_bytes of it), summed in part order by a second kernel.
+// once) share one round of workgroups: their (tile, K step) work is cut into
+// `parts` equal contiguous ranges, one per workgroup, each range's pieces of
+// a tile (segments) writing fp32 tile-local partials to workspace
+// (gemm_workspace_bytes of it), summed in K order by a second kernel.
 struct GemmSplitPlan {
   int64_t full;  // tiles run whole
-  int64_t tail;  // tiles run as `splits` K parts
-  int splits;
+  int64_t tail;  // tiles shared by `parts` workgroups (0: none)
+  int parts;
+  int max_seg;   // most segments of one tail tile (partial slots per tile)
+  bool own_launch;  // the shared round is a launch of its own (every tile is shared);
+                    // otherwise its workgroups follow the whole tiles' in one launch,
+                    // one segment each
 };
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);

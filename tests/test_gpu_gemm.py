@@ -342,6 +342,34 @@ def test_mfma_tail_tiles_split(nv, orc):
     _assert_close(y[:, cols], ref, what="tail split")
     torch.cuda.synchronize()
 
+@pytest.mark.parametrize("M,K,N,slots", [(256, 5120, 256, 8), (300, 3136, 700, 6),
+                                         (512, 5120, 1100, 8), (65, 2080, 4100, 5)])
+def test_mfma_shared_round(nv, orc, M, K, N, slots):
+    """Fewer 256 x 256 tiles than CUs: every tile is shared by one round of
+    workgroups, each taking an equal range of all the tiles' K steps -- the end
+    of one tile and the start of the next -- summed per tile in K order by the
+    reduce (`slots` = most segments of one tile, read off the workspace size).
+    One tile in 8 segments, ragged tiles and N, a partial last K step
+    (K % 64 == 32); every output against the oracle, guarded output, run-to-run
+    bit-identical, and the fused W4A4 tile loads bit-identical to quantize + the
+    W4A4 GEMM on the same partition."""
+    import torch
+    helpers.announce(f"gemm mfma shared round M={M} K={K} N={N}")
+    tiles = -(-M // 256) * -(-N // 256)
+    assert nv.gemm_workspace_size(M, N, K, N) == tiles * slots * 256 * 256 * 4
+    rng = np.random.default_rng(M + K + N)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    y = _run(nv, x, w, out_f32=True)
+    _assert_close(y, orc.gemm_w4a16(x, M, K, w.codes, w.scales), out_f32=True, what="shared")
+    assert np.array_equal(y.view(np.int32), _run(nv, x, w, out_f32=True).view(np.int32))
+    xd, wc, ws = helpers.dev_bf16(x), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    fused = nv.gemm_w4a4(xd, wc, ws, out_dtype=torch.float32, plan={"w4a4_fuse": 1})
+    ac, as_ = nv.quantize(xd)
+    ref = nv.gemm(ac, wc, ws, a_scales=as_, out_dtype=torch.float32)
+    assert torch.equal(fused.view(torch.int32), ref.view(torch.int32))
+
+
 @pytest.mark.parametrize("K,N", [(5120, 17408), (17408, 5120)])
 def test_prefill_full_size_sampled(nv, orc, K, N):
     """The prefill shapes at full size (M = 8192, outlier activations), in the
