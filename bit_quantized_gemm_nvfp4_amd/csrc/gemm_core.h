@@ -231,13 +231,17 @@ __device__ __forceinline__ void read_w(Frags& f, char* lds, const LdsOffsets& o,
                                        int kk, int j) {
   f.w[j] = lds_ref<const u32x4>(lds, o.rd_w[kk ^ (2 * (j & 1))] + buf * kTileBytes + j * 4096);
 }
-// The fragments chunk i (0, 1) of a substep reads for its successor: x[i],
-// w[2i], w[2i+1].
+// The fragments chunk i (0, 1) of a substep reads for its successor: x[i]
+// (if block i is one of the wave's XL live activation blocks), w[2i],
+// w[2i+1] (if any block is live).
+template <int XL>
 __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets& o, uint32_t buf,
                                           int kk, int i) {
-  read_x(f, lds, o, buf, kk, i);
-  read_w(f, lds, o, buf, kk, 2 * i);
-  read_w(f, lds, o, buf, kk, 2 * i + 1);
+  if (i < XL) read_x(f, lds, o, buf, kk, i);
+  if (XL > 0) {
+    read_w(f, lds, o, buf, kk, 2 * i);
+    read_w(f, lds, o, buf, kk, 2 * i + 1);
+  }
 }
 
 // One 64-element step on LDS buffer `cur` while set L is decoded into buffer
@@ -247,8 +251,10 @@ __device__ __forceinline__ void read_frag(Frags& f, char* lds, const LdsOffsets&
 // next step's substep-0 fragments from it into f[0] while its MFMAs run, so no
 // fragment read is left exposed behind the barrier.  (Chunk i of a substep
 // uses all four weight fragments of the substep: its successor's fragments
-// go to the other set.)
-template <bool A_FQ>
+// go to the other set.)  XL: the wave's live activation blocks (2: all; 1:
+// block 0 only; 0: none -- the wave only loads, decodes and meets the others);
+// the MFMAs and operand reads of a dead block are skipped.
+template <bool A_FQ, int XL>
 __device__ __forceinline__ void gemm_step(f32x16 (&acc)[kXBlocks][kWBlocks], Frags (&f)[2],
                                           char* lds, const LdsOffsets& o, uint32_t cur,
                                           uint32_t nxt, const GemmLoad<A_FQ>& L, int kval) {
@@ -259,18 +265,20 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[kXBlocks][kWBlocks], Fra
 #pragma unroll
     for (int i = 0; i < kXBlocks; ++i) {
       if (kk < 3)
-        read_frag(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
+        read_frag<XL>(f[(kk + 1) & 1], lds, o, cur, kk + 1, i);
       else
-        read_frag(f[0], lds, o, nxt, 0, i);
+        read_frag<XL>(f[0], lds, o, nxt, 0, i);
       const int c = 2 * kk + i;  // chunk 0..5 carries pieces c and c + 6
       if (kk < 3) {
         if (c < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c, kval);
         if (c + 6 < kPieces) gemm_store_piece<A_FQ>(lds, o, nxt, L, c + 6, kval);
       }
-      const Frags& fc = f[kk & 1];
+      if (i < XL) {
+        const Frags& fc = f[kk & 1];
 #pragma unroll
-      for (int j = 0; j < kWBlocks; ++j)
-        acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
+        for (int j = 0; j < kWBlocks; ++j)
+          acc[i][j] = mfma_32x32x16_bf16(fc.w[j], fc.x[i], acc[i][j]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -280,19 +288,32 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[kXBlocks][kWBlocks], Fra
 // gives the global row (clamped to a valid one) of tile row t for t < 256;
 // bf16 offsets are relative to `a_base`.  Weight and A_FQ activation rows: the
 // pointer to this lane's half of the row at k = 0.
-template <typename ARow>
-__device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_t K) {
+// The tile row of this thread's copy i (0..3) of a step's activation tile.
+__device__ __forceinline__ int gemm_copy_row(int i) {
+  return 32 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3);
+}
+
+// The same from the global rows of this thread's four copies.
+__device__ __forceinline__ void gemm_src_bf16_rows(GemmSrc& src, const int64_t (&r)[4],
+                                                   int64_t K) {
   const int t = threadIdx.x;
-  const int lw = t & 63, wave = t >> 6, band = 32 * wave;
+  const int lw = t & 63, wave = t >> 6;
   const uint32_t lp = (uint32_t)((lw & 7) ^ (lw >> 3));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t r = abs_row(band + 8 * i + (lw >> 3));
     const uint32_t piece = (lp ^ (uint32_t)(4 * wave + i)) & 7u;  // logical piece
-    src.a_off[i] = (uint32_t)((r * K + 8 * piece) * 2);
+    src.a_off[i] = (uint32_t)((r[i] * K + 8 * piece) * 2);
     // partial step: logical pieces 4..7 step back 32 elements
     src.a_back[i] = (piece & 4) ? 64u : 0u;
   }
+}
+
+template <typename ARow>
+__device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_t K) {
+  int64_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = abs_row(gemm_copy_row(i));
+  gemm_src_bf16_rows(src, r, K);
 }
 
 __device__ __forceinline__ void gemm_src_nvfp4_row(const uint8_t*& c, const uint8_t*& s,
@@ -312,12 +333,15 @@ __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[kXBlocks][kWBlocks])
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-// The whole K loop of one tile: acc += a_tile . w_tile^T.  `lds` is the
-// kLdsBytes of dynamic LDS; every thread of the workgroup calls it.
-template <bool A_FQ>
-__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
-                                              const GemmSrc& src, const uint8_t* a_tile_base,
-                                              int64_t K) {
+// The whole K loop of one tile for a wave with XL live activation blocks;
+// dma_live: the wave's 32-row band of the activation copy is needed.
+// late(src) completes the sources after the first weight loads are issued and
+// before the first activation copy (gathered rows: the weight loads then
+// overlap the wait for the row indices).
+template <bool A_FQ, int XL, typename Late>
+__device__ __forceinline__ void gemm_mainloop_xl(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
+                                                 GemmSrc& src, const uint8_t* a_tile_base,
+                                                 int64_t K, bool dma_live, Late late) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int steps = (int)((K + BK - 1) / BK);
@@ -337,19 +361,21 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks],
   // that publishes the buffer.
   auto dma = [&](int s, uint32_t buf) {
     if constexpr (!A_FQ)
-      dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
+      if (dma_live)
+        dma_a_tile(lds + buf * kTileBytes, src, a_tile_base, kstep(s), kstep(s) + BK <= K);
   };
 
   GemmLoad<A_FQ> L0, L1;
   Frags f[2];
-  dma(0, 0);
   gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(0));
   gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(1));
+  late(src);
+  dma(0, 0);
 #pragma unroll
   for (int c = 0; c < 8; ++c) gemm_store_piece<A_FQ>(lds, o, 0, L0, c, kval(0));
   lds_barrier<A_FQ ? -1 : 0>();
 #pragma unroll
-  for (int i = 0; i < kXBlocks; ++i) read_frag(f[0], lds, o, 0, 0, i);
+  for (int i = 0; i < kXBlocks; ++i) read_frag<XL>(f[0], lds, o, 0, 0, i);
   // At step s: buffer s&1 holds step s, set L[(s+1)&1] holds step s+1 (loaded
   // during step s-1) and set L[s&1] is free and takes step s+2.  The buffer
   // written during the last step is not read.  The scheduling barriers keep
@@ -359,12 +385,42 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks],
     __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_FQ>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
+    gemm_step<A_FQ, XL>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
     dma(s + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
-    gemm_step<A_FQ>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
+    gemm_step<A_FQ, XL>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
+  }
+}
+
+// The whole K loop of one tile: acc += a_tile . w_tile^T.  `lds` is the
+// kLdsBytes of dynamic LDS; every thread of the workgroup calls it.
+// PARTIAL: only tile rows below live_rows are ever stored, so a wave skips the
+// MFMAs and operand reads of its 32-row activation blocks past them and a
+// wave whose copy band lies past them skips its activation copy (each wave
+// runs the loop specialised for its live blocks; all of them still load and
+// decode the weight tile and meet at every barrier).
+struct NoLateSrc {
+  __device__ void operator()(GemmSrc&) const {}
+};
+
+template <bool A_FQ, bool PARTIAL = false, typename Late = NoLateSrc>
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
+                                              GemmSrc& src, const uint8_t* a_tile_base, int64_t K,
+                                              int live_rows = BM, Late late = Late()) {
+  if constexpr (PARTIAL) {
+    const int wave = threadIdx.x >> 6;
+    const int first = (wave >> 1) * 64;  // the wave's first activation row
+    const bool dma_live = 32 * wave < live_rows;
+    if (live_rows > first + 32)
+      gemm_mainloop_xl<A_FQ, 2>(acc, lds, src, a_tile_base, K, dma_live, late);
+    else if (live_rows > first)
+      gemm_mainloop_xl<A_FQ, 1>(acc, lds, src, a_tile_base, K, dma_live, late);
+    else
+      gemm_mainloop_xl<A_FQ, 0>(acc, lds, src, a_tile_base, K, dma_live, late);
+  } else {
+    gemm_mainloop_xl<A_FQ, 2>(acc, lds, src, a_tile_base, K, true, late);
   }
 }
 

@@ -172,29 +172,50 @@ struct GroupedArgs {
 };
 
 // Find (expert, chunk) of workgroup `bx` in the device-side schedule where
-// expert e owns ceil(rows_e / chunk_rows) consecutive chunks.  Wave-uniform.
+// expert e owns ceil(rows_e / chunk_rows) consecutive chunks, and the chunk's
+// first grouped row r0 and its row count.  Wave-uniform.  The offsets of up
+// to 256 experts are loaded in one round (one memory latency, not one per 64
+// experts plus one more for the chunk's rows).
+struct ChunkPos {
+  int e, c, rows;
+  int64_t r0;
+};
 __device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx, int chunk_rows,
-                                           int& e_out, int& c_out) {
+                                           ChunkPos& pos) {
+  constexpr int kRound = 4;  // 64-expert groups per round of loads
   const int lane = threadIdx.x & 63;
   int run = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int ch = e < E ? (offsets[e + 1] - offsets[e] + chunk_rows - 1) / chunk_rows : 0;
-    int inc = ch;  // inclusive prefix over the wave
+  for (int base = 0; base < E; base += 64 * kRound) {
+    int lo[kRound], hi[kRound];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += v;
+    for (int u = 0; u < kRound; ++u) {
+      const int e = base + 64 * u + lane;
+      lo[u] = e < E ? offsets[e] : 0;
+      hi[u] = e < E ? offsets[e + 1] : 0;
     }
-    const int total = __shfl(inc, 63, 64);
-    if (bx < run + total) {
-      const unsigned long long hit = __ballot(run + inc > bx);
-      const int l = __builtin_ctzll(hit);
-      e_out = base + l;
-      c_out = bx - run - (__shfl(inc, l, 64) - __shfl(ch, l, 64));
-      return true;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int gb = base + 64 * u;
+      if (gb >= E) return false;
+      const int ch = gb + lane < E ? (hi[u] - lo[u] + chunk_rows - 1) / chunk_rows : 0;
+      int inc = ch;  // inclusive prefix over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += v;
+      }
+      const int total = __shfl(inc, 63, 64);
+      if (bx < run + total) {
+        const unsigned long long hit = __ballot(run + inc > bx);
+        const int l = __builtin_ctzll(hit);
+        pos.e = gb + l;
+        pos.c = bx - run - (__shfl(inc, l, 64) - __shfl(ch, l, 64));
+        pos.r0 = (int64_t)__shfl(lo[u], l, 64) + (int64_t)pos.c * chunk_rows;
+        pos.rows = (int)min((int64_t)__shfl(hi[u], l, 64) - pos.r0, (int64_t)chunk_rows);
+        return true;
+      }
+      run += total;
     }
-    run += total;
   }
   return false;
 }
@@ -209,11 +230,10 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
   const int ln = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
 
-  int e, c;
-  if (!find_chunk(g.offsets, g.E, blockIdx.x, kGroupRows, e, c)) return;  // uniform
-  const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * kGroupRows;
-  const int64_t r1 = min((int64_t)g.offsets[e + 1], r0 + kGroupRows);
-  const int rows = (int)(r1 - r0);
+  ChunkPos pos;
+  if (!find_chunk(g.offsets, g.E, blockIdx.x, kGroupRows, pos)) return;  // uniform
+  const int e = pos.e, rows = pos.rows;
+  const int64_t r0 = pos.r0;
   const uint16_t* a = g.a;
   const int32_t* gather = g.gather;
   const int stride = lds_x_stride(g.steps);
@@ -311,19 +331,32 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
   const int chunk = (k / g.n_tiles) * 8 + xcd, tn = k % g.n_tiles;
   if (chunk >= g.chunks) return;
-  int e, c;
-  if (!find_chunk(g.offsets, g.E, chunk, BM, e, c)) return;  // uniform over the workgroup
-  const int64_t r0 = (int64_t)g.offsets[e] + (int64_t)c * BM;
-  const int rows = (int)(min((int64_t)g.offsets[e + 1], r0 + BM) - r0);
+  ChunkPos pos;
+  if (!find_chunk(g.offsets, g.E, chunk, BM, pos)) return;  // uniform over the workgroup
+  const int e = pos.e, rows = pos.rows;
+  const int64_t r0 = pos.r0;
   const int64_t K = g.K, N = g.N, half_n = N / 2;
   const int t = threadIdx.x;
 
+  // The gathered row indices of this thread's activation copies (rows past
+  // the chunk repeat its last row) are loaded now and used only after the
+  // first weight loads are issued; the epilogue's row and expert scales are
+  // loaded now too, so no memory latency is left at either end of the tile.
+  int64_t arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + min(gemm_copy_row(i), rows - 1);
+    arow[i] = g.gather ? (int64_t)g.gather[r] : r;
+  }
+  float rs[kXBlocks];
+#pragma unroll
+  for (int i = 0; i < kXBlocks; ++i) {
+    const int tr = gemm_tile_row(i);
+    rs[i] = g.row_scale && tr < rows ? g.row_scale[r0 + tr] : 1.0f;
+  }
+  const float ge = g.wg ? g.wg[e] : 1.0f;  // the sums are h / g_e
+
   GemmSrc src;
-  const int32_t* gather = g.gather;
-  gemm_src_bf16(src, [&](int tr) {
-    const int64_t r = r0 + min(tr, rows - 1);  // rows past the chunk repeat its last row
-    return (int64_t)(gather ? gather[r] : r);
-  }, K);
   const uint8_t* we_c = g.wc + (int64_t)e * N * (K / 2);
   const uint8_t* we_s = g.ws + (int64_t)e * N * (K / 16);
   {
@@ -341,16 +374,16 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
 
   f32x16 acc[kXBlocks][kWBlocks];
   gemm_zero_acc(acc);
-  gemm_mainloop<false>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K);
+  // (an expert's last chunk is partly filled: waves skip the 32-row blocks past it)
+  gemm_mainloop<false, true>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K, rows,
+                             [&](GemmSrc& s) { gemm_src_bf16_rows(s, arow, K); });
 
   const int wn = (t >> 6) & 1, h = (t & 63) >> 5;
-  const float ge = g.wg ? g.wg[e] : 1.0f;  // the sums are h / g_e
 #pragma unroll
   for (int i = 0; i < kXBlocks; ++i) {
     const int tr = gemm_tile_row(i);
     if (tr >= rows) continue;
     const int64_t row = r0 + tr;
-    const float rs = g.row_scale ? g.row_scale[row] : 1.0f;
     if (g.swiglu) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -367,7 +400,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
               const float hg = acc[i][j][4 * q + 2 * p + w] * ge;
               const float hu = acc[i][j + 2][4 * q + 2 * p + w] * ge;
               v[w] = hg / (1.0f + expf(-hg)) * hu;
-              if (g.row_scale) v[w] *= rs;
+              if (g.row_scale) v[w] *= rs[i];
             }
             pk[p] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
           }
@@ -385,7 +418,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             float v0 = acc[i][j][4 * q + 2 * p] * ge, v1 = acc[i][j][4 * q + 2 * p + 1] * ge;
-            if (g.row_scale) v0 *= rs, v1 *= rs;
+            if (g.row_scale) v0 *= rs[i], v1 *= rs[i];
             pk[p] = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
           }
           *reinterpret_cast<u32x2*>(g.out + row * N + col) = u32x2{pk[0], pk[1]};

@@ -102,15 +102,26 @@ def test_grouped_mfma_matches_oracle(nv, orc, epi, gathered, scaled):
     assert ok, (rf, worst)
 
 
+# Last-chunk fills: 127, 128, 129, 255, 1 and 0 rows, with and without whole
+# chunks before them; then every boundary of the 32-row activation blocks the
+# tile's waves skip (a wave holds rows 64 q .. 64 q + 63 of the chunk as two
+# blocks), with a partial last K step (K % 64 == 32).
+_PARTIAL_CHUNKS = {
+    "fills": (320, [128, 129, 255, 257, 384, 385, 127, 0, 513]),
+    "blocks": (352, [1, 31, 32, 33, 64, 65, 96, 97, 160, 161, 192, 193, 224, 225, 287]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_PARTIAL_CHUNKS))
 @pytest.mark.parametrize("epi", [0, 1])
-def test_grouped_mfma_partial_chunks(nv, orc, epi):
-    """Experts whose last 256-row chunk holds 127, 128, 129, 255, 1 and 0 rows,
-    with and without whole chunks before it: every row against the oracle,
-    guarded output."""
-    helpers.announce(f"moe grouped mfma partial chunks epi={epi}")
-    rng = np.random.default_rng(80 + epi)
-    E, K, N = 9, 320, 288
-    counts = np.array([128, 129, 255, 257, 384, 385, 127, 0, 513])
+def test_grouped_mfma_partial_chunks(nv, orc, epi, case):
+    """Experts with partly filled 256-row chunks through the grouped MFMA
+    kernel: every row against the oracle, guarded output."""
+    helpers.announce(f"moe grouped mfma partial chunks {case} epi={epi}")
+    rng = np.random.default_rng(80 + epi + (10 if case == "blocks" else 0))
+    K, counts = _PARTIAL_CHUNKS[case]
+    counts = np.array(counts)
+    E, N = len(counts), 288
     R = int(counts.sum())
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     a = workloads.normal_bf16(rng, 700, K)
