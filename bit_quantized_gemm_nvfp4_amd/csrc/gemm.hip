@@ -65,8 +65,8 @@ __device__ __forceinline__ void gemm_tile_of(int lin, int tiles_m, int tiles_n, 
 }
 
 // Tile `lin` over K steps [s0, s1): the output (dst null, whole K) or the
-// tile-local fp32 partial at dst.
-template <bool A_FQ>
+// tile-local fp32 partial at dst (always, when PART_ONLY).
+template <bool A_FQ, bool PART_ONLY = false>
 __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int lin, int s0,
                                               int s1, float* dst) {
   int tm, tn;
@@ -99,7 +99,7 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's part.
-  if (dst) {  // fp32 partial of this segment, tile-local [256][256]
+  if (PART_ONLY || dst) {  // fp32 partial of this segment, tile-local [256][256]
 #pragma unroll
     for (int i = 0; i < kXBlocks; ++i)
 #pragma unroll
@@ -113,6 +113,27 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
   }
   const bool scaled = g.ga || g.gw;
   const float alpha = scaled ? alpha_of(g.ga, g.gw) : 1.0f;
+  if (!g.out_f32 && (g.N & 7) == 0) {  // (the output is 16-byte aligned)
+    __syncthreads();  // every wave is done with the operand buffers
+#pragma unroll
+    for (int i = 0; i < kXBlocks; ++i)
+#pragma unroll
+      for (int j = 0; j < kWBlocks; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+          float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+          if (scaled) v0 *= alpha, v1 *= alpha, v2 *= alpha, v3 *= alpha;
+          stage_put<BN>(lds, gemm_tile_row(i), gemm_tile_col(j, q),
+                        u32x2{(uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16),
+                              (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16)});
+        }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(g.out) + m0 * g.N + n0;
+    stage_store<BN>(lds, (int)min((int64_t)BM, g.M - m0), (int)min((int64_t)BN, g.N - n0),
+                    [&](int r) { return out + (int64_t)r * g.N; });
+    return;
+  }
   const bool vec = (g.N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < kXBlocks; ++i) {
@@ -211,8 +232,8 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
     const int seg = w - sk_owner((int64_t)tt * g.steps, F, g.parts);
     if (!first) __syncthreads();  // every wave is done with the last segment's LDS
     first = false;
-    gemm_tile_run<A_FQ>(g, lds, g.full + tt, s0, s1,
-                        g.partial + ((int64_t)tt * g.max_seg + seg) * (BM * BN));
+    gemm_tile_run<A_FQ, true>(g, lds, g.full + tt, s0, s1,
+                              g.partial + ((int64_t)tt * g.max_seg + seg) * (BM * BN));
     f += s1 - s0;
   }
 }

@@ -434,4 +434,37 @@ __device__ __forceinline__ int gemm_tile_col(int j, int q) {
   return ((threadIdx.x >> 6) & 1) * 128 + j * 32 + 8 * q + 4 * ((threadIdx.x & 63) >> 5);
 }
 
+// Output staging.  An accumulator block's natural store writes 16 bytes into
+// each of 32 rows per instruction (32 partly written cache lines); once the K
+// loop is done the operand buffers are free, so the bf16 output tile is
+// written to LDS as [256 rows][C columns] (16-byte pieces of a row swizzled
+// by the row, so the 32 rows of one write land on distinct banks) and stored
+// from there a whole row run per 16 lanes (C = 256: 64 lanes cover two rows
+// of 512 contiguous bytes).
+template <int C>
+__device__ __forceinline__ uint32_t stage_off(int row, int col) {
+  constexpr int P = C / 8;  // 16-byte pieces per row
+  return (uint32_t)(row * (C * 2) + (((col >> 3) ^ (row % P)) << 4) + (col & 7) * 2);
+}
+
+// Four consecutive bf16 outputs (packed) at tile (row, col), col % 4 == 0.
+template <int C>
+__device__ __forceinline__ void stage_put(char* lds, int row, int col, const u32x2& v) {
+  lds_ref<u32x2>(lds, stage_off<C>(row, col)) = v;
+}
+
+// Store tile rows [0, nrows) x columns [0, ncols) (ncols % 8 == 0) of the
+// staged tile; row_ptr(r) is the 16-byte aligned output address of row r's
+// first tile column.  Every thread of the workgroup calls it, after a
+// barrier that follows the last stage_put.
+template <int C, typename RowPtr>
+__device__ __forceinline__ void stage_store(char* lds, int nrows, int ncols, RowPtr row_ptr) {
+  constexpr int P = C / 8, kRowsPerPass = kGemmThreads / P;
+  const int t = threadIdx.x, p = t % P;
+  if (8 * p >= ncols) return;
+  for (int r = t / P; r < nrows; r += kRowsPerPass)
+    *reinterpret_cast<u32x4*>(row_ptr(r) + 8 * p) =
+        lds_ref<const u32x4>(lds, (uint32_t)(r * (C * 2)) + ((p ^ (r % P)) << 4));
+}
+
 }  // namespace nvfp4

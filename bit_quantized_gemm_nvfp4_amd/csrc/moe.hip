@@ -150,6 +150,13 @@ __global__ void __launch_bounds__(256) k_align_scatter(const int32_t* __restrict
   if (gates) row_gates[dest] = gates[p];
 }
 
+// SwiGLU of one output: silu(g) * u = g / (1 + e^-g) * u, in fp32 with the
+// hardware exponential and reciprocal (a few ulp of fp32, far below the bf16
+// rounding of the stored result).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __frcp_rn(1.0f + __expf(-g)) * u;
+}
+
 // ---- grouped GEMV -------------------------------------------------------------
 
 constexpr int kGroupRows = 16;  // rows of one expert per workgroup (one 16-row MFMA tile)
@@ -277,7 +284,7 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
       const int64_t col = gt * 16 + ln;
       if (col < width) {
         const float hg = acc[0][0][r] * ge, hu = acc[TR - 1][0][r] * ge;
-        float v = hg / (1.0f + expf(-hg)) * hu;
+        float v = silu_mul(hg, hu);
         if (g.row_scale) v *= rs;
         g.out[row * width + col] = f32_to_bf16_bits(v);
       }
@@ -378,19 +385,19 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   gemm_mainloop<false, true>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K, rows,
                              [&](GemmSrc& s) { gemm_src_bf16_rows(s, arow, K); });
 
+  // Staged output (N % 16 == 0 and a 16-byte aligned output: every row run is
+  // aligned); the blocks past the chunk's rows are not written.
+  __syncthreads();  // every wave is done with the operand buffers
   const int wn = (t >> 6) & 1, h = (t & 63) >> 5;
+  if (g.swiglu) {
 #pragma unroll
-  for (int i = 0; i < kXBlocks; ++i) {
-    const int tr = gemm_tile_row(i);
-    if (tr >= rows) continue;
-    const int64_t row = r0 + tr;
-    if (g.swiglu) {
+    for (int i = 0; i < kXBlocks; ++i) {
+      const int tr = gemm_tile_row(i);
+      if (tr >= rows) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t col = (int64_t)tn * 128 + wn * 64 + j * 32 + 8 * q + 4 * h;
-          if (col >= half_n) continue;  // half_n % 16 == 0: the 4 columns are in or out
           uint32_t pk[2];
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -399,21 +406,28 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
             for (int w = 0; w < 2; ++w) {
               const float hg = acc[i][j][4 * q + 2 * p + w] * ge;
               const float hu = acc[i][j + 2][4 * q + 2 * p + w] * ge;
-              v[w] = hg / (1.0f + expf(-hg)) * hu;
+              v[w] = silu_mul(hg, hu);
               if (g.row_scale) v[w] *= rs[i];
             }
             pk[p] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
           }
-          *reinterpret_cast<u32x2*>(g.out + row * half_n + col) = u32x2{pk[0], pk[1]};
+          stage_put<BN / 2>(lds, tr, wn * 64 + j * 32 + 8 * q + 4 * h, u32x2{pk[0], pk[1]});
         }
       }
-    } else {
+    }
+    __syncthreads();
+    uint16_t* out = g.out + r0 * half_n + (int64_t)tn * 128;
+    stage_store<BN / 2>(lds, rows, (int)min((int64_t)128, half_n - (int64_t)tn * 128),
+                        [&](int r) { return out + (int64_t)r * half_n; });
+  } else {
+#pragma unroll
+    for (int i = 0; i < kXBlocks; ++i) {
+      const int tr = gemm_tile_row(i);
+      if (tr >= rows) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t col = (int64_t)tn * BN + gemm_tile_col(j, q);
-          if (col >= N) continue;  // N % 16 == 0
           uint32_t pk[2];
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -421,10 +435,14 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
             if (g.row_scale) v0 *= rs[i], v1 *= rs[i];
             pk[p] = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
           }
-          *reinterpret_cast<u32x2*>(g.out + row * N + col) = u32x2{pk[0], pk[1]};
+          stage_put<BN>(lds, tr, gemm_tile_col(j, q), u32x2{pk[0], pk[1]});
         }
       }
     }
+    __syncthreads();
+    uint16_t* out = g.out + r0 * N + (int64_t)tn * BN;
+    stage_store<BN>(lds, rows, (int)min((int64_t)BN, N - (int64_t)tn * BN),
+                    [&](int r) { return out + (int64_t)r * N; });
   }
 }
 
