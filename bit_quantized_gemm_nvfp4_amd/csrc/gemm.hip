@@ -99,14 +99,14 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's part.
-  if (PART_ONLY || dst) {  // fp32 partial of this segment, tile-local [256][256]
+  if (PART_ONLY || dst) {  // fp32 partial of this segment, in register order
 #pragma unroll
     for (int i = 0; i < kXBlocks; ++i)
 #pragma unroll
       for (int j = 0; j < kWBlocks; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(dst + gemm_tile_row(i) * BN + gemm_tile_col(j, q)) =
+          reinterpret_cast<f32x4*>(dst)[((i * kWBlocks + j) * 4 + q) * kGemmThreads + t] =
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                     acc[i][j][4 * q + 3]};
     return;
@@ -238,53 +238,79 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   }
 }
 
-// Shared tiles: out = sum over the tile's segments (in K order) of its
-// tile-local fp32 partials.  64 workgroups per tile, 4 rows of 256 columns each
-// (4 columns per thread).  Z = max_seg (a template argument: all loads are
-// issued before the adds, which run in K order, so the sum waits one memory
-// latency, not Z).
+// Shared tiles: out = sum over the tile's segments (in K order) of its fp32
+// partials.  A workgroup takes 32 rows x 128 columns of a tile: the rows of
+// accumulator block i of wave pair wm and the columns of weight half wn, i.e.
+// groups (i, j, q) of the 64 lanes of wave 2 wm + wn -- 16 runs of 1 KB of
+// the register order.  Each thread reads 4 f32x4 per segment, sums them in K
+// order, stages the sums in LDS as [32][128] and the workgroup stores whole
+// row runs.  Z = max_seg (a template argument: all loads of a group are
+// issued before the adds, so the sum waits one memory latency, not Z).
+constexpr int kReduceRows = 32, kReduceCols = 128, kReducePad = 4;
 template <int Z>
 __global__ void __launch_bounds__(256) k_gemm_reduce(GemmArgs g) {
-  const int tail = blockIdx.x >> 6;
-  const int lr = (blockIdx.x & 63) * 4 + (threadIdx.x >> 6);
-  const int lc = (threadIdx.x & 63) * 4;
+  __shared__ float st[kReduceRows][kReduceCols + kReducePad];
+  const int tail = blockIdx.x >> 4, part = blockIdx.x & 15;
+  const int wm = part >> 2, i = (part >> 1) & 1, wn = part & 1;
   int tm, tn;
   gemm_tile_of(g.full + tail, g.tiles_m, g.tiles_n, tm, tn);
-  const int64_t row = (int64_t)tm * BM + lr, col = (int64_t)tn * BN + lc;
-  if (row >= g.M || col >= g.N) return;
   const int64_t F = (int64_t)g.tail * g.steps;
   const int nseg = sk_owner((int64_t)(tail + 1) * g.steps - 1, F, g.parts) -
                    sk_owner((int64_t)tail * g.steps, F, g.parts) + 1;
-  const float* p = g.partial + (int64_t)tail * g.max_seg * (BM * BN) + lr * BN + lc;
-  f32x4 q[Z];
+  const f32x4* p = reinterpret_cast<const f32x4*>(g.partial + (int64_t)tail * g.max_seg * (BM * BN));
+  const int lane = threadIdx.x & 63, tt = (2 * wm + wn) * 64 + lane;
+  const float alpha = (g.ga || g.gw) ? alpha_of(g.ga, g.gw) : 1.0f;
 #pragma unroll
-  for (int z = 0; z < Z; ++z)
-    q[z] = z < nseg ? *reinterpret_cast<const f32x4*>(p + (int64_t)z * (BM * BN))
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 v = q[0];
+  for (int s = 0; s < 4; ++s) {
+    const int jq = 4 * s + (threadIdx.x >> 6);  // (j, q) of this group
+    const int grp = (i * kWBlocks + (jq >> 2)) * 4 + (jq & 3);
+    const int64_t idx = (int64_t)grp * kGemmThreads + tt;
+    f32x4 q[Z];
 #pragma unroll
-  for (int z = 1; z < Z; ++z)
-    if (z < nseg) v[0] += q[z][0], v[1] += q[z][1], v[2] += q[z][2], v[3] += q[z][3];
-  if (g.ga || g.gw) {
-    const float alpha = alpha_of(g.ga, g.gw);
-    v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
+    for (int z = 0; z < Z; ++z)
+      q[z] = z < nseg ? p[(int64_t)z * (BM * BN / 4) + idx] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 v = q[0];
+#pragma unroll
+    for (int z = 1; z < Z; ++z)
+      if (z < nseg) v[0] += q[z][0], v[1] += q[z][1], v[2] += q[z][2], v[3] += q[z][3];
+    if (g.ga || g.gw) v[0] *= alpha, v[1] *= alpha, v[2] *= alpha, v[3] *= alpha;
+    const int c = acc_col(tt, jq >> 2, jq & 3) - wn * 128;
+    *reinterpret_cast<f32x4*>(&st[lane & 31][c]) = v;
   }
-  const int64_t off = row * g.N + col;
-  if ((g.N & 3) == 0 && col + 3 < g.N) {
-    if (g.out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + off) = v;
+  __syncthreads();
+  // 32 rows x 128 columns: 16 threads per row, 8 columns each, two passes
+  const int64_t row0 = (int64_t)tm * BM + wm * 64 + i * 32;
+  const int64_t col0 = (int64_t)tn * BN + wn * 128;
+  const int c8 = (threadIdx.x & 15) * 8;
+  const int64_t col = col0 + c8;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = pass * 16 + (threadIdx.x >> 4);
+    const int64_t row = row0 + r;
+    if (row >= g.M || col >= g.N) continue;
+    const float* v = &st[r][c8];
+    const int64_t off = row * g.N + col;
+    if ((g.N & 7) == 0 && col + 7 < g.N) {
+      if (g.out_f32) {
+        float* o = static_cast<float*>(g.out) + off;
+        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      } else {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pk[e] = (uint32_t)f32_to_bf16_bits(v[2 * e]) |
+                  ((uint32_t)f32_to_bf16_bits(v[2 * e + 1]) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + off) = pk;
+      }
     } else {
-      const u32x2 pk = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
-                        (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = pk;
+      for (int e = 0; e < 8 && col + e < g.N; ++e) {
+        if (g.out_f32)
+          static_cast<float*>(g.out)[off + e] = v[e];
+        else
+          static_cast<uint16_t*>(g.out)[off + e] = f32_to_bf16_bits(v[e]);
+      }
     }
-    return;
-  }
-  for (int e = 0; e < 4 && col + e < g.N; ++e) {
-    if (g.out_f32)
-      static_cast<float*>(g.out)[off + e] = v[e];
-    else
-      static_cast<uint16_t*>(g.out)[off + e] = f32_to_bf16_bits(v[e]);
   }
 }
 
@@ -423,7 +449,7 @@ int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* 
   }
   if (hipGetLastError() != hipSuccess) return -1;
   if (g.parts > 0) {
-    const dim3 rg((unsigned)(g.tail * 64));
+    const dim3 rg((unsigned)(g.tail * 16));
     switch (g.max_seg) {
       case 1: hipLaunchKernelGGL(k_gemm_reduce<1>, rg, dim3(256), 0, stream, g); break;
       case 2: hipLaunchKernelGGL(k_gemm_reduce<2>, rg, dim3(256), 0, stream, g); break;

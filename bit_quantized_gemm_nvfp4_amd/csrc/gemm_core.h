@@ -424,15 +424,24 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks],
   }
 }
 
-// Output coordinates of accumulator register e of acc[i][j] in this lane:
+// Output coordinates of accumulator register e of acc[i][j] in thread t:
 // tile row wm*64 + i*32 + l%32, tile column wn*128 + j*32 + 8*(e/4) +
-// 4*(l/32) + e%4 (registers 4q .. 4q+3 are 4 consecutive columns).
-__device__ __forceinline__ int gemm_tile_row(int i) {
-  return ((threadIdx.x >> 6) >> 1) * 64 + i * 32 + (threadIdx.x & 31);
+// 4*(l/32) + e%4 (registers 4q .. 4q+3 are 4 consecutive columns; wave
+// t/64 = 2 wm + wn, lane l = t%64).
+__device__ __forceinline__ int acc_row(int t, int i) {
+  return ((t >> 6) >> 1) * 64 + i * 32 + (t & 31);
 }
-__device__ __forceinline__ int gemm_tile_col(int j, int q) {
-  return ((threadIdx.x >> 6) & 1) * 128 + j * 32 + 8 * q + 4 * ((threadIdx.x & 63) >> 5);
+__device__ __forceinline__ int acc_col(int t, int j, int q) {
+  return ((t >> 6) & 1) * 128 + j * 32 + 8 * q + 4 * ((t & 63) >> 5);
 }
+__device__ __forceinline__ int gemm_tile_row(int i) { return acc_row(threadIdx.x, i); }
+__device__ __forceinline__ int gemm_tile_col(int j, int q) { return acc_col(threadIdx.x, j, q); }
+
+// A tile's fp32 partial sums (a shared tile's segment) are kept in register
+// order: group g = (i * kWBlocks + j) * 4 + q (4 consecutive columns) of
+// thread t at f32x4 index g * kGemmThreads + t, so each store instruction of
+// a wave writes 1 KB contiguous (the tile's row-major order put 16 bytes into
+// each of 32 rows per instruction: 7.6 us of stores per segment against 2.7).
 
 // Output staging.  An accumulator block's natural store writes 16 bytes into
 // each of 32 rows per instruction (32 partly written cache lines); once the K
