@@ -322,6 +322,28 @@ def test_mfma_w4a4_ragged(nv, orc, M, K, N):
 
 
 
+@pytest.mark.parametrize("M,K,N,shared", [(300, 3136, 712, True), (1300, 2560, 12808, False)])
+def test_mfma_split_tiles_partial_last_column_tile(nv, orc, M, K, N, shared):
+    """Split tiles whose last column tile is partial with N % 8 == 0, so the
+    reduce stores whole 8-column runs up to the edge: a shared round (6 tiles)
+    and a split last round (306 tiles: 50 split, the last 8 columns wide).
+    bf16 and fp32 outputs, guarded; columns around every tile edge against the
+    oracle (all of them for the shared round)."""
+    helpers.announce(f"gemm mfma split tiles partial column tile M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + N + 5)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    if shared:
+        cols = np.arange(N, dtype=np.int32)
+    else:
+        edges = np.arange(0, N + 1, 256)
+        cols = np.unique(np.clip(np.concatenate([edges - 1, edges, edges + 7, [N - 8, N - 1]]),
+                                 0, N - 1)).astype(np.int32)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=cols)
+    _assert_close(_run(nv, x, w)[:, cols], ref, what="bf16")
+    _assert_close(_run(nv, x, w, out_f32=True)[:, cols], ref, out_f32=True, what="fp32")
+
+
 def test_mfma_tail_tiles_split(nv, orc):
     """300 tiles on 256 CUs: the first 256 run whole, the last 44 (columns
     10752 .. 12796 in the tile order) run as 5 K parts summed by the reduce
