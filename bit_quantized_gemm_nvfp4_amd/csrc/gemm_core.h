@@ -284,16 +284,17 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[kXBlocks][kWBlocks], Fra
   }
 }
 
-// Sources of the tile's rows for this thread.  Activation rows: abs_row(t)
-// gives the global row (clamped to a valid one) of tile row t for t < 256;
-// bf16 offsets are relative to `a_base`.  Weight and A_FQ activation rows: the
-// pointer to this lane's half of the row at k = 0.
 // The tile row of this thread's copy i (0..3) of a step's activation tile.
 __device__ __forceinline__ int gemm_copy_row(int i) {
   return 32 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3);
 }
 
-// The same from the global rows of this thread's four copies.
+// Sources of the tile's rows for this thread.  bf16 activation rows: the byte
+// offsets (relative to the tile's base, k = 0) of this thread's four copies
+// from their global rows r[i] (gemm_src_bf16_rows), or from abs_row(t), the
+// global row (clamped to a valid one) of tile row t (gemm_src_bf16).  Weight
+// and A_FQ activation rows: the pointer to this lane's half of the row at k =
+// 0 (gemm_src_nvfp4_row).
 __device__ __forceinline__ void gemm_src_bf16_rows(GemmSrc& src, const int64_t (&r)[4],
                                                    int64_t K) {
   const int t = threadIdx.x;
