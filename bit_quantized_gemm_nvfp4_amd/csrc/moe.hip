@@ -24,17 +24,21 @@ constexpr int kAlignBlock = 256;  // assignments per align workgroup
 // ---- align: block histograms -> per-(block, expert) bases -> ranked scatter ----
 
 // Entries of sid[base .. p) equal to e (base 16-byte aligned): 16-byte LDS
-// reads, several in flight, instead of one dependent read per entry.
-__device__ __forceinline__ int count_before(const int* sid, int base, int p, int e) {
-  const int n = p - base;
+// reads, several in flight, instead of one dependent read per entry.  With G
+// threads per entry, thread g of them counts the 4-entry groups g, g + G, ...
+// (and g = 0 the last partial group); their counts add up to the total.
+__device__ __forceinline__ int count_before(const int* sid, int base, int p, int e, int g = 0,
+                                            int G = 1) {
+  const int n = p - base, n4 = n >> 2;
   const int4* v = reinterpret_cast<const int4*>(sid + base);
-  int r = 0, q = 0;
+  int r = 0;
 #pragma unroll 4
-  for (; q + 4 <= n; q += 4) {
-    const int4 x = v[q >> 2];
+  for (int j = g; j < n4; j += G) {
+    const int4 x = v[j];
     r += (x.x == e) + (x.y == e) + (x.z == e) + (x.w == e);
   }
-  for (; q < n; ++q) r += sid[base + q] == e;
+  if (g == 0)
+    for (int q = 4 * n4; q < n; ++q) r += sid[base + q] == e;
   return r;
 }
 
@@ -489,6 +493,9 @@ __global__ void __launch_bounds__(256) k_moe_combine(const uint16_t* __restrict_
 // Small batches (R <= 2048 assignments, a decode step): the same three phases
 // in one workgroup of 1024 threads, through LDS, with the same result (the
 // per-(block, expert) bases and the in-block ranks define one stable order).
+// The ids and gates are read together at the start (one memory latency), the
+// expert totals are scanned by wave shuffles (two barriers), and up to four
+// threads share the ranking of one entry when there are threads to spare.
 constexpr int kAlignSmallMax = 2048;
 
 __global__ void __launch_bounds__(1024) k_align_small(const int32_t* __restrict__ ids,
@@ -499,12 +506,16 @@ __global__ void __launch_bounds__(1024) k_align_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ slot_pos,
                                                       float* __restrict__ row_gates) {
   __shared__ __attribute__((aligned(16))) int sid[kAlignSmallMax];
+  __shared__ float sg[kAlignSmallMax];
   __shared__ int hist[(kAlignSmallMax / kAlignBlock) * kMoeMaxExperts];
-  __shared__ int tot[kMoeMaxExperts];
-  const int t = threadIdx.x;
+  __shared__ int wsum[kMoeMaxExperts / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nb = (R + kAlignBlock - 1) / kAlignBlock;
+  for (int p = t; p < R; p += blockDim.x) {
+    sid[p] = ids[p];
+    if (gates) sg[p] = gates[p];
+  }
   for (int i = t; i < nb * E; i += blockDim.x) hist[i] = 0;
-  for (int p = t; p < R; p += blockDim.x) sid[p] = ids[p];
   __syncthreads();
   for (int p = t; p < R; p += blockDim.x) {
     const int e = sid[p];
@@ -518,29 +529,39 @@ __global__ void __launch_bounds__(1024) k_align_small(const int32_t* __restrict_
       hist[b * E + t] = total;
       total += h;
     }
-  tot[t] = t < E ? total : 0;
-  __syncthreads();
-  for (int d = 1; d < kMoeMaxExperts; d <<= 1) {  // inclusive scan of the totals
-    const int v = t >= d ? tot[t - d] : 0;
-    __syncthreads();
-    tot[t] += v;
-    __syncthreads();
+  // inclusive scan of the totals over the threads: within each wave, then
+  // the sums of the waves before it
+  int inc = total;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += v;
   }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += wsum[w];
   if (t < E) {
-    const int excl = tot[t] - total;
+    const int excl = inc - total;
     offsets[t] = excl;
     for (int b = 0; b < nb; ++b) hist[b * E + t] += excl;
   }
-  if (t == E - 1) offsets[E] = tot[t];
+  if (t == E - 1) offsets[E] = inc;
   __syncthreads();
-  for (int p = t; p < R; p += blockDim.x) {
+  // G neighbouring threads rank entry p; their partial counts meet in lane g = 0
+  const int lg = R <= 256 ? 2 : (R <= 512 ? 1 : 0), G = 1 << lg;
+  for (int i = t; i < (R << lg); i += blockDim.x) {
+    const int p = i >> lg, g = i & (G - 1);
     const int e = sid[p];
-    if (e < 0 || e >= E) continue;
+    const bool valid = e >= 0 && e < E;
     const int b = p / kAlignBlock;
-    const int dest = hist[b * E + e] + count_before(sid, b * kAlignBlock, p, e);
-    gather_idx[dest] = p / topk;
-    slot_pos[p] = dest;
-    if (gates) row_gates[dest] = gates[p];
+    int r = valid ? count_before(sid, b * kAlignBlock, p, e, g, G) : 0;
+    for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o, 64);
+    if (valid && g == 0) {
+      const int dest = hist[b * E + e] + r;
+      gather_idx[dest] = p / topk;
+      slot_pos[p] = dest;
+      if (gates) row_gates[dest] = sg[p];
+    }
   }
 }
 
