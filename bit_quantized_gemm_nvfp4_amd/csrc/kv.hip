@@ -43,6 +43,21 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
   return ((b >> 24) & 0x80u) | c;
 }
 
+// q = v / d, r = v - q*d for 0 <= v < bound, d > 0 (d uniform).  When the
+// index range and d fit 31 bits (a uniform test) the division is 32-bit, a
+// few instructions instead of the long 64-bit sequence.
+__device__ __forceinline__ void divmod_index(int64_t v, int64_t d, int64_t bound, int64_t& q,
+                                             int64_t& r) {
+  if (bound < ((int64_t)1 << 31) && d < ((int64_t)1 << 31)) {
+    const uint32_t q32 = (uint32_t)v / (uint32_t)d;
+    q = q32;
+    r = (int64_t)((uint32_t)v - q32 * (uint32_t)d);
+  } else {
+    q = v / d;
+    r = v - q * d;
+  }
+}
+
 // 8 bf16 values (one 16-byte word) -> 8 codes (two 32-bit words).
 __device__ __forceinline__ u32x2 encode8(u32x4 xw, float scale) {
   uint32_t w[2] = {0u, 0u};
@@ -89,12 +104,18 @@ __global__ void __launch_bounds__(256) k_kv_load(const uint8_t* __restrict__ cac
                                                  uint16_t* __restrict__ out) {
   const int64_t per_row = W / 16;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * max_len * per_row) return;
-  const int64_t row = idx / per_row, c = idx - row * per_row;
-  const int64_t b = row / max_len, i = row - b * max_len;
+  const int64_t n = B * max_len * per_row;
+  if (idx >= n) return;
+  int64_t row, c, b, i, page, pos;
+  divmod_index(idx, per_row, n, row, c);
+  divmod_index(row, max_len, n, b, i);
+  divmod_index(i, page_size, n, page, pos);
+  // the length and the page entry are loaded together (the entry is in the
+  // table whenever its index is; it is used only below the length)
+  const int32_t len = seq_lens[b];
+  const int32_t entry = page < max_pages ? block_table[b * max_pages + page] : -1;
   int64_t slot = -1;
-  if (i < seq_lens[b] && i / page_size < max_pages)
-    slot = (int64_t)block_table[b * max_pages + i / page_size] * page_size + i % page_size;
+  if (i < len && entry >= 0) slot = (int64_t)entry * page_size + pos;
   u32x4* dst = reinterpret_cast<u32x4*>(out + row * W + c * 16);
   if (slot < 0 || slot >= num_slots) {
     dst[0] = u32x4{0u, 0u, 0u, 0u};
