@@ -38,8 +38,34 @@ __global__ void __launch_bounds__(256) k_dequantize(const uint8_t* __restrict__ 
   o[3] = dequant8_bf16(w[3], s1);
 }
 
+// Launches that fit one round of the chip (kPiecesMax lanes, 8 resident
+// 256-thread workgroups per CU) are bound by each thread's serial instruction
+// stream, not by memory: they take one lane per 8 elements (one 16-byte piece
+// of bf16) instead of 32 or 16 per thread.  Larger ones keep the wider
+// threads, which move the same bytes with fewer instructions.
+constexpr int64_t kPiecesMax = 256 * 8 * 256;
+
+// One lane per 8 elements: 4 code bytes and the block's scale byte in, one
+// 16-byte piece of bf16 out.
+__global__ void __launch_bounds__(256) k_dequantize_pieces(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           int64_t pieces,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= pieces) return;
+  const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[t];
+  const float s = e4m3_to_f32<0>((uint32_t)scales[t >> 1]);
+  reinterpret_cast<u32x4*>(out)[t] = dequant8_bf16(w, s);
+}
+
 int launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
                       uint16_t* out, hipStream_t stream) {
+  const int64_t pieces = N * (K / 8);
+  if (pieces <= kPiecesMax) {
+    hipLaunchKernelGGL(k_dequantize_pieces, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       stream, codes, scales, pieces, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   int64_t cpr = K / 32, total = N * cpr;
   int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(k_dequantize, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales,
@@ -99,8 +125,30 @@ __global__ void __launch_bounds__(256) k_quantize(const uint16_t* __restrict__ x
   *reinterpret_cast<uint16_t*>(scales + m * (K / 16) + c * 2) = (uint16_t)(s0 | (s1 << 8));
 }
 
+// One lane per 8 elements: the two lanes of a 16-element block exchange their
+// maxima, each writes its 4 code bytes and the even one the scale byte.  The
+// element count is a multiple of 32 (K % 32 == 0), so the lanes of a block
+// are present or absent together.
+__global__ void __launch_bounds__(256) k_quantize_pieces(const uint16_t* __restrict__ x,
+                                                         int64_t pieces,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= pieces) return;
+  const u32x4 v = reinterpret_cast<const u32x4*>(x)[t];
+  const uint32_t sc = pair_scale_code(v);
+  reinterpret_cast<uint32_t*>(codes)[t] = piece_codes(v, sc, e4m3_to_f32<0>(sc));
+  if ((t & 1) == 0) scales[t >> 1] = (uint8_t)sc;
+}
+
 int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                     hipStream_t stream) {
+  const int64_t pieces = M * (K / 8);
+  if (pieces <= kPiecesMax) {
+    hipLaunchKernelGGL(k_quantize_pieces, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       stream, x, pieces, codes, scales);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   int64_t cpr = K / 32, total = M * cpr;
   int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, x, cpr, total,
@@ -123,7 +171,23 @@ __global__ void __launch_bounds__(256) k_fakequant(const uint16_t* __restrict__ 
   dst[1] = v1;
 }
 
+// One lane per 8 elements (fakequant_piece: the block's two lanes exchange
+// their maxima).
+__global__ void __launch_bounds__(256) k_fakequant_pieces(const uint16_t* __restrict__ x,
+                                                          int64_t pieces,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= pieces) return;
+  reinterpret_cast<u32x4*>(out)[t] = fakequant_piece(reinterpret_cast<const u32x4*>(x)[t]);
+}
+
 int launch_fakequant(const uint16_t* x, int64_t M, int64_t K, uint16_t* out, hipStream_t stream) {
+  const int64_t pieces = M * (K / 8);
+  if (pieces <= kPiecesMax) {
+    hipLaunchKernelGGL(k_fakequant_pieces, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       stream, x, pieces, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int64_t blocks = M * (K / 16);
   hipLaunchKernelGGL(k_fakequant, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream, x,
                      blocks, out);

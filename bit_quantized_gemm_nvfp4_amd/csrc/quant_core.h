@@ -58,12 +58,12 @@ __device__ __forceinline__ uint32_t e2m1_index(float ax, const Thresholds& th) {
   return (hi ? 4u : 0u) | (mid ? 2u : 0u) | (lo ? 1u : 0u);
 }
 
-// The 8 values of one 16-byte piece quantized with a block's scale code sc
-// and dequantized: e2m1(code) * e4m3(sc) rounded to bf16 (exact).
-__device__ __forceinline__ u32x4 fakequant_with(u32x4 v, uint32_t sc) {
-  const float s = e4m3_to_f32<0>(sc);
+// The 8 codes of one 16-byte piece (8 bf16 values) under its block's scale
+// code sc (value s): element e in nibble e, so element 2j is the low nibble
+// of byte j.
+__device__ __forceinline__ uint32_t piece_codes(u32x4 v, uint32_t sc, float s) {
   const Thresholds th = make_thresholds(s);
-  uint32_t codes = 0;  // 8 codes, element 2i in nibble 2i
+  uint32_t codes = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -73,7 +73,14 @@ __device__ __forceinline__ u32x4 fakequant_with(u32x4 v, uint32_t sc) {
       codes |= (mag | ((bits >> 12) & 8u)) << (4 * (2 * i + h));
     }
   }
-  return dequant8_bf16(codes, s);
+  return codes;
+}
+
+// The 8 values of one 16-byte piece quantized with a block's scale code sc
+// and dequantized: e2m1(code) * e4m3(sc) rounded to bf16 (exact).
+__device__ __forceinline__ u32x4 fakequant_with(u32x4 v, uint32_t sc) {
+  const float s = e4m3_to_f32<0>(sc);
+  return dequant8_bf16(piece_codes(v, sc, s), s);
 }
 
 __device__ __forceinline__ uint32_t piece_amax_bits(u32x4 v) {
@@ -83,14 +90,20 @@ __device__ __forceinline__ uint32_t piece_amax_bits(u32x4 v) {
   return m;  // non-negative finite bf16: integer order
 }
 
+// Scale code of the block whose two 16-byte pieces sit in this lane and the
+// neighbouring one (lane ^ 1): both lanes must be active.
+__device__ __forceinline__ uint32_t pair_scale_code(u32x4 v) {
+  uint32_t amax_bits = piece_amax_bits(v);
+  amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 1, 64));
+  return scale_code_from_amax(bf16_bits_to_f32(amax_bits));
+}
+
 // Fake quantization of one 16-byte piece (8 bf16 values) of a block whose
 // other 8 values sit in the neighbouring lane (lane ^ 1): both lanes must be
 // active.  Returns the 8 values quantized and dequantized, bit-identical to
 // nvfp4_quantize followed by nvfp4_dequantize.
 __device__ __forceinline__ u32x4 fakequant_piece(u32x4 v) {
-  uint32_t amax_bits = piece_amax_bits(v);
-  amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 1, 64));
-  return fakequant_with(v, scale_code_from_amax(bf16_bits_to_f32(amax_bits)));
+  return fakequant_with(v, pair_scale_code(v));
 }
 
 // The same for a whole block held by one thread (pieces v0, v1).

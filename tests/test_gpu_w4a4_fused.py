@@ -27,10 +27,12 @@ def _x(rng, M, K):
     return x
 
 
+# Up to (300, 1056) the quantizer launches take one lane per 8 elements;
+# (1040, 4096) is past one round of the chip and takes the wider threads.
 @pytest.mark.parametrize("M,K,N", [
     (1, 512, 1024), (3, 800, 333), (4, 5120, 4096), (5, 512, 1000), (8, 5120, 17408),
     (16, 800, 300), (17, 2048, 520), (32, 5120, 4000), (40, 1024, 777), (64, 512, 64),
-    (65, 512, 300), (300, 1056, 520),
+    (65, 512, 300), (300, 1056, 520), (1040, 4096, 64),
 ])
 def test_fused_equals_quantize_then_gemm(nv, M, K, N):
     import torch
