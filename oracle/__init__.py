@@ -83,6 +83,8 @@ def lib():
         L.oracle_e2m1_encode_array.restype = None
         L.oracle_dequantize.argtypes = [_U8, _U8, _i64, _i64, _U16]
         L.oracle_dequantize.restype = None
+        L.oracle_tile_weight.argtypes = [_U8, _U8, _i64, _i64, _U8]
+        L.oracle_tile_weight.restype = None
         L.oracle_quantize.argtypes = [_U16, _i64, _i64, _U8, _U8]
         L.oracle_quantize.restype = None
         L.oracle_gemm_w4a16.argtypes = [_U16, _i64, _i64, _U8, _U8, _nullable(_I32), _i64, _F64]
@@ -185,6 +187,17 @@ def bf16_to_f64(bits) -> np.ndarray:
     """bf16 bit patterns -> fp64 values (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def tiled_weight_bytes(N: int, K: int) -> int:
+    return ((N + 15) // 16) * ((K + 255) // 256) * 2304
+
+
+def tile_weight(codes, scales, N: int, K: int) -> np.ndarray:
+    """The tiled byte order of NF4W(N, K) (uint8, tiled_weight_bytes(N, K))."""
+    out = np.empty(tiled_weight_bytes(N, K), dtype=np.uint8)
+    lib().oracle_tile_weight(_c(codes, np.uint8), _c(scales, np.uint8), N, K, out)
+    return out
 
 
 def dequantize(codes, scales, N: int, K: int) -> np.ndarray:

@@ -146,6 +146,40 @@ void oracle_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t N, i
     }
 }
 
+/* Tiled NVFP4 weights: the library's own byte order for streaming (not from
+ * the pages; its definition is the one stated in the library's public header
+ * for nvfp4_tile_weight).  Rows are grouped in tiles of 16, K in steps of 256
+ * elements; block (t, s) occupies bytes [(t*S + s)*2304, +2304), S =
+ * ceil(K/256).  Written here element by element: code element (r, k) of the
+ * row-major matrix goes to
+ *     block (r/16, k/256), byte 1024*h + 16*(16*q + r%16) + (k%32)/2,
+ *     nibble k%2 (low nibble = even k),
+ * with q = (k%256)/64, h = (k%64)/32; scale byte (r, b) of elements
+ * 16b .. 16b+15 goes to
+ *     block (r/16, b/16), byte 2048 + 4*(16*q + r%16) + b%4, q = (b%16)/4.
+ * Every other byte (rows past N, elements past K) is zero.  `out` holds
+ * ceil(N/16) * S * 2304 bytes. */
+void oracle_tile_weight(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                        uint8_t *out)
+{
+    int64_t T = (N + 15) / 16, S = (K + 255) / 256;
+    memset(out, 0, (size_t)(T * S * 2304));
+    for (int64_t r = 0; r < N; ++r) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t kk = k % 256, q = kk / 64, h = (kk % 64) / 32;
+            int64_t off = ((r / 16) * S + k / 256) * 2304 + 1024 * h + 16 * (16 * q + r % 16) +
+                          (k % 32) / 2;
+            unsigned code = code_at(codes + r * (K / 2), k);
+            out[off] |= (uint8_t)(code << (4 * (k % 2)));
+        }
+        for (int64_t b = 0; b < K / 16; ++b) {
+            int64_t q = (b % 16) / 4;
+            int64_t off = ((r / 16) * S + b / 16) * 2304 + 2048 + 4 * (16 * q + r % 16) + b % 4;
+            out[off] = scales[r * (K / 16) + b];
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Quantization                                                               */
 /* ------------------------------------------------------------------------ */
