@@ -20,7 +20,8 @@ __all__ = [
     "library_path", "dequantize", "quantize", "gemm", "gemm_workspace_size", "moe_align",
     "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3",
     "kv_load_e4m3", "quantize_scaled", "quantize_weight", "gemm_w4a4", "dequantize_scaled",
-    "gemm_scaled", "Plan", "make_plan", "BF16", "FP32", "NVFP4", "EPI_NONE", "EPI_SWIGLU",
+    "gemm_scaled", "tiled_weight_bytes", "tile_weight", "gemm_tiled", "gemm_tiled_workspace_size",
+    "Plan", "make_plan", "BF16", "FP32", "NVFP4", "EPI_NONE", "EPI_SWIGLU",
 ]
 
 BF16, FP32, NVFP4 = 0, 1, 2
@@ -68,6 +69,10 @@ _SIGS = {
     "nvfp4_grouped_gemm_scaled": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                    _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_moe_combine": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_tiled_weight_bytes": ([_i64, _i64], _sz),
+    "nvfp4_tile_weight": ([_vp, _vp, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_gemm_tiled_workspace_size": ([_int, _i64, _i64, _i64], _sz),
+    "nvfp4_gemm_tiled": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_noalloc_scratch_bytes": ([], _sz),
     "nvfp4_gemm_noalloc": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp,
                             _vp], _int),
@@ -91,6 +96,9 @@ _SIGS.update({
     "nvfp4_gemm_w4a4_bf16_workspace_size_planned": ([_pp, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_gemm_w4a4_bf16_planned": ([_pp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp,
                                       _vp, _sz, _vp], _int),
+    "nvfp4_gemm_tiled_workspace_size_planned": ([_pp, _int, _i64, _i64, _i64], _sz),
+    "nvfp4_gemm_tiled_planned": ([_pp, _int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _sz,
+                                  _vp], _int),
     "nvfp4_grouped_gemm_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                     _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_scaled_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp,
@@ -312,6 +320,58 @@ def gemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, a_scale
         _check(lib().nvfp4_gemm_planned(_plan_ref(plan), *args))
     else:
         _check(lib().nvfp4_gemm(*args))
+    return out
+
+
+# ---- tiled weights (include/nvfp4.h: NF4T) ----------------------------------------------
+
+def tiled_weight_bytes(N: int, K: int) -> int:
+    """Bytes of the tiled layout of an N x K NVFP4 matrix (0 for an invalid shape)."""
+    return int(lib().nvfp4_tiled_weight_bytes(N, K))
+
+
+def tile_weight(w_codes: torch.Tensor, w_scales: torch.Tensor, out=None) -> torch.Tensor:
+    """The tiled layout (a 1-d uint8 tensor) of NVFP4 weights [N, K/2] + [N, K/16]."""
+    N, K = _weights(w_codes, w_scales)
+    nbytes = tiled_weight_bytes(N, K)
+    _arg(out, "out", torch.uint8, (nbytes,), optional=True)
+    _gpu(w_codes, w_scales, out)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w_codes.device)
+    _check(lib().nvfp4_tile_weight(_ptr(w_codes), _ptr(w_scales), N, K, _ptr(out),
+                                   _stream(w_codes.device)))
+    return out
+
+
+def gemm_tiled_workspace_size(M: int, N: int, K: int, w4a4: bool = False, plan=None) -> int:
+    dt = NVFP4 if w4a4 else BF16
+    if plan is not None:
+        return int(lib().nvfp4_gemm_tiled_workspace_size_planned(_plan_ref(plan), dt, M, N, K))
+    return int(lib().nvfp4_gemm_tiled_workspace_size(dt, M, N, K))
+
+
+def gemm_tiled(a: torch.Tensor, w_tiled: torch.Tensor, N: int, a_scales=None,
+               out_dtype=torch.bfloat16, out=None, workspace=None, plan=None) -> torch.Tensor:
+    """y = a . W^T with W given in the tiled layout (tile_weight) of N rows; a
+    as in gemm (bf16 [M, K], or NVFP4 codes with a_scales)."""
+    M, K, w4a4 = _activations(a, a_scales)
+    if K % 32:
+        raise ValueError(f"K={K} is not a multiple of 32")
+    if int(N) < 1:
+        raise ValueError("N must be positive")
+    _arg(w_tiled, "w_tiled", torch.uint8, (tiled_weight_bytes(N, K),))
+    odt = _out_dtype(out_dtype)
+    _arg(out, "out", out_dtype, (M, N), optional=True)
+    _gpu(a, a_scales, w_tiled, out, workspace)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    ws, wsz = _workspace(gemm_tiled_workspace_size(M, N, K, w4a4, plan), a.device, workspace)
+    args = (NVFP4 if w4a4 else BF16, _ptr(a), _ptr(a_scales), M, N, K, _ptr(w_tiled), odt,
+            _ptr(out), _ptr(ws), wsz, _stream(a.device))
+    if plan is not None:
+        _check(lib().nvfp4_gemm_tiled_planned(_plan_ref(plan), *args))
+    else:
+        _check(lib().nvfp4_gemm_tiled(*args))
     return out
 
 

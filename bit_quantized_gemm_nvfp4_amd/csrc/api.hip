@@ -99,6 +99,19 @@ bool gemv_plan_ok(const PlanOverride& ov, int64_t M, int64_t K, bool fused) {
   return true;
 }
 
+// Whether a plan's GEMV fields name a built tiled layout: the 16x16 kernel
+// with 1, 2 or 4 (one activation tile) tiles per wave and 4, 8 or 16 (two
+// activation tiles) waves; no K parts inside a workgroup.
+bool tiled_plan_ok(const PlanOverride& ov, int64_t M, int64_t K) {
+  if (ov.gemv_kparts > 1 || ov.gemv_small_max > 8) return false;
+  if (ov.gemv_lds_kib >= 0 && (ov.gemv_lds_kib < 8 || ov.gemv_lds_kib > 160)) return false;
+  const GemvPlan p = plan_gemv(M, 1, K, kNumCUs, ov, true);
+  if (p.small) return (p.tr == 1 || (p.tr == 2 && p.mt == 1)) && p.nw >= 1 && p.nw <= 8;
+  const bool tr_ok = p.tr == 1 || p.tr == 2 || (p.tr == 4 && p.mt == 1);
+  const bool nw_ok = p.nw == 4 || p.nw == 8 || (p.nw == 16 && p.mt == 2);
+  return tr_ok && nw_ok;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +292,126 @@ int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
   return gemm_impl(a_dtype, a, a_scales, M, N, K, w_codes, w_scales, row_idx, n_out, out_dtype,
                    out, workspace, workspace_bytes, stream, alpha, PlanOverride{});
 }
+
+// ---- tiled weights --------------------------------------------------------------
+
+namespace {
+
+struct TiledPlan {
+  GemvPlan gemv;
+  int64_t m_chunk;
+  size_t a_dequant_bytes;
+  size_t partial_bytes;
+};
+
+TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool w4a4, const PlanOverride& ov) {
+  TiledPlan t;
+  t.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
+  t.gemv = plan_gemv(t.m_chunk, N, K, kNumCUs, ov, true);
+  t.partial_bytes = gemv_workspace_bytes(t.gemv, t.m_chunk, N);
+  t.a_dequant_bytes = w4a4 ? (size_t)M * (size_t)K * 2 : 0;
+  return t;
+}
+
+size_t tiled_workspace(int a_dtype, int64_t M, int64_t N, int64_t K, const PlanOverride& ov) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const TiledPlan t = plan_tiled(M, N, K, a_dtype == NVFP4_NVFP4, ov);
+  const size_t p_off = round_up(t.a_dequant_bytes, 256);
+  return p_off + t.partial_bytes == 0 ? 0 : p_off + t.partial_bytes;
+}
+
+int gemm_tiled_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+                    int64_t K, const uint8_t* w_tiled, int out_dtype, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream, const PlanOverride& ov) {
+  if (a_dtype != NVFP4_BF16 && a_dtype != NVFP4_NVFP4) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!a || !w_tiled || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (M <= 0 || N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_FP32) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (N > INT32_MAX || M > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(a) || !aligned16(w_tiled) || !aligned16(out)) return NVFP4_ERROR_INVALID_VALUE;
+  if ((a_dtype == NVFP4_BF16) != (a_scales == nullptr)) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_scales && !aligned16(a_scales)) return NVFP4_ERROR_INVALID_VALUE;
+  const bool w4a4 = a_dtype == NVFP4_NVFP4;
+  const TiledPlan t = plan_tiled(M, N, K, w4a4, ov);
+  const size_t p_off = round_up(t.a_dequant_bytes, 256);
+  const size_t need = p_off + t.partial_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return NVFP4_ERROR_INVALID_VALUE;
+  hipStream_t st = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(a);
+  if (w4a4) {
+    uint16_t* xa = static_cast<uint16_t*>(workspace);
+    if (launch_dequantize(static_cast<const uint8_t*>(a), a_scales, M, K, xa, st) != 0)
+      return NVFP4_ERROR_LAUNCH;
+    x = xa;
+  }
+  void* partial = t.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
+  const size_t osz = out_dtype == NVFP4_FP32 ? 4 : 2;
+  if (log_enabled())
+    fprintf(stderr, "[nvfp4] gemm_tiled M=%lld N=%lld K=%lld: mt=%d tr=%d nw=%d z=%d\n",
+            (long long)M, (long long)N, (long long)K, t.gemv.mt, t.gemv.tr, t.gemv.nw, t.gemv.z);
+  for (int64_t m0 = 0; m0 < M; m0 += t.m_chunk) {
+    const int64_t mc = (M - m0) < t.m_chunk ? (M - m0) : t.m_chunk;
+    if (launch_gemv_tiled(t.gemv, x + m0 * K, mc, K, w_tiled, N, out_dtype == NVFP4_FP32,
+                          static_cast<char*>(out) + m0 * N * osz, partial, st) != 0)
+      return NVFP4_ERROR_LAUNCH;
+  }
+  return NVFP4_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_tiled_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return tiled_weight_bytes(N, K);
+}
+
+int nvfp4_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                      uint8_t* w_tiled, void* stream) {
+  if (!codes || !scales || !w_tiled) return NVFP4_ERROR_INVALID_VALUE;
+  if (N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_tiled))
+    return NVFP4_ERROR_INVALID_VALUE;
+  return launched(launch_tile_weight(codes, scales, N, K, w_tiled, as_stream(stream)));
+}
+
+size_t nvfp4_gemm_tiled_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K) {
+  return tiled_workspace(a_dtype, M, N, K, PlanOverride{});
+}
+
+int nvfp4_gemm_tiled(int a_dtype, const void* a, const uint8_t* a_scales, int64_t M, int64_t N,
+                     int64_t K, const uint8_t* w_tiled, int out_dtype, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_tiled_impl(a_dtype, a, a_scales, M, N, K, w_tiled, out_dtype, out, workspace,
+                         workspace_bytes, stream, PlanOverride{});
+}
+
+size_t nvfp4_gemm_tiled_workspace_size_planned(const nvfp4_plan_t* plan, int a_dtype, int64_t M,
+                                               int64_t N, int64_t K) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return 0;
+  return tiled_workspace(a_dtype, M, N, K, ov);
+}
+
+int nvfp4_gemm_tiled_planned(const nvfp4_plan_t* plan, int a_dtype, const void* a,
+                             const uint8_t* a_scales, int64_t M, int64_t N, int64_t K,
+                             const uint8_t* w_tiled, int out_dtype, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  if (M > 0 && K > 0 && K % 32 == 0 && !tiled_plan_ok(ov, M < 32 ? M : 32, K))
+    return NVFP4_ERROR_INVALID_VALUE;
+  return gemm_tiled_impl(a_dtype, a, a_scales, M, N, K, w_tiled, out_dtype, out, workspace,
+                         workspace_bytes, stream, ov);
+}
+
+}  // extern "C"
 
 // W4A4 from bf16 activations.  The kernel can quantize the activations
 // itself as it loads them (no extra launch and no activation copy in memory),

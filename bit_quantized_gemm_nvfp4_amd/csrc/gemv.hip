@@ -40,7 +40,9 @@ struct GemvArgs {
   const float* gw;         // *ga * *gw (null: 1); applied to final sums only
 };
 
-template <int MT, int TR, int NW, bool FQ>
+// TL: the weights are tiled (tile.hip; a.wc is the tiled array, a.ws unused)
+// and every step is whole.
+template <int MT, int TR, int NW, bool FQ, bool TL = false>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
   // Scale blocks and the fp16 path fit the register budget of 4 waves per SIMD
@@ -48,11 +50,12 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   // window piece per thread); with two tiles in smaller workgroups they cost a
   // wave per SIMD, more than the fetched bytes and vector instructions they
   // save.
-  constexpr bool BLK = MT == 1 || NW == 16;
+  // Tiled weights bring their scales in the step's own loads: no scale blocks.
+  constexpr bool BLK = !TL && (MT == 1 || NW == 16);
   // fp16 path (plain W4A16): steps whose activations are exact in fp16 run
   // the fp16 MFMA on weights decoded with packed fp16 multiplies (half the
   // vector instructions).  The fused W4A4 staging keeps the bf16 path.
-  constexpr bool H = !FQ && BLK;
+  constexpr bool H = !FQ && (MT == 1 || NW == 16);
   __shared__ uint16_t win[2 * 16 * MT * kXWin];  // bf16, or fp16 (H)
   __shared__ int hflag[2];
   __shared__ uint32_t scl[BLK ? NW * TR * 512 : 1];
@@ -67,13 +70,24 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   const int64_t tile0 = ((int64_t)blockIdx.x * NW + wave) * TR;
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
+  if constexpr (TL) {
+    const int64_t last = (a.n_out + 15) / 16 - 1;
 #pragma unroll
-  for (int t = 0; t < TR; ++t) {
-    int64_t j = (tile0 + t) * 16 + ln;
-    if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
-    const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
-    cptr[t] = a.wc + row * (K / 2);
-    sptr[t] = a.ws + row * (K / 16);
+    for (int t = 0; t < TR; ++t) {
+      const int64_t tile = min(tile0 + t, last);  // padding tile: never stored
+      const uint8_t* tb = a.wc + tile * a.steps * 2304;
+      cptr[t] = tb + 16 * lane;
+      sptr[t] = tb + 2048 + 4 * lane;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      int64_t j = (tile0 + t) * 16 + ln;
+      if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
+      const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
+      cptr[t] = a.wc + row * (K / 2);
+      sptr[t] = a.ws + row * (K / 16);
+    }
   }
   int xrow_off[MT];
 #pragma unroll
@@ -100,8 +114,9 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
                                                  zs0, zs1, row_ptr);
   }
   if (!blocks)
-    gemv_accumulate_win<MT, TR, XP, FQ, H>(acc, cptr, sptr, win, hflag, xrow_off, a.M,
-                                           K, zs0, zs1, (int)(K / kGemvStep), row_ptr);
+    gemv_accumulate_win<MT, TR, XP, FQ, H, TL>(acc, cptr, sptr, win, hflag, xrow_off, a.M, K,
+                                               zs0, zs1, TL ? a.steps : (int)(K / kGemvStep),
+                                               row_ptr);
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
   const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
@@ -282,6 +297,82 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
   }
 }
 
+// Very small M (<= 8) on tiled weights: the 4x4x4-block MFMA with per-block
+// scaling (g4t_compute).  blockIdx.x picks nw*TR tiles of 16 weight rows, a
+// wave TR of them; blockIdx.y a contiguous part of K (256-element steps).
+template <int MG, int TR>
+__global__ void __launch_bounds__(512) k_gemv4_tiled(GemvArgs a) {
+  extern __shared__ uint16_t xs[];  // [M][steps of this part * 256 + kXPad]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int ln = lane & 15, q = lane >> 4;
+  const int64_t K = a.K;
+
+  const int zs0 = (int)(((int64_t)a.steps * blockIdx.y) / gridDim.y);
+  const int zs1 = (int)(((int64_t)a.steps * (blockIdx.y + 1)) / gridDim.y);
+  const int nsteps = zs1 - zs0;
+  const uint16_t* x = a.x;
+  const int stride = nsteps * kTileStep + kXPad;
+  auto stage = [&]() {
+    stage_activations<false>(xs, a.M, (int64_t)zs0 * kTileStep, nsteps * kTileStep, stride, K,
+                             [x, K](int m) { return x + (int64_t)m * K; });
+  };
+
+  const int64_t tile0 = ((int64_t)blockIdx.x * nw + wave) * TR;
+  const int64_t last = (a.n_out + 15) / 16 - 1;
+  const uint8_t* cptr[TR];
+  const uint8_t* sptr[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const int64_t tile = min(tile0 + t, last);  // padding tile: never stored
+    const uint8_t* tb = a.wc + tile * a.steps * 2304;
+    cptr[t] = tb + 16 * lane;
+    sptr[t] = tb + 2048 + 4 * lane;
+  }
+  const uint16_t* xl[MG];
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int m = min(4 * g + (lane & 3), a.M - 1);  // padding row: never stored
+    xl[g] = xs + m * stride + 64 * q;
+  }
+
+  f32x4 acc[TR][MG];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  g4t_accumulate<MG, TR>(acc, cptr, sptr, xl, zs0, zs1, stage);
+
+  // acc[t][g][r] of lane (q, ln) is quarter q's part of activation row 4g+r,
+  // weight row 16*tile + ln; sum the quarters, then lane q == r % 4 stores.
+  const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
+  const float alpha = scaled ? alpha_of(a.ga, a.gw) : 1.0f;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    const int64_t j = (tile0 + t) * 16 + ln;
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * g + r;
+        if (m >= a.M) continue;  // uniform
+        const float s4 = gemv4t_reduce(acc[t][g][r]);
+        const float v = scaled ? s4 * alpha : s4;
+        if (q != r || j >= a.n_out) continue;
+        const int64_t o = (int64_t)m * a.n_out + j;
+        if (gridDim.y > 1)
+          a.partial[(int64_t)blockIdx.y * a.M * a.n_out + o] = v;
+        else if (a.out_f32)
+          static_cast<float*>(a.out)[o] = v;
+        else
+          static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
 // Sum of the K parts of a split-K launch, in part order (bit-identical from
 // run to run).  A thread owns V consecutive outputs (V = 4 when count % 4 ==
 // 0 and the output is aligned for 4-element stores).  The parts are loaded in
@@ -372,6 +463,42 @@ void launch_gemv_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
     hipLaunchKernelGGL((k_gemv<MT, TR, 4, FQ>), grid, dim3(256), 0, stream, a);
 }
 
+// Sum of the z > 1 K parts of a split-K GEMV launch (nothing when z == 1).
+int splitk_reduce(int z, int64_t M, int64_t n_out, bool out_f32, void* out, void* workspace,
+                  Alpha alpha, hipStream_t stream) {
+  if (z <= 1) return 0;
+  const int64_t count = M * n_out;
+  const float* part = static_cast<const float*>(workspace);
+  const uintptr_t oa = reinterpret_cast<uintptr_t>(out) % (out_f32 ? 16 : 8);
+  if (count % 4 == 0 && oa == 0)
+    hipLaunchKernelGGL(k_splitk_reduce<4>, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256),
+                       0, stream, part, z, count, out_f32 ? 1 : 0, alpha.a, alpha.w, out);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                       stream, part, z, count, out_f32 ? 1 : 0, alpha.a, alpha.w, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int MT, int TR>
+int launch_gemv_tiled_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
+  const int64_t tiles = (a.n_out + 15) / 16;
+  const int64_t per_wg = (int64_t)nw * TR;
+  dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
+  if constexpr (MT == 2) {
+    if (nw == 16) {
+      hipLaunchKernelGGL((k_gemv<MT, TR, 16, false, true>), grid, dim3(1024), 0, stream, a);
+      return 0;
+    }
+  }
+  if (nw == 8)
+    hipLaunchKernelGGL((k_gemv<MT, TR, 8, false, true>), grid, dim3(512), 0, stream, a);
+  else if (nw == 4)
+    hipLaunchKernelGGL((k_gemv<MT, TR, 4, false, true>), grid, dim3(256), 0, stream, a);
+  else
+    return -2;
+  return 0;
+}
+
 // The K-parts layouts that are built: (tiles per wave, tile groups, parts).
 struct KpLayout {
   int tr, g, kp;
@@ -431,13 +558,15 @@ int launch_plan(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
 
 }  // namespace
 
-GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanOverride& ov) {
+GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanOverride& ov,
+                   bool tiled) {
   GemvPlan p;
   // largest M for the 4x4x4-block kernel with per-block scaling
   const int64_t small_max = ov.gemv_small_max >= 0 ? ov.gemv_small_max : 4;
   p.small = M <= small_max;
   p.mt = p.small ? (int)((M + 3) / 4) : (M <= 16 ? 1 : 2);
-  p.tr = 2;
+  // tiled weights: the 4x4x4 kernel's tiles are 16 rows, one per wave
+  p.tr = tiled && p.small ? 1 : 2;
   // Wide workgroups (8 waves; on the 16x16 path they share one activation
   // window) when there are rows enough to fill the chip with them, 4 waves
   // otherwise (measured: the 248,320-row head at M = 1 takes ~10% less time
@@ -458,8 +587,8 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
   if (ov.gemv_tiles >= 0) p.tr = ov.gemv_tiles;
   if (ov.gemv_waves >= 0) p.nw = ov.gemv_waves;
   const int64_t lds_budget = ov.gemv_lds_kib >= 0 ? (int64_t)ov.gemv_lds_kib * 1024 : 64 * 1024;
-  const int64_t step = p.small ? kG4Step : kGemvStep;
-  const int64_t rows_per_tile = p.small ? 4 : 16;
+  const int64_t step = p.small && !tiled ? kG4Step : kGemvStep;
+  const int64_t rows_per_tile = p.small && !tiled ? 4 : 16;
   const int64_t steps = (K + step - 1) / step;
   int64_t z = 1;
   if (p.small) {  // the 4x4x4 kernel stages its whole K part: it must fit LDS
@@ -500,7 +629,7 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
   // layers wide enough for 1.5 workgroups of 4 tiles per CU (measured at M = 8:
   // the 32,768-row masked head 27.7 -> 23.8 us; on the 17,408-row layer the
   // 272 workgroups leave some CUs with two and the split-K launch is as fast)
-  const bool kp_default = ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
+  const bool kp_default = !tiled && ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
                           ov.gemv_splits < 0 && !p.small && M <= 8 && K % kGemvStep == 0 &&
                           p.z >= 2 && steps >= 2 && (tiles + 3) / 4 >= (int64_t)num_cus * 3 / 2;
   if (kp_default) {
@@ -509,7 +638,7 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
     p.kp = 2;
     p.z = 1;
   }
-  if (ov.gemv_kparts > 1 && !p.small && K % kGemvStep == 0) {
+  if (!tiled && ov.gemv_kparts > 1 && !p.small && K % kGemvStep == 0) {
     p.kp = ov.gemv_kparts;
     if (ov.gemv_splits <= 0) p.z = 1;
     if ((int64_t)p.z * p.kp > steps) p.z = (int)(steps / p.kp);  // every part >= 1 step
@@ -596,20 +725,60 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
     rc = launch_plan<false, 2, 1>(a, p, stream);
   if (rc != 0) return rc;
   if (hipGetLastError() != hipSuccess) return -1;
-  if (p.z > 1) {
-    const int64_t count = M * n_out;
-    const float* part = static_cast<const float*>(workspace);
-    const uintptr_t oa = reinterpret_cast<uintptr_t>(out) % (out_f32 ? 16 : 8);
-    if (count % 4 == 0 && oa == 0)
-      hipLaunchKernelGGL(k_splitk_reduce<4>, dim3((unsigned)((count / 4 + 255) / 256)),
-                         dim3(256), 0, stream, part, p.z, count, out_f32 ? 1 : 0, alpha.a,
-                         alpha.w, out);
-    else
-      hipLaunchKernelGGL(k_splitk_reduce<1>, dim3((unsigned)((count + 255) / 256)), dim3(256),
-                         0, stream, part, p.z, count, out_f32 ? 1 : 0, alpha.a, alpha.w, out);
-    if (hipGetLastError() != hipSuccess) return -1;
-  }
+  return splitk_reduce(p.z, M, n_out, out_f32, out, workspace, alpha, stream);
+}
+
+template <int MG, int TR>
+int launch_gemv4_tiled_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
+  const int64_t tiles = (a.n_out + 15) / 16;
+  const int64_t per_wg = (int64_t)nw * TR;
+  dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
+  const int max_steps = (a.steps + zsplit - 1) / zsplit;
+  const size_t lds = (size_t)a.M * (max_steps * kTileStep + kXPad) * sizeof(uint16_t);
+  hipLaunchKernelGGL((k_gemv4_tiled<MG, TR>), grid, dim3(64 * nw), lds, stream, a);
   return 0;
+}
+
+int launch_gemv_tiled(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                      const uint8_t* wt, int64_t N, bool out_f32, void* out, void* workspace,
+                      hipStream_t stream, Alpha alpha) {
+  GemvArgs a;
+  a.fq = 0;
+  a.ga = alpha.a;
+  a.gw = alpha.w;
+  a.x = x;
+  a.wc = wt;
+  a.ws = nullptr;
+  a.row_idx = nullptr;
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.K = K;
+  a.n_out = N;
+  a.M = (int)M;
+  a.steps = (int)((K + kTileStep - 1) / kTileStep);
+  a.out_f32 = out_f32 ? 1 : 0;
+  int rc = -2;
+  if (p.kp > 1) return -2;
+  if (p.small) {
+    if (p.mt == 1 && p.tr == 1)
+      rc = launch_gemv4_tiled_t<1, 1>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 2)
+      rc = launch_gemv4_tiled_t<1, 2>(a, p.nw, p.z, stream);
+    else if (p.mt == 2 && p.tr == 1)
+      rc = launch_gemv4_tiled_t<2, 1>(a, p.nw, p.z, stream);
+  } else if (p.mt == 1 && p.tr == 2)
+    rc = launch_gemv_tiled_t<1, 2>(a, p.nw, p.z, stream);
+  else if (p.mt == 1 && p.tr == 1)
+    rc = launch_gemv_tiled_t<1, 1>(a, p.nw, p.z, stream);
+  else if (p.mt == 1 && p.tr == 4)
+    rc = launch_gemv_tiled_t<1, 4>(a, p.nw, p.z, stream);
+  else if (p.mt == 2 && p.tr == 2)
+    rc = launch_gemv_tiled_t<2, 2>(a, p.nw, p.z, stream);
+  else if (p.mt == 2 && p.tr == 1)
+    rc = launch_gemv_tiled_t<2, 1>(a, p.nw, p.z, stream);
+  if (rc != 0) return rc;
+  if (hipGetLastError() != hipSuccess) return -1;
+  return splitk_reduce(p.z, M, N, out_f32, out, workspace, alpha, stream);
 }
 
 }  // namespace nvfp4

@@ -20,6 +20,7 @@
 #pragma once
 
 #include "device.h"
+#include "gemv_core.h"
 
 namespace nvfp4 {
 
@@ -138,6 +139,110 @@ __device__ __forceinline__ void g4_accumulate(f32x4 (&acc)[TR][MG],
     g4_load<TR, true>(bt, cptr, sptr, K, steps_full);
     g4_compute<MG, TR>(acc, bt, xl);
   }
+}
+
+// ---- tiled weights ----------------------------------------------------------------
+// With tiled weights (tile.hip) a wave streams whole 16-row tiles, and lane l
+// takes the same 64 elements as the 16x16 GEMV's lane: row l % 16 of the
+// tile, elements [64 q, 64 q + 64) of each 256-element step, q = l / 16
+// (WStep, load_wstep_tiled).  The 4x4x4 blocks are assigned accordingly:
+// block b = l / 4 holds rows 4 (b % 4) .. + 3 of the tile (one per lane) and
+// the quarter q = b / 4, which all four of its lanes share, so an MFMA's four
+// k-slots are the same four elements for the block's A rows (activation rows
+// 4 g + l % 4, read from LDS) and B columns.  Lane l accumulates C[4 g + r][row
+// l % 16] over its quarter; the four quarters are summed across lanes at the
+// end (gemv4t_reduce).
+
+// One tiled step (16 MFMAs per m-group and tile: 4 blocks of 16 elements x 4
+// k-slots).  xl[g]: this lane's activation row of m-group g in LDS at element
+// 64 q of the step.
+template <int MG, int TR>
+__device__ __forceinline__ void g4t_compute(f32x4 (&acc)[TR][MG], const WStep<TR>& b,
+                                            const uint16_t* const (&xl)[MG]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // the lane's block of 16 elements (scale byte j)
+    u32x4 a[MG][2];  // 16 activations per m-group: words 2u, 2u+1 feed MFMA u
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      a[g][0] = *reinterpret_cast<const u32x4*>(xl[g] + 16 * j);
+      a[g][1] = *reinterpret_cast<const u32x4*>(xl[g] + 16 * j + 8);
+    }
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      f32x4 ct[MG];
+#pragma unroll
+      for (int g = 0; g < MG; ++g) ct[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // 4 elements = 2 code bytes per MFMA
+        const uint32_t w = b.c[t][j >> 1][2 * (j & 1) + (u >> 1)];
+        const uint32_t b01 = __builtin_bit_cast(uint32_t, (u & 1) ? e2m1x2_to_bf16<2>(w)
+                                                                   : e2m1x2_to_bf16<0>(w));
+        const uint32_t b23 = __builtin_bit_cast(uint32_t, (u & 1) ? e2m1x2_to_bf16<3>(w)
+                                                                   : e2m1x2_to_bf16<1>(w));
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+          const u32x4& av = a[g][u >> 1];
+          const int wi = 2 * (u & 1);  // words of av holding the MFMA's four elements
+          ct[g] = mfma_4x4x4_bf16(av[wi], av[wi + 1], b01, b23, ct[g]);
+        }
+      }
+      float sc;
+      switch (j) {
+        case 0: sc = e4m3_to_f32<0>(b.sc[t]); break;
+        case 1: sc = e4m3_to_f32<1>(b.sc[t]); break;
+        case 2: sc = e4m3_to_f32<2>(b.sc[t]); break;
+        default: sc = e4m3_to_f32<3>(b.sc[t]); break;
+      }
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][g][r] += sc * ct[g][r];
+    }
+  }
+}
+
+// Steps [s0, s1) of tiled weights, all whole; the same unconditional-prefetch
+// double buffer as g4_accumulate.  `stage` is called after the first weight
+// loads are issued and before any activation is read.
+template <int MG, int TR, typename Stage>
+__device__ __forceinline__ void g4t_accumulate(f32x4 (&acc)[TR][MG],
+                                               const uint8_t* const (&cptr)[TR],
+                                               const uint8_t* const (&sptr)[TR],
+                                               const uint16_t* const (&xl0)[MG], int s0, int s1,
+                                               Stage stage) {
+  int s = s0;
+  const uint16_t* xl[MG];
+#pragma unroll
+  for (int g = 0; g < MG; ++g) xl[g] = xl0[g];
+  if (s >= s1) {
+    stage();
+    return;
+  }
+  WStep<TR> b0, b1;
+  load_wstep_tiled<TR, true>(b0, cptr, sptr, s);
+  stage();
+  while (true) {
+    load_wstep_tiled<TR, true>(b1, cptr, sptr, min(s + 1, s1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    g4t_compute<MG, TR>(acc, b0, xl);
+#pragma unroll
+    for (int g = 0; g < MG; ++g) xl[g] += kGemvStep;
+    if (++s >= s1) break;
+    load_wstep_tiled<TR, true>(b0, cptr, sptr, min(s + 1, s1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    g4t_compute<MG, TR>(acc, b1, xl);
+#pragma unroll
+    for (int g = 0; g < MG; ++g) xl[g] += kGemvStep;
+    if (++s >= s1) break;
+  }
+}
+
+// Sum v over the four lanes of one tile row (the quarters q = lane / 16), in
+// a fixed order; every lane ends with the total.
+__device__ __forceinline__ float gemv4t_reduce(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
 }
 
 // Sum v over the 16 lanes that share lane % 4 (the 16 MFMA blocks), in a fixed

@@ -18,6 +18,16 @@ int launch_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uin
 // out = dequantize(quantize(x)) in bf16 (exact), without the codes in memory.
 int launch_fakequant(const uint16_t* x, int64_t M, int64_t K, uint16_t* out, hipStream_t stream);
 
+// Tiled NVFP4 weights (tile.hip): blocks of 16 rows x 256 elements, 2,304
+// bytes each (two 1 KB halves of codes in lane order, then 256 B of scales),
+// tile-major; rows past N and elements past K are zero.
+constexpr int kTileRows = 16;
+constexpr int kTileStep = 256;
+constexpr int kTileBlockBytes = 2304;
+size_t tiled_weight_bytes(int64_t N, int64_t K);
+int launch_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                       uint8_t* out, hipStream_t stream);
+
 // Two-level NVFP4 (per-tensor fp32 scale g, a device scalar).  Quantize with
 // a given g; the offline weight quantizer (g from the tensor's amax, written
 // to *g; kAbsmaxParts partial maxima in workspace); dequantize with g.
@@ -61,8 +71,10 @@ struct GemvPlan {
   int kp;  // K parts inside a workgroup (nw = tile groups * kp), summed in LDS
 };
 
+// tiled: the plan of launch_gemv_tiled (16x16 kernel only, K parts across
+// workgroups only).
 GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus,
-                   const PlanOverride& ov = PlanOverride{});
+                   const PlanOverride& ov = PlanOverride{}, bool tiled = false);
 // Whether the override's GEMV fields name a layout that exists for this M.
 bool gemv_override_valid(int64_t M, int64_t K, const PlanOverride& ov);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t n_out);
@@ -73,6 +85,11 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32,
                 void* out, void* workspace, hipStream_t stream, Alpha alpha = {},
                 bool fakequant = false);
+// The same product with tiled weights (wt: tiled_weight_bytes(N, K), all N
+// rows; no row_idx and no fused quantizer).
+int launch_gemv_tiled(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                      const uint8_t* wt, int64_t N, bool out_f32, void* out, void* workspace,
+                      hipStream_t stream, Alpha alpha = {});
 
 // Large-M path: LDS-tiled MFMA GEMM, 256 x 256 output tiles.  a is bf16 [M][K];
 // with GemmA::kFakeQuant its tiles are quantized to NVFP4 and dequantized as

@@ -151,6 +151,48 @@ int nvfp4_gemm_noalloc(int a_dtype, const void *a, const uint8_t *a_scales, int6
                        void *stream);
 
 /*
+ * Tiled NVFP4 weights ("NF4T"): the same matrix NF4W(N, K), bytes reordered
+ * once when the weights are loaded so that the weight-streaming kernels read
+ * every step of a wave as contiguous, fully used runs, the scales in the same
+ * stream as the codes (the pages' Marlin-class kernels also take weights
+ * repacked offline: "Serving Qwen3.8-27B in 4-bit ...", sections "What the
+ * artifact is" and "The masked head trick").  Rows are grouped in tiles of 16
+ * and K in steps of 256 elements; block (t, s) is 2,304 bytes at offset
+ * (t * S + s) * 2304, S = ceil(K / 256):
+ *   bytes [1024 h + 16 L, +16), h = 0, 1, L = 16 q + n (n, q < 16, 4): the
+ *     code bytes of row 16 t + n, elements 256 s + 64 q + 32 h .. + 31, in
+ *     the row-major nibble order;
+ *   bytes [2048 + 4 L, +4): that row's scale bytes of elements
+ *     256 s + 64 q .. + 63 (four blocks of 16).
+ * Rows past N and elements past K hold zero codes and zero scales.  The array
+ * holds nvfp4_tiled_weight_bytes(N, K) = ceil(N/16) * S * 2304 bytes, equal to
+ * the row-major bytes when N % 16 == 0 and K % 256 == 0.
+ */
+size_t nvfp4_tiled_weight_bytes(int64_t N, int64_t K);
+
+/*
+ * Write the tiled layout of NF4W(N, K) (codes [N][K/2], scales [N][K/16]) to
+ * w_tiled (nvfp4_tiled_weight_bytes(N, K) bytes, every byte written).  A pure
+ * byte permutation plus zero padding.  K % 32 == 0.
+ */
+int nvfp4_tile_weight(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                      uint8_t *w_tiled, void *stream);
+
+/*
+ * nvfp4_gemm on tiled weights, all N rows (no row_idx: a masked head gathers
+ * rows from the row-major layout): out[m][n] = sum_k a[m][k] * w[n][k],
+ * out [M][N] in out_dtype, a_dtype / a / a_scales as in nvfp4_gemm.  The
+ * weights are streamed by the split-K GEMV, 32 activation rows per launch.
+ * Same products, fp32 accumulation, tolerance and run-to-run determinism as
+ * nvfp4_gemm.  workspace: >= nvfp4_gemm_tiled_workspace_size(a_dtype, M, N,
+ * K) bytes (may be NULL when that is 0).  K % 32 == 0.
+ */
+size_t nvfp4_gemm_tiled_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K);
+int nvfp4_gemm_tiled(int a_dtype, const void *a, const uint8_t *a_scales, int64_t M, int64_t N,
+                     int64_t K, const uint8_t *w_tiled, int out_dtype, void *out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * W4A4 linear layer from bf16 activations: the activation quantizer fused into
  * the product ("52.6% more tokens, 1.53x less GPU time ...": NVFP4 W4A4
  * execution).  Bit-identical to nvfp4_quantize(a) followed by nvfp4_gemm

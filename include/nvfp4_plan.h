@@ -89,6 +89,17 @@ int nvfp4_grouped_gemm_scaled_planned(const nvfp4_plan_t *plan, const uint16_t *
                                       int epilogue, uint16_t *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* nvfp4_gemm_tiled with a plan: gemv_tiles {1, 2, 4 (M <= 16)}, gemv_waves
+ * {4, 8, or 16 with 16 < M <= 32}, gemv_splits; the tiled GEMV has no
+ * 4x4x4-block kernel and no K parts inside a workgroup (gemv_small_max and
+ * gemv_kparts must be < 1). */
+size_t nvfp4_gemm_tiled_workspace_size_planned(const nvfp4_plan_t *plan, int a_dtype, int64_t M,
+                                               int64_t N, int64_t K);
+int nvfp4_gemm_tiled_planned(const nvfp4_plan_t *plan, int a_dtype, const void *a,
+                             const uint8_t *a_scales, int64_t M, int64_t N, int64_t K,
+                             const uint8_t *w_tiled, int out_dtype, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -393,3 +393,48 @@ def test_kparts_plan_validation(L):
     assert gp(gemv_tiles=2, gemv_waves=16, gemv_kparts=4) == INVALID   # no (2, 16, 4)
     assert gp(M=12, gemv_tiles=2, gemv_waves=16, gemv_kparts=8) == INVALID  # 8 parts need M <= 8
     assert (L.nvfp4_gemm_workspace_size_planned(_plan(**ok), 0, 8, 64, 4096, 64) == 0)
+
+
+def test_tiled_validation(L):
+    """nvfp4_tiled_weight_bytes, nvfp4_tile_weight and nvfp4_gemm_tiled reject
+    bad arguments on the host."""
+    assert L.nvfp4_tiled_weight_bytes(17, 288) == 2 * 2 * 2304
+    assert L.nvfp4_tiled_weight_bytes(248320, 5120) == 248320 * 5120 * 9 // 16
+    assert L.nvfp4_tiled_weight_bytes(16, 48) == 0  # K % 32 != 0
+    assert L.nvfp4_tiled_weight_bytes(0, 64) == 0
+    assert L.nvfp4_tile_weight(NULL, P2, 4, 64, P3, NULL) == INVALID
+    assert L.nvfp4_tile_weight(P, P2, 4, 64, NULL, NULL) == INVALID
+    assert L.nvfp4_tile_weight(P, P2, 0, 64, P3, NULL) == INVALID
+    assert L.nvfp4_tile_weight(P, P2, 4, 48, P3, NULL) == NOT_SUPPORTED
+    assert L.nvfp4_tile_weight(MIS, P2, 4, 64, P3, NULL) == INVALID
+    g = L.nvfp4_gemm_tiled
+    # (a_dtype, a, a_scales, M, N, K, w_tiled, out_dtype, out, ws, ws_bytes, stream)
+    assert g(0, NULL, NULL, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID
+    assert g(0, P, NULL, 1, 16, 64, NULL, 0, P3, NULL, 0, NULL) == INVALID
+    assert g(0, P, NULL, 0, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID
+    assert g(0, P, NULL, 1, 16, 48, P2, 0, P3, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(0, P, NULL, 1, 16, 64, P2, 7, P3, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(5, P, NULL, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(0, P, NULL, 1, 16, 64, MIS, 0, P3, NULL, 0, NULL) == INVALID
+    assert g(0, P, P4, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID  # bf16 with scales
+    assert g(2, P, NULL, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID  # NVFP4 without
+    need = L.nvfp4_gemm_tiled_workspace_size(0, 8, 17408, 5120)
+    assert need > 0
+    assert g(0, P, NULL, 8, 17408, 5120, P2, 0, P3, NULL, 0, NULL) == WORKSPACE
+    assert g(0, P, NULL, 8, 17408, 5120, P2, 0, P3, P4, need - 1, NULL) == WORKSPACE
+    # W4A4 needs room for the dequantized activations
+    assert L.nvfp4_gemm_tiled_workspace_size(2, 8, 17408, 5120) >= need + 8 * 5120 * 2
+
+
+def test_tiled_plan_validation(L):
+    """Tiled plans that name no built layout are refused before any launch."""
+    def planned(**f):
+        p = nv.make_plan(**f)
+        return L.nvfp4_gemm_tiled_planned(ctypes.byref(p), 0, P, NULL, 8, 1024, 2048, P2, 0, P3,
+                                          P4, 1 << 30, NULL)
+    assert planned(gemv_kparts=2) == INVALID
+    assert planned(gemv_small_max=9) == INVALID
+    assert planned(gemv_tiles=3) == INVALID
+    assert planned(gemv_waves=16) == INVALID  # 16 waves need two activation tiles
+    assert planned(gemv_small_max=8, gemv_tiles=4) == INVALID
+    assert planned(gemv_lds_kib=4) == INVALID
