@@ -4,12 +4,17 @@
 Workload of the headline metric (weight-stream GB/s at M = 1..32): the
 decode-shaped W4A16 set -- M in {1, 8, 32} x (K, N) in {(5120, 17408),
 (17408, 5120), (5120, 248320)} plus the masked head (32,768 of the 248,320
-rows) -- 12 nvfp4_gemm calls.  One step runs all 12 calls once; `value` is the
-weight bytes the step streams (rows * K * 9/16 per call) divided by the step
-time, with every input resident in HBM before the timed region starts.  The
-step is captured once as a HIP graph and replayed (as a serving engine replays
-its decode step); the same calls launched one by one give config.eager_GBs and
-the per-call event times of the roofline.
+rows) -- 12 calls.  The dense weights are tiled once before timing
+(nvfp4_tile_weight: the same bytes in the streaming kernels' order, as a serving
+engine lays out its weights at load) and the nine dense calls run
+nvfp4_gemm_tiled; the masked head gathers its rows from the row-major head with
+nvfp4_gemm.  One step runs all 12 calls once; `value` is the weight bytes the
+step streams (rows * K * 9/16 per call) divided by the step time, with every
+input resident in HBM before the timed region starts.  The step is captured
+once as a HIP graph and replayed (as a serving engine replays its decode
+step); the same calls launched one by one give config.eager_GBs and the
+per-call event times of the roofline.  config.row_major repeats the step with
+every call on the row-major layout (nvfp4_gemm).
 
 Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies that
 calls alternate, and the head in three: the full-head calls alternate copies 0
@@ -93,9 +98,15 @@ def weight_bytes(rows: int, K: int) -> int:
 
 
 class Decode:
-    """The 12-call decode set with its weight copies, all resident on the GPU."""
+    """The 12-call decode set with its weight copies, all resident on the GPU.
 
-    def __init__(self, nv, torch, helpers_dev):
+    With tiled=True (the serving configuration) the nine dense calls read their
+    weights in the tiled layout (nvfp4_tile_weight, done once here, as an engine
+    does when it loads the weights) through nvfp4_gemm_tiled; the masked head
+    gathers its rows from the row-major head (nvfp4_gemm with row_idx).  With
+    tiled=False every call reads the row-major layout through nvfp4_gemm."""
+
+    def __init__(self, nv, torch, helpers_dev, tiled=True):
         import workloads as wl
         self.nv, self.torch = nv, torch
         dev_u8, dev_bf16, dev_i32 = helpers_dev
@@ -114,12 +125,19 @@ class Decode:
         self.x = {(M, K): dev_bf16(wl.decode_activations(M, K))
                   for M in wl.DECODE_M for K in {s[0] for s in shapes}}
         self.keep = []
+        self.tiled = tiled
+        if tiled:  # the dense calls' copies 0 and 1 in the tiled layout
+            self.tiled_weights = {s: [nv.tile_weight(*self.weights[s][c]) for c in range(2)]
+                                  for s in shapes}
         head = (wl.HIDDEN, wl.VOCAB)
         call_no = 0
         for M in wl.DECODE_M:
             for (K, N) in shapes:
                 c = call_no % 2
-                self._add(f"M{M}_K{K}_N{N}", M, K, N, self.weights[(K, N)][c], None, N)
+                if tiled:
+                    self._add_tiled(f"M{M}_K{K}_N{N}", M, K, N, self.tiled_weights[(K, N)][c])
+                else:
+                    self._add(f"M{M}_K{K}_N{N}", M, K, N, self.weights[(K, N)][c], None, N)
                 call_no += 1
             # masked head: its own copy, which no full-head call reads
             K, N = head
@@ -151,6 +169,28 @@ class Decode:
                 raise RuntimeError(nv.lib().nvfp4_status_string(rc).decode())
 
         self.calls.append((name, M, K, n_out, fn))
+
+    def _add_tiled(self, name, M, K, N, wt):
+        """One nvfp4_gemm_tiled call, arguments marshalled once."""
+        import ctypes
+        torch, nv = self.torch, self.nv
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        wsb = nv.gemm_tiled_workspace_size(M, N, K)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+        x = self.x[(M, K)]
+        self.keep.append((out, ws))
+        vp = ctypes.c_void_p
+        args = (nv.BF16, vp(x.data_ptr()), None, M, N, K, vp(wt.data_ptr()), nv.BF16,
+                vp(out.data_ptr()), None if ws is None else vp(ws.data_ptr()), wsb)
+        f = nv.lib().nvfp4_gemm_tiled
+
+        def fn(stream=None, f=f, args=args):
+            st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+            rc = f(*args, vp(st))
+            if rc != 0:
+                raise RuntimeError(nv.lib().nvfp4_status_string(rc).decode())
+
+        self.calls.append((name, M, K, N, fn))
 
     def step_bytes(self):
         return sum(weight_bytes(rows, K) for (_, _, K, rows, _) in self.calls)
@@ -633,6 +673,19 @@ def main():
         draft = time_draft(dec, torch, nv)
     del dec
     torch.cuda.empty_cache()
+    # the same step with every call on the row-major layout (nvfp4_gemm)
+    log("the decode step on row-major weights (graph-replayed)")
+    dec_r = Decode(nv, torch, hd, tiled=False)
+    wall_r = time_decode_graph(dec_r, torch, args.steps, args.warmup)
+    _, per_call_r = time_decode(dec_r, torch, args.steps, args.warmup)
+    row_major = {
+        "value_GBs": round(step_bytes * args.steps / wall_r / 1e9, 2),
+        "ms_per_step": round(wall_r / args.steps * 1e3, 4),
+        "per_call_us": {c[0]: round(float(t * 1e3), 2)
+                        for c, t in zip(dec_r.calls, per_call_r.mean(axis=0))},
+    }
+    del dec_r
+    torch.cuda.empty_cache()
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -671,8 +724,11 @@ def main():
                          "(17408,5120),(5120,248320)} + masked head 32768/248320 rows"),
             "step_weight_bytes": int(step_bytes),
             "calls_per_step": len(per_call_us),
-            "step": "12 nvfp4_gemm calls captured as one HIP graph, replayed",
+            "step": ("12 calls captured as one HIP graph, replayed: 9 nvfp4_gemm_tiled on "
+                     "weights tiled once at load (nvfp4_tile_weight), the 3 masked-head "
+                     "nvfp4_gemm gathering rows of the row-major head"),
             "eager_GBs": round(eager_value, 2),
+            "row_major": row_major,
         },
         "roofline": {
             "bound": "hbm",
@@ -682,7 +738,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes": int(step_bytes),
-            "kernel": "k_gemv / k_gemv4 (decode GEMV, all 12 launches of a step; bytes per step)",
+            "kernel": ("k_gemv4_tiled / k_gemv<TL> / k_gemv4 (decode GEMV, all 12 launches "
+                       "of a step; bytes per step)"),
         },
         "per_call_GBs": per_call_gbs,
         "per_call_us": per_call_us,
