@@ -4,17 +4,17 @@
 Workload of the headline metric (weight-stream GB/s at M = 1..32): the
 decode-shaped W4A16 set -- M in {1, 8, 32} x (K, N) in {(5120, 17408),
 (17408, 5120), (5120, 248320)} plus the masked head (32,768 of the 248,320
-rows) -- 12 calls.  The dense weights are tiled once before timing
+rows) -- 12 calls.  The weights are tiled once before timing
 (nvfp4_tile_weight: the same bytes in the streaming kernels' order, as a serving
-engine lays out its weights at load) and the nine dense calls run
-nvfp4_gemm_tiled; the masked head gathers its rows from the row-major head with
-nvfp4_gemm.  One step runs all 12 calls once; `value` is the weight bytes the
+engine lays out its weights at load; the masked head's fixed id set of 32,768
+rows as a matrix of its own) and every call runs nvfp4_gemm_tiled.  One step runs all 12 calls once; `value` is the weight bytes the
 step streams (rows * K * 9/16 per call) divided by the step time, with every
 input resident in HBM before the timed region starts.  The step is captured
 once as a HIP graph and replayed (as a serving engine replays its decode
 step); the same calls launched one by one give config.eager_GBs and the
 per-call event times of the roofline.  config.row_major repeats the step with
-every call on the row-major layout (nvfp4_gemm).
+every call on the row-major layout (nvfp4_gemm; the masked head gathering its
+rows per call through row_idx).
 
 Infinity-cache (MALL, 256 MB) hygiene: dense weights exist in two copies that
 calls alternate, and the head in three: the full-head calls alternate copies 0
@@ -100,11 +100,13 @@ def weight_bytes(rows: int, K: int) -> int:
 class Decode:
     """The 12-call decode set with its weight copies, all resident on the GPU.
 
-    With tiled=True (the serving configuration) the nine dense calls read their
-    weights in the tiled layout (nvfp4_tile_weight, done once here, as an engine
-    does when it loads the weights) through nvfp4_gemm_tiled; the masked head
-    gathers its rows from the row-major head (nvfp4_gemm with row_idx).  With
-    tiled=False every call reads the row-major layout through nvfp4_gemm."""
+    With tiled=True (the serving configuration) every call reads weights in the
+    tiled layout (nvfp4_tile_weight, done once here, as an engine does when it
+    loads the weights) through nvfp4_gemm_tiled: the nine dense calls their
+    whole matrices, the masked head the 32,768 rows of its fixed id set, tiled
+    as a matrix of their own.  With tiled=False every call reads the row-major
+    layout through nvfp4_gemm, the masked head gathering its rows per call
+    (row_idx)."""
 
     def __init__(self, nv, torch, helpers_dev, tiled=True):
         import workloads as wl
@@ -126,9 +128,12 @@ class Decode:
                   for M in wl.DECODE_M for K in {s[0] for s in shapes}}
         self.keep = []
         self.tiled = tiled
-        if tiled:  # the dense calls' copies 0 and 1 in the tiled layout
+        if tiled:  # the dense calls' copies 0 and 1 in the tiled layout, and the
+            # masked head's rows (its id set is fixed) tiled from head copy 2
             self.tiled_weights = {s: [nv.tile_weight(*self.weights[s][c]) for c in range(2)]
                                   for s in shapes}
+            self.tiled_masked = nv.tile_weight(*self.weights[(wl.HIDDEN, wl.VOCAB)][2],
+                                               row_idx=self.idx)
         head = (wl.HIDDEN, wl.VOCAB)
         call_no = 0
         for M in wl.DECODE_M:
@@ -141,8 +146,11 @@ class Decode:
                 call_no += 1
             # masked head: its own copy, which no full-head call reads
             K, N = head
-            self._add(f"M{M}_masked_head", M, K, N, self.weights[head][2], self.idx,
-                      self.idx.numel())
+            if tiled:
+                self._add_tiled(f"M{M}_masked_head", M, K, self.idx.numel(), self.tiled_masked)
+            else:
+                self._add(f"M{M}_masked_head", M, K, N, self.weights[head][2], self.idx,
+                          self.idx.numel())
         torch.cuda.synchronize()
 
     def _add(self, name, M, K, N, w, idx, n_out):
@@ -724,9 +732,9 @@ def main():
                          "(17408,5120),(5120,248320)} + masked head 32768/248320 rows"),
             "step_weight_bytes": int(step_bytes),
             "calls_per_step": len(per_call_us),
-            "step": ("12 calls captured as one HIP graph, replayed: 9 nvfp4_gemm_tiled on "
-                     "weights tiled once at load (nvfp4_tile_weight), the 3 masked-head "
-                     "nvfp4_gemm gathering rows of the row-major head"),
+            "step": ("12 nvfp4_gemm_tiled calls captured as one HIP graph, replayed, on "
+                     "weights tiled once at load (nvfp4_tile_weight; the masked head's fixed "
+                     "32,768-row id set tiled as its own matrix)"),
             "eager_GBs": round(eager_value, 2),
             "row_major": row_major,
         },
@@ -738,8 +746,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes": int(step_bytes),
-            "kernel": ("k_gemv4_tiled / k_gemv<TL> / k_gemv4 (decode GEMV, all 12 launches "
-                       "of a step; bytes per step)"),
+            "kernel": ("k_gemv4_tiled / k_gemv<TL> (decode GEMV on tiled weights, all 12 "
+                       "launches of a step; bytes per step)"),
         },
         "per_call_GBs": per_call_gbs,
         "per_call_us": per_call_us,

@@ -70,7 +70,7 @@ _SIGS = {
                                    _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_moe_combine": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
     "nvfp4_tiled_weight_bytes": ([_i64, _i64], _sz),
-    "nvfp4_tile_weight": ([_vp, _vp, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_tile_weight": ([_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp], _int),
     "nvfp4_gemm_tiled_workspace_size": ([_int, _i64, _i64, _i64], _sz),
     "nvfp4_gemm_tiled": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_noalloc_scratch_bytes": ([], _sz),
@@ -330,16 +330,19 @@ def tiled_weight_bytes(N: int, K: int) -> int:
     return int(lib().nvfp4_tiled_weight_bytes(N, K))
 
 
-def tile_weight(w_codes: torch.Tensor, w_scales: torch.Tensor, out=None) -> torch.Tensor:
-    """The tiled layout (a 1-d uint8 tensor) of NVFP4 weights [N, K/2] + [N, K/16]."""
+def tile_weight(w_codes: torch.Tensor, w_scales: torch.Tensor, row_idx=None,
+                out=None) -> torch.Tensor:
+    """The tiled layout (a 1-d uint8 tensor) of NVFP4 weights [N, K/2] + [N, K/16],
+    or of the rows row_idx (int32) of them, in that order."""
     N, K = _weights(w_codes, w_scales)
-    nbytes = tiled_weight_bytes(N, K)
+    n_rows = _rows(row_idx, N)
+    nbytes = tiled_weight_bytes(n_rows, K)
     _arg(out, "out", torch.uint8, (nbytes,), optional=True)
-    _gpu(w_codes, w_scales, out)
+    _gpu(w_codes, w_scales, row_idx, out)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=w_codes.device)
-    _check(lib().nvfp4_tile_weight(_ptr(w_codes), _ptr(w_scales), N, K, _ptr(out),
-                                   _stream(w_codes.device)))
+    _check(lib().nvfp4_tile_weight(_ptr(w_codes), _ptr(w_scales), N, K, _ptr(row_idx), n_rows,
+                                   _ptr(out), _stream(w_codes.device)))
     return out
 
 

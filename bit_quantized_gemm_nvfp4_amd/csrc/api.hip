@@ -103,10 +103,25 @@ bool gemv_plan_ok(const PlanOverride& ov, int64_t M, int64_t K, bool fused) {
 // with 1, 2 or 4 (one activation tile) tiles per wave and 4, 8 or 16 (two
 // activation tiles) waves; no K parts inside a workgroup.
 bool tiled_plan_ok(const PlanOverride& ov, int64_t M, int64_t K) {
-  if (ov.gemv_kparts > 1 || ov.gemv_small_max > 8) return false;
+  if (ov.gemv_small_max > 8) return false;
   if (ov.gemv_lds_kib >= 0 && (ov.gemv_lds_kib < 8 || ov.gemv_lds_kib > 160)) return false;
   const GemvPlan p = plan_gemv(M, 1, K, kNumCUs, ov, true);
-  if (p.small) return (p.tr == 1 || (p.tr == 2 && p.mt == 1)) && p.nw >= 1 && p.nw <= 8;
+  if (p.small) {
+    if (p.kp > 1)  // one tile per wave, one m-group, 2..16 parts, nw = groups x parts
+      return p.mt == 1 && p.tr == 1 && (p.kp == 2 || p.kp == 4 || p.kp == 8 || p.kp == 16) &&
+             p.nw % p.kp == 0 && p.nw <= 16 && K / kTileStep >= p.kp;
+    return (p.tr == 1 || (p.tr == 2 && p.mt == 1)) && p.nw >= 1 && p.nw <= 8;
+  }
+  if (p.kp > 1) {  // the built K-parts layouts (as nvfp4_gemm's)
+    if ((K + kTileStep - 1) / kTileStep < p.kp) return false;
+    if (p.mt == 2) return p.tr == 1 && p.nw == 16 && p.kp == 2;
+    if (p.kp == 8 && M > 8) return false;
+    static const int lay[][3] = {{2, 2, 4}, {2, 4, 2}, {1, 4, 4}, {1, 4, 2}, {2, 2, 8}, {1, 2, 8},
+                                 {2, 1, 8}};
+    for (const auto& l : lay)
+      if (l[0] == p.tr && l[1] * l[2] == p.nw && l[2] == p.kp) return true;
+    return false;
+  }
   const bool tr_ok = p.tr == 1 || p.tr == 2 || (p.tr == 4 && p.mt == 1);
   const bool nw_ok = p.nw == 4 || p.nw == 8 || (p.nw == 16 && p.mt == 2);
   return tr_ok && nw_ok;
@@ -371,14 +386,17 @@ size_t nvfp4_tiled_weight_bytes(int64_t N, int64_t K) {
 }
 
 int nvfp4_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
-                      uint8_t* w_tiled, void* stream) {
+                      const int32_t* row_idx, int64_t n_rows, uint8_t* w_tiled, void* stream) {
   if (!codes || !scales || !w_tiled) return NVFP4_ERROR_INVALID_VALUE;
-  if (N <= 0 || K <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (N <= 0 || K <= 0 || n_rows <= 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (row_idx ? n_rows > N : n_rows != N) return NVFP4_ERROR_INVALID_VALUE;
   if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
-  if (N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
-  if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_tiled))
+  if (N > INT32_MAX || N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_tiled) ||
+      (row_idx && !aligned16(row_idx)))
     return NVFP4_ERROR_INVALID_VALUE;
-  return launched(launch_tile_weight(codes, scales, N, K, w_tiled, as_stream(stream)));
+  return launched(launch_tile_weight(codes, scales, row_idx, n_rows, K, w_tiled,
+                                     as_stream(stream)));
 }
 
 size_t nvfp4_gemm_tiled_workspace_size(int a_dtype, int64_t M, int64_t N, int64_t K) {

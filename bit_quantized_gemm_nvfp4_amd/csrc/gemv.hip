@@ -150,7 +150,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
 // second kernel nor fp32 partials in memory.  Plain W4A16, one or two
 // activation tiles, K % 256 == 0.  blockIdx.x picks G*TR tiles, blockIdx.y a
 // K range (z > 1: fp32 partials summed by k_splitk_reduce, as k_gemv).
-template <int MT, int TR, int G, int KP, int WR>
+// TL: tiled weights (a.wc; K need not be a multiple of 256).
+template <int MT, int TR, int G, int KP, int WR, bool TL = false>
 __global__ void __launch_bounds__(64 * G * KP) k_gemv_kp(GemvArgs a) {
   constexpr int NW = G * KP;
   constexpr int RPP = WR * MT;
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(64 * G * KP) k_gemv_kp(GemvArgs a) {
                 "the parts' sums must fit the window");
   __shared__ __attribute__((aligned(16))) uint16_t win[2 * KP * RPP * kXWin];
   __shared__ int hflag[2 * KP];
-  __shared__ uint32_t scl[NW * TR * 512];
+  __shared__ uint32_t scl[TL ? 1 : NW * TR * 512];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = wave % G, part = wave / G;
@@ -172,13 +173,24 @@ __global__ void __launch_bounds__(64 * G * KP) k_gemv_kp(GemvArgs a) {
   const int64_t tile0 = ((int64_t)blockIdx.x * G + g) * TR;
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
+  if constexpr (TL) {
+    const int64_t last = (a.n_out + 15) / 16 - 1;
 #pragma unroll
-  for (int t = 0; t < TR; ++t) {
-    int64_t j = (tile0 + t) * 16 + ln;
-    if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
-    const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
-    cptr[t] = a.wc + row * (K / 2);
-    sptr[t] = a.ws + row * (K / 16);
+    for (int t = 0; t < TR; ++t) {
+      const int64_t tile = min(tile0 + t, last);  // padding tile: never stored
+      const uint8_t* tb = a.wc + tile * a.steps * 2304;
+      cptr[t] = tb + 16 * lane;
+      sptr[t] = tb + 2048 + 4 * lane;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      int64_t j = (tile0 + t) * 16 + ln;
+      if (j >= a.n_out) j = a.n_out - 1;  // padding column: any valid row, never stored
+      const int64_t row = a.row_idx ? (int64_t)a.row_idx[j] : j;
+      cptr[t] = a.wc + row * (K / 2);
+      sptr[t] = a.ws + row * (K / 16);
+    }
   }
   f32x4 acc[TR][MT];
 #pragma unroll
@@ -188,8 +200,9 @@ __global__ void __launch_bounds__(64 * G * KP) k_gemv_kp(GemvArgs a) {
   if (threadIdx.x < 2 * KP) hflag[threadIdx.x] = -1;  // no step is marked inexact yet
   __syncthreads();
   const uint16_t* x = a.x;
-  gemv_accumulate_kp<MT, TR, XP, KP, WR, true>(acc, cptr, sptr, win, hflag,
-                                               scl + wave * TR * 512, part, a.M, K, zs0,
+  gemv_accumulate_kp<MT, TR, XP, KP, WR, true, TL>(acc, cptr, sptr, win, hflag,
+                                                   scl + (TL ? 0 : wave * TR * 512), part, a.M,
+                                                   K, zs0,
                                                zs1 - zs0,
                                                [x, K](int m) { return x + (int64_t)m * K; });
   gemv_kp_reduce<MT, TR, KP>(acc, reinterpret_cast<f32x4*>(win), part, g, G);
@@ -298,14 +311,19 @@ __global__ void __launch_bounds__(512) k_gemv4(GemvArgs a) {
 }
 
 // Very small M (<= 8) on tiled weights: the 4x4x4-block MFMA with per-block
-// scaling (g4t_compute).  blockIdx.x picks nw*TR tiles of 16 weight rows, a
-// wave TR of them; blockIdx.y a contiguous part of K (256-element steps).
-template <int MG, int TR>
-__global__ void __launch_bounds__(512) k_gemv4_tiled(GemvArgs a) {
-  extern __shared__ uint16_t xs[];  // [M][steps of this part * 256 + kXPad]
+// scaling (g4t_compute).  blockIdx.x picks G*TR tiles of 16 weight rows
+// (G = waves / KP), blockIdx.y a contiguous range of K steps (256 elements)
+// whose activations are staged in LDS.  Wave w streams the TR tiles of group
+// w % G over part w / G of that range (KP contiguous parts); the parts' sums
+// are added in LDS in part order (gemv_kp_reduce), so a K range too long for
+// the rows alone to fill the chip needs no second kernel.
+template <int MG, int TR, int KP>
+__global__ void __launch_bounds__(KP > 1 ? 1024 : 512) k_gemv4_tiled(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [M][range * 256 + kXPad]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int nw = (blockDim.x >> 6) / KP;  // tile groups
+  const int g = wave % nw, part = wave / nw;
   const int ln = lane & 15, q = lane >> 4;
   const int64_t K = a.K;
 
@@ -319,7 +337,7 @@ __global__ void __launch_bounds__(512) k_gemv4_tiled(GemvArgs a) {
                              [x, K](int m) { return x + (int64_t)m * K; });
   };
 
-  const int64_t tile0 = ((int64_t)blockIdx.x * nw + wave) * TR;
+  const int64_t tile0 = ((int64_t)blockIdx.x * nw + g) * TR;
   const int64_t last = (a.n_out + 15) / 16 - 1;
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
@@ -330,20 +348,26 @@ __global__ void __launch_bounds__(512) k_gemv4_tiled(GemvArgs a) {
     cptr[t] = tb + 16 * lane;
     sptr[t] = tb + 2048 + 4 * lane;
   }
+  const KParts me = kpart(zs0, nsteps, part, KP);
   const uint16_t* xl[MG];
 #pragma unroll
-  for (int g = 0; g < MG; ++g) {
-    const int m = min(4 * g + (lane & 3), a.M - 1);  // padding row: never stored
-    xl[g] = xs + m * stride + 64 * q;
+  for (int mg = 0; mg < MG; ++mg) {
+    const int m = min(4 * mg + (lane & 3), a.M - 1);  // padding row: never stored
+    xl[mg] = xs + m * stride + (me.start - zs0) * kTileStep + 64 * q;
   }
 
   f32x4 acc[TR][MG];
 #pragma unroll
   for (int t = 0; t < TR; ++t)
 #pragma unroll
-    for (int g = 0; g < MG; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mg = 0; mg < MG; ++mg) acc[t][mg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  g4t_accumulate<MG, TR>(acc, cptr, sptr, xl, zs0, zs1, stage);
+  g4t_accumulate<MG, TR>(acc, cptr, sptr, xl, me.start, me.start + me.len, stage);
+  if constexpr (KP > 1) {
+    __syncthreads();  // every wave is done with the staged activations
+    gemv_kp_reduce<MG, TR, KP>(acc, reinterpret_cast<f32x4*>(xs), part, g, nw);
+    if (part != 0) return;
+  }
 
   // acc[t][g][r] of lane (q, ln) is quarter q's part of activation row 4g+r,
   // weight row 16*tile + ln; sum the quarters, then lane q == r % 4 stores.
@@ -353,12 +377,12 @@ __global__ void __launch_bounds__(512) k_gemv4_tiled(GemvArgs a) {
   for (int t = 0; t < TR; ++t) {
     const int64_t j = (tile0 + t) * 16 + ln;
 #pragma unroll
-    for (int g = 0; g < MG; ++g) {
+    for (int mg = 0; mg < MG; ++mg) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = 4 * g + r;
+        const int m = 4 * mg + r;
         if (m >= a.M) continue;  // uniform
-        const float s4 = gemv4t_reduce(acc[t][g][r]);
+        const float s4 = gemv4t_reduce(acc[t][mg][r]);
         const float v = scaled ? s4 * alpha : s4;
         if (q != r || j >= a.n_out) continue;
         const int64_t o = (int64_t)m * a.n_out + j;
@@ -506,13 +530,25 @@ struct KpLayout {
 constexpr KpLayout kKpLayouts[] = {{2, 2, 4}, {2, 4, 2}, {1, 4, 4}, {2, 2, 8}, {1, 2, 8},
                                    {2, 1, 8}, {1, 4, 2}};
 
-template <int MT, int WR, int TR, int G, int KP>
+template <int MT, int WR, int TR, int G, int KP, bool TL = false>
 bool try_kp(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
   if (p.tr != TR || p.nw != G * KP || p.kp != KP) return false;
   const int64_t tiles = (a.n_out + 15) / 16;
   dim3 grid((unsigned)((tiles + G * TR - 1) / (G * TR)), (unsigned)p.z);
-  hipLaunchKernelGGL((k_gemv_kp<MT, TR, G, KP, WR>), grid, dim3(64 * G * KP), 0, stream, a);
+  hipLaunchKernelGGL((k_gemv_kp<MT, TR, G, KP, WR, TL>), grid, dim3(64 * G * KP), 0, stream, a);
   return true;
+}
+
+template <int MT, int WR>
+int launch_gemv_kp_tl(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+  bool ok = try_kp<MT, WR, 2, 2, 4, true>(a, p, stream) ||
+            try_kp<MT, WR, 2, 4, 2, true>(a, p, stream) ||
+            try_kp<MT, WR, 1, 4, 4, true>(a, p, stream) ||
+            try_kp<MT, WR, 1, 4, 2, true>(a, p, stream);
+  if constexpr (WR == 8)
+    ok = ok || try_kp<MT, WR, 2, 2, 8, true>(a, p, stream) ||
+         try_kp<MT, WR, 1, 2, 8, true>(a, p, stream) || try_kp<MT, WR, 2, 1, 8, true>(a, p, stream);
+  return ok ? 0 : -2;
 }
 
 template <int MT, int WR>
@@ -629,8 +665,11 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
   // layers wide enough for 1.5 workgroups of 4 tiles per CU (measured at M = 8:
   // the 32,768-row masked head 27.7 -> 23.8 us; on the 17,408-row layer the
   // 272 workgroups leave some CUs with two and the split-K launch is as fast)
-  const bool kp_default = !tiled && ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
-                          ov.gemv_splits < 0 && !p.small && M <= 8 && K % kGemvStep == 0 &&
+  // (the same on tiled weights: the 32,768-row masked head at M = 8 25.9 ->
+  // 19.3 us graph-replayed)
+  const bool kp_default = ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
+                          ov.gemv_splits < 0 && !p.small && M <= 8 &&
+                          (tiled || K % kGemvStep == 0) &&
                           p.z >= 2 && steps >= 2 && (tiles + 3) / 4 >= (int64_t)num_cus * 3 / 2;
   if (kp_default) {
     p.tr = 1;
@@ -638,10 +677,28 @@ GemvPlan plan_gemv(int64_t M, int64_t n_out, int64_t K, int num_cus, const PlanO
     p.kp = 2;
     p.z = 1;
   }
-  if (!tiled && ov.gemv_kparts > 1 && !p.small && K % kGemvStep == 0) {
+  // Tiled weights, 4x4x4 kernel, layers of fewer than 8 tiles per CU: K parts
+  // inside the workgroup instead of across workgroups (no reduce launch), two
+  // tile groups per workgroup, enough parts for about 2,048 waves (measured at
+  // M = 1, graph-replayed: the 17,408 x 5,120 layer 13.0 -> 11.5 us with 2
+  // parts, the 5,120 x 17,408 layer 13.2 -> 12.0 us with 8)
+  if (tiled && p.small && ov.gemv_kparts < 0 && ov.gemv_tiles < 0 && ov.gemv_waves < 0 &&
+      ov.gemv_splits < 0 && tiles < (int64_t)num_cus * 8) {
+    int64_t kp = 2;
+    while (kp < 8 && tiles * kp < 2048) kp *= 2;
+    while (kp > 1 && kp * z_lds > steps) kp /= 2;
+    if (kp > 1) {
+      p.kp = (int)kp;
+      p.tr = 1;
+      p.nw = 2 * (int)kp;
+      p.z = (int)z_lds;
+    }
+  }
+  if (ov.gemv_kparts > 1 && (tiled || (!p.small && K % kGemvStep == 0))) {
     p.kp = ov.gemv_kparts;
-    if (ov.gemv_splits <= 0) p.z = 1;
+    if (ov.gemv_splits <= 0) p.z = z_lds;
     if ((int64_t)p.z * p.kp > steps) p.z = (int)(steps / p.kp);  // every part >= 1 step
+    if (p.z < 1) p.z = 1;
   }
   return p;
 }
@@ -728,14 +785,17 @@ int launch_gemv(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K, cons
   return splitk_reduce(p.z, M, n_out, out_f32, out, workspace, alpha, stream);
 }
 
-template <int MG, int TR>
+// nw waves = tile groups x kp parts.
+template <int MG, int TR, int KP>
 int launch_gemv4_tiled_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 15) / 16;
-  const int64_t per_wg = (int64_t)nw * TR;
+  const int64_t per_wg = (int64_t)(nw / KP) * TR;
   dim3 grid((unsigned)((tiles + per_wg - 1) / per_wg), (unsigned)zsplit);
   const int max_steps = (a.steps + zsplit - 1) / zsplit;
-  const size_t lds = (size_t)a.M * (max_steps * kTileStep + kXPad) * sizeof(uint16_t);
-  hipLaunchKernelGGL((k_gemv4_tiled<MG, TR>), grid, dim3(64 * nw), lds, stream, a);
+  const size_t stage = (size_t)a.M * (max_steps * kTileStep + kXPad) * sizeof(uint16_t);
+  const size_t red = (size_t)(KP - 1) * (nw / KP) * TR * MG * 64 * 16;
+  hipLaunchKernelGGL((k_gemv4_tiled<MG, TR, KP>), grid, dim3(64 * nw),
+                     stage > red ? stage : red, stream, a);
   return 0;
 }
 
@@ -758,14 +818,28 @@ int launch_gemv_tiled(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K
   a.steps = (int)((K + kTileStep - 1) / kTileStep);
   a.out_f32 = out_f32 ? 1 : 0;
   int rc = -2;
-  if (p.kp > 1) return -2;
   if (p.small) {
-    if (p.mt == 1 && p.tr == 1)
-      rc = launch_gemv4_tiled_t<1, 1>(a, p.nw, p.z, stream);
-    else if (p.mt == 1 && p.tr == 2)
-      rc = launch_gemv4_tiled_t<1, 2>(a, p.nw, p.z, stream);
-    else if (p.mt == 2 && p.tr == 1)
-      rc = launch_gemv4_tiled_t<2, 1>(a, p.nw, p.z, stream);
+    if (p.mt == 1 && p.tr == 1 && p.kp == 1)
+      rc = launch_gemv4_tiled_t<1, 1, 1>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 2 && p.kp == 1)
+      rc = launch_gemv4_tiled_t<1, 2, 1>(a, p.nw, p.z, stream);
+    else if (p.mt == 2 && p.tr == 1 && p.kp == 1)
+      rc = launch_gemv4_tiled_t<2, 1, 1>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 1 && p.kp == 2)
+      rc = launch_gemv4_tiled_t<1, 1, 2>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 1 && p.kp == 4)
+      rc = launch_gemv4_tiled_t<1, 1, 4>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 1 && p.kp == 8)
+      rc = launch_gemv4_tiled_t<1, 1, 8>(a, p.nw, p.z, stream);
+    else if (p.mt == 1 && p.tr == 1 && p.kp == 16)
+      rc = launch_gemv4_tiled_t<1, 1, 16>(a, p.nw, p.z, stream);
+  } else if (p.kp > 1) {
+    if (p.mt == 1 && a.M <= 8)
+      rc = launch_gemv_kp_tl<1, 8>(a, p, stream);
+    else if (p.mt == 1)
+      rc = launch_gemv_kp_tl<1, 16>(a, p, stream);
+    else if (p.mt == 2 && try_kp<2, 16, 1, 8, 2, true>(a, p, stream))
+      rc = 0;
   } else if (p.mt == 1 && p.tr == 2)
     rc = launch_gemv_tiled_t<1, 2>(a, p.nw, p.z, stream);
   else if (p.mt == 1 && p.tr == 1)

@@ -574,9 +574,12 @@ __device__ __forceinline__ KParts kpart(int s0, int S, int p, int KP) {
 // Window pieces of iteration i: piece c of the buffer is row (c >> 5) % (WR*MT)
 // of part (c >> 5) / (WR*MT), 8 elements at (c & 31) * 8 of that part's step
 // (clamped to the part's last step); rows past M repeat row M-1.
-template <int XP, int KP, int RPP, typename RowPtr>
+// KCHK: elements at or past K (the last step of tiled weights) read a clamped
+// address and are replaced by zero.
+template <int XP, int KP, int RPP, bool KCHK = false, typename RowPtr>
 __device__ __forceinline__ void xwin_load_kp(u32x4 (&v)[XP], int M, int64_t K, int s0, int S,
                                              int i, RowPtr row_ptr) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < XP; ++u) {
     const int c = threadIdx.x + u * blockDim.x;
@@ -584,7 +587,13 @@ __device__ __forceinline__ void xwin_load_kp(u32x4 (&v)[XP], int M, int64_t K, i
     const KParts kp = kpart(s0, S, p, KP);
     const int s = kp.start + min(i, kp.len - 1);
     const int m = min(r, M - 1);
-    v[u] = *reinterpret_cast<const u32x4*>(row_ptr(m) + (int64_t)s * kGemvStep + (c & 31) * 8);
+    const int64_t k = (int64_t)s * kGemvStep + (c & 31) * 8;
+    if constexpr (KCHK) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(row_ptr(m) + min(k, K - 8));
+      v[u] = k < K ? t : z;
+    } else {
+      v[u] = *reinterpret_cast<const u32x4*>(row_ptr(m) + k);
+    }
   }
 }
 
@@ -607,7 +616,9 @@ __device__ __forceinline__ void xwin_store_kp(uint16_t* buf, int* hflag_buf, boo
   }
 }
 
-template <int MT, int TR, int XP, int KP, int WR, bool H, typename RowPtr>
+// TL: tiled weights (load_wstep_tiled: codes and scales of a step in one
+// set of loads, no scale blocks; K need not be a multiple of 256).
+template <int MT, int TR, int XP, int KP, int WR, bool H, bool TL = false, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
                                                    const uint8_t* const (&cptr)[TR],
                                                    const uint8_t* const (&sptr)[TR],
@@ -626,14 +637,20 @@ __device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
   const int L = (S + KP - 1) / KP;          // iterations (the longest part)
   const int last = me.start + me.len - 1;
   WStep<TR> b0, b1;
-  load_wcodes<TR>(b0, cptr, me.start);
   u32x4 ph[TR], ph1[TR];
-  load_shalf<TR>(ph, sptr, me.start, 0, last);
-  load_shalf<TR>(ph1, sptr, me.start, 1, last);
+  if constexpr (TL) {
+    load_wstep_tiled<TR, true>(b0, cptr, sptr, me.start);
+  } else {
+    load_wcodes<TR>(b0, cptr, me.start);
+    load_shalf<TR>(ph, sptr, me.start, 0, last);
+    load_shalf<TR>(ph1, sptr, me.start, 1, last);
+  }
   u32x4 xv[XP];
-  xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, 0, row_ptr);
-  store_shalf<TR>(my, ph, 0);
-  store_shalf<TR>(my, ph1, 1);
+  xwin_load_kp<XP, KP, RPP, TL>(xv, M, K, s0, S, 0, row_ptr);
+  if constexpr (!TL) {
+    store_shalf<TR>(my, ph, 0);
+    store_shalf<TR>(my, ph1, 1);
+  }
   bool on = true;
   int fails = 0;
   xwin_store_kp<H, XP, RPP>(win, hflag, on, xv, 0);
@@ -650,20 +667,23 @@ __device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
         marked = marked || __builtin_amdgcn_readfirstlane(hflag[cur * KP + p]) == i;
       f16 = !marked;
       if (marked) {
-        xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, i, row_ptr);
+        xwin_load_kp<XP, KP, RPP, TL>(xv, M, K, s0, S, i, row_ptr);
         xwin_store_kp<false, XP, RPP>(win + cur * wsz, nullptr, false, xv, 0);
         __syncthreads();
         on = ++fails < 2;
       }
     }
     const int j = i & 7;
-    const bool sh = j >= 6;  // scale halves first, as in gemv_accumulate_win_blk
+    const bool sh = !TL && j >= 6;  // scale halves first, as in gemv_accumulate_win_blk
     if (sh) load_shalf<TR>(ph, sptr, me.start + i + 8 - j, j - 6, last);
-    xwin_load_kp<XP, KP, RPP>(xv, M, K, s0, S, min(i + 1, L - 1), row_ptr);
-    load_wcodes<TR>(bn, cptr, min(me.start + i + 1, last));
+    xwin_load_kp<XP, KP, RPP, TL>(xv, M, K, s0, S, min(i + 1, L - 1), row_ptr);
+    if constexpr (TL)
+      load_wstep_tiled<TR, true>(bn, cptr, sptr, min(me.start + i + 1, last));
+    else
+      load_wcodes<TR>(bn, cptr, min(me.start + i + 1, last));
     __builtin_amdgcn_sched_barrier(0);
     if (i < me.len) {
-      read_sblock<TR>(bc, my, j);
+      if constexpr (!TL) read_sblock<TR>(bc, my, j);
       const uint16_t* xl[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];

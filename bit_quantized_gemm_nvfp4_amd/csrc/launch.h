@@ -25,8 +25,9 @@ constexpr int kTileRows = 16;
 constexpr int kTileStep = 256;
 constexpr int kTileBlockBytes = 2304;
 size_t tiled_weight_bytes(int64_t N, int64_t K);
-int launch_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
-                       uint8_t* out, hipStream_t stream);
+// Tiled rows r < R are row-major rows row_idx[r] (r when row_idx is null).
+int launch_tile_weight(const uint8_t* codes, const uint8_t* scales, const int32_t* row_idx,
+                       int64_t R, int64_t K, uint8_t* out, hipStream_t stream);
 
 // Two-level NVFP4 (per-tensor fp32 scale g, a device scalar).  Quantize with
 // a given g; the offline weight quantizer (g from the tensor's amax, written

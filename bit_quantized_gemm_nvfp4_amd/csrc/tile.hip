@@ -1,5 +1,6 @@
 // tile.hip -- the tiled NVFP4 weight layout ("NF4T"): conversion from the
-// row-major pair of arrays (codes [N][K/2], scales [N][K/16]).
+// row-major pair of arrays (codes [N][K/2], scales [N][K/16]), all rows or a
+// listed subset of them (a fixed row set such as a masked head's ids).
 //
 // The elements and their values are those of the row-major matrix (NVFP4 as
 // in "Serving Qwen3.8-27B in 4-bit with a masked speculative decoding head",
@@ -32,9 +33,11 @@ namespace {
 // One thread per 16-byte piece of the tiled array: pieces 0..127 of a block
 // are code pieces (half = p / 64, lane = p % 64), 128..143 scale pieces (four
 // lanes each).
+// Tiled row r is row-major row row_idx[r] (r when row_idx is null), r < R.
 __global__ void __launch_bounds__(256) k_tile_weight(const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales,
-                                                     int64_t N, int64_t K, int64_t S,
+                                                     const int32_t* __restrict__ row_idx,
+                                                     int64_t R, int64_t K, int64_t S,
                                                      int64_t pieces, uint8_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= pieces) return;
@@ -44,18 +47,21 @@ __global__ void __launch_bounds__(256) k_tile_weight(const uint8_t* __restrict__
   u32x4 v = {0u, 0u, 0u, 0u};
   if (p < 128) {
     const int h = p >> 6, lane = p & 63;
-    const int64_t row = t * 16 + (lane & 15);
+    const int64_t r = t * 16 + (lane & 15);
     const int64_t k = s * kTileStep + 64 * (lane >> 4) + 32 * h;  // K % 32 == 0: all or none
-    if (row < N && k < K)
+    if (r < R && k < K) {
+      const int64_t row = row_idx ? (int64_t)row_idx[r] : r;
       v = *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + k / 2);
+    }
   } else {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int lane = 4 * (p - 128) + j;
-      const int64_t row = t * 16 + (lane & 15);
+      const int64_t r = t * 16 + (lane & 15);
       const int64_t b0 = s * (kTileStep / 16) + 4 * (lane >> 4);  // first scale block
-      if (row >= N) continue;
+      if (r >= R) continue;
+      const int64_t row = row_idx ? (int64_t)row_idx[r] : r;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (b0 + e < K / 16) w[j] |= (uint32_t)scales[row * (K / 16) + b0 + e] << (8 * e);
@@ -72,14 +78,14 @@ size_t tiled_weight_bytes(int64_t N, int64_t K) {
   return (size_t)T * (size_t)S * kTileBlockBytes;
 }
 
-int launch_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
-                       uint8_t* out, hipStream_t stream) {
-  const int64_t T = (N + kTileRows - 1) / kTileRows, S = (K + kTileStep - 1) / kTileStep;
+int launch_tile_weight(const uint8_t* codes, const uint8_t* scales, const int32_t* row_idx,
+                       int64_t R, int64_t K, uint8_t* out, hipStream_t stream) {
+  const int64_t T = (R + kTileRows - 1) / kTileRows, S = (K + kTileStep - 1) / kTileStep;
   const int64_t pieces = T * S * (kTileBlockBytes / 16);
   const int64_t blocks = (pieces + 255) / 256;
   if (blocks > INT32_MAX) return -2;
   hipLaunchKernelGGL(k_tile_weight, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales,
-                     N, K, S, pieces, out);
+                     row_idx, R, K, S, pieces, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

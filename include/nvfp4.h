@@ -172,15 +172,20 @@ size_t nvfp4_tiled_weight_bytes(int64_t N, int64_t K);
 
 /*
  * Write the tiled layout of NF4W(N, K) (codes [N][K/2], scales [N][K/16]) to
- * w_tiled (nvfp4_tiled_weight_bytes(N, K) bytes, every byte written).  A pure
- * byte permutation plus zero padding.  K % 32 == 0.
+ * w_tiled, every byte written: a pure byte permutation plus zero padding.
+ * row_idx (optional, int32 [n_rows], each < N): tile only those rows, in that
+ * order -- tiled row r is row row_idx[r] -- as for a masked head whose id set
+ * is fixed when the weights are loaded ("Serving Qwen3.8-27B in 4-bit ...",
+ * section "The masked head trick": the top 32,768 of 248,320 ids).  NULL
+ * means all rows (n_rows must equal N).  w_tiled holds
+ * nvfp4_tiled_weight_bytes(n_rows, K) bytes.  K % 32 == 0.
  */
 int nvfp4_tile_weight(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                      uint8_t *w_tiled, void *stream);
+                      const int32_t *row_idx, int64_t n_rows, uint8_t *w_tiled, void *stream);
 
 /*
- * nvfp4_gemm on tiled weights, all N rows (no row_idx: a masked head gathers
- * rows from the row-major layout): out[m][n] = sum_k a[m][k] * w[n][k],
+ * nvfp4_gemm on tiled weights of N rows (all rows of the tiled matrix; a row
+ * subset is tiled as its own matrix): out[m][n] = sum_k a[m][k] * w[n][k],
  * out [M][N] in out_dtype, a_dtype / a / a_scales as in nvfp4_gemm.  The
  * weights are streamed by the split-K GEMV, 32 activation rows per launch.
  * Same products, fp32 accumulation, tolerance and run-to-run determinism as

@@ -402,11 +402,16 @@ def test_tiled_validation(L):
     assert L.nvfp4_tiled_weight_bytes(248320, 5120) == 248320 * 5120 * 9 // 16
     assert L.nvfp4_tiled_weight_bytes(16, 48) == 0  # K % 32 != 0
     assert L.nvfp4_tiled_weight_bytes(0, 64) == 0
-    assert L.nvfp4_tile_weight(NULL, P2, 4, 64, P3, NULL) == INVALID
-    assert L.nvfp4_tile_weight(P, P2, 4, 64, NULL, NULL) == INVALID
-    assert L.nvfp4_tile_weight(P, P2, 0, 64, P3, NULL) == INVALID
-    assert L.nvfp4_tile_weight(P, P2, 4, 48, P3, NULL) == NOT_SUPPORTED
-    assert L.nvfp4_tile_weight(MIS, P2, 4, 64, P3, NULL) == INVALID
+    t = L.nvfp4_tile_weight  # (codes, scales, N, K, row_idx, n_rows, w_tiled, stream)
+    assert t(NULL, P2, 4, 64, NULL, 4, P3, NULL) == INVALID
+    assert t(P, P2, 4, 64, NULL, 4, NULL, NULL) == INVALID
+    assert t(P, P2, 0, 64, NULL, 0, P3, NULL) == INVALID
+    assert t(P, P2, 4, 48, NULL, 4, P3, NULL) == NOT_SUPPORTED
+    assert t(MIS, P2, 4, 64, NULL, 4, P3, NULL) == INVALID
+    assert t(P, P2, 4, 64, NULL, 3, P3, NULL) == INVALID  # all rows: n_rows == N
+    assert t(P, P2, 4, 64, P4, 5, P3, NULL) == INVALID    # a subset: n_rows <= N
+    assert t(P, P2, 4, 64, P4, 0, P3, NULL) == INVALID
+    assert t(P, P2, 4, 64, MIS, 2, P3, NULL) == INVALID
     g = L.nvfp4_gemm_tiled
     # (a_dtype, a, a_scales, M, N, K, w_tiled, out_dtype, out, ws, ws_bytes, stream)
     assert g(0, NULL, NULL, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID

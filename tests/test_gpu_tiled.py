@@ -59,6 +59,27 @@ def test_tile_weight_matches_oracle(nv, orc, N, K):
     assert np.array_equal(g.t.cpu().numpy(), orc.tile_weight(codes, scales, N, K))
 
 
+@pytest.mark.parametrize("N,K,n_rows", [(40, 544, 17), (1000, 1312, 333), (300, 5120, 300)])
+def test_tile_rows_matches_oracle(nv, orc, N, K, n_rows):
+    """A listed row subset tiled as its own matrix: the oracle's tiling of the
+    gathered rows, byte for byte."""
+    import torch
+    helpers.announce(f"tile_weight rows N={N} K={K} n_rows={n_rows}")
+    rng = np.random.default_rng(N + K + n_rows)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (N, K // 16), dtype=np.uint8)
+    idx = np.sort(rng.choice(N, n_rows, replace=False)).astype(np.int32)
+    if n_rows == N:
+        idx = rng.permutation(N).astype(np.int32)  # any order, not only sorted
+    g = helpers.Guarded((nv.tiled_weight_bytes(n_rows, K),), torch.uint8)
+    g.t.fill_(0x5A)
+    nv.tile_weight(helpers.dev_u8(codes), helpers.dev_u8(scales), row_idx=helpers.dev_i32(idx),
+                   out=g.t)
+    g.check()
+    ref = orc.tile_weight(codes[idx], scales[idx], n_rows, K)
+    assert np.array_equal(g.t.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("M,K,N", [
     (1, 32, 16), (1, 64, 5), (2, 288, 33), (3, 544, 100), (4, 1024, 560), (5, 2080, 48),
     (8, 1312, 300), (13, 256, 17), (16, 4096, 40), (17, 512, 48), (32, 1536, 272),
@@ -90,6 +111,17 @@ LAYOUTS = [
     (20, dict(gemv_tiles=1, gemv_waves=16)), (32, dict(gemv_tiles=2, gemv_waves=16)),
     (32, dict(gemv_tiles=2, gemv_waves=8)), (25, dict(gemv_tiles=1, gemv_waves=4, gemv_splits=7)),
     (2, dict(gemv_tiles=1, gemv_waves=8, gemv_lds_kib=8)),
+    # K parts inside the workgroup: the 4x4x4 kernel (1 tile per wave, nw = groups x parts)
+    (1, dict(gemv_kparts=2, gemv_waves=4)), (1, dict(gemv_kparts=8, gemv_waves=16)),
+    (4, dict(gemv_kparts=4, gemv_waves=8)), (3, dict(gemv_kparts=8, gemv_waves=8, gemv_splits=1)),
+    (2, dict(gemv_kparts=2, gemv_waves=8, gemv_lds_kib=8)),
+    # ... and the 16x16 kernel
+    (8, dict(gemv_kparts=4, gemv_tiles=2, gemv_waves=8)),
+    (6, dict(gemv_kparts=8, gemv_tiles=1, gemv_waves=16)),
+    (5, dict(gemv_kparts=8, gemv_tiles=2, gemv_waves=8)),
+    (16, dict(gemv_kparts=2, gemv_tiles=2, gemv_waves=8)),
+    (13, dict(gemv_kparts=4, gemv_tiles=1, gemv_waves=16, gemv_splits=2)),
+    (32, dict(gemv_kparts=2, gemv_tiles=1, gemv_waves=16)),
 ]
 
 
@@ -185,3 +217,23 @@ def test_decode_full_size_sampled(nv, orc, K, N):
     x = workloads.decode_activations(32, K)
     y2 = helpers.host_bits(nv.gemm_tiled(helpers.dev_bf16(x), wt, N))
     assert np.array_equal(y2, ref_all[32])
+
+
+def test_masked_head_rows_tiled_full_size_sampled(nv, orc):
+    """The masked head's 32,768 of 248,320 rows tiled once (row_idx) and streamed
+    as a dense 32,768-row layer, M in {1, 8, 32}; sampled output columns against
+    the oracle's masked product."""
+    import torch
+    K, N = workloads.HIDDEN, workloads.VOCAB
+    w = workloads.decode_weights(K, N)
+    idx = workloads.decode_masked_rows()
+    wt = nv.tile_weight(helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                        row_idx=helpers.dev_i32(idx))
+    sel = np.sort(np.random.default_rng(3).choice(len(idx), 256, replace=False))
+    for M in workloads.DECODE_M:
+        helpers.announce(f"gemm_tiled masked head rows M={M}")
+        x = workloads.decode_activations(M, K)
+        y = helpers.host_bits(nv.gemm_tiled(helpers.dev_bf16(x), wt, len(idx)))
+        ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx[sel])
+        _assert_close(y[:, sel], ref, what=f"masked M={M}")
+        torch.cuda.synchronize()
