@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   }
   int xrow_off[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow_off[mt] = (16 * mt + ln) * kXWin + 64 * q;
+  for (int mt = 0; mt < MT; ++mt) xrow_off[mt] = (16 * mt + ln) * kXWin + 64 * win_quarter(q);
 
   f32x4 acc[TR][MT];
 #pragma unroll

@@ -273,6 +273,19 @@ __device__ __forceinline__ void gemv_accumulate(f32x4 (&acc)[TR][MT],
 // past K read a clamped address and are replaced by zero.
 constexpr int kXWin = kGemvStep + kXPad;  // LDS row stride of the window
 
+// Inside a window row the 64-element quarters 1 and 2 trade places.  gfx950
+// serves a 16-byte LDS read 32 lanes at a time over 512 bytes of banks; the
+// operand reads of lanes (n, q) and (n, q + 1) fall on rows n and n' with
+// chunks 16 n and 16 n' + 128 modulo 512 bytes (rows 528 bytes apart), which
+// collide for n = n' + 8.  With the swap the two quarters of a 32-lane group
+// sit 256 bytes apart and all 32 chunks differ (measured with
+// SQ_LDS_BANK_CONFLICT: 4 conflict cycles per read -> 0).
+__host__ __device__ constexpr int win_quarter(int q) { return ((q & 1) << 1) | (q >> 1); }
+// Element offset, inside a window row, of its 8-element chunk cc (0..31).
+__device__ __forceinline__ int win_chunk(int cc) {
+  return 64 * win_quarter(cc >> 3) + 8 * (cc & 7);
+}
+
 template <int XP, typename RowPtr>
 __device__ __forceinline__ void xwin_load(u32x4 (&v)[XP], int M, int64_t K, int s,
                                           RowPtr row_ptr) {
@@ -304,7 +317,7 @@ __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) 
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
-    *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = v[i];
+    *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + win_chunk(c & 31)) = v[i];
   }
 }
 
@@ -339,7 +352,7 @@ __device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int b
         const int c = threadIdx.x + i * blockDim.x;
         u32x4 h;
         ok = bf16x8_to_f16(v[i], h) && ok;
-        *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + (c & 31) * 8) = h;
+        *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + win_chunk(c & 31)) = h;
       }
       if (!ok) hw.flag[bufidx] = s;
       return;
@@ -386,7 +399,7 @@ __device__ __forceinline__ void compute_wstep_win(f32x4 (&acc)[TR][MT], const WS
 
 // Accumulate steps [s0, s1) with the activations streamed through the LDS
 // window `win` ([2][16*MT][kXWin]; bf16, or fp16 with `hflag` when H).
-// xrow_off[mt] = (16*mt + lane%16) * kXWin + 64q (rows past M hold copies,
+// xrow_off[mt] = (16*mt + lane%16) * kXWin + 64 * win_quarter(q) (rows past M hold copies,
 // their results are never stored).  Every thread of the workgroup calls this
 // with the same arguments except the weight pointers.  blockDim.x * XP ==
 // 16*MT*32.
@@ -605,7 +618,7 @@ __device__ __forceinline__ void xwin_store_kp(uint16_t* buf, int* hflag_buf, boo
 #pragma unroll
   for (int u = 0; u < XP; ++u) {
     const int c = threadIdx.x + u * blockDim.x;
-    uint16_t* dst = buf + (c >> 5) * kXWin + (c & 31) * 8;
+    uint16_t* dst = buf + (c >> 5) * kXWin + win_chunk(c & 31);
     if (H && on) {
       u32x4 h;
       if (!bf16x8_to_f16(v[u], h)) hflag_buf[(c >> 5) / RPP] = tag;
@@ -633,7 +646,8 @@ __device__ __forceinline__ void gemv_accumulate_kp(f32x4 (&acc)[TR][MT],
   int xrow_off[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    xrow_off[mt] = part * psz + (WR == 8 ? min(ln, 7) : 16 * mt + ln) * kXWin + 64 * q;
+    xrow_off[mt] =
+        part * psz + (WR == 8 ? min(ln, 7) : 16 * mt + ln) * kXWin + 64 * win_quarter(q);
   const int L = (S + KP - 1) / KP;          // iterations (the longest part)
   const int last = me.start + me.len - 1;
   WStep<TR> b0, b1;
