@@ -89,10 +89,13 @@ int nvfp4_grouped_gemm_scaled_planned(const nvfp4_plan_t *plan, const uint16_t *
                                       int epilogue, uint16_t *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
-/* nvfp4_gemm_tiled with a plan: gemv_tiles {1, 2, 4 (M <= 16)}, gemv_waves
- * {4, 8, or 16 with 16 < M <= 32}, gemv_splits; the tiled GEMV has no
- * 4x4x4-block kernel and no K parts inside a workgroup (gemv_small_max and
- * gemv_kparts must be < 1). */
+/* nvfp4_gemm_tiled with a plan.  4x4x4-block kernel (M <= gemv_small_max,
+ * default 4, at most 8): one tile of 16 rows per wave (two with M <= 4), 1..8
+ * waves; with gemv_kparts in {2, 4, 8, 16} (M <= 4, one tile per wave)
+ * gemv_waves = tile groups x parts, at most 16.  16x16 kernel: gemv_tiles
+ * {1, 2, 4 (M <= 16)}, gemv_waves {4, 8, or 16 with 16 < M <= 32}, or the
+ * K-parts layouts of gemv_kparts.  gemv_splits and gemv_lds_kib as for
+ * nvfp4_gemm. */
 size_t nvfp4_gemm_tiled_workspace_size_planned(const nvfp4_plan_t *plan, int a_dtype, int64_t M,
                                                int64_t N, int64_t K);
 int nvfp4_gemm_tiled_planned(const nvfp4_plan_t *plan, int a_dtype, const void *a,
