@@ -21,6 +21,7 @@ __all__ = [
     "grouped_gemm", "moe_combine", "moe_layer", "topk", "head_topk", "kv_store_e4m3",
     "kv_load_e4m3", "quantize_scaled", "quantize_weight", "gemm_w4a4", "dequantize_scaled",
     "gemm_scaled", "tiled_weight_bytes", "tile_weight", "gemm_tiled", "gemm_tiled_workspace_size",
+    "tile_experts", "grouped_gemm_tiled", "moe_layer_tiled",
     "Plan", "make_plan", "BF16", "FP32", "NVFP4", "EPI_NONE", "EPI_SWIGLU",
 ]
 
@@ -73,6 +74,8 @@ _SIGS = {
     "nvfp4_tile_weight": ([_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp], _int),
     "nvfp4_gemm_tiled_workspace_size": ([_int, _i64, _i64, _i64], _sz),
     "nvfp4_gemm_tiled": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_grouped_gemm_tiled": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                  _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_noalloc_scratch_bytes": ([], _sz),
     "nvfp4_gemm_noalloc": ([_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _int, _vp,
                             _vp], _int),
@@ -99,6 +102,8 @@ _SIGS.update({
     "nvfp4_gemm_tiled_workspace_size_planned": ([_pp, _int, _i64, _i64, _i64], _sz),
     "nvfp4_gemm_tiled_planned": ([_pp, _int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _sz,
                                   _vp], _int),
+    "nvfp4_grouped_gemm_tiled_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp,
+                                          _vp, _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                     _vp, _int, _vp, _vp, _sz, _vp], _int),
     "nvfp4_grouped_gemm_scaled_planned": ([_pp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp,
@@ -643,6 +648,47 @@ def grouped_gemm(a: torch.Tensor, gather_idx, expert_offsets: torch.Tensor,
     return out
 
 
+def tile_experts(w_codes: torch.Tensor, w_scales: torch.Tensor) -> torch.Tensor:
+    """Expert weights [E, N, K/2] + [E, N, K/16] (N % 16 == 0) in the tiled layout:
+    the stacked E*N-row matrix tiled, so expert e's N/16 tiles follow expert e-1's."""
+    E, N, half = _dims(w_codes, "w_codes", 3)
+    if N % 16:
+        raise ValueError(f"expert rows N={N} must be a multiple of 16")
+    _arg(w_scales, "w_scales", torch.uint8, (E, N, 2 * half // 16))
+    return tile_weight(w_codes.view(E * N, half), w_scales.view(E * N, 2 * half // 16))
+
+
+def grouped_gemm_tiled(a: torch.Tensor, gather_idx, expert_offsets: torch.Tensor,
+                       w_tiled: torch.Tensor, E: int, N: int, rows: int, row_scale=None,
+                       epilogue: int = EPI_NONE, out=None, plan=None,
+                       w_global=None) -> torch.Tensor:
+    """grouped_gemm on tiled expert weights (tile_experts) of E experts x N rows."""
+    a_rows, K = _dims(a, "a", 2)
+    _arg(a, "a", torch.bfloat16)
+    if K % 32 or N % 16 or E < 1:
+        raise ValueError(f"unsupported grouped shape E={E} N={N} K={K}")
+    _arg(w_tiled, "w_tiled", torch.uint8, (tiled_weight_bytes(E * N, K),))
+    _arg(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _arg(gather_idx, "gather_idx", torch.int32, (rows,), optional=True)
+    _arg(row_scale, "row_scale", torch.float32, (rows,), optional=True)
+    _arg(w_global, "w_global", torch.float32, (E,), optional=True)
+    width = N // 2 if epilogue == EPI_SWIGLU else N
+    _arg(out, "out", torch.bfloat16, (rows, width), optional=True)
+    _gpu(a, gather_idx, expert_offsets, w_tiled, row_scale, w_global, out)
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.bfloat16, device=a.device)
+    nbytes = int(lib().nvfp4_grouped_gemm_workspace_size(rows, E, N, K))
+    ws, wsz = _workspace(nbytes, a.device)
+    args = (_ptr(a), a_rows, K, _ptr(gather_idx), _ptr(expert_offsets), E, rows, N,
+            _ptr(w_tiled), _ptr(w_global), _ptr(row_scale), epilogue, _ptr(out), _ptr(ws), wsz,
+            _stream(a.device))
+    if plan is not None:
+        _check(lib().nvfp4_grouped_gemm_tiled_planned(_plan_ref(plan), *args))
+    else:
+        _check(lib().nvfp4_grouped_gemm_tiled(*args))
+    return out
+
+
 def moe_combine(y: torch.Tensor, slot_pos: torch.Tensor, out=None) -> torch.Tensor:
     T, topk = _dims(slot_pos, "slot_pos", 2)
     _arg(slot_pos, "slot_pos", torch.int32)
@@ -673,4 +719,19 @@ def moe_layer(x, topk_ids, gates, w1_codes, w1_scales, w2_codes, w2_scales, w1_g
                        w_global=w1_global)
     y = grouped_gemm(act, None, offsets, w2_codes, w2_scales, R, row_scale=row_gate,
                      w_global=w2_global)
+    return moe_combine(y, slot)
+
+
+def moe_layer_tiled(x, topk_ids, gates, w1_tiled, w2_tiled, E: int, I: int, w1_global=None,
+                    w2_global=None):
+    """moe_layer on tiled expert weights: w1_tiled = tile_experts of the gate+up
+    weights [E, 2I, H/2], w2_tiled of the down weights [E, H, I/2]."""
+    T, topk = _dims(topk_ids, "topk_ids", 2)
+    H = x.shape[1]
+    R = T * topk
+    offsets, gather, slot, row_gate = moe_align(topk_ids, E, gates)
+    act = grouped_gemm_tiled(x, gather, offsets, w1_tiled, E, 2 * I, R, epilogue=EPI_SWIGLU,
+                             w_global=w1_global)
+    y = grouped_gemm_tiled(act, None, offsets, w2_tiled, E, H, R, row_scale=row_gate,
+                           w_global=w2_global)
     return moe_combine(y, slot)

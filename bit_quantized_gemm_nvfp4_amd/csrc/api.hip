@@ -313,6 +313,7 @@ int nvfp4_gemm_scaled(int a_dtype, const void* a, const uint8_t* a_scales,
 namespace {
 
 struct TiledPlan {
+  bool mfma;  // large M: the MFMA GEMM reading tiled weights
   GemvPlan gemv;
   int64_t m_chunk;
   size_t a_dequant_bytes;
@@ -321,9 +322,12 @@ struct TiledPlan {
 
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool w4a4, const PlanOverride& ov) {
   TiledPlan t;
+  const int64_t min_m = ov.gemm_min_m >= 1 ? ov.gemm_min_m : kGemmMinM;
+  t.mfma = M >= min_m;
   t.m_chunk = M < kGemvMaxM ? M : kGemvMaxM;
   t.gemv = plan_gemv(t.m_chunk, N, K, kNumCUs, ov, true);
-  t.partial_bytes = gemv_workspace_bytes(t.gemv, t.m_chunk, N);
+  t.partial_bytes = t.mfma ? gemm_workspace_bytes(M, N, K, kNumCUs)
+                           : gemv_workspace_bytes(t.gemv, t.m_chunk, N);
   t.a_dequant_bytes = w4a4 ? (size_t)M * (size_t)K * 2 : 0;
   return t;
 }
@@ -350,6 +354,8 @@ int gemm_tiled_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t
   if (a_scales && !aligned16(a_scales)) return NVFP4_ERROR_INVALID_VALUE;
   const bool w4a4 = a_dtype == NVFP4_NVFP4;
   const TiledPlan t = plan_tiled(M, N, K, w4a4, ov);
+  if (t.mfma && K > kGemmMaxK) return NVFP4_ERROR_NOT_SUPPORTED;
+  if (t.mfma && ((M + 255) / 256) * ((N + 255) / 256) > INT32_MAX) return NVFP4_ERROR_NOT_SUPPORTED;
   const size_t p_off = round_up(t.a_dequant_bytes, 256);
   const size_t need = p_off + t.partial_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
@@ -363,6 +369,9 @@ int gemm_tiled_impl(int a_dtype, const void* a, const uint8_t* a_scales, int64_t
     x = xa;
   }
   void* partial = t.partial_bytes ? static_cast<char*>(workspace) + p_off : nullptr;
+  if (t.mfma)
+    return launched(launch_gemm(GemmA::kBf16, x, M, K, w_tiled, nullptr, nullptr, N,
+                                out_dtype == NVFP4_FP32, out, partial, st, Alpha{}, true));
   const size_t osz = out_dtype == NVFP4_FP32 ? 4 : 2;
   if (log_enabled())
     fprintf(stderr, "[nvfp4] gemm_tiled M=%lld N=%lld K=%lld: mt=%d tr=%d nw=%d z=%d\n",
@@ -683,8 +692,10 @@ static int grouped_impl(const PlanOverride& ov, const uint16_t* a, int64_t a_row
                         const int32_t* gather_idx, const int32_t* expert_offsets, int64_t E,
                         int64_t R, int64_t N, const uint8_t* w_codes, const uint8_t* w_scales,
                         const float* w_global, const float* row_scale, int epilogue,
-                        uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!a || !expert_offsets || !w_codes || !w_scales || !out) return NVFP4_ERROR_INVALID_VALUE;
+                        uint16_t* out, void* workspace, size_t workspace_bytes, void* stream,
+                        bool tiled = false) {
+  if (!a || !expert_offsets || !w_codes || (!tiled && !w_scales) || !out)
+    return NVFP4_ERROR_INVALID_VALUE;
   if (w_global && reinterpret_cast<uintptr_t>(w_global) % alignof(float) != 0)
     return NVFP4_ERROR_INVALID_VALUE;
   if (a_rows <= 0 || K <= 0 || E <= 0 || R <= 0 || N <= 0) return NVFP4_ERROR_INVALID_VALUE;
@@ -695,16 +706,16 @@ static int grouped_impl(const PlanOverride& ov, const uint16_t* a, int64_t a_row
     return NVFP4_ERROR_NOT_SUPPORTED;
   if (!gather_idx && a_rows < R) return NVFP4_ERROR_INVALID_VALUE;
   if (!aligned16(a) || !aligned16(expert_offsets) || !aligned16(w_codes) ||
-      !aligned16(w_scales) || !aligned16(out) || (gather_idx && !aligned16(gather_idx)) ||
-      (row_scale && !aligned16(row_scale)))
+      (!tiled && !aligned16(w_scales)) || !aligned16(out) ||
+      (gather_idx && !aligned16(gather_idx)) || (row_scale && !aligned16(row_scale)))
     return NVFP4_ERROR_INVALID_VALUE;
   if (grouped_path(a_rows, K, E, R, ov) == GroupedPath::kNone) return NVFP4_ERROR_NOT_SUPPORTED;
   const size_t need = moe_grouped_workspace_bytes(R, E, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERROR_WORKSPACE;
   return launched(launch_grouped_gemm(a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes,
-                                      w_scales, w_global, row_scale,
+                                      tiled ? nullptr : w_scales, w_global, row_scale,
                                       epilogue == NVFP4_EPI_SWIGLU, out, workspace,
-                                      as_stream(stream), ov));
+                                      as_stream(stream), ov, tiled));
 }
 
 extern "C" {
@@ -754,6 +765,31 @@ int nvfp4_grouped_gemm_scaled_planned(const nvfp4_plan_t* plan, const uint16_t* 
   return grouped_impl(ov, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_codes, w_scales,
                       w_global_scales, row_scale, epilogue, out, workspace, workspace_bytes,
                       stream);
+}
+
+int nvfp4_grouped_gemm_tiled(const uint16_t* a, int64_t a_rows, int64_t K,
+                             const int32_t* gather_idx, const int32_t* expert_offsets, int64_t E,
+                             int64_t R, int64_t N, const uint8_t* w_tiled,
+                             const float* w_global_scales, const float* row_scale, int epilogue,
+                             uint16_t* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return grouped_impl(PlanOverride{}, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_tiled,
+                      nullptr, w_global_scales, row_scale, epilogue, out, workspace,
+                      workspace_bytes, stream, true);
+}
+
+int nvfp4_grouped_gemm_tiled_planned(const nvfp4_plan_t* plan, const uint16_t* a, int64_t a_rows,
+                                     int64_t K, const int32_t* gather_idx,
+                                     const int32_t* expert_offsets, int64_t E, int64_t R,
+                                     int64_t N, const uint8_t* w_tiled,
+                                     const float* w_global_scales, const float* row_scale,
+                                     int epilogue, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  PlanOverride ov;
+  if (!to_override(plan, ov)) return NVFP4_ERROR_INVALID_VALUE;
+  return grouped_impl(ov, a, a_rows, K, gather_idx, expert_offsets, E, R, N, w_tiled, nullptr,
+                      w_global_scales, row_scale, epilogue, out, workspace, workspace_bytes,
+                      stream, true);
 }
 
 int nvfp4_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,

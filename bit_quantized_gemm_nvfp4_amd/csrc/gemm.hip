@@ -27,8 +27,9 @@ namespace {
 
 struct GemmArgs {
   const uint16_t* a;        // bf16 [M][K]
-  const uint8_t* wc;        // weight codes [rows][K/2]
-  const uint8_t* ws;        // weight scales [rows][K/16]
+  const uint8_t* wc;        // weight codes [rows][K/2], or the tiled weights (tiled)
+  const uint8_t* ws;        // weight scales [rows][K/16] (row-major only)
+  int tiled;                // the weights are tiled (tile.hip)
   const int32_t* row_idx;   // output column n uses weight row row_idx[n]; null: row n
   void* out;                // [M][N] bf16 or fp32
   float* partial;           // shared tiles: fp32 [tail][max_seg][256 * 256], tile-local
@@ -84,7 +85,10 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
   {
     const int64_t n = min(n0 + (t >> 1), g.N - 1);
     const int64_t wr = g.row_idx ? (int64_t)g.row_idx[n] : n;
-    gemm_src_nvfp4_row(src.wc, src.ws, g.wc + k_lo / 2, g.ws + k_lo / 16, wr, K);
+    if (g.tiled)
+      gemm_src_tiled_row(src, g.wc, wr, K, k_lo);
+    else
+      gemm_src_nvfp4_row(src, g.wc, g.ws, wr, K, k_lo);
     if constexpr (A_FQ) {
       const int64_t ar = min(m0 + (t >> 1), g.M - 1);
       src.ar = g.a + ar * K + k_lo + 32 * (t & 1);
@@ -393,7 +397,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus) {
 
 int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32, void* out,
-                void* workspace, hipStream_t stream, Alpha alpha) {
+                void* workspace, hipStream_t stream, Alpha alpha, bool tiled) {
   // activation offsets inside a 256-row tile are 32-bit byte offsets (the
   // entry points reject a longer K before launching)
   if (K > ((int64_t)1 << 22)) return -1;
@@ -401,6 +405,7 @@ int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* 
   g.a = static_cast<const uint16_t*>(a);
   g.wc = wc;
   g.ws = ws;
+  g.tiled = tiled ? 1 : 0;
   g.row_idx = row_idx;
   g.out = out;
   g.M = M;

@@ -121,21 +121,50 @@ struct GemmLoad<true> {
 // base pointer at k = 0 (see dma_a_tile); its NVFP4 weight row as pointers to
 // this lane's half of row t/2 at k = 0 (gemm_src_nvfp4_row); an A_FQ
 // activation row as a pointer to this lane's half of row t/2.
+//
+// Weight addresses: the element k of the weight row sits at byte offset
+// (k / 256) * step + ((k / 64) % 4) * quarter from the lane's pointer (codes;
+// scales with their own two constants), k a multiple of 64.  Row-major
+// weights: step 128 / quarter 32 (codes), 16 / 4 (scales), i.e. k / 2 and
+// k / 16.  Tiled weights (tile.hip): 2304 / 256 and 2304 / 64 -- the 64
+// elements [k, k + 64) of a row are lane (row % 16, (k / 64) % 4) of block
+// k / 256.  The steps and quarters are workgroup-uniform, so the offsets stay
+// scalar arithmetic.
+struct WAddr {
+  int64_t k_lo;           // first element of the workgroup's K range
+  int c_step, c_quarter;  // codes
+  int s_step, s_quarter;  // scales
+  int pad;                // 1: row-major (a partial last step re-reads inside the row);
+                          // 0: tiled (the layout pads K with zeros)
+};
+
+__device__ __forceinline__ WAddr waddr_row_major(int64_t k_lo) {
+  return WAddr{k_lo, 128, 32, 16, 4, 1};
+}
+__device__ __forceinline__ WAddr waddr_tiled(int64_t k_lo) {
+  return WAddr{k_lo, 2304, 256, 2304, 64, 0};
+}
+
 struct GemmSrc {
   uint32_t a_off[4];
   uint32_t a_back[4];
   const uint16_t* ar;
-  const uint8_t* wc;
+  const uint8_t* wc;  // this lane's codes and scales at k = 0 of its row
   const uint8_t* ws;
+  WAddr wa;
 };
 
-__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const uint8_t* c, const uint8_t* s,
-                                                int64_t k0, bool kfull) {
+__device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const GemmSrc& src, int64_t k0,
+                                                bool kfull) {
   const int hh = threadIdx.x & 1;
-  const int64_t coff = k0 / 2 - (kfull ? 0 : 16 * hh);
-  const int64_t soff = k0 / 16 - (kfull ? 0 : 2 * hh);
-  R.c = *reinterpret_cast<const u32x4*>(c + coff);
-  R.s = *reinterpret_cast<const uint16_t*>(s + soff);
+  const WAddr& w = src.wa;
+  const int64_t k = w.k_lo + k0;
+  const int64_t blk = k >> 8, q = (k >> 6) & 3;
+  const int back = (kfull || !w.pad) ? 0 : hh;
+  const int64_t coff = blk * w.c_step + q * w.c_quarter - 16 * back;
+  const int64_t soff = blk * w.s_step + q * w.s_quarter - 2 * back;
+  R.c = *reinterpret_cast<const u32x4*>(src.wc + coff);
+  R.s = *reinterpret_cast<const uint16_t*>(src.ws + soff);
 }
 
 // A_FQ: 32 bf16 activations of this lane's half of its row (a partial last
@@ -153,7 +182,7 @@ __device__ __forceinline__ void gemm_load(GemmLoad<A_FQ>& L, const GemmSrc& src,
                                           const uint8_t* a_tile_base, int64_t K, int64_t k0) {
   const bool kfull = k0 + BK <= K;
   if constexpr (A_FQ) load_bf16_rows(L.a, src.ar, k0, kfull);
-  load_nvfp4_rows(L.w, src.wc, src.ws, k0, kfull);
+  load_nvfp4_rows(L.w, src, k0, kfull);
 }
 
 // bf16 activation tile of the step at k0 -> LDS A buffer at `dst`, straight
@@ -317,12 +346,27 @@ __device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_
   gemm_src_bf16_rows(src, r, K);
 }
 
-__device__ __forceinline__ void gemm_src_nvfp4_row(const uint8_t*& c, const uint8_t*& s,
-                                                   const uint8_t* codes, const uint8_t* scales,
-                                                   int64_t row, int64_t K) {
+// This lane's pointers (its half of weight row `row`, k = 0) and the address
+// constants, for a workgroup whose K range starts at k_lo.
+__device__ __forceinline__ void gemm_src_nvfp4_row(GemmSrc& src, const uint8_t* codes,
+                                                   const uint8_t* scales, int64_t row, int64_t K,
+                                                   int64_t k_lo) {
   const int hh = threadIdx.x & 1;
-  c = codes + row * (K / 2) + 16 * hh;
-  s = scales + row * (K / 16) + 2 * hh;
+  src.wc = codes + row * (K / 2) + 16 * hh;
+  src.ws = scales + row * (K / 16) + 2 * hh;
+  src.wa = waddr_row_major(k_lo);
+}
+
+// The same on tiled weights `wt` (ceil(K / 256) blocks per 16-row tile).
+__device__ __forceinline__ void gemm_src_tiled_row(GemmSrc& src, const uint8_t* wt, int64_t row,
+                                                   int64_t K, int64_t k_lo) {
+  const int hh = threadIdx.x & 1;
+  const int64_t S = (K + 255) / 256;
+  const uint8_t* tb = wt + (row >> 4) * S * 2304;
+  const int n = (int)(row & 15);
+  src.wc = tb + 1024 * hh + 16 * n;
+  src.ws = tb + 2048 + 4 * n + 2 * hh;
+  src.wa = waddr_tiled(k_lo);
 }
 
 __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[kXBlocks][kWBlocks]) {

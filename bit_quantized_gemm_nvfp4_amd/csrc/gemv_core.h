@@ -224,7 +224,8 @@ __device__ __forceinline__ void compute_wstep(f32x4 (&acc)[TR][MT], const WStep<
 // lane's activation row in LDS at element 64q of step s0.  `steps_full` is the
 // number of complete 256-element steps of K; step steps_full (if < s1) is the
 // partial last step.
-template <int MT, int TR>
+// TL: tiled weights (load_wstep_tiled pointers), every step whole.
+template <int MT, int TR, bool TL = false>
 __device__ __forceinline__ void gemv_accumulate(f32x4 (&acc)[TR][MT],
                                                 const uint8_t* const (&cptr)[TR],
                                                 const uint8_t* const (&sptr)[TR],
@@ -242,15 +243,15 @@ __device__ __forceinline__ void gemv_accumulate(f32x4 (&acc)[TR][MT],
     // scheduling barriers keep each prefetch batch ahead of the compute it
     // overlaps.
     WStep<TR> b0, b1;
-    load_wstep<TR, false>(b0, cptr, sptr, K, sdw, s);
+    load_wstep_full<TR, TL>(b0, cptr, sptr, K, sdw, s);
     while (true) {
-      load_wstep<TR, false>(b1, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      load_wstep_full<TR, TL>(b1, cptr, sptr, K, sdw, min(s + 1, e - 1));
       __builtin_amdgcn_sched_barrier(0);
       compute_wstep<MT, TR>(acc, b0, xl);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) xl[mt] += kGemvStep;
       if (++s >= e) break;
-      load_wstep<TR, false>(b0, cptr, sptr, K, sdw, min(s + 1, e - 1));
+      load_wstep_full<TR, TL>(b0, cptr, sptr, K, sdw, min(s + 1, e - 1));
       __builtin_amdgcn_sched_barrier(0);
       compute_wstep<MT, TR>(acc, b1, xl);
 #pragma unroll
@@ -258,7 +259,7 @@ __device__ __forceinline__ void gemv_accumulate(f32x4 (&acc)[TR][MT],
       if (++s >= e) break;
     }
   }
-  if (s == steps_full && s < s1) {  // partial last step
+  if (!TL && s == steps_full && s < s1) {  // partial last step
     WStep<TR> bt;
     load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
     compute_wstep<MT, TR>(acc, bt, xl);

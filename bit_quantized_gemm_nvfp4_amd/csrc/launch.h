@@ -112,9 +112,10 @@ struct GemmSplitPlan {
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t n_out, int64_t K, int num_cus);
 size_t gemm_workspace_bytes(int64_t M, int64_t n_out, int64_t K, int num_cus);
 enum class GemmA { kBf16, kFakeQuant };
+// tiled: wc is the tiled weights (tile.hip), ws and row_idx unused.
 int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* wc,
                 const uint8_t* ws, const int32_t* row_idx, int64_t n_out, bool out_f32, void* out,
-                void* workspace, hipStream_t stream, Alpha alpha = {});
+                void* workspace, hipStream_t stream, Alpha alpha = {}, bool tiled = false);
 
 // Top-k of each row of fp32 logits [M][n] (k <= kTopkMaxK), best first: larger
 // value, then smaller column; -0 below +0.  ids are ids_map[column] (or the

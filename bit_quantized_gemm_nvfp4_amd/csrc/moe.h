@@ -30,7 +30,8 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
                         const int32_t* offsets, int64_t E, int64_t R, int64_t N,
                         const uint8_t* wc, const uint8_t* ws, const float* wg,
                         const float* row_scale, bool swiglu, uint16_t* out, void* workspace,
-                        hipStream_t stream, const PlanOverride& ov = PlanOverride{});
+                        hipStream_t stream, const PlanOverride& ov = PlanOverride{},
+                        bool tiled = false);  // wc: tiled experts (tile.hip), ws unused
 
 int launch_moe_combine(const uint16_t* y, const int32_t* slot_pos, int64_t T, int64_t topk,
                        int64_t H, uint16_t* out, hipStream_t stream);

@@ -170,7 +170,7 @@ struct GroupedArgs {
   const uint16_t* a;
   const int32_t* gather;
   const int32_t* offsets;
-  const uint8_t* wc;
+  const uint8_t* wc;  // row-major codes [E][N][K/2], or the tiled experts (k_grouped_gemv<TR, true>)
   const uint8_t* ws;
   const float* wg;  // per-expert global scales [E] of two-level weights, or NULL
   const float* row_scale;
@@ -233,7 +233,7 @@ __device__ __forceinline__ bool find_chunk(const int32_t* offsets, int E, int bx
 
 // One workgroup: up to 16 grouped rows of one expert (staged in LDS) against
 // kGroupWaves weight tiles (SWIGLU: tile pairs gate/up) of that expert.
-template <int TR>
+template <int TR, bool TL = false>
 __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
   extern __shared__ uint16_t xs[];  // [kGroupRows][lds_x_stride(steps)]
   const int lane = threadIdx.x & 63;
@@ -256,16 +256,27 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
   // weight rows: NONE -> tiles (blockIdx.y*nw + wave)*TR + t; SWIGLU (TR == 2) ->
   // gate tile blockIdx.y*nw + wave and the matching up tile N/2 further.
   const int64_t gt = (int64_t)blockIdx.y * kGroupWaves + wave;
-  const uint8_t* we_c = g.wc + (int64_t)e * g.N * (K / 2);
-  const uint8_t* we_s = g.ws + (int64_t)e * g.N * (K / 16);
   const uint8_t* cptr[TR];
   const uint8_t* sptr[TR];
+  if constexpr (TL) {  // expert e's N / 16 tiles of g.steps blocks
+    const uint8_t* we = g.wc + (int64_t)e * (g.N / 16) * g.steps * 2304;
 #pragma unroll
-  for (int t = 0; t < TR; ++t) {
-    int64_t n = g.swiglu ? (int64_t)t * (g.N / 2) + gt * 16 + ln : (gt * TR + t) * 16 + ln;
-    if (n >= g.N) n = g.N - 1;  // padding column: never stored
-    cptr[t] = we_c + n * (K / 2);
-    sptr[t] = we_s + n * (K / 16);
+    for (int t = 0; t < TR; ++t) {
+      int64_t tile = g.swiglu ? (int64_t)t * (g.N / 32) + gt : gt * TR + t;
+      if (tile >= g.N / 16) tile = g.N / 16 - 1;  // padding tile: never stored
+      cptr[t] = we + tile * g.steps * 2304 + 16 * lane;
+      sptr[t] = we + tile * g.steps * 2304 + 2048 + 4 * lane;
+    }
+  } else {
+    const uint8_t* we_c = g.wc + (int64_t)e * g.N * (K / 2);
+    const uint8_t* we_s = g.ws + (int64_t)e * g.N * (K / 16);
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      int64_t n = g.swiglu ? (int64_t)t * (g.N / 2) + gt * 16 + ln : (gt * TR + t) * 16 + ln;
+      if (n >= g.N) n = g.N - 1;  // padding column: never stored
+      cptr[t] = we_c + n * (K / 2);
+      sptr[t] = we_s + n * (K / 16);
+    }
   }
   const uint16_t* xl[1] = {xs + min(ln, rows - 1) * stride + 64 * q};
 
@@ -273,7 +284,8 @@ __global__ void __launch_bounds__(256) k_grouped_gemv(GroupedArgs g) {
 #pragma unroll
   for (int t = 0; t < TR; ++t) acc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemv_accumulate<1, TR>(acc, cptr, sptr, xl, K, 0, g.steps, (int)(K / kGemvStep));
+  gemv_accumulate<1, TR, TL>(acc, cptr, sptr, xl, K, 0, g.steps,
+                             TL ? g.steps : (int)(K / kGemvStep));
 
   // lane holds C[m = 4*q + r][column 16*tile + ln]; the sums are h / g_e
   const float ge = g.wg ? g.wg[e] : 1.0f;
@@ -312,8 +324,9 @@ struct GroupedMfmaArgs {
   const uint16_t* a;
   const int32_t* gather;
   const int32_t* offsets;
-  const uint8_t* wc;
+  const uint8_t* wc;  // row-major codes [E][N][K/2], or the tiled experts (tiled)
   const uint8_t* ws;
+  int tiled;
   const float* wg;  // per-expert global scales [E] of two-level weights, or NULL
   const float* row_scale;
   uint16_t* out;
@@ -368,8 +381,10 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   const float ge = g.wg ? g.wg[e] : 1.0f;  // the sums are h / g_e
 
   GemmSrc src;
-  const uint8_t* we_c = g.wc + (int64_t)e * N * (K / 2);
-  const uint8_t* we_s = g.ws + (int64_t)e * N * (K / 16);
+  // row-major: expert e's rows; tiled: its N / 16 tiles of ceil(K / 256) blocks
+  const uint8_t* we_c = g.tiled ? g.wc + (int64_t)e * (N / 16) * ((K + 255) / 256) * 2304
+                                : g.wc + (int64_t)e * N * (K / 2);
+  const uint8_t* we_s = g.tiled ? nullptr : g.ws + (int64_t)e * N * (K / 16);
   {
     const int row = t >> 1;  // tile row u + 128 q
     const int q = row >> 7, u = row & 127;
@@ -380,7 +395,10 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
     } else {
       n = min((int64_t)tn * BN + row, N - 1);
     }
-    gemm_src_nvfp4_row(src.wc, src.ws, we_c, we_s, n, K);
+    if (g.tiled)
+      gemm_src_tiled_row(src, we_c, n, K, 0);
+    else
+      gemm_src_nvfp4_row(src, we_c, we_s, n, K, 0);
   }
 
   f32x16 acc[kXBlocks][kWBlocks];
@@ -626,7 +644,7 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
                         const int32_t* offsets, int64_t E, int64_t R, int64_t N,
                         const uint8_t* wc, const uint8_t* ws, const float* wg,
                         const float* row_scale, bool swiglu, uint16_t* out, void* workspace,
-                        hipStream_t stream, const PlanOverride& ov) {
+                        hipStream_t stream, const PlanOverride& ov, bool tiled) {
   (void)workspace;
   const GroupedPath path = grouped_path(a_rows, K, E, R, ov);
   if (path == GroupedPath::kNone) return -2;
@@ -637,6 +655,7 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
     m.offsets = offsets;
     m.wc = wc;
     m.ws = ws;
+    m.tiled = tiled ? 1 : 0;
     m.wg = wg;
     m.row_scale = row_scale;
     m.out = out;
@@ -669,8 +688,12 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
   const int64_t tiles_y = swiglu ? (N / 2 + 15) / 16 : (N + 31) / 32;  // gate tiles or tile pairs
   const int64_t ytiles = (tiles_y + kGroupWaves - 1) / kGroupWaves;
   const size_t lds = grouped_gemv_lds_bytes(K);
-  hipLaunchKernelGGL(k_grouped_gemv<2>, dim3((unsigned)chunks, (unsigned)ytiles),
-                     dim3(64 * kGroupWaves), lds, stream, g);
+  if (tiled)
+    hipLaunchKernelGGL((k_grouped_gemv<2, true>), dim3((unsigned)chunks, (unsigned)ytiles),
+                       dim3(64 * kGroupWaves), lds, stream, g);
+  else
+    hipLaunchKernelGGL((k_grouped_gemv<2, false>), dim3((unsigned)chunks, (unsigned)ytiles),
+                       dim3(64 * kGroupWaves), lds, stream, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -186,8 +186,9 @@ int nvfp4_tile_weight(const uint8_t *codes, const uint8_t *scales, int64_t N, in
 /*
  * nvfp4_gemm on tiled weights of N rows (all rows of the tiled matrix; a row
  * subset is tiled as its own matrix): out[m][n] = sum_k a[m][k] * w[n][k],
- * out [M][N] in out_dtype, a_dtype / a / a_scales as in nvfp4_gemm.  The
- * weights are streamed by the split-K GEMV, 32 activation rows per launch.
+ * out [M][N] in out_dtype, a_dtype / a / a_scales as in nvfp4_gemm.  Decode
+ * shapes stream the weights with the split-K GEMV, 32 activation rows per
+ * launch; large M runs the MFMA GEMM, as nvfp4_gemm does.
  * Same products, fp32 accumulation, tolerance and run-to-run determinism as
  * nvfp4_gemm.  workspace: >= nvfp4_gemm_tiled_workspace_size(a_dtype, M, N,
  * K) bytes (may be NULL when that is 0).  K % 32 == 0.
@@ -395,6 +396,23 @@ int nvfp4_grouped_gemm_scaled(const uint16_t *a, int64_t a_rows, int64_t K,
                               const uint8_t *w_scales, const float *w_global_scales,
                               const float *row_scale, int epilogue, uint16_t *out,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * nvfp4_grouped_gemm_scaled on tiled expert weights: w_tiled is
+ * nvfp4_tile_weight of the stacked E*N-row matrix (codes [E*N][K/2], scales
+ * [E*N][K/16]; N % 16 == 0, so expert e's N/16 tiles follow expert e-1's),
+ * nvfp4_tiled_weight_bytes(E*N, K) bytes ("What 350+ Experiments ...",
+ * section 7: NVFP4 expert weights served by a grouped kernel).
+ * w_global_scales may be NULL (single-level experts).  Same operation,
+ * arguments, results (bit-identical to the row-major call of the same kernel
+ * choice), errors and workspace as nvfp4_grouped_gemm_scaled.
+ */
+int nvfp4_grouped_gemm_tiled(const uint16_t *a, int64_t a_rows, int64_t K,
+                             const int32_t *gather_idx, const int32_t *expert_offsets, int64_t E,
+                             int64_t R, int64_t N, const uint8_t *w_tiled,
+                             const float *w_global_scales, const float *row_scale, int epilogue,
+                             uint16_t *out, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Combine the per-slot expert outputs of a routed layer ("What 350+

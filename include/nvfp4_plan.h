@@ -103,6 +103,14 @@ int nvfp4_gemm_tiled_planned(const nvfp4_plan_t *plan, int a_dtype, const void *
                              const uint8_t *w_tiled, int out_dtype, void *out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+int nvfp4_grouped_gemm_tiled_planned(const nvfp4_plan_t *plan, const uint16_t *a,
+                                     int64_t a_rows, int64_t K, const int32_t *gather_idx,
+                                     const int32_t *expert_offsets, int64_t E, int64_t R,
+                                     int64_t N, const uint8_t *w_tiled,
+                                     const float *w_global_scales, const float *row_scale,
+                                     int epilogue, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@ sampled decode shapes, and bit-identity with the row-major kernel of the same
 launch layout."""
 import numpy as np
 import pytest
+import torch
 
 import helpers
 import workloads
@@ -237,3 +238,100 @@ def test_masked_head_rows_tiled_full_size_sampled(nv, orc):
         ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales, row_idx=idx[sel])
         _assert_close(y[:, sel], ref, what=f"masked M={M}")
         torch.cuda.synchronize()
+
+
+# ---- the MFMA GEMM on tiled weights (M >= 65) ------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(65, 256, 40), (300, 1312, 700), (512, 2080, 272),
+                                   (1000, 4096, 1000), (2048, 544, 5000)])
+def test_mfma_tiled_matches_oracle(nv, orc, M, K, N):
+    """Ragged M, N (partial 256 x 256 tiles and 16-row weight tiles), K % 64 == 32
+    and K % 256 != 0, whole and shared rounds; every output against the oracle,
+    guarded; fp32 outputs identical to the row-major MFMA GEMM (same partition,
+    same products in the same order)."""
+    import torch
+    helpers.announce(f"gemm_tiled mfma M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + N)
+    x = workloads.normal_bf16(rng, M, K)
+    w = workloads.nvfp4_weight(rng, N, K)
+    ref = orc.gemm_w4a16(x, M, K, w.codes, w.scales)
+    wt = _tiled(nv, w)
+    _assert_close(_run(nv, x, wt, N), ref, what=f"{M}x{K}x{N}")
+    got = _run(nv, x, wt, N, out_f32=True)
+    _assert_close(got, ref, out_f32=True, what=f"{M}x{K}x{N} fp32")
+    row = nv.gemm(helpers.dev_bf16(x), helpers.dev_u8(w.codes), helpers.dev_u8(w.scales),
+                  out_dtype=torch.float32)
+    assert np.array_equal(row.cpu().numpy(), got)
+
+
+def test_mfma_tiled_prefill_full_size_sampled(nv, orc):
+    """Prefill M = 8192, K = 5120, N = 17408 on tiled weights: 256 sampled rows x
+    all columns against the oracle."""
+    helpers.announce("gemm_tiled prefill 8192x5120x17408")
+    M, K, N = 8192, workloads.HIDDEN, workloads.MLP
+    x, w = workloads.prefill(K, N)
+    wt = _tiled(nv, w)
+    y = helpers.host_bits(nv.gemm_tiled(helpers.dev_bf16(x), wt, N))
+    rows = np.sort(np.random.default_rng(9).choice(M, 64, replace=False))
+    ref = orc.gemm_w4a16(x[rows], len(rows), K, w.codes, w.scales)
+    _assert_close(y[rows], ref, what="prefill tiled")
+
+
+# ---- grouped GEMMs on tiled expert weights -----------------------------------------------
+
+def _grouped_case(rng, E, K, N, counts, rows):
+    counts = np.array(counts)
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = workloads.normal_bf16(rng, rows, K)
+    w = workloads.nvfp4_weight(rng, E, N, K)
+    gather = rng.integers(0, rows, R).astype(np.int32)
+    rs = (rng.random(R) + 0.5).astype(np.float32)
+    return R, off, a, w, gather, rs
+
+
+@pytest.mark.parametrize("mfma", [False, True])
+@pytest.mark.parametrize("epi,scaled", [(0, False), (1, False), (0, True), (1, True)])
+def test_grouped_tiled(nv, orc, mfma, epi, scaled):
+    """Both grouped kernels on tiled experts (the MFMA one forced through the
+    plan), both epilogues, single- and two-level experts, uneven groups (empty,
+    one row, several chunks), K % 256 != 0: against the oracle, guarded, and
+    bit-identical to the row-major call of the same kernel."""
+    helpers.announce(f"grouped tiled mfma={mfma} epi={epi} scaled={scaled}")
+    rng = np.random.default_rng(7 + 2 * epi + scaled + 4 * mfma)
+    E, K, N = 6, 544 if not mfma else 416, 96 if not mfma else 352
+    counts = [0, 1, 40, 0, 70, 9] if not mfma else [0, 1, 300, 256, 600, 37]
+    R, off, a, w, gather, rs = _grouped_case(rng, E, K, N, counts, 120)
+    gs = (2.0 ** rng.integers(-3, 4, E) * (1 + rng.random(E))).astype(np.float32) if scaled else None
+    plan = {"grouped_mfma_min_rows": 1} if mfma else {"grouped_mfma_min_rows": 1 << 20}
+    wc, wsc = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
+    wt = nv.tile_experts(wc, wsc)
+    kw = dict(row_scale=helpers.dev_f32(rs), epilogue=epi, plan=plan,
+              w_global=None if gs is None else helpers.dev_f32(gs))
+    g = helpers.Guarded((R, N // 2 if epi else N), torch.bfloat16)
+    y = nv.grouped_gemm_tiled(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+                              wt, E, N, R, out=g.t, **kw)
+    g.check()
+    ref = orc.grouped_gemm(a, K, gather, off, E, R, N, w.codes, w.scales, row_scale=rs,
+                           epilogue=epi, w_global=gs)
+    ok, rf, worst = helpers.gemm_close(helpers.host_bits(y), ref)
+    assert ok, (rf, worst)
+    yr = nv.grouped_gemm(helpers.dev_bf16(a), helpers.dev_i32(gather), helpers.dev_i32(off),
+                         wc, wsc, R, **kw)
+    assert torch.equal(y, yr)
+
+
+@pytest.mark.parametrize("T", [32, 4096])
+def test_moe_layer_tiled_equals_row_major(nv, T):
+    """The routed layer (hidden 2048, 128 experts, top-8, expert intermediate
+    768) on tiled experts gives the row-major layer's output bit for bit (the
+    row-major layer is checked against the oracle in test_gpu_moe.py)."""
+    helpers.announce(f"moe layer tiled T={T}")
+    m = workloads.moe(T)
+    E, I = 128, m.w2.codes.shape[2] * 2
+    args = (helpers.dev_bf16(m.x), helpers.dev_i32(m.ids), helpers.dev_f32(m.gates))
+    w1c, w1s = helpers.dev_u8(m.w1.codes), helpers.dev_u8(m.w1.scales)
+    w2c, w2s = helpers.dev_u8(m.w2.codes), helpers.dev_u8(m.w2.scales)
+    row = nv.moe_layer(*args, w1c, w1s, w2c, w2s)
+    til = nv.moe_layer_tiled(*args, nv.tile_experts(w1c, w1s), nv.tile_experts(w2c, w2s), E, I)
+    assert torch.equal(row, til)
