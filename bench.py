@@ -33,7 +33,8 @@ Also reported on the same JSON line:
                    same workload (a subset of output rows), scaled to GB/s;
   secondary     -- the other rows of the layer, each graph-replayed (prefill GEMM TFLOP/s,
                    quantizer GB/s, W4A4 GEMM TFLOP/s, FP8 KV-cache store/load
-                   GB/s, MoE layer T=32 / T=4096);
+                   GB/s, MoE layer T=32 / T=4096); prefill and MoE also on tiled
+                   weights (*_tiled_* rows);
   draft_proposal -- the masked head with its top-8 proposal (nvfp4_head_topk)
                    against the head GEMV alone, graph-replayed, M in {1, 8, 32}.
 
@@ -436,6 +437,12 @@ def secondary(nv, torch, helpers_dev, cases=None):
         wsb = torch.empty(max(wsz, 1), dtype=torch.uint8, device="cuda")
         t = timeit(lambda: nv.gemm(xd, wc, ws, out=out, workspace=wsb), n=1)
         res[f"prefill_M8192_K{K}_N{N}"] = _tf(2 * 8192 * N * K, t)
+        # the same product on weights tiled once (nvfp4_gemm_tiled: MFMA GEMM)
+        wt = nv.tile_weight(wc, ws)
+        wszt = nv.gemm_tiled_workspace_size(8192, N, K)
+        wsbt = torch.empty(max(wszt, 1), dtype=torch.uint8, device="cuda")
+        t = timeit(lambda: nv.gemm_tiled(xd, wt, N, out=out, workspace=wsbt), n=1)
+        res[f"prefill_tiled_M8192_K{K}_N{N}"] = _tf(2 * 8192 * N * K, t)
 
     if "prefill_K5120" in cases:
         prefill(wl.HIDDEN, wl.MLP)
@@ -546,6 +553,23 @@ def secondary(nv, torch, helpers_dev, cases=None):
             res[f"moe_T{T}_{name}_us"] = round(ts * 1e6, 2)
             if fl and T > 32:
                 res[f"moe_T{T}_{name}"] = _tf(fl, ts)
+        # the layer on expert weights tiled once (nvfp4_grouped_gemm_tiled)
+        w1t, w2t = nv.tile_experts(w1c, w1s), nv.tile_experts(w2c, w2s)
+        t = timeit(lambda: nv.moe_layer_tiled(x, ids, gates, w1t, w2t, E, 768))
+        res[f"moe_tiled_T{T}_layer"] = dict(_tf(flop, t) if T > 32 else _gb(wbytes, t),
+                                            ms=round(t * 1e3, 4))
+        steps_t = {
+            "gate_up": (lambda: nv.grouped_gemm_tiled(x, gat, off, w1t, E, 1536, R,
+                                                      epilogue=nv.EPI_SWIGLU, out=act),
+                        2 * R * 1536 * 2048),
+            "down": (lambda: nv.grouped_gemm_tiled(act, None, off, w2t, E, 2048, R, row_scale=rg,
+                                                   out=y), 2 * R * 2048 * 768),
+        }
+        for name, (fn, fl) in steps_t.items():
+            ts = timeit(fn)
+            res[f"moe_tiled_T{T}_{name}_us"] = round(ts * 1e6, 2)
+            if T > 32:
+                res[f"moe_tiled_T{T}_{name}"] = _tf(fl, ts)
     return res
 
 
