@@ -87,7 +87,8 @@ class Plan(ctypes.Structure):
     a field < 0 keeps the library's own choice."""
     _fields_ = [(n, ctypes.c_int) for n in (
         "gemm_min_m", "gemv_small_max", "gemv_tiles", "gemv_waves", "gemv_lds_kib",
-        "gemv_splits", "w4a4_fuse", "grouped_mfma_min_rows", "gemv_kparts")]
+        "gemv_splits", "w4a4_fuse", "grouped_mfma_min_rows", "gemv_kparts",
+        "grouped_gemv_waves")]
 
 
 _pp = ctypes.POINTER(Plan)

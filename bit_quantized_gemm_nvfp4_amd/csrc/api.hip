@@ -83,7 +83,11 @@ bool to_override(const nvfp4_plan_t* plan, PlanOverride& ov) {
   ov.w4a4_fuse = plan->w4a4_fuse;
   ov.grouped_mfma_min_rows = plan->grouped_mfma_min_rows;
   ov.gemv_kparts = plan->gemv_kparts;
+  ov.grouped_gemv_waves = plan->grouped_gemv_waves;
   if (ov.gemm_min_m == 0 || ov.w4a4_fuse > 1) return false;
+  if (ov.grouped_gemv_waves >= 0 && ov.grouped_gemv_waves != 4 && ov.grouped_gemv_waves != 8 &&
+      ov.grouped_gemv_waves != 16)
+    return false;
   return true;
 }
 
@@ -172,7 +176,7 @@ void nvfp4_plan_default(nvfp4_plan_t* plan) {
   if (!plan) return;
   plan->gemm_min_m = plan->gemv_small_max = plan->gemv_tiles = plan->gemv_waves = -1;
   plan->gemv_lds_kib = plan->gemv_splits = plan->w4a4_fuse = plan->grouped_mfma_min_rows = -1;
-  plan->gemv_kparts = -1;
+  plan->gemv_kparts = plan->grouped_gemv_waves = -1;
 }
 
 size_t nvfp4_gemm_workspace_size_planned(const nvfp4_plan_t* plan, int a_dtype, int64_t M,

@@ -61,6 +61,7 @@ struct PlanOverride {
   int gemv_kparts = -1;            // K parts inside a workgroup (16x16 GEMV, K % 256 == 0)
   int w4a4_fuse = -1;              // W4A4 from bf16: quantize inside the kernel (1) or in a pass (0)
   int grouped_mfma_min_rows = -1;  // average rows per expert from which the grouped MFMA runs
+  int grouped_gemv_waves = -1;     // waves per workgroup of the grouped GEMV (4, 8, 16)
 };
 
 struct GemvPlan {

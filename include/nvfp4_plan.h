@@ -53,6 +53,9 @@ typedef struct {
      * and for M <= 8 also (2,16,8) (1,16,8) (2,8,8); two activation tiles
      * (16 < M <= 32) (1,16,2). */
     int gemv_kparts;
+    /* Waves per workgroup of the grouped GEMV, which share one staged copy of
+     * the chunk's activation rows: 4, 8 or 16. */
+    int grouped_gemv_waves;
 } nvfp4_plan_t;
 
 /* Every field set to -1 (the library's own choice). */

@@ -303,7 +303,8 @@ def test_grouped_tiled(nv, orc, mfma, epi, scaled):
     counts = [0, 1, 40, 0, 70, 9] if not mfma else [0, 1, 300, 256, 600, 37]
     R, off, a, w, gather, rs = _grouped_case(rng, E, K, N, counts, 120)
     gs = (2.0 ** rng.integers(-3, 4, E) * (1 + rng.random(E))).astype(np.float32) if scaled else None
-    plan = {"grouped_mfma_min_rows": 1} if mfma else {"grouped_mfma_min_rows": 1 << 20}
+    plan = {"grouped_mfma_min_rows": 1} if mfma else {"grouped_mfma_min_rows": 1 << 20,
+                                                       "grouped_gemv_waves": 4 << (epi + scaled)}
     wc, wsc = helpers.dev_u8(w.codes), helpers.dev_u8(w.scales)
     wt = nv.tile_experts(wc, wsc)
     kw = dict(row_scale=helpers.dev_f32(rs), epilogue=epi, plan=plan,
