@@ -182,12 +182,15 @@ def test_activations_outside_fp16(nv, orc):
         _assert_close(_run(nv, xx, wt, N, out_f32=True), rr, out_f32=True, what=f"M={M2}")
 
 
-def test_w4a4_codes(nv, orc):
-    """NVFP4 activations (a_dtype NVFP4) on tiled weights."""
+@pytest.mark.parametrize("M", [5, 300])
+def test_w4a4_codes(nv, orc, M):
+    """NVFP4 activations (a_dtype NVFP4) on tiled weights: the GEMV (M = 5) and
+    the MFMA GEMM (M = 300, a shared round) after the activations' dequantize
+    pass."""
     import torch
-    helpers.announce("gemm_tiled W4A4 codes")
-    M, K, N = 5, 1024, 300
-    rng = np.random.default_rng(5)
+    helpers.announce(f"gemm_tiled W4A4 codes M={M}")
+    K, N = 1024, 300
+    rng = np.random.default_rng(5 + M)
     x = workloads.normal_bf16(rng, M, K)
     ac, asc = nv.quantize(helpers.dev_bf16(x))
     w = workloads.nvfp4_weight(rng, N, K)
