@@ -29,7 +29,6 @@ struct GemmArgs {
   const uint16_t* a;        // bf16 [M][K]
   const uint8_t* wc;        // weight codes [rows][K/2], or the tiled weights (tiled)
   const uint8_t* ws;        // weight scales [rows][K/16] (row-major only)
-  int tiled;                // the weights are tiled (tile.hip)
   const int32_t* row_idx;   // output column n uses weight row row_idx[n]; null: row n
   void* out;                // [M][N] bf16 or fp32
   float* partial;           // shared tiles: fp32 [tail][max_seg][256 * 256], tile-local
@@ -67,7 +66,7 @@ __device__ __forceinline__ void gemm_tile_of(int lin, int tiles_m, int tiles_n, 
 
 // Tile `lin` over K steps [s0, s1): the output (dst null, whole K) or the
 // tile-local fp32 partial at dst (always, when PART_ONLY).
-template <bool A_FQ, bool PART_ONLY = false>
+template <bool A_FQ, bool PART_ONLY = false, bool TW = false>
 __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int lin, int s0,
                                               int s1, float* dst) {
   int tm, tn;
@@ -85,7 +84,7 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
   {
     const int64_t n = min(n0 + (t >> 1), g.N - 1);
     const int64_t wr = g.row_idx ? (int64_t)g.row_idx[n] : n;
-    if (g.tiled)
+    if constexpr (TW)
       gemm_src_tiled_row(src, g.wc, wr, K, k_lo);
     else
       gemm_src_nvfp4_row(src, g.wc, g.ws, wr, K, k_lo);
@@ -99,7 +98,7 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
 
   f32x16 acc[kXBlocks][kWBlocks];
   gemm_zero_acc(acc);
-  gemm_mainloop<A_FQ>(acc, lds, src, a_tile_base, k_len);
+  gemm_mainloop<A_FQ, false, TW>(acc, lds, src, a_tile_base, k_len);
 
   // acc[i][j] = y^T block (n-block j, m-block i): register e of lane l is output
   // row i*32 + l%32, column j*32 + 8*(e/4) + 4*(l/32) + e%4 of the wave's part.
@@ -192,7 +191,8 @@ __device__ __forceinline__ void gemm_tile_run(const GemmArgs& g, char* lds, int 
 // the end of one tile and the start of the next, run one after the other.
 // (The loop over segments would raise the registers of the whole-tile
 // kernel, hence two instantiations.)
-template <bool A_FQ, bool SEGS>
+// TW: tiled weights (tile.hip).
+template <bool A_FQ, bool SEGS, bool TW = false>
 __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
   extern __shared__ char lds[];
   const int b = blockIdx.x;
@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
       s1 = (seg + 1) * g.steps / z;
       dst = g.partial + ((int64_t)tt * z + seg) * (BM * BN);
     }
-    gemm_tile_run<A_FQ>(g, lds, lin, s0, s1, dst);
+    gemm_tile_run<A_FQ, false, TW>(g, lds, lin, s0, s1, dst);
     return;
   }
   const int per_xcd = (g.parts + 7) / 8;
@@ -236,8 +236,8 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs g) {
     const int seg = w - sk_owner((int64_t)tt * g.steps, F, g.parts);
     if (!first) __syncthreads();  // every wave is done with the last segment's LDS
     first = false;
-    gemm_tile_run<A_FQ, true>(g, lds, g.full + tt, s0, s1,
-                              g.partial + ((int64_t)tt * g.max_seg + seg) * (BM * BN));
+    gemm_tile_run<A_FQ, true, TW>(g, lds, g.full + tt, s0, s1,
+                                  g.partial + ((int64_t)tt * g.max_seg + seg) * (BM * BN));
     f += s1 - s0;
   }
 }
@@ -405,7 +405,6 @@ int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* 
   g.a = static_cast<const uint16_t*>(a);
   g.wc = wc;
   g.ws = ws;
-  g.tiled = tiled ? 1 : 0;
   g.row_idx = row_idx;
   g.out = out;
   g.M = M;
@@ -437,7 +436,15 @@ int launch_gemm(GemmA mode, const void* a, int64_t M, int64_t K, const uint8_t* 
   if (grid > INT32_MAX) return -1;
   // (Both activation modes take the same partition, so the fused-quantizer
   // product stays bit-identical to quantize + the W4A4 GEMM.)
-  if (p.own_launch) {
+  if (tiled) {  // (bf16 activations only)
+    if (fq) return -1;
+    if (p.own_launch)
+      hipLaunchKernelGGL((k_gemm<false, true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                         kLdsBytes, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm<false, false, true>), dim3((unsigned)grid),
+                         dim3(kGemmThreads), kLdsBytes, stream, g);
+  } else if (p.own_launch) {
     if (fq)
       hipLaunchKernelGGL((k_gemm<true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
                          kLdsBytes, stream, g);

@@ -122,49 +122,37 @@ struct GemmLoad<true> {
 // this lane's half of row t/2 at k = 0 (gemm_src_nvfp4_row); an A_FQ
 // activation row as a pointer to this lane's half of row t/2.
 //
-// Weight addresses: the element k of the weight row sits at byte offset
-// (k / 256) * step + ((k / 64) % 4) * quarter from the lane's pointer (codes;
-// scales with their own two constants), k a multiple of 64.  Row-major
-// weights: step 128 / quarter 32 (codes), 16 / 4 (scales), i.e. k / 2 and
-// k / 16.  Tiled weights (tile.hip): 2304 / 256 and 2304 / 64 -- the 64
-// elements [k, k + 64) of a row are lane (row % 16, (k / 64) % 4) of block
-// k / 256.  The steps and quarters are workgroup-uniform, so the offsets stay
-// scalar arithmetic.
-struct WAddr {
-  int64_t k_lo;           // first element of the workgroup's K range
-  int c_step, c_quarter;  // codes
-  int s_step, s_quarter;  // scales
-  int pad;                // 1: row-major (a partial last step re-reads inside the row);
-                          // 0: tiled (the layout pads K with zeros)
-};
-
-__device__ __forceinline__ WAddr waddr_row_major(int64_t k_lo) {
-  return WAddr{k_lo, 128, 32, 16, 4, 1};
-}
-__device__ __forceinline__ WAddr waddr_tiled(int64_t k_lo) {
-  return WAddr{k_lo, 2304, 256, 2304, 64, 0};
-}
-
+// Weight addresses (TW: tiled weights).  Row-major: element k of the lane's
+// row is at byte k / 2 of its codes and k / 16 of its scales.  Tiled
+// (tile.hip): the 64 elements [k, k + 64) of a row (k a multiple of 64) are
+// lane (row % 16, (k / 64) % 4) of block k / 256, so the codes of the lane's
+// half sit at (k / 256) * 2304 + ((k / 64) % 4) * 256 from its pointer and
+// the scales at (k / 256) * 2304 + ((k / 64) % 4) * 64.  k is
+// workgroup-uniform, so on tiled weights the whole offset is scalar.
 struct GemmSrc {
   uint32_t a_off[4];
   uint32_t a_back[4];
   const uint16_t* ar;
   const uint8_t* wc;  // this lane's codes and scales at k = 0 of its row
   const uint8_t* ws;
-  WAddr wa;
+  int64_t k_lo;       // first element of the workgroup's K range
 };
 
+template <bool TW>
 __device__ __forceinline__ void load_nvfp4_rows(Nvfp4Rows& R, const GemmSrc& src, int64_t k0,
                                                 bool kfull) {
-  const int hh = threadIdx.x & 1;
-  const WAddr& w = src.wa;
-  const int64_t k = w.k_lo + k0;
-  const int64_t blk = k >> 8, q = (k >> 6) & 3;
-  const int back = (kfull || !w.pad) ? 0 : hh;
-  const int64_t coff = blk * w.c_step + q * w.c_quarter - 16 * back;
-  const int64_t soff = blk * w.s_step + q * w.s_quarter - 2 * back;
-  R.c = *reinterpret_cast<const u32x4*>(src.wc + coff);
-  R.s = *reinterpret_cast<const uint16_t*>(src.ws + soff);
+  const int64_t k = src.k_lo + k0;
+  if constexpr (TW) {  // the layout pads K with zeros: no re-read on a partial step
+    const int64_t blk = (k >> 8) * 2304, q = (k >> 6) & 3;
+    R.c = *reinterpret_cast<const u32x4*>(src.wc + blk + 256 * q);
+    R.s = *reinterpret_cast<const uint16_t*>(src.ws + blk + 64 * q);
+  } else {
+    const int hh = threadIdx.x & 1;
+    const int64_t coff = k / 2 - (kfull ? 0 : 16 * hh);
+    const int64_t soff = k / 16 - (kfull ? 0 : 2 * hh);
+    R.c = *reinterpret_cast<const u32x4*>(src.wc + coff);
+    R.s = *reinterpret_cast<const uint16_t*>(src.ws + soff);
+  }
 }
 
 // A_FQ: 32 bf16 activations of this lane's half of its row (a partial last
@@ -177,12 +165,12 @@ __device__ __forceinline__ void load_bf16_rows(Bf16Rows& R, const uint16_t* a, i
   for (int j = 0; j < 4; ++j) R.v[j] = *reinterpret_cast<const u32x4*>(a + off + 8 * j);
 }
 
-template <bool A_FQ>
+template <bool A_FQ, bool TW>
 __device__ __forceinline__ void gemm_load(GemmLoad<A_FQ>& L, const GemmSrc& src,
                                           const uint8_t* a_tile_base, int64_t K, int64_t k0) {
   const bool kfull = k0 + BK <= K;
   if constexpr (A_FQ) load_bf16_rows(L.a, src.ar, k0, kfull);
-  load_nvfp4_rows(L.w, src, k0, kfull);
+  load_nvfp4_rows<TW>(L.w, src, k0, kfull);
 }
 
 // bf16 activation tile of the step at k0 -> LDS A buffer at `dst`, straight
@@ -346,15 +334,15 @@ __device__ __forceinline__ void gemm_src_bf16(GemmSrc& src, ARow abs_row, int64_
   gemm_src_bf16_rows(src, r, K);
 }
 
-// This lane's pointers (its half of weight row `row`, k = 0) and the address
-// constants, for a workgroup whose K range starts at k_lo.
+// This lane's pointers (its half of weight row `row`, k = 0), for a workgroup
+// whose K range starts at k_lo.
 __device__ __forceinline__ void gemm_src_nvfp4_row(GemmSrc& src, const uint8_t* codes,
                                                    const uint8_t* scales, int64_t row, int64_t K,
                                                    int64_t k_lo) {
   const int hh = threadIdx.x & 1;
   src.wc = codes + row * (K / 2) + 16 * hh;
   src.ws = scales + row * (K / 16) + 2 * hh;
-  src.wa = waddr_row_major(k_lo);
+  src.k_lo = k_lo;
 }
 
 // The same on tiled weights `wt` (ceil(K / 256) blocks per 16-row tile).
@@ -366,7 +354,7 @@ __device__ __forceinline__ void gemm_src_tiled_row(GemmSrc& src, const uint8_t* 
   const int n = (int)(row & 15);
   src.wc = tb + 1024 * hh + 16 * n;
   src.ws = tb + 2048 + 4 * n + 2 * hh;
-  src.wa = waddr_tiled(k_lo);
+  src.k_lo = k_lo;
 }
 
 __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[kXBlocks][kWBlocks]) {
@@ -383,7 +371,7 @@ __device__ __forceinline__ void gemm_zero_acc(f32x16 (&acc)[kXBlocks][kWBlocks])
 // late(src) completes the sources after the first weight loads are issued and
 // before the first activation copy (gathered rows: the weight loads then
 // overlap the wait for the row indices).
-template <bool A_FQ, int XL, typename Late>
+template <bool A_FQ, int XL, bool TW, typename Late>
 __device__ __forceinline__ void gemm_mainloop_xl(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
                                                  GemmSrc& src, const uint8_t* a_tile_base,
                                                  int64_t K, bool dma_live, Late late) {
@@ -412,8 +400,8 @@ __device__ __forceinline__ void gemm_mainloop_xl(f32x16 (&acc)[kXBlocks][kWBlock
 
   GemmLoad<A_FQ> L0, L1;
   Frags f[2];
-  gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(0));
-  gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(1));
+  gemm_load<A_FQ, TW>(L0, src, a_tile_base, K, kstep(0));
+  gemm_load<A_FQ, TW>(L1, src, a_tile_base, K, kstep(1));
   late(src);
   dma(0, 0);
 #pragma unroll
@@ -428,12 +416,12 @@ __device__ __forceinline__ void gemm_mainloop_xl(f32x16 (&acc)[kXBlocks][kWBlock
   for (int s = 0; s < steps2; s += 2) {
     dma(s + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load<A_FQ>(L0, src, a_tile_base, K, kstep(s + 2));
+    gemm_load<A_FQ, TW>(L0, src, a_tile_base, K, kstep(s + 2));
     __builtin_amdgcn_sched_barrier(0);
     gemm_step<A_FQ, XL>(acc, f, lds, o, 0, 1, L1, kval(s + 1));
     dma(s + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load<A_FQ>(L1, src, a_tile_base, K, kstep(s + 3));
+    gemm_load<A_FQ, TW>(L1, src, a_tile_base, K, kstep(s + 3));
     __builtin_amdgcn_sched_barrier(0);
     gemm_step<A_FQ, XL>(acc, f, lds, o, 1, 0, L0, kval(s + 2));
   }
@@ -450,7 +438,7 @@ struct NoLateSrc {
   __device__ void operator()(GemmSrc&) const {}
 };
 
-template <bool A_FQ, bool PARTIAL = false, typename Late = NoLateSrc>
+template <bool A_FQ, bool PARTIAL = false, bool TW = false, typename Late = NoLateSrc>
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks], char* lds,
                                               GemmSrc& src, const uint8_t* a_tile_base, int64_t K,
                                               int live_rows = BM, Late late = Late()) {
@@ -459,13 +447,13 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[kXBlocks][kWBlocks],
     const int first = (wave >> 1) * 64;  // the wave's first activation row
     const bool dma_live = 32 * wave < live_rows;
     if (live_rows > first + 32)
-      gemm_mainloop_xl<A_FQ, 2>(acc, lds, src, a_tile_base, K, dma_live, late);
+      gemm_mainloop_xl<A_FQ, 2, TW>(acc, lds, src, a_tile_base, K, dma_live, late);
     else if (live_rows > first)
-      gemm_mainloop_xl<A_FQ, 1>(acc, lds, src, a_tile_base, K, dma_live, late);
+      gemm_mainloop_xl<A_FQ, 1, TW>(acc, lds, src, a_tile_base, K, dma_live, late);
     else
-      gemm_mainloop_xl<A_FQ, 0>(acc, lds, src, a_tile_base, K, dma_live, late);
+      gemm_mainloop_xl<A_FQ, 0, TW>(acc, lds, src, a_tile_base, K, dma_live, late);
   } else {
-    gemm_mainloop_xl<A_FQ, 2>(acc, lds, src, a_tile_base, K, true, late);
+    gemm_mainloop_xl<A_FQ, 2, TW>(acc, lds, src, a_tile_base, K, true, late);
   }
 }
 

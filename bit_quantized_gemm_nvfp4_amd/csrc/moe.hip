@@ -324,9 +324,8 @@ struct GroupedMfmaArgs {
   const uint16_t* a;
   const int32_t* gather;
   const int32_t* offsets;
-  const uint8_t* wc;  // row-major codes [E][N][K/2], or the tiled experts (tiled)
+  const uint8_t* wc;  // row-major codes [E][N][K/2], or the tiled experts (k_grouped_mfma<true>)
   const uint8_t* ws;
-  int tiled;
   const float* wg;  // per-expert global scales [E] of two-level weights, or NULL
   const float* row_scale;
   uint16_t* out;
@@ -345,6 +344,7 @@ struct GroupedMfmaArgs {
 // (h = 0, 1; u < 64) at tile columns 128 h + u and 128 h + 64 + u: each gate
 // accumulator and its up partner sit in the same lane and register (blocks j
 // and j + 2 of the wave), so the epilogue needs no exchange.
+template <bool TW>
 __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g) {
   extern __shared__ char lds[];
   // Consecutive workgroups go to consecutive XCDs.  Chunk c runs on XCD c % 8,
@@ -382,9 +382,9 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
 
   GemmSrc src;
   // row-major: expert e's rows; tiled: its N / 16 tiles of ceil(K / 256) blocks
-  const uint8_t* we_c = g.tiled ? g.wc + (int64_t)e * (N / 16) * ((K + 255) / 256) * 2304
-                                : g.wc + (int64_t)e * N * (K / 2);
-  const uint8_t* we_s = g.tiled ? nullptr : g.ws + (int64_t)e * N * (K / 16);
+  const uint8_t* we_c = TW ? g.wc + (int64_t)e * (N / 16) * ((K + 255) / 256) * 2304
+                           : g.wc + (int64_t)e * N * (K / 2);
+  const uint8_t* we_s = TW ? nullptr : g.ws + (int64_t)e * N * (K / 16);
   {
     const int row = t >> 1;  // tile row u + 128 q
     const int q = row >> 7, u = row & 127;
@@ -395,7 +395,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
     } else {
       n = min((int64_t)tn * BN + row, N - 1);
     }
-    if (g.tiled)
+    if constexpr (TW)
       gemm_src_tiled_row(src, we_c, n, K, 0);
     else
       gemm_src_nvfp4_row(src, we_c, we_s, n, K, 0);
@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_grouped_mfma(GroupedMfmaArgs g
   f32x16 acc[kXBlocks][kWBlocks];
   gemm_zero_acc(acc);
   // (an expert's last chunk is partly filled: waves skip the 32-row blocks past it)
-  gemm_mainloop<false, true>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K, rows,
+  gemm_mainloop<false, true, TW>(acc, lds, src, reinterpret_cast<const uint8_t*>(g.a), K, rows,
                              [&](GemmSrc& s) { gemm_src_bf16_rows(s, arow, K); });
 
   // Staged output (N % 16 == 0 and a 16-byte aligned output: every row run is
@@ -655,7 +655,6 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
     m.offsets = offsets;
     m.wc = wc;
     m.ws = ws;
-    m.tiled = tiled ? 1 : 0;
     m.wg = wg;
     m.row_scale = row_scale;
     m.out = out;
@@ -667,7 +666,12 @@ int launch_grouped_gemm(const uint16_t* a, int64_t a_rows, int64_t K, const int3
     const int64_t chunks = (R + BM - 1) / BM + E;  // upper bound
     m.chunks = (int)chunks;
     const int grid = (int)(((chunks + 7) / 8) * 8 * m.n_tiles);
-    hipLaunchKernelGGL(k_grouped_mfma, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream, m);
+    if (tiled)
+      hipLaunchKernelGGL(k_grouped_mfma<true>, dim3(grid), dim3(kGemmThreads), kLdsBytes, stream,
+                         m);
+    else
+      hipLaunchKernelGGL(k_grouped_mfma<false>, dim3(grid), dim3(kGemmThreads), kLdsBytes,
+                         stream, m);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   GroupedArgs g;
