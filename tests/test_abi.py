@@ -443,3 +443,52 @@ def test_tiled_plan_validation(L):
     assert planned(gemv_waves=16) == INVALID  # 16 waves need two activation tiles
     assert planned(gemv_small_max=8, gemv_tiles=4) == INVALID
     assert planned(gemv_lds_kib=4) == INVALID
+
+
+def test_grouped_tiled_validation(L):
+    """nvfp4_grouped_gemm_tiled: the grouped checks with the tiled weights in
+    place of the codes/scales pair (no scales pointer); the planned variant
+    refuses a grouped GEMV wave count that is not built."""
+    g = L.nvfp4_grouped_gemm_tiled
+    # (a, a_rows, K, gather, offsets, E, R, N, w_tiled, w_global, row_scale, epi, out, ws, wsb, st)
+    assert g(NULL, 32, 256, P, P2, 4, 32, 64, P3, NULL, NULL, 0, P, NULL, 0, NULL) == INVALID
+    assert g(P, 32, 256, P, P2, 4, 32, 64, NULL, NULL, NULL, 0, P, NULL, 0, NULL) == INVALID
+    assert g(P, 32, 240, P, P2, 4, 32, 64, P3, NULL, NULL, 0, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 32, 256, P, P2, 4, 32, 48, P3, NULL, NULL, 1, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 32, 256, P, P2, 4, 32, 56, P3, NULL, NULL, 0, P, NULL, 0, NULL) == NOT_SUPPORTED
+    assert g(P, 32, 256, P, P2, 4, 32, 64, MIS, NULL, NULL, 0, P, NULL, 0, NULL) == INVALID
+    assert g(P, 32, 256, P, P2, 4, 32, 64, P3, ctypes.c_void_p(0x10002), NULL, 0, P, NULL, 0,
+             NULL) == INVALID
+    gp = L.nvfp4_grouped_gemm_tiled_planned
+    for waves in (3, 12, 32):
+        p = nv.make_plan(grouped_gemv_waves=waves)
+        assert gp(ctypes.byref(p), P, 32, 256, P, P2, 4, 32, 64, P3, NULL, NULL, 0, P, NULL, 0,
+                  NULL) == INVALID
+
+
+def test_binding_checks_tiled_shapes(L):
+    """The tiled binding functions check sizes and dtypes before any GPU work."""
+    import torch
+    bf, u8 = torch.bfloat16, torch.uint8
+    x = torch.zeros(4, 256, dtype=bf)
+    wc = torch.zeros(64, 128, dtype=u8)
+    ws = torch.zeros(64, 16, dtype=u8)
+    nb = nv.tiled_weight_bytes(64, 256)
+    assert nb == 4 * 1 * 2304
+
+    def raises(match, fn, *a, **k):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **k)
+    raises("w_scales", nv.tile_weight, wc, torch.zeros(64, 15, dtype=u8))
+    raises("out", nv.tile_weight, wc, ws, out=torch.zeros(nb - 1, dtype=u8))
+    raises("row_idx", nv.tile_weight, wc, ws, row_idx=torch.zeros(65, dtype=torch.int32))
+    raises("w_tiled", nv.gemm_tiled, x, torch.zeros(nb + 16, dtype=u8), 64)
+    raises("w_tiled", nv.gemm_tiled, x, torch.zeros(nb, dtype=u8), 65)
+    raises("out", nv.gemm_tiled, x, torch.zeros(nb, dtype=u8), 64,
+           out=torch.zeros(4, 64, dtype=bf), out_dtype=torch.float32)
+    raises("multiple of 16", nv.tile_experts, torch.zeros(2, 24, 128, dtype=u8),
+           torch.zeros(2, 24, 16, dtype=u8))
+    off = torch.zeros(3, dtype=torch.int32)
+    raises("w_tiled", nv.grouped_gemm_tiled, x, None, off, torch.zeros(nb, dtype=u8), 2, 64, 4)
+    raises("expert_offsets", nv.grouped_gemm_tiled, x, None, torch.zeros(2, dtype=torch.int32),
+           torch.zeros(nv.tiled_weight_bytes(128, 256), dtype=u8), 2, 64, 4)
