@@ -405,6 +405,9 @@ int nvfp4_tile_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, in
   if (row_idx ? n_rows > N : n_rows != N) return NVFP4_ERROR_INVALID_VALUE;
   if (K % 32 != 0) return NVFP4_ERROR_NOT_SUPPORTED;
   if (N > INT32_MAX || N * (K / 32) > ((int64_t)1 << 40)) return NVFP4_ERROR_NOT_SUPPORTED;
+  // one thread per 16-byte piece, in workgroups of 256
+  if (tiled_weight_bytes(n_rows, K) / 16 / 256 >= (size_t)INT32_MAX)
+    return NVFP4_ERROR_NOT_SUPPORTED;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_tiled) ||
       (row_idx && !aligned16(row_idx)))
     return NVFP4_ERROR_INVALID_VALUE;

@@ -412,6 +412,8 @@ def test_tiled_validation(L):
     assert t(P, P2, 4, 64, P4, 5, P3, NULL) == INVALID    # a subset: n_rows <= N
     assert t(P, P2, 4, 64, P4, 0, P3, NULL) == INVALID
     assert t(P, P2, 4, 64, MIS, 2, P3, NULL) == INVALID
+    # more 16-byte pieces than one launch of 256-thread workgroups covers
+    assert t(P, P2, 1 << 30, 32768, NULL, 1 << 30, P3, NULL) == NOT_SUPPORTED
     g = L.nvfp4_gemm_tiled
     # (a_dtype, a, a_scales, M, N, K, w_tiled, out_dtype, out, ws, ws_bytes, stream)
     assert g(0, NULL, NULL, 1, 16, 64, P2, 0, P3, NULL, 0, NULL) == INVALID
