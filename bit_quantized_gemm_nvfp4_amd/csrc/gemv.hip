@@ -41,10 +41,15 @@ struct GemvArgs {
 };
 
 // TL: the weights are tiled (tile.hip; a.wc is the tiled array, a.ws unused)
-// and every step is whole.
-template <int MT, int TR, int NW, bool FQ, bool TL = false>
+// and every step is whole.  WR: rows of the activation window, 16, or 8 for
+// M <= 8 on tiled weights (half the window's loads, conversions and LDS
+// stores; lanes 8..15 read row 7, whose results are never stored).
+template <int MT, int TR, int NW, bool FQ, bool TL = false, int WR = 16>
 __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
-  constexpr int XP = 16 * MT * 32 / (64 * NW);  // activation pieces per thread and step
+  static_assert(WR == 16 || (WR == 8 && MT == 1 && TL), "8-row window: tiled, one tile");
+  // activation pieces per thread and step (with 8 rows and 8 waves, half the
+  // threads stage one piece each)
+  constexpr int XP = (WR * MT * 32 + 64 * NW - 1) / (64 * NW);
   // Scale blocks and the fp16 path fit the register budget of 4 waves per SIMD
   // with one activation tile, and with two tiles in 16-wave workgroups (one
   // window piece per thread); with two tiles in smaller workgroups they cost a
@@ -56,7 +61,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   // the fp16 MFMA on weights decoded with packed fp16 multiplies (half the
   // vector instructions).  The fused W4A4 staging keeps the bf16 path.
   constexpr bool H = !FQ && (MT == 1 || NW == 16);
-  __shared__ uint16_t win[2 * 16 * MT * kXWin];  // bf16, or fp16 (H)
+  __shared__ uint16_t win[2 * WR * MT * kXWin];  // bf16, or fp16 (H)
   __shared__ int hflag[2];
   __shared__ uint32_t scl[BLK ? NW * TR * 512 : 1];
   const int lane = threadIdx.x & 63;
@@ -91,7 +96,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
   }
   int xrow_off[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow_off[mt] = (16 * mt + ln) * kXWin + 64 * win_quarter(q);
+  for (int mt = 0; mt < MT; ++mt)
+    xrow_off[mt] = (WR == 8 ? min(ln, 7) : 16 * mt + ln) * kXWin + 64 * win_quarter(q);
 
   f32x4 acc[TR][MT];
 #pragma unroll
@@ -114,9 +120,9 @@ __global__ void __launch_bounds__(64 * NW) k_gemv(GemvArgs a) {
                                                  zs0, zs1, row_ptr);
   }
   if (!blocks)
-    gemv_accumulate_win<MT, TR, XP, FQ, H, TL>(acc, cptr, sptr, win, hflag, xrow_off, a.M, K,
-                                               zs0, zs1, TL ? a.steps : (int)(K / kGemvStep),
-                                               row_ptr);
+    gemv_accumulate_win<MT, TR, XP, FQ, H, TL, WR>(acc, cptr, sptr, win, hflag, xrow_off, a.M,
+                                                   K, zs0, zs1,
+                                                   TL ? a.steps : (int)(K / kGemvStep), row_ptr);
 
   // lane holds C[m = 16*mt + 4*q + r][column 16*tile + ln]
   const bool scaled = gridDim.y == 1 && (a.ga || a.gw);
@@ -503,7 +509,7 @@ int splitk_reduce(int z, int64_t M, int64_t n_out, bool out_f32, void* out, void
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int MT, int TR>
+template <int MT, int TR, int WR = 16>
 int launch_gemv_tiled_t(const GemvArgs& a, int nw, int zsplit, hipStream_t stream) {
   const int64_t tiles = (a.n_out + 15) / 16;
   const int64_t per_wg = (int64_t)nw * TR;
@@ -515,9 +521,9 @@ int launch_gemv_tiled_t(const GemvArgs& a, int nw, int zsplit, hipStream_t strea
     }
   }
   if (nw == 8)
-    hipLaunchKernelGGL((k_gemv<MT, TR, 8, false, true>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_gemv<MT, TR, 8, false, true, WR>), grid, dim3(512), 0, stream, a);
   else if (nw == 4)
-    hipLaunchKernelGGL((k_gemv<MT, TR, 4, false, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_gemv<MT, TR, 4, false, true, WR>), grid, dim3(256), 0, stream, a);
   else
     return -2;
   return 0;
@@ -840,6 +846,14 @@ int launch_gemv_tiled(const GemvPlan& p, const uint16_t* x, int64_t M, int64_t K
       rc = launch_gemv_kp_tl<1, 16>(a, p, stream);
     else if (p.mt == 2 && try_kp<2, 16, 1, 8, 2, true>(a, p, stream))
       rc = 0;
+  } else if (p.mt == 1 && M <= 8) {  // 8-row window (measured, graph-replayed at M = 8:
+    // 16.2 -> 15.7 us on the 17,408 x 5,120 layer, 115.4 -> 113.1 us on the 248,320-row head)
+    if (p.tr == 2)
+      rc = launch_gemv_tiled_t<1, 2, 8>(a, p.nw, p.z, stream);
+    else if (p.tr == 1)
+      rc = launch_gemv_tiled_t<1, 1, 8>(a, p.nw, p.z, stream);
+    else if (p.tr == 4)
+      rc = launch_gemv_tiled_t<1, 4, 8>(a, p.nw, p.z, stream);
   } else if (p.mt == 1 && p.tr == 2)
     rc = launch_gemv_tiled_t<1, 2>(a, p.nw, p.z, stream);
   else if (p.mt == 1 && p.tr == 1)

@@ -287,13 +287,16 @@ __device__ __forceinline__ int win_chunk(int cc) {
   return 64 * win_quarter(cc >> 3) + 8 * (cc & 7);
 }
 
-template <int XP, typename RowPtr>
+// WR: window rows (16, or 8 for M <= 8 with one activation tile: 256 pieces,
+// threads past them idle).
+template <int XP, int WR = 16, typename RowPtr>
 __device__ __forceinline__ void xwin_load(u32x4 (&v)[XP], int M, int64_t K, int s,
                                           RowPtr row_ptr) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
+    if (WR < 16 && c >= WR * 32) continue;
     const int m = min(c >> 5, M - 1), c8 = c & 31;
     const int64_t k = (int64_t)s * kGemvStep + c8 * 8;
     const u32x4 t = *reinterpret_cast<const u32x4*>(row_ptr(m) + min(k, K - 8));
@@ -313,11 +316,12 @@ __device__ __forceinline__ void xwin_fakequant(u32x4 (&v)[XP]) {
   }
 }
 
-template <int XP>
+template <int XP, int WR = 16>
 __device__ __forceinline__ void xwin_store(uint16_t* buf, const u32x4 (&v)[XP]) {
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
+    if (WR < 16 && c >= WR * 32) continue;
     *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + win_chunk(c & 31)) = v[i];
   }
 }
@@ -342,7 +346,7 @@ struct HWin {
   bool on;    // the window is being filled in fp16
 };
 
-template <bool H, int XP>
+template <bool H, int XP, int WR = 16>
 __device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int bufidx,
                                             const u32x4 (&v)[XP], int s) {
   if constexpr (H) {
@@ -351,6 +355,7 @@ __device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int b
 #pragma unroll
       for (int i = 0; i < XP; ++i) {
         const int c = threadIdx.x + i * blockDim.x;
+        if (WR < 16 && c >= WR * 32) continue;
         u32x4 h;
         ok = bf16x8_to_f16(v[i], h) && ok;
         *reinterpret_cast<u32x4*>(buf + (c >> 5) * kXWin + win_chunk(c & 31)) = h;
@@ -359,7 +364,7 @@ __device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int b
       return;
     }
   }
-  xwin_store<XP>(buf, v);
+  xwin_store<XP, WR>(buf, v);
 }
 
 // Before step s is computed from window buffer `buf` (H): true when the
@@ -368,15 +373,15 @@ __device__ __forceinline__ void xwin_store2(uint16_t* buf, const HWin& hw, int b
 // same buffer, with a barrier (the flag is workgroup-uniform, so every wave
 // takes this branch together), and false.  `xv` is free at this point (the next
 // step's prefetch is issued after).
-template <bool H, int XP, typename RowPtr>
+template <bool H, int XP, int WR = 16, typename RowPtr>
 __device__ __forceinline__ bool xwin_fp16_or_restage(uint16_t* buf, HWin& hw, int bufidx,
                                                      u32x4 (&xv)[XP], int M, int64_t K, int s,
                                                      RowPtr row_ptr) {
   if constexpr (H) {
     if (!hw.on) return false;
     if (__builtin_amdgcn_readfirstlane(hw.flag[bufidx]) != s) return true;
-    xwin_load<XP>(xv, M, K, s, row_ptr);
-    xwin_store<XP>(buf, xv);
+    xwin_load<XP, WR>(xv, M, K, s, row_ptr);
+    xwin_store<XP, WR>(buf, xv);
     __syncthreads();
     hw.on = ++hw.fails < 2;
   }
@@ -384,11 +389,11 @@ __device__ __forceinline__ bool xwin_fp16_or_restage(uint16_t* buf, HWin& hw, in
 }
 
 // One step from window buffer `cur`: fp16 MFMA path or bf16 path.
-template <int MT, int TR>
+template <int MT, int TR, int WR = 16>
 __device__ __forceinline__ void compute_wstep_win(f32x4 (&acc)[TR][MT], const WStep<TR>& b,
                                                   const uint16_t* win, int cur, bool f16,
                                                   const int (&xrow_off)[MT]) {
-  constexpr int wsz = 16 * MT * kXWin;
+  constexpr int wsz = WR * MT * kXWin;
   const uint16_t* xl[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xl[mt] = win + cur * wsz + xrow_off[mt];
@@ -399,13 +404,14 @@ __device__ __forceinline__ void compute_wstep_win(f32x4 (&acc)[TR][MT], const WS
 }
 
 // Accumulate steps [s0, s1) with the activations streamed through the LDS
-// window `win` ([2][16*MT][kXWin]; bf16, or fp16 with `hflag` when H).
+// window `win` ([2][WR*MT][kXWin]; bf16, or fp16 with `hflag` when H).
 // xrow_off[mt] = (16*mt + lane%16) * kXWin + 64 * win_quarter(q) (rows past M hold copies,
-// their results are never stored).  Every thread of the workgroup calls this
-// with the same arguments except the weight pointers.  blockDim.x * XP ==
-// 16*MT*32.
+// their results are never stored); with 8 window rows (WR = 8, MT = 1, M <= 8)
+// lanes 8..15 read row 7 (min(lane%16, 7)).  Every thread of the workgroup
+// calls this with the same arguments except the weight pointers.  blockDim.x *
+// XP >= WR*MT*32 (equal when WR = 16).
 template <int MT, int TR, int XP, bool FQ = false, bool H = false, bool TL = false,
-          typename RowPtr>
+          int WR = 16, typename RowPtr>
 __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
                                                     const uint8_t* const (&cptr)[TR],
                                                     const uint8_t* const (&sptr)[TR],
@@ -415,7 +421,7 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
                                                     RowPtr row_ptr) {
   if (s0 >= s1) return;
   const bool sdw = (K % 64) == 0;  // scale rows 4-byte aligned
-  constexpr int wsz = 16 * MT * kXWin;
+  constexpr int wsz = WR * MT * kXWin;
   const int e = s1 < steps_full ? s1 : steps_full;  // end of the full steps
   int s = s0, cur = 0;
   // The first step's weights are requested before the activations are staged,
@@ -423,22 +429,23 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
   WStep<TR> b0, b1;
   if (s < e) load_wstep_full<TR, TL>(b0, cptr, sptr, K, sdw, s);
   u32x4 xv[XP];
-  xwin_load<XP>(xv, M, K, s0, row_ptr);
+  xwin_load<XP, WR>(xv, M, K, s0, row_ptr);
   xwin_fakequant<FQ, XP>(xv);
   HWin hw{hflag, 0, true};
-  xwin_store2<H, XP>(win, hw, 0, xv, s0);
+  xwin_store2<H, XP, WR>(win, hw, 0, xv, s0);
   __syncthreads();
   // One step: prefetch the activations of step s+1 and the weights of step
   // s+1 (unconditional: past the end they re-read a valid step and the data
   // is unused), compute step s, publish the activations of step s+1.
   auto stage = [&](WStep<TR>& bc, WStep<TR>& bn) {
-    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
-    xwin_load<XP>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
+    const bool f16 =
+        xwin_fp16_or_restage<H, XP, WR>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
+    xwin_load<XP, WR>(xv, M, K, min(s + 1, s1 - 1), row_ptr);
     load_wstep_full<TR, TL>(bn, cptr, sptr, K, sdw, min(s + 1, e - 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute_wstep_win<MT, TR>(acc, bc, win, cur, f16, xrow_off);
+    compute_wstep_win<MT, TR, WR>(acc, bc, win, cur, f16, xrow_off);
     xwin_fakequant<FQ, XP>(xv);
-    xwin_store2<H, XP>(win + (cur ^ 1) * wsz, hw, cur ^ 1, xv, s + 1);
+    xwin_store2<H, XP, WR>(win + (cur ^ 1) * wsz, hw, cur ^ 1, xv, s + 1);
     __syncthreads();
     cur ^= 1;
     return ++s >= e;
@@ -452,8 +459,9 @@ __device__ __forceinline__ void gemv_accumulate_win(f32x4 (&acc)[TR][MT],
   if (!TL && s == steps_full && s < s1) {  // partial last step; its activations are in `cur`
     WStep<TR> bt;
     load_wstep<TR, true>(bt, cptr, sptr, K, sdw, steps_full);
-    const bool f16 = xwin_fp16_or_restage<H, XP>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
-    compute_wstep_win<MT, TR>(acc, bt, win, cur, f16, xrow_off);
+    const bool f16 =
+        xwin_fp16_or_restage<H, XP, WR>(win + cur * wsz, hw, cur, xv, M, K, s, row_ptr);
+    compute_wstep_win<MT, TR, WR>(acc, bt, win, cur, f16, xrow_off);
   }
 }
 

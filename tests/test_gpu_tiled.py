@@ -101,14 +101,17 @@ def test_ragged_shapes(nv, orc, M, K, N):
 
 # (M, plan): every built tiled layout -- the 4x4x4 kernel (M <= 8 with
 # gemv_small_max) with 1 or 2 tiles per wave, the 16x16 kernel with 1, 2, 4
-# tiles and 4, 8, 16 waves, K parts across workgroups
+# tiles and 4, 8, 16 waves (8-row activation window for M <= 8), K parts
+# across workgroups
 LAYOUTS = [
     (1, dict(gemv_tiles=1, gemv_waves=4)), (1, dict(gemv_tiles=2, gemv_waves=8)),
     (3, dict(gemv_tiles=1, gemv_waves=2, gemv_splits=3)), (4, dict(gemv_tiles=2, gemv_waves=4)),
     (7, dict(gemv_small_max=8, gemv_tiles=1, gemv_waves=4)),
     (1, dict(gemv_small_max=0, gemv_tiles=2, gemv_waves=8)),
     (8, dict(gemv_tiles=1, gemv_waves=4)), (8, dict(gemv_tiles=2, gemv_waves=8, gemv_splits=5)),
-    (11, dict(gemv_tiles=4, gemv_waves=4)), (16, dict(gemv_tiles=2, gemv_waves=4, gemv_splits=1)),
+    (11, dict(gemv_tiles=4, gemv_waves=4)), (6, dict(gemv_tiles=4, gemv_waves=4)),
+    (7, dict(gemv_tiles=1, gemv_waves=8, gemv_splits=2)),
+    (16, dict(gemv_tiles=2, gemv_waves=4, gemv_splits=1)),
     (20, dict(gemv_tiles=1, gemv_waves=16)), (32, dict(gemv_tiles=2, gemv_waves=16)),
     (32, dict(gemv_tiles=2, gemv_waves=8)), (25, dict(gemv_tiles=1, gemv_waves=4, gemv_splits=7)),
     (2, dict(gemv_tiles=1, gemv_waves=8, gemv_lds_kib=8)),
